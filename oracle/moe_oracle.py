@@ -1,0 +1,319 @@
+"""Plain CPU oracle for the sparse mixture-of-experts layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, constants or
+helpers with the HIP library; it takes plain NumPy arrays (already decoded to
+float32/float64 by the caller) and computes everything in float64 except the
+two places where floating point decides an integer (the routing keys), which it
+takes in float32 exactly as the pages' method would on fp32 logits.
+
+What it computes, and where the pages define it:
+
+* O1 router scores ``r = x W_r`` -- one linear layer, no bias, one score per
+  expert.  "Mixture of experts and speculative decoding", section "Opening the
+  hood: the MoE layer precisely" (equation for r) and step 1 of "Following one
+  token through an MoE layer"; "MoE inference: the call centre with 256
+  specialists ...", section "The bare mechanism" (Router).
+* O2 selection keys: the logits plus an optional per-expert bias that only
+  influences which experts are picked ("The bare mechanism", auxiliary-loss-free
+  routing variant).
+* O3 top-k: the k highest keys; ties go to the lower expert index; slot 0 holds
+  the highest key ("Opening the hood", TopK; step 2 of "Following one token").
+* O4 gates: softmax over the k kept *unbiased* logits, so they sum to one
+  ("Opening the hood", g(x) = softmax(r_TopK); "The bare mechanism", Top-k
+  selection).
+* O5 experts: SwiGLU feed-forward networks, down( SiLU(gate(x)) * up(x) )
+  ("The bare mechanism", the dense FFN it replaces), evaluated only on the
+  tokens routed to each expert ("A toy MoE layer in PyTorch": an expert no
+  token picked never runs).
+* O6 combine: y = sum over the kept experts of g_i(x) E_i(x), plus every
+  always-on shared expert with weight one ("Opening the hood", equation for y;
+  "The bare mechanism", Weighted combination and Shared experts).
+* O7 balance statistics: f_i = share of routed (token, slot) assignments that
+  went to expert i, P_i = mean over tokens of the router's softmax probability
+  for i, loss = alpha * N * sum_i f_i P_i ("Keeping the experts busy", balance
+  loss equation; "Mixture of Experts and Guided Decoding", routing-collapse
+  passage and its auxiliary-loss equation and worked example).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+ties in top-k go to the lower index under IEEE comparison (+0 == -0); f_i
+divides by T*k so that sum f = 1 for any k; P_i uses the full N-way softmax of
+the unbiased logits; shared experts have gate 1 and count in neither k, f nor
+P; no biases inside experts or router.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+(worked examples of the pages, closed forms, brute force, library special
+cases).  SwiGLU numerics at the real layer shapes have no printed values on the
+pages; they are pinned only through the N = 1, k = 1 reduction to a library
+SwiGLU and the dense cross-path.
+"""
+
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+__all__ = [
+    "router_logits",
+    "selection_keys",
+    "topk_by_rank",
+    "kept_softmax",
+    "full_softmax",
+    "silu",
+    "swiglu_expert",
+    "route_from_logits",
+    "combine",
+    "stats",
+    "balance",
+    "moe_forward",
+    "BALANCE_ALPHA",
+]
+
+# Switch Transformer's coefficient, quoted on "Mixture of Experts and Guided
+# Decoding" (auxiliary-loss passage).
+BALANCE_ALPHA = 0.01
+
+ExpertSource = Union[
+    Tuple[np.ndarray, np.ndarray, np.ndarray],
+    Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]],
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------- O1
+def router_logits(x, w_router, logit_bias=None) -> np.ndarray:
+    """O1: r[t, e] = sum_j x[t, j] * W_r[e, j] (+ logit_bias[e]), rounded to fp32.
+
+    W_r is stored one row per expert (the linear layer's [out, in] layout).
+    The sum is formed in float64, then rounded once to float32 (the precision
+    the routing decision is taken in).  The optional ``logit_bias`` is a
+    per-expert offset that is part of the logits themselves (it moves
+    selection, gates and P alike).
+    """
+    x64 = _f64(x)
+    w64 = _f64(w_router)
+    r = x64 @ w64.T
+    if logit_bias is not None:
+        r = r + _f64(logit_bias)[None, :]
+    return r.astype(np.float32)
+
+
+# --------------------------------------------------------------------------- O2
+def selection_keys(r32, select_bias=None) -> np.ndarray:
+    """O2: key = fp32(r + b) with one round-to-nearest-even float32 addition.
+
+    Without a selection bias the key is the logit itself.  The bias steers only
+    which experts are chosen ("The bare mechanism", auxiliary-loss-free
+    routing); gates and P keep using the unbiased logits.
+    """
+    r32 = np.asarray(r32, dtype=np.float32)
+    if select_bias is None:
+        return r32.copy()
+    b32 = np.asarray(select_bias, dtype=np.float32)
+    return (r32 + b32[None, :]).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- O3
+def topk_by_rank(keys, k: int, chunk: int = 256) -> np.ndarray:
+    """O3: the k experts with the highest keys, ties to the lower index.
+
+    Definition used: the rank of expert e for token t is the number of experts
+    that beat it, where e' beats e when key[e'] > key[e], or the keys compare
+    equal (IEEE, so +0 == -0) and e' < e.  Expert e is kept when its rank is
+    below k, and it lands in slot rank(e).  Slot 0 therefore holds the highest
+    key.  Returns int32 [T, k].
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    T, N = keys.shape
+    if not 1 <= k <= N:
+        raise ValueError("need 1 <= k <= n_experts")
+    out = np.empty((T, k), dtype=np.int32)
+    lower = np.tri(N, N, -1, dtype=bool)  # lower[e, e2] is True when e2 < e
+    step = max(1, min(chunk, (1 << 24) // max(1, N * N)))
+    for t0 in range(0, T, step):
+        kk = keys[t0:t0 + step]
+        mine = kk[:, :, None]     # key[e]
+        other = kk[:, None, :]    # key[e']
+        beats = (other > mine) | ((other == mine) & lower[None, :, :])
+        rank = beats.sum(axis=2)  # [t, e]
+        for t in range(kk.shape[0]):
+            sel = np.nonzero(rank[t] < k)[0]
+            out[t0 + t, rank[t, sel]] = sel
+    return out
+
+
+# --------------------------------------------------------------------------- O4
+def kept_softmax(r32, idx) -> np.ndarray:
+    """O4: g[t, j] = exp(r[t, idx[t, j]]) / sum_l exp(r[t, idx[t, l]]) in float64.
+
+    The unbiased logits of the kept experts only; the largest kept logit is
+    subtracted first (it cancels in the ratio).
+    """
+    r = _f64(r32)
+    idx = np.asarray(idx)
+    kept = np.take_along_axis(r, idx.astype(np.int64), axis=1)
+    if kept.shape[0] == 0:
+        return kept
+    z = np.exp(kept - kept.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def full_softmax(r32) -> np.ndarray:
+    """Softmax over all N experts per token (float64): the router's probabilities."""
+    r = _f64(r32)
+    if r.shape[0] == 0:
+        return r
+    z = np.exp(r - r.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------- O5
+def silu(a) -> np.ndarray:
+    """SiLU (swish with beta = 1): a * sigmoid(a) = a / (1 + e^-a)."""
+    a = _f64(a)
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu_expert(X, w_gate, w_up, w_down) -> np.ndarray:
+    """O5: one SwiGLU expert on a block of rows.
+
+    a = X W_gate^T, b = X W_up^T (both [rows, F]); h = SiLU(a) * b;
+    out = h W_down^T ([rows, d]).  W_gate and W_up are [F, d] and W_down is
+    [d, F], each in the linear layer's [out, in] layout.
+    """
+    X = _f64(X)
+    a = X @ _f64(w_gate).T
+    b = X @ _f64(w_up).T
+    h = silu(a) * b
+    return h @ _f64(w_down).T
+
+
+# ------------------------------------------------------------------ O2+O3+O4
+def route_from_logits(r32, k: int, select_bias=None):
+    """Selection and gates from given fp32 logits: returns (idx int32 [T,k], g f64 [T,k])."""
+    keys = selection_keys(r32, select_bias)
+    idx = topk_by_rank(keys, k)
+    return idx, kept_softmax(r32, idx)
+
+
+# --------------------------------------------------------------------------- O6
+def combine(gates, expert_outputs) -> np.ndarray:
+    """O6 for one token: sum_j gates[j] * expert_outputs[j] (float64).
+
+    ``gates`` has shape [k] and ``expert_outputs`` [k, dim].
+    """
+    g = _f64(gates)
+    E = _f64(expert_outputs)
+    out = np.zeros(E.shape[1:], dtype=np.float64)
+    for j in range(g.shape[0]):
+        out += g[j] * E[j]
+    return out
+
+
+# --------------------------------------------------------------------------- O7
+def stats(idx, r32, n_experts: int):
+    """O7 counts, f and P.
+
+    counts[e] = number of (token, slot) assignments to expert e;
+    f[e] = counts[e] / (T * k); P[e] = mean over tokens of the full softmax of
+    the (unbiased) logits.  With T = 0 every value is 0.
+    """
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    k = idx.shape[1] if idx.ndim == 2 else 0
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in idx.reshape(-1):
+        counts[int(e)] += 1
+    if T == 0:
+        return counts, np.zeros(n_experts), np.zeros(n_experts)
+    f = counts.astype(np.float64) / float(T * k)
+    P = full_softmax(r32).mean(axis=0)
+    return counts, f, P
+
+
+def balance(f, P, alpha: float = BALANCE_ALPHA):
+    """Balance loss: returns (N * sum_i f_i P_i, alpha * that)."""
+    f = _f64(f)
+    P = _f64(P)
+    raw = float(f.shape[0]) * float(np.sum(f * P))
+    return raw, alpha * raw
+
+
+# ------------------------------------------------------------------ O1..O7
+def _expert_getter(experts: ExpertSource):
+    if callable(experts):
+        return experts
+    wg, wu, wd = experts
+    return lambda e: (wg[e], wu[e], wd[e])
+
+
+def moe_forward(
+    x,
+    w_router,
+    experts: ExpertSource,
+    k: int,
+    *,
+    logit_bias=None,
+    select_bias=None,
+    shared: Optional[Sequence[np.ndarray]] = None,
+    route_logits=None,
+    alpha: float = BALANCE_ALPHA,
+    n_experts: Optional[int] = None,
+):
+    """The whole layer forward, O1..O7, with the experts looped one at a time.
+
+    ``experts`` is either a tuple (W_gate [N,F,d], W_up [N,F,d], W_down [N,d,F])
+    or a callable e -> (W_gate[e], W_up[e], W_down[e]) so that large layers can
+    hand over one expert's weights at a time.  ``shared`` is an optional tuple
+    of [S,F,d], [S,F,d], [S,d,F] arrays for always-on experts.
+
+    ``route_logits`` (fp32 [T, N]) replaces O1 when given: the routing is then
+    taken on those logits, which is how a caller checks another implementation's
+    routing bit for bit on its own logits.
+
+    Returns a dict with y (float64 [T, d]), logits, idx, gates, counts, f, P,
+    aux_raw and aux.
+    """
+    x64 = _f64(x)
+    T, d = x64.shape
+    if route_logits is None:
+        r32 = router_logits(x64, w_router, logit_bias)
+    else:
+        r32 = np.asarray(route_logits, dtype=np.float32)
+    N = r32.shape[1] if n_experts is None else n_experts
+    idx, g = route_from_logits(r32, k, select_bias) if T else (
+        np.zeros((0, k), np.int32), np.zeros((0, k)))
+    get = _expert_getter(experts)
+
+    y = np.zeros((T, d), dtype=np.float64)
+    for e in range(N):
+        tok, slot = np.nonzero(idx == e)
+        if tok.size == 0:
+            continue  # an expert that no token picked does no work
+        wg, wu, wd = get(e)
+        E = swiglu_expert(x64[tok], wg, wu, wd)
+        y[tok] += g[tok, slot][:, None] * E
+    if shared is not None:
+        sg, su, sd = shared
+        for s in range(np.asarray(sg).shape[0]):
+            y += swiglu_expert(x64, sg[s], su[s], sd[s])
+
+    counts, f, P = stats(idx, r32, N)
+    aux_raw, aux = balance(f, P, alpha)
+    return {
+        "y": y,
+        "logits": r32,
+        "idx": idx,
+        "gates": g,
+        "counts": counts,
+        "f": f,
+        "P": P,
+        "aux_raw": aux_raw,
+        "aux": aux,
+    }
+

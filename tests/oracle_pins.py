@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes the oracle module ``O`` and raises when the
+oracle disagrees with: a value printed on the pages (fixtures in
+``tests/golden/worked_examples.json``, each carrying its citation), a closed
+form, an exhaustive search on tiny inputs, or a library routine that the layer
+reduces to in a special case (PyTorch / SciPy, float64, CPU).
+
+The functions are shared by ``test_oracle_pins.py`` (the real oracle must pass
+every pin) and ``test_oracle_mutations.py`` (oracles with a planted mistake
+must fail at least one pin).
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import scipy.special
+import torch
+import torch.nn.functional as Fnn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+def _close(a, b, atol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape or not np.all(np.abs(a - b) <= atol):
+        raise AssertionError(f"{what}: got {a.tolist()} expected {b.tolist()} (atol {atol})")
+
+
+def _half_ulp(dec):
+    return 0.5 * 10.0 ** (-dec) + 1e-12
+
+
+# ----------------------------------------------------------- printed examples
+def pin_e1_top2(O):
+    ex = golden()["E1_top2_single_token"]
+    r = np.array([ex["logits"]], dtype=np.float32)
+    idx, g = O.route_from_logits(r, ex["k"])
+    want = [e - 1 for e in ex["kept_experts_1based"]]
+    if idx[0].tolist() != want:
+        raise AssertionError(f"E1 experts {idx[0].tolist()} != {want}")
+    _close(g[0], ex["gates"], _half_ulp(ex["decimals"]), "E1 gates")
+    p = O.full_softmax(r)[0]
+    _close(p[want], ex["softmax_all_for_kept"], _half_ulp(ex["decimals"]), "E1 softmax-all")
+    _close(p[want] / p[want].sum(), g[0], 1e-12, "E1 renormalised softmax-all")
+
+
+def pin_e2_blend(O):
+    ex = golden()["E2_blend"]
+    y = O.combine(ex["gates"], ex["expert_outputs"])
+    _close(y, ex["y"], _half_ulp(ex["decimals"]), "E2 blend (page gates)")
+    # the same blend with the exact E1 gates still rounds to the printed row
+    e1 = golden()["E1_top2_single_token"]
+    _, g = O.route_from_logits(np.array([e1["logits"]], np.float32), e1["k"])
+    _close(O.combine(g[0], ex["expert_outputs"]), ex["y"], _half_ulp(ex["decimals"]),
+           "E2 blend (exact gates)")
+
+
+def pin_e3_top2(O):
+    ex = golden()["E3_top2_guided_page"]
+    r = np.array([ex["logits"]], dtype=np.float32)
+    idx, g = O.route_from_logits(r, ex["k"])
+    want = [e - 1 for e in ex["kept_experts_1based"]]
+    if idx[0].tolist() != want:
+        raise AssertionError(f"E3 experts {idx[0].tolist()} != {want}")
+    _close(g[0], ex["gates"], _half_ulp(ex["decimals"]), "E3 gates")
+    dense = np.zeros(4)
+    dense[idx[0]] = g[0]
+    _close(dense, ex["final_weights"], _half_ulp(ex["decimals"]), "E3 final weights")
+
+
+def pin_e4_dense(O):
+    ex = golden()["E4_dense_gate"]
+    y = O.combine(ex["G"], np.array(ex["E"])[:, None])
+    _close(y, [ex["y"]], 1e-12, "E4 dense gate")
+    ex = golden()["E4b_dense_softmax"]
+    p = O.full_softmax(np.array([ex["logits"]], np.float32))[0]
+    _close(p, ex["softmax_printed"], ex["tolerance"], "E4b dense softmax")
+    # dense MoE is the k = N special case: gates are the full softmax
+    idx, g = O.route_from_logits(np.array([ex["logits"]], np.float32), 4)
+    _close(g[0], p[idx[0]], 1e-12, "k = N gates vs full softmax")
+
+
+def pin_e5_balance(O):
+    ex = golden()["E5_balance_loss"]
+    for case in ("balanced", "collapsed"):
+        c = ex[case]
+        raw, aux = O.balance(c["f"], c["P"], ex["alpha_switch"])
+        _close(raw, c["loss_over_alpha"], 1e-12, f"E5 {case} loss/alpha")
+        _close(aux, ex["alpha_switch"] * c["loss_over_alpha"], 1e-14, f"E5 {case} loss")
+
+
+def pin_e6_toy_routing(O):
+    """Replays the toy layer's random draws with torch's CPU generator.
+
+    Construction order of the toy: eight experts, each a Linear(d, h) then a
+    Linear(h, d), then the bias-free router Linear(d, N); then the token batch.
+    Only the router weights and the tokens matter for the routing; the expert
+    layers are drawn to advance the generator exactly as the toy does.
+    """
+    ex = golden()["E6_toy_layer"]
+    d, h, N, k, T = ex["d_model"], ex["d_hidden"], ex["n_experts"], ex["top_k"], ex["tokens"]
+    torch.manual_seed(ex["torch_seed"])
+    experts = [(torch.nn.Linear(d, h), torch.nn.Linear(h, d)) for _ in range(N)]
+    router = torch.nn.Linear(d, N, bias=False)
+    x = torch.randn(T, d)
+    total = sum(p.numel() for a, b in experts for p in list(a.parameters()) + list(b.parameters()))
+    total += router.weight.numel()
+    active = k * sum(p.numel() for p in list(experts[0][0].parameters()) +
+                     list(experts[0][1].parameters())) + router.weight.numel()
+    if (total, active) != (ex["total_params"], ex["active_params"]):
+        raise AssertionError(f"toy parameter counts {(total, active)}")
+    r32 = O.router_logits(x.numpy(), router.weight.detach().numpy())
+    idx = O.topk_by_rank(O.selection_keys(r32), k)
+    hist = np.bincount(idx.reshape(-1), minlength=N).tolist()
+    if hist != ex["tokens_per_expert"]:
+        raise AssertionError(f"toy tokens per expert {hist} != {ex['tokens_per_expert']}")
+
+
+# ---------------------------------------------------------- exhaustive search
+def _brute_topk(keys_row, k):
+    """Top-k of one row by trying every k-subset (higher key wins, ties to lower index)."""
+    keys_row = np.asarray(keys_row, dtype=np.float32)
+    N = keys_row.shape[0]
+
+    def beats(a, b):
+        return keys_row[a] > keys_row[b] or (keys_row[a] == keys_row[b] and a < b)
+
+    hits = [S for S in itertools.combinations(range(N), k)
+            if all(beats(a, b) for a in S for b in range(N) if b not in S)]
+    assert len(hits) == 1
+    members, ordered = list(hits[0]), []
+    while members:
+        best = members[0]
+        for m in members[1:]:
+            if beats(m, best):
+                best = m
+        ordered.append(best)
+        members.remove(best)
+    return ordered
+
+
+def pin_topk_brute_force(O):
+    rng = np.random.default_rng(1234)
+    for trial in range(300):
+        N = int(rng.integers(1, 9))
+        k = int(rng.integers(1, N + 1))
+        mode = trial % 3
+        if mode == 0:
+            keys = rng.standard_normal(N).astype(np.float32)
+        elif mode == 1:   # many exact ties
+            keys = rng.integers(-2, 3, N).astype(np.float32)
+        else:             # signed zeros compare equal
+            keys = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), N)
+        got = O.topk_by_rank(keys[None, :], k)[0].tolist()
+        want = _brute_topk(keys, k)
+        if got != want:
+            raise AssertionError(f"top-k {keys.tolist()} k={k}: {got} != {want}")
+
+
+def pin_select_bias_semantics(O):
+    # the bias moves the choice, the gates come from the unbiased logits
+    r = np.array([[1.0, 0.9, 0.0]], np.float32)
+    idx, g = O.route_from_logits(r, 2, select_bias=np.array([0.0, 0.0, 2.0], np.float32))
+    if idx[0].tolist() != [2, 0]:
+        raise AssertionError(f"biased selection {idx[0].tolist()}")
+    _close(g[0], scipy.special.softmax([0.0, 1.0]), 1e-12, "gates use unbiased logits")
+    # the key is one fp32 addition: 1 + 2^-25 rounds to 1, so the tie goes to expert 0
+    r = np.array([[1.0, 1.0]], np.float32)
+    idx, _ = O.route_from_logits(r, 1, select_bias=np.array([0.0, 2.0 ** -25], np.float32))
+    if idx[0].tolist() != [0]:
+        raise AssertionError("selection key is not a single fp32 addition")
+
+
+# ------------------------------------------------------------ library routes
+def _torch_swiglu(x, wg, wu, wd):
+    x, wg, wu, wd = (torch.as_tensor(np.asarray(a, np.float64)) for a in (x, wg, wu, wd))
+    return Fnn.linear(Fnn.silu(Fnn.linear(x, wg)) * Fnn.linear(x, wu), wd).numpy()
+
+
+def _layer(rng, T, d, F, N, S=0):
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d)) * 0.3
+    wg = rng.standard_normal((N, F, d)) * 0.2
+    wu = rng.standard_normal((N, F, d)) * 0.2
+    wd = rng.standard_normal((N, d, F)) * 0.2
+    sh = None
+    if S:
+        sh = (rng.standard_normal((S, F, d)) * 0.2, rng.standard_normal((S, F, d)) * 0.2,
+              rng.standard_normal((S, d, F)) * 0.2)
+    return x, wr, (wg, wu, wd), sh
+
+
+def pin_swiglu_closed_form(O):
+    # one unit: y = w_d * SiLU(w_g x) * (w_u x); SiLU(2) = 2 * sigmoid(2)
+    y = O.swiglu_expert([[1.0]], [[2.0]], [[-1.0]], [[0.5]])
+    _close(y, [[-0.5 * 2.0 * scipy.special.expit(2.0)]], 1e-15, "SwiGLU closed form")
+
+
+def pin_single_expert_is_swiglu(O):
+    rng = np.random.default_rng(7)
+    x, wr, (wg, wu, wd), _ = _layer(rng, 9, 12, 20, 1)
+    out = O.moe_forward(x, wr, (wg, wu, wd), 1)
+    _close(out["gates"], np.ones((9, 1)), 0, "N = 1 gates")
+    _close(out["y"], _torch_swiglu(x, wg[0], wu[0], wd[0]), 1e-12, "N = 1 layer vs SwiGLU")
+
+
+def pin_router_linear(O):
+    x = np.array([[1.0, 2.0]])
+    w = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    _close(O.router_logits(x, w), [[1.0, 2.0, 3.0]], 0, "router hand example")
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((11, 13))
+    w = rng.standard_normal((5, 13))
+    lb = rng.standard_normal(5)
+    ref = Fnn.linear(torch.as_tensor(x), torch.as_tensor(w)).numpy()
+    _close(O.router_logits(x, w), ref.astype(np.float32), 1e-6, "router vs linear")
+    _close(O.router_logits(x, w, lb), (ref + lb).astype(np.float32), 1e-6,
+           "router with logit offset")
+
+
+def pin_dense_crosspath(O):
+    """Dense formulation: every expert on every token, gate zero outside the top-k."""
+    rng = np.random.default_rng(11)
+    T, d, F, N, k = 37, 24, 40, 6, 3
+    x, wr, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    out = O.moe_forward(x, wr, (wg, wu, wd), k)
+    logits = torch.as_tensor(out["logits"].astype(np.float64))
+    top_v, top_i = torch.topk(logits, k, dim=1)
+    G = torch.zeros(T, N, dtype=torch.float64).scatter(1, top_i, torch.softmax(top_v, dim=1))
+    y = np.zeros((T, d))
+    for e in range(N):
+        y += G[:, e].numpy()[:, None] * _torch_swiglu(x, wg[e], wu[e], wd[e])
+    _close(out["y"], y, 1e-12, "per-expert loop vs dense gate")
+    if not np.array_equal(out["idx"], top_i.numpy()):
+        raise AssertionError("idx vs torch.topk")
+
+
+def pin_k_equals_n_is_dense_softmax(O):
+    rng = np.random.default_rng(5)
+    T, d, F, N = 8, 10, 14, 4
+    x, wr, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    out = O.moe_forward(x, wr, (wg, wu, wd), N)
+    p = scipy.special.softmax(out["logits"].astype(np.float64), axis=1)
+    y = sum(p[:, e:e + 1] * _torch_swiglu(x, wg[e], wu[e], wd[e]) for e in range(N))
+    _close(out["y"], y, 1e-12, "k = N layer vs dense softmax MoE")
+
+
+def pin_shared_expert(O):
+    rng = np.random.default_rng(9)
+    x, wr, ex, sh = _layer(rng, 10, 16, 24, 5, S=1)
+    with_s = O.moe_forward(x, wr, ex, 2, shared=sh)
+    without = O.moe_forward(x, wr, ex, 2)
+    _close(with_s["y"] - without["y"], _torch_swiglu(x, sh[0][0], sh[1][0], sh[2][0]), 1e-12,
+           "shared expert adds with gate 1")
+    for key in ("counts", "f", "P"):
+        _close(with_s[key], without[key], 0, f"shared expert leaves {key}")
+
+
+def pin_relabel_and_chunking(O):
+    rng = np.random.default_rng(21)
+    T, d, F, N, k = 30, 16, 24, 7, 3
+    x, wr, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    base = O.moe_forward(x, wr, (wg, wu, wd), k)
+    perm = rng.permutation(N)
+    inv = np.argsort(perm)
+    rel = O.moe_forward(x, wr[perm], (wg[perm], wu[perm], wd[perm]), k)
+    _close(rel["y"], base["y"], 1e-12, "expert relabelling leaves y")
+    if not np.array_equal(perm[rel["idx"]], base["idx"]):
+        raise AssertionError("relabelled idx")
+    tperm = rng.permutation(T)
+    sh = O.moe_forward(x[tperm], wr, (wg, wu, wd), k)
+    _close(sh["y"], base["y"][tperm], 1e-12, "token shuffle commutes")
+    a = O.moe_forward(x[:11], wr, (wg, wu, wd), k)
+    b = O.moe_forward(x[11:], wr, (wg, wu, wd), k)
+    _close(np.concatenate([a["y"], b["y"]]), base["y"], 1e-12, "token chunking")
+
+
+def pin_stats(O):
+    idx = np.array([[0, 1], [0, 2]], np.int32)
+    r = np.array([[0.0, 0.0, 0.0, 0.0], [np.log(2.0), 0.0, 0.0, 0.0]], np.float32)
+    counts, f, P = O.stats(idx, r, 4)
+    _close(counts, [2, 1, 1, 0], 0, "counts")
+    _close(f, [0.5, 0.25, 0.25, 0.0], 0, "f = counts / (T k)")
+    _close(P, [(0.25 + 0.4) / 2, (0.25 + 0.2) / 2, (0.25 + 0.2) / 2, (0.25 + 0.2) / 2],
+           1e-7, "P = mean full softmax")
+
+
+def pin_invariants(O):
+    rng = np.random.default_rng(17)
+    for (T, N, k) in [(40, 8, 2), (25, 5, 1), (16, 16, 16), (33, 12, 5)]:
+        x, wr, ex, _ = _layer(rng, T, 8, 16, N)
+        out = O.moe_forward(x, wr, ex, k)
+        g = out["gates"]
+        _close(g.sum(axis=1), np.ones(T), 1e-12, "gates sum to 1")
+        if not (np.all(g > 0) and np.all(g <= 1)):
+            raise AssertionError("gates outside (0, 1]")
+        if int(out["counts"].sum()) != T * k:
+            raise AssertionError("counts do not add to T k")
+        _close(out["f"].sum(), 1.0, 1e-12, "sum f")
+        _close(out["P"].sum(), 1.0, 1e-12, "sum P")
+        p = scipy.special.softmax(out["logits"].astype(np.float64), axis=1).mean(axis=0)
+        _close(out["P"], p, 1e-12, "P vs scipy softmax")
+        raw, _ = O.balance(np.full(N, 1.0 / N), out["P"])
+        _close(raw, 1.0, 1e-12, "uniform f gives loss/alpha = 1")
+        if k == 1 and np.allclose(out["P"], out["f"]):
+            raise AssertionError("P must come from the full softmax, not the hard choice")
+        srt = out["idx"]
+        keys = out["logits"]
+        kept = np.take_along_axis(keys, srt.astype(np.int64), axis=1)
+        if np.any(np.diff(kept, axis=1) > 0):
+            raise AssertionError("slots not in descending key order")
+
+
+def pin_unused_expert_never_read(O):
+    rng = np.random.default_rng(23)
+    T, d, F, N, k = 12, 8, 16, 6, 2
+    x, wr, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    lb = np.zeros(N)
+    lb[5] = -1.0e4                      # expert 5 can never be among the top k
+    base = O.moe_forward(x, wr, (wg, wu, wd), k, logit_bias=lb)
+    if base["counts"][5] != 0:
+        raise AssertionError("setup: expert 5 was chosen")
+    wg[5] = np.nan
+    wu[5] = np.nan
+    wd[5] = np.nan
+    out = O.moe_forward(x, wr, (wg, wu, wd), k, logit_bias=lb)
+    _close(out["y"], base["y"], 0, "unchosen expert's weights are never read")
+
+
+def pin_empty_batch(O):
+    out = O.moe_forward(np.zeros((0, 8)), np.ones((4, 8)),
+                        (np.ones((4, 16, 8)), np.ones((4, 16, 8)), np.ones((4, 8, 16))), 2)
+    if out["y"].shape != (0, 8) or out["counts"].sum() != 0 or out["aux_raw"] != 0.0:
+        raise AssertionError("T = 0")
+
+
+ALL_PINS = [
+    pin_e1_top2, pin_e2_blend, pin_e3_top2, pin_e4_dense, pin_e5_balance, pin_e6_toy_routing,
+    pin_topk_brute_force, pin_select_bias_semantics, pin_swiglu_closed_form,
+    pin_single_expert_is_swiglu, pin_router_linear, pin_dense_crosspath,
+    pin_k_equals_n_is_dense_softmax, pin_shared_expert, pin_relabel_and_chunking, pin_stats,
+    pin_invariants, pin_unused_expert_never_read, pin_empty_batch,
+]
