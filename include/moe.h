@@ -1,0 +1,165 @@
+/*
+ * moe.h -- C ABI of libmoe.so, a sparse mixture-of-experts layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (defined on "Mixture of experts and speculative decoding", section
+ * "Opening the hood: the MoE layer precisely", and on "MoE inference: the call
+ * centre with 256 specialists ...", section "The bare mechanism"):
+ *
+ *   r      = x W_r^T (+ logit_bias)                 router scores, fp32
+ *   key    = r + select_bias                        selection key (one fp32 add)
+ *   TopK   = the k largest keys, ties to the lower expert index,
+ *            slot 0 = largest key
+ *   g      = softmax over the k kept r (unbiased)   gates, sum to 1
+ *   E_e(x) = W_down[e] ( SiLU(W_gate[e] x) * (W_up[e] x) )   SwiGLU expert
+ *   y      = sum_{slot} g_slot E_{TopK_slot}(x) + sum_s E_shared_s(x)
+ *
+ * plus the load-balance statistics of "Keeping the experts busy" (same page)
+ * and of the routing-collapse passage of "Mixture of Experts and Guided
+ * Decoding": f_e = count_e / (T k), P_e = mean_t softmax(r_t)_e,
+ * loss = alpha * N * sum_e f_e P_e.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to a dense row-major array owned
+ *    by the caller.  The library never allocates, frees, or synchronises the
+ *    device; all work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and completes asynchronously.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched and the status says why.  A HIP launch failure
+ *    returns MOE_ERR_HIP.
+ *  - Weights use the linear layer's [out, in] layout: W_r [N, d],
+ *    W_gate/W_up [N, F, d], W_down [N, d, F]; shared experts [S, F, d] and
+ *    [S, d, F].  x and y are [T, d].  The element type of x, y and every weight
+ *    is cfg->dtype; biases, logits, gates and statistics are fp32.
+ *  - Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32
+ *    accumulation; the expert hidden activations and per-expert outputs are
+ *    held in the input dtype (bf16 rounding to nearest even); y is rounded once.
+ *  - Results are deterministic: the same inputs give bitwise the same outputs.
+ *  - Calls are thread-safe; concurrent calls must use distinct workspaces.
+ *  - Supported sizes: 1 <= k <= min(N, 16), N <= 512, 0 <= S <= 4,
+ *    d and F positive multiples of 64, T >= 0 (T = 0 launches nothing and
+ *    returns MOE_OK).  Other sizes return MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, k > N, negative size ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside the supported sizes above */
+  MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_size */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer sizes.  T tokens, d_model, N routed experts, top_k kept per token,
+ * d_ff hidden size of every expert (routed and shared), n_shared always-on
+ * experts, dtype a moe_dtype. */
+typedef struct {
+  int32_t T;
+  int32_t d_model;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t d_ff;
+  int32_t n_shared;
+  int32_t dtype;
+} moe_config;
+
+/* Layer parameters (device pointers, caller-owned, read-only). */
+typedef struct {
+  const void* w_router;     /* [N, d]                                         */
+  const void* w_gate;       /* [N, F, d]   (unused by moe_route)              */
+  const void* w_up;         /* [N, F, d]   (unused by moe_route)              */
+  const void* w_down;       /* [N, d, F]   (unused by moe_route)              */
+  const void* ws_gate;      /* [S, F, d] or NULL when S = 0                   */
+  const void* ws_up;        /* [S, F, d] or NULL when S = 0                   */
+  const void* ws_down;      /* [S, d, F] or NULL when S = 0                   */
+  const float* logit_bias;  /* [N] added to the logits (moves selection,
+                               gates and P), or NULL                          */
+  const float* select_bias; /* [N] added to the selection key only (the
+                               auxiliary-loss-free routing bias of "The bare
+                               mechanism"), or NULL                           */
+} moe_weights;
+
+/* Routing outputs (device pointers, caller-owned, written by the call).  For
+ * moe_layer_forward every field is optional (NULL = not wanted); moe_route
+ * requires topk_idx and topk_gate. */
+typedef struct {
+  float* logits;      /* [T, N]  r including logit_bias                       */
+  int32_t* topk_idx;  /* [T, k]  chosen experts, slot 0 = largest key          */
+  float* topk_gate;   /* [T, k]  softmax over the kept unbiased logits        */
+  int32_t* counts;    /* [N]     (token, slot) assignments per routed expert  */
+  float* prob_sum;    /* [N]     sum over tokens of softmax(r_t) over all N   */
+} moe_routing;
+
+/* Stage markers for moe_layer_forward_timed. */
+enum {
+  MOE_STAGE_ROUTE = 0,      /* router GEMM + top-k + gates + block statistics */
+  MOE_STAGE_PERMUTE = 1,    /* per-expert offsets, tile lists, token grouping  */
+  MOE_STAGE_EXPERT_UP = 2,  /* grouped gate/up GEMM with SiLU(gate)*up         */
+  MOE_STAGE_EXPERT_DOWN = 3,/* grouped down GEMM                               */
+  MOE_STAGE_COMBINE = 4,    /* gate-weighted combine into y                    */
+  MOE_STAGE_COUNT = 5
+};
+
+/* Bytes of device workspace moe_layer_forward / moe_route need for `cfg`
+ * (a multiple of 256).  Returns 0 for an invalid or unsupported cfg. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* Detail of the last MOE_ERR_* returned on the calling thread (static text
+ * or a thread-local buffer; never NULL, "" when none). */
+const char* moe_last_error(void);
+
+/* Routing only (steps r, key, TopK, g and the statistics' raw sums):
+ * x [T, d]; w->w_router, optional w->logit_bias / w->select_bias; writes
+ * out->topk_idx and out->topk_gate (required) and out->logits, out->counts,
+ * out->prob_sum when non-NULL.  `workspace` must hold moe_workspace_size(cfg)
+ * bytes, 256-byte aligned; its contents are scratch. */
+moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
+                     moe_routing* out, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Whole layer forward: routing as moe_route, then the SwiGLU experts on the
+ * tokens routed to them (experts no token chose are never read), the shared
+ * experts on every token, and the combine y [T, d] (required).  Optional
+ * routing outputs as described at moe_routing. */
+moe_status moe_layer_forward(const moe_config* cfg, const void* x,
+                             const moe_weights* w, void* y, moe_routing* out,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward that also records stage_events[i] (hipEvent_t, created by
+ * the caller) on `stream` before stage i and stage_events[MOE_STAGE_COUNT]
+ * after the last one, so the caller can time each stage.  stage_events may be
+ * NULL (then identical to moe_layer_forward). */
+moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x,
+                                   const moe_weights* w, void* y,
+                                   moe_routing* out, void* workspace,
+                                   size_t ws_bytes, void* stream,
+                                   void* const* stage_events);
+
+/* Balance statistics from the routing sums of T tokens, N experts, top-k:
+ * f_out[e] = counts[e] / (T k), P_out[e] = prob_sum[e] / T,
+ * aux_out[0] = N * sum_e f_e P_e, aux_out[1] = alpha * aux_out[0]
+ * (all fp32 device arrays; T = 0 writes zeros).  Enqueued on `stream`. */
+moe_status moe_balance_stats(int32_t T, int32_t N, int32_t k,
+                             const int32_t* counts, const float* prob_sum,
+                             float alpha, float* f_out, float* P_out,
+                             float* aux_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,255 @@
+"""Sparse mixture-of-experts layer forward on AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libmoe.so``: every function below only marshals
+PyTorch tensors (device memory) and the current HIP stream into the C ABI
+declared in ``include/moe.h``; every step of the layer runs in the library's
+HIP kernels.  There is no CPU fallback: if the library is not built, calls
+raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+    "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "STAGES", "MoEError", "MoEConfig", "MoEWeights",
+    "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
+    "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+STAGES = ("route", "permute", "expert_up", "expert_down", "combine")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        msg = moe_status_string(status)
+        super().__init__(f"{msg} ({detail})" if detail else msg)
+
+
+class MoEConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MoEWeights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p),
+                ("ws_down", ctypes.c_void_p), ("logit_bias", ctypes.c_void_p),
+                ("select_bias", ctypes.c_void_p)]
+
+
+class MoERouting(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
+                ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("prob_sum", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m sparse_mixture_experts_router_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        cfgp, wp, rp = (ctypes.POINTER(MoEConfig), ctypes.POINTER(MoEWeights),
+                        ctypes.POINTER(MoERouting))
+        L.moe_workspace_size.argtypes = [cfgp]
+        L.moe_workspace_size.restype = sz
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_route.argtypes = [cfgp, vp, wp, rp, vp, sz, vp]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, rp, vp, sz, vp]
+        L.moe_layer_forward.restype = ctypes.c_int
+        L.moe_layer_forward_timed.argtypes = [cfgp, vp, wp, vp, rp, vp, sz, vp,
+                                              ctypes.POINTER(vp)]
+        L.moe_layer_forward_timed.restype = ctypes.c_int
+        L.moe_balance_stats.argtypes = [i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+        L.moe_balance_stats.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoEError(status, lib().moe_last_error().decode())
+
+
+_TORCH_DTYPE = {MOE_BF16: torch.bfloat16, MOE_F32: torch.float32}
+
+
+def make_config(T: int, d_model: int, n_experts: int, top_k: int, d_ff: int,
+                n_shared: int = 0, dtype=torch.bfloat16) -> MoEConfig:
+    code = MOE_BF16 if dtype in (torch.bfloat16, "bf16", MOE_BF16) else MOE_F32
+    return MoEConfig(int(T), int(d_model), int(n_experts), int(top_k), int(d_ff),
+                     int(n_shared), code)
+
+
+def moe_workspace_size(cfg: MoEConfig) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(cfg)))
+
+
+def alloc_workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
+    n = moe_workspace_size(cfg)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "configuration rejected")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _weights(cfg: MoEConfig, w: Dict[str, Optional[torch.Tensor]], experts=True) -> MoEWeights:
+    dt = _TORCH_DTYPE[cfg.dtype]
+    names = ["w_router"] + (["w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"]
+                            if experts else [])
+    args = {n: _ptr(w.get(n), dt, n) for n in names}
+    args["logit_bias"] = _ptr(w.get("logit_bias"), torch.float32, "logit_bias")
+    args["select_bias"] = _ptr(w.get("select_bias"), torch.float32, "select_bias")
+    return MoEWeights(**args)
+
+
+def _routing(logits=None, topk_idx=None, topk_gate=None, counts=None, prob_sum=None):
+    return MoERouting(_ptr(logits, torch.float32, "logits"),
+                      _ptr(topk_idx, torch.int32, "topk_idx"),
+                      _ptr(topk_gate, torch.float32, "topk_gate"),
+                      _ptr(counts, torch.int32, "counts"),
+                      _ptr(prob_sum, torch.float32, "prob_sum"))
+
+
+def moe_route(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]], *,
+              topk_idx: torch.Tensor, topk_gate: torch.Tensor, workspace: torch.Tensor,
+              logits=None, counts=None, prob_sum=None, stream=None) -> None:
+    """Routing only; see ``moe_route`` in include/moe.h."""
+    w = _weights(cfg, weights, experts=False)
+    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum)
+    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x, _TORCH_DTYPE[cfg.dtype], "x"),
+                           ctypes.byref(w), ctypes.byref(r), _ptr(workspace, None, "workspace"),
+                           workspace.numel(), _stream(stream)))
+
+
+def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]],
+                      y: torch.Tensor, *, workspace: torch.Tensor, logits=None, topk_idx=None,
+                      topk_gate=None, counts=None, prob_sum=None, stream=None,
+                      stage_events: Optional[Sequence[torch.cuda.Event]] = None) -> None:
+    """Whole layer forward into ``y``; see ``moe_layer_forward`` in include/moe.h.
+
+    ``stage_events``: optional list of len(STAGES) + 1 ``torch.cuda.Event``
+    (enable_timing=True) recorded before each stage and after the last.
+    """
+    dt = _TORCH_DTYPE[cfg.dtype]
+    w = _weights(cfg, weights)
+    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum)
+    args = (ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(y, dt, "y"),
+            ctypes.byref(r), _ptr(workspace, None, "workspace"), workspace.numel(),
+            _stream(stream))
+    if stage_events is None:
+        _check(lib().moe_layer_forward(*args))
+        return
+    if len(stage_events) != len(STAGES) + 1:
+        raise ValueError("need one event per stage plus one")
+    s = torch.cuda.current_stream() if stream is None else stream
+    for ev in stage_events:      # torch creates the HIP event on first record
+        if not ev.cuda_event:
+            ev.record(s)
+    arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+    _check(lib().moe_layer_forward_timed(*args, arr))
+
+
+def moe_balance_stats(T: int, N: int, k: int, counts: torch.Tensor, prob_sum: torch.Tensor,
+                      alpha: float, f: torch.Tensor, P: torch.Tensor, aux: torch.Tensor,
+                      stream=None) -> None:
+    """f = counts / (T k), P = prob_sum / T, aux = [N sum f P, alpha N sum f P]."""
+    _check(lib().moe_balance_stats(
+        int(T), int(N), int(k), _ptr(counts, torch.int32, "counts"),
+        _ptr(prob_sum, torch.float32, "prob_sum"), float(alpha), _ptr(f, torch.float32, "f"),
+        _ptr(P, torch.float32, "P"), _ptr(aux, torch.float32, "aux"), _stream(stream)))
+
+
+class MoELayer:
+    """Convenience holder: config, device weights and a workspace sized once.
+
+    ``forward(x)`` allocates the outputs with torch (device memory only) and
+    calls ``moe_layer_forward`` followed by ``moe_balance_stats``.
+    """
+
+    def __init__(self, weights: Dict[str, Optional[torch.Tensor]], top_k: int,
+                 alpha: float = 0.01):
+        wg = weights["w_gate"]
+        self.weights = weights
+        self.N, self.F, self.d = wg.shape
+        self.S = 0 if weights.get("ws_gate") is None else weights["ws_gate"].shape[0]
+        self.k = int(top_k)
+        self.dtype = wg.dtype
+        self.alpha = alpha
+        self._ws = None
+        self._ws_T = -1
+
+    def config(self, T: int) -> MoEConfig:
+        return make_config(T, self.d, self.N, self.k, self.F, self.S, self.dtype)
+
+    def forward(self, x: torch.Tensor, want_logits: bool = False):
+        T = x.shape[0]
+        cfg = self.config(T)
+        if self._ws is None or self._ws_T < T:
+            self._ws = alloc_workspace(cfg, x.device)
+            self._ws_T = T
+        dev = x.device
+        out = {
+            "y": torch.empty_like(x),
+            "topk_idx": torch.empty((T, self.k), dtype=torch.int32, device=dev),
+            "topk_gate": torch.empty((T, self.k), dtype=torch.float32, device=dev),
+            "counts": torch.zeros(self.N, dtype=torch.int32, device=dev),
+            "prob_sum": torch.zeros(self.N, dtype=torch.float32, device=dev),
+            "logits": (torch.empty((T, self.N), dtype=torch.float32, device=dev)
+                       if want_logits else None),
+            "f": torch.empty(self.N, dtype=torch.float32, device=dev),
+            "P": torch.empty(self.N, dtype=torch.float32, device=dev),
+            "aux": torch.empty(2, dtype=torch.float32, device=dev),
+        }
+        moe_layer_forward(cfg, x, self.weights, out["y"], workspace=self._ws,
+                          logits=out["logits"], topk_idx=out["topk_idx"],
+                          topk_gate=out["topk_gate"], counts=out["counts"],
+                          prob_sum=out["prob_sum"])
+        moe_balance_stats(T, self.N, self.k, out["counts"], out["prob_sum"], self.alpha,
+                          out["f"], out["P"], out["aux"])
+        return out

@@ -1,0 +1,137 @@
+// Gate-weighted combine and the balance statistics.
+//
+// Combine ("Mixture of experts and speculative decoding", "Opening the hood:
+// the MoE layer precisely", equation for y; "MoE inference: the call centre
+// with 256 specialists ...", "The bare mechanism", weighted combination and
+// shared experts):
+//   y[t] = sum_{slot < k} g[t, slot] * Y[inv_row[t, slot]]  +  sum_s Yshared_s[t]
+// accumulated in fp32 in slot order, then rounded once to the output type.
+//
+// Balance statistics ("Keeping the experts busy", balance-loss equation;
+// "Mixture of Experts and Guided Decoding", auxiliary-loss equation):
+//   f_e = counts_e / (T k), P_e = prob_sum_e / T, loss = alpha N sum_e f_e P_e.
+#include "mfma.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int kN = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int kN = 4;
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yperm,
+                                                      const int32_t* __restrict__ inv_row,
+                                                      const float* __restrict__ gate, int n_tok,
+                                                      int d, int k, int S, T* __restrict__ y) {
+  constexpr int V = Vec<T>::kN;
+  const int t = blockIdx.x;
+  __shared__ int s_row[kMaxTopK + kMaxShared];
+  __shared__ float s_g[kMaxTopK];
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = inv_row[static_cast<size_t>(t) * k + threadIdx.x];
+    s_g[threadIdx.x] = gate[static_cast<size_t>(t) * k + threadIdx.x];
+  } else if (threadIdx.x < k + S) {
+    const int s = threadIdx.x - k;
+    s_row[threadIdx.x] = n_tok * k + s * n_tok + t;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * V; c < d; c += 256 * V) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int s = 0; s < k + S; ++s) {
+      float v[V];
+      Vec<T>::load(yperm + static_cast<size_t>(s_row[s]) * d + c, v);
+      const float gs = s < k ? s_g[s] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(gs, v[i], acc[i]);
+    }
+    Vec<T>::store(y + static_cast<size_t>(t) * d + c, acc);
+  }
+}
+
+__global__ __launch_bounds__(256) void balance_kernel(int n_tok, int N, int k,
+                                                      const int32_t* __restrict__ counts,
+                                                      const float* __restrict__ prob_sum,
+                                                      float alpha, float* __restrict__ f_out,
+                                                      float* __restrict__ P_out,
+                                                      float* __restrict__ aux_out) {
+  __shared__ float s_part[256];
+  float part = 0.f;
+  for (int e = threadIdx.x; e < N; e += 256) {
+    float f = 0.f, p = 0.f;
+    if (n_tok > 0) {
+      f = static_cast<float>(counts[e]) / (static_cast<float>(n_tok) * static_cast<float>(k));
+      p = prob_sum[e] / static_cast<float>(n_tok);
+    }
+    f_out[e] = f;
+    P_out[e] = p;
+    part = fmaf(f, p, part);
+  }
+  s_part[threadIdx.x] = part;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) s_part[threadIdx.x] += s_part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float raw = static_cast<float>(N) * s_part[0];
+    aux_out[0] = raw;
+    aux_out[1] = alpha * raw;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* yperm, const int32_t* inv_row,
+                          const float* topk_gate, int T_, int d, int k, int S, void* y,
+                          hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T_), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(yperm), inv_row, topk_gate, T_, d, k, S,
+                       static_cast<bf16_t*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T_), dim3(256), 0, s,
+                       static_cast<const float*>(yperm), inv_row, topk_gate, T_, d, k, S,
+                       static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_balance(int T_, int N, int k, const int32_t* counts, const float* prob_sum,
+                          float alpha, float* f_out, float* P_out, float* aux_out,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(256), 0, s, T_, N, k, counts, prob_sum, alpha,
+                     f_out, P_out, aux_out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

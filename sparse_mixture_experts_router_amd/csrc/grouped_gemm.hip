@@ -1,0 +1,219 @@
+// Grouped expert GEMMs on the matrix cores.
+//
+// Each expert is a SwiGLU feed-forward network ("MoE inference: the call
+// centre with 256 specialists ...", "The bare mechanism": the FFN it replaces
+// is down(act(gate(x)) * up(x)) with SiLU as the activation), run only on the
+// rows routed to it.  With the rows of every expert laid out contiguously
+// (expert-major, see permute.hip):
+//
+//   up pass    H[row, n] = SiLU(sum_j X[tok(row), j] Wg[e][n, j])
+//                          * (sum_j X[tok(row), j] Wu[e][n, j])
+//   down pass  Y[row, c] = sum_n H[row, n] Wd[e][c, n]
+//
+// Both are C = A B^T with the reduction dimension contiguous in A and B (the
+// weights' [out, in] layout), so the MFMA fragments are plain 16-byte row
+// reads.  A workgroup owns one BM-row tile of one expert (from the device-built
+// tile list) and a BN-column slice; shared experts are extra groups whose
+// rows are all tokens.  The up pass gathers X rows through sorted_tok instead
+// of materialising a permuted copy, keeps gate and up accumulators side by
+// side and applies SiLU(gate) * up in the epilogue, so the gate and up
+// activations never reach memory.
+//
+// Pipeline: 4 wavefronts; per K step (128 bytes of every row) the next
+// tile's A and B slices are fetched into registers while the current ones
+// are multiplied out of LDS, double-buffered with one barrier per step.
+#include "mfma.h"
+
+namespace moe {
+namespace {
+
+template <typename T, bool GATED, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr int ROWB = 128;
+  constexpr int NMAT = GATED ? 2 : 1;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MB = WTM / 16, NBK = WTN / 16;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int STAGE = A_BYTES + NMAT * B_BYTES;
+  constexpr int A_LD = BM * 8 / 256;  // 16-byte chunks per thread per K step
+  constexpr int B_LD = BN * 8 / 256;
+  static_assert(WM * WN == 4, "4 wavefronts");
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
+  static_assert(MB >= 1 && NBK >= 1, "wave tile below one MFMA block");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tile = blockIdx.x;
+  if (tile >= *g.ntiles) return;
+  const int2 te = g.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int seg = g.offsets[e];
+  const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+  const int n0 = blockIdx.y * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const size_t row_bytes = static_cast<size_t>(g.k_dim) * sizeof(T);
+  const size_t mat_elems = static_cast<size_t>(g.n_dim) * g.k_dim;
+  const bool routed = e < g.n_experts;
+  const int es = routed ? e : e - g.n_experts;
+  const char* w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_elems * sizeof(T);
+  const char* w1 = GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_elems * sizeof(T)
+                         : nullptr;
+
+  // per-thread global sources as byte offsets (rows beyond the tile are
+  // clamped to a valid row; their results are discarded in the epilogue)
+  const char* a_base = reinterpret_cast<const char*>(g.a);
+  size_t a_off[A_LD];
+  int a_dst[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, ch = c & 7;
+    const int grow = seg + m0 + min(r, mvalid - 1);
+    const int src_row = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
+    a_off[i] = static_cast<size_t>(src_row) * row_bytes + ch * 16;
+    a_dst[i] = lds_swz(r, ch);
+  }
+  size_t b_off[B_LD];
+  int b_dst[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, ch = c & 7;
+    const int n = min(n0 + r, g.n_dim - 1);
+    b_off[i] = static_cast<size_t>(n) * row_bytes + ch * 16;
+    b_dst[i] = lds_swz(r, ch);
+  }
+
+  f32x4 acc[NMAT][MB][NBK];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[A_LD], rb0[B_LD], rb1[B_LD];
+  const int nsteps = static_cast<int>(row_bytes / ROWB);
+
+  // prologue: K step 0 into stage 0
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i]);
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    rb0[i] = *reinterpret_cast<const u32x4*>(w0 + b_off[i]);
+    if (GATED) rb1[i] = *reinterpret_cast<const u32x4*>(w1 + b_off[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(smem + a_dst[i]) = ra[i];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    *reinterpret_cast<u32x4*>(smem + A_BYTES + b_dst[i]) = rb0[i];
+    if (GATED) *reinterpret_cast<u32x4*>(smem + A_BYTES + B_BYTES + b_dst[i]) = rb1[i];
+  }
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) {
+      const size_t koff = static_cast<size_t>(s + 1) * ROWB;
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + koff);
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) {
+        rb0[i] = *reinterpret_cast<const u32x4*>(w0 + b_off[i] + koff);
+        if (GATED) rb1[i] = *reinterpret_cast<const u32x4*>(w1 + b_off[i] + koff);
+      }
+    }
+    const char* st = smem + (s & 1) * STAGE;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int ch = kc * 4 + (lane >> 4);
+      u32x4 af[MB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(st + lds_swz(wm * WTM + i * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) {
+        const int br = wn * WTN + j * 16 + (lane & 15);
+        const u32x4 bf0 = *reinterpret_cast<const u32x4*>(st + A_BYTES + lds_swz(br, ch));
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[0][i][j] = Mfma<T>::step(af[i], bf0, acc[0][i][j]);
+        if (GATED) {
+          const u32x4 bf1 = *reinterpret_cast<const u32x4*>(st + A_BYTES + B_BYTES + lds_swz(br, ch));
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            acc[NMAT - 1][i][j] = Mfma<T>::step(af[i], bf1, acc[NMAT - 1][i][j]);
+        }
+      }
+    }
+    if (more) {
+      char* nx = smem + ((s + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(nx + a_dst[i]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) {
+        *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = rb0[i];
+        if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = rb1[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue
+  T* out = static_cast<T*>(g.out);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wm * WTM + i * 16 + 4 * (lane >> 4) + r;
+      if (row >= mvalid) continue;
+      T* orow = out + static_cast<size_t>(seg + m0 + row) * g.n_dim;
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + (lane & 15);
+        if (col >= g.n_dim) continue;
+        float v;
+        if (GATED) {
+          const float a = acc[0][i][j][r];
+          v = a / (1.0f + __expf(-a)) * acc[NMAT - 1][i][j][r];
+        } else {
+          v = acc[0][i][j][r];
+        }
+        orow[col] = from_f32<T>(v);
+      }
+    }
+  }
+}
+
+template <typename T, bool GATED, int BM, int BN, int WM, int WN>
+hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
+  dim3 grid(g.tiles_cap, (g.n_dim + BN - 1) / BN);
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <typename T, bool GATED>
+hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
+  if (bm == 32) return launch_t<T, GATED, 32, 128, 1, 4>(g, s);
+  return launch_t<T, GATED, 128, 128, 2, 2>(g, s);
+}
+
+}  // namespace
+
+int pick_bm_up(int /*dtype*/, long rows_per_expert) { return rows_per_expert <= 48 ? 32 : 128; }
+int pick_bm_down(int /*dtype*/, long rows_per_expert) { return rows_per_expert <= 48 ? 32 : 128; }
+
+hipError_t launch_gemm_up(int dtype, const GemmArgs& g, int bm, hipStream_t s) {
+  if (dtype == 1) return launch_bm<bf16_t, true>(g, bm, s);
+  return launch_bm<float, true>(g, bm, s);
+}
+
+hipError_t launch_gemm_down(int dtype, const GemmArgs& g, int bm, hipStream_t s) {
+  if (dtype == 1) return launch_bm<bf16_t, false>(g, bm, s);
+  return launch_bm<float, false>(g, bm, s);
+}
+
+}  // namespace moe

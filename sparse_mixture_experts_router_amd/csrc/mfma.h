@@ -1,0 +1,50 @@
+// MFMA step shared by the router and the grouped GEMMs (gfx950).
+//
+// Every operand fragment is 16 contiguous bytes of one row, taken at byte
+// offset 16 * (lane / 16) of a 64-byte slice of the reduction dimension:
+//   row  = lane % 16 of the 16-row block (A: token row, B: weight row)
+//   bf16 : 8 elements -> one v_mfma_f32_16x16x32_bf16 covers the 32 elements
+//          of the slice (lane group q supplies elements 8q .. 8q+7);
+//   fp32 : 4 elements -> four v_mfma_f32_16x16x4_f32, the j-th taking element
+//          j of every lane's four, so together they cover the 16 elements of
+//          the slice (lane group q supplies elements 4q .. 4q+3).
+// A and B use the same element-to-lane assignment, so each MFMA sums matching
+// products.  The 16x16 fp32 result lives in lane l, register r as
+// C[4 * (l / 16) + r][l % 16].
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+  static __device__ __forceinline__ f32x4 step(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static __device__ __forceinline__ f32x4 step(u32x4 a, u32x4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
+    return c;
+  }
+};
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// Byte offset of 16-byte chunk `ch` (0..7) of row `r` in an LDS tile whose
+// rows are 128 bytes: the chunk index is XOR-ed with the row's low 3 bits so
+// that 8 consecutive rows read at the same logical chunk hit 8 different
+// 16-byte bank groups.
+__device__ __forceinline__ int lds_swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+
+}  // namespace moe

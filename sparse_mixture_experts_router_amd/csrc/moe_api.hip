@@ -1,0 +1,326 @@
+// Host side of libmoe.so: argument validation, workspace carve-out and the
+// launch sequence of the layer forward.  Every launch goes on the caller's
+// stream; nothing here allocates, frees or waits on the device.
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+#include <stdio.h>
+#include <string.h>
+
+namespace moe {
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+moe_status fail(moe_status st, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  return st;
+}
+
+moe_status hip_fail(hipError_t err, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(err));
+  return MOE_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Row tiles that a grouped GEMM with `bm`-row tiles can need in the worst
+// case: each routed expert with c_e > 0 rows needs ceil(c_e / bm) tiles, and
+// sum_e ceil(c_e / bm) <= (T k + N (bm - 1)) / bm; each shared expert needs
+// ceil(T / bm).
+long tile_capacity(const moe_config& c, int bm) {
+  const long tk = static_cast<long>(c.T) * c.top_k;
+  const long routed = (tk + static_cast<long>(c.n_experts) * (bm - 1)) / bm;
+  const long routed_cap = routed < tk ? routed : tk;
+  return routed_cap + static_cast<long>(c.n_shared) * ((c.T + bm - 1) / bm);
+}
+
+struct Plan {
+  int bm_up, bm_down;
+  int cap_up, cap_down;
+  size_t total;
+  size_t off[17];
+};
+
+enum {
+  R_IDX, R_GATE, R_LRANK, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
+  R_TUP, R_TDN, R_NT, R_HID, R_YP, R_COUNT
+};
+
+Plan make_plan(const moe_config& c) {
+  Plan p{};
+  const long rows_per_expert = static_cast<long>(c.T) * c.top_k / c.n_experts;
+  p.bm_up = pick_bm_up(c.dtype, rows_per_expert);
+  p.bm_down = pick_bm_down(c.dtype, rows_per_expert);
+  p.cap_up = static_cast<int>(tile_capacity(c, p.bm_up));
+  p.cap_down = static_cast<int>(tile_capacity(c, p.bm_down));
+  const size_t T = c.T, N = c.n_experts, k = c.top_k, S = c.n_shared;
+  const size_t B = (T + kRouteTokens - 1) / kRouteTokens;
+  const size_t rows = T * k + S * T;
+  const size_t eb = c.dtype == MOE_BF16 ? 2 : 4;
+  size_t sz[R_COUNT];
+  sz[R_IDX] = T * k * 4;
+  sz[R_GATE] = T * k * 4;
+  sz[R_LRANK] = T * k * 4;
+  sz[R_BCNT] = B * N * 4;
+  sz[R_BPS] = B * N * 4;
+  sz[R_BBASE] = B * N * 4;
+  sz[R_CNT] = (N + S) * 4;
+  sz[R_PS] = N * 4;
+  sz[R_OFF] = (N + S + 1) * 4;
+  sz[R_SORT] = rows * 4;
+  sz[R_INV] = T * k * 4;
+  sz[R_TUP] = static_cast<size_t>(p.cap_up) * 8;
+  sz[R_TDN] = static_cast<size_t>(p.cap_down) * 8;
+  sz[R_NT] = 2 * 4;
+  sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
+  sz[R_YP] = rows * static_cast<size_t>(c.d_model) * eb;
+  size_t o = 0;
+  for (int i = 0; i < R_COUNT; ++i) {
+    p.off[i] = o;
+    o += align_up(sz[i] ? sz[i] : 1);
+  }
+  p.total = o;
+  return p;
+}
+
+Workspace carve(const Plan& p, void* base) {
+  char* b = static_cast<char*>(base);
+  Workspace w{};
+  w.topk_idx = reinterpret_cast<int32_t*>(b + p.off[R_IDX]);
+  w.topk_gate = reinterpret_cast<float*>(b + p.off[R_GATE]);
+  w.lrank = reinterpret_cast<int32_t*>(b + p.off[R_LRANK]);
+  w.blk_counts = reinterpret_cast<int32_t*>(b + p.off[R_BCNT]);
+  w.blk_psum = reinterpret_cast<float*>(b + p.off[R_BPS]);
+  w.blk_base = reinterpret_cast<int32_t*>(b + p.off[R_BBASE]);
+  w.counts = reinterpret_cast<int32_t*>(b + p.off[R_CNT]);
+  w.prob_sum = reinterpret_cast<float*>(b + p.off[R_PS]);
+  w.offsets = reinterpret_cast<int32_t*>(b + p.off[R_OFF]);
+  w.sorted_tok = reinterpret_cast<int32_t*>(b + p.off[R_SORT]);
+  w.inv_row = reinterpret_cast<int32_t*>(b + p.off[R_INV]);
+  w.tiles_up = reinterpret_cast<int2*>(b + p.off[R_TUP]);
+  w.tiles_down = reinterpret_cast<int2*>(b + p.off[R_TDN]);
+  w.ntiles = reinterpret_cast<int32_t*>(b + p.off[R_NT]);
+  w.hidden = b + p.off[R_HID];
+  w.yperm = b + p.off[R_YP];
+  return w;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->T < 0 || c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 ||
+      c->n_shared < 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T, S >= 0)");
+  if (c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k > n_experts");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad dtype");
+  if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
+  if (c->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
+  if (c->n_shared > kMaxShared) return fail(MOE_ERR_UNSUPPORTED, "n_shared > 4");
+  if (c->d_model % 64 != 0 || c->d_ff % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+  const long rows = static_cast<long>(c->T) * (c->top_k + c->n_shared);
+  if (rows >= (1L << 30)) return fail(MOE_ERR_UNSUPPORTED, "T * (k + S) too large");
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_config& c, const moe_weights* w, bool experts) {
+  if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (w->w_router == nullptr) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+  if (!aligned16(w->w_router)) return fail(MOE_ERR_INVALID_ARG, "w_router not 16-byte aligned");
+  if (!experts) return MOE_OK;
+  const void* req[3] = {w->w_gate, w->w_up, w->w_down};
+  for (const void* p : req) {
+    if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "expert weight is NULL");
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "expert weight not 16-byte aligned");
+  }
+  if (c.n_shared > 0) {
+    const void* sh[3] = {w->ws_gate, w->ws_up, w->ws_down};
+    for (const void* p : sh) {
+      if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "shared expert weight is NULL");
+      if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "shared weight not 16-byte aligned");
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p.total) return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size");
+  return MOE_OK;
+}
+
+void mark(void* const* ev, int i, hipStream_t s) {
+  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
+
+// Shared by moe_route and moe_layer_forward: route + block statistics + scan.
+moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, const void* x,
+                     const moe_weights& w, moe_routing* out, int32_t* idx, float* gate,
+                     hipStream_t s) {
+  hipError_t err = launch_route(c.dtype, x, w.w_router, w.logit_bias, w.select_bias, c.T,
+                                c.d_model, c.n_experts, c.top_k, out ? out->logits : nullptr, idx,
+                                gate, ws.lrank, ws.blk_counts, ws.blk_psum, s);
+  if (err != hipSuccess) return hip_fail(err, "route kernel");
+  return MOE_OK;
+}
+
+moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
+                    hipStream_t s) {
+  hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
+                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, ws.blk_base, ws.counts,
+                               ws.prob_sum, out ? out->counts : nullptr,
+                               out ? out->prob_sum : nullptr, ws.offsets, ws.tiles_up,
+                               ws.tiles_down, ws.ntiles, s);
+  if (err != hipSuccess) return hip_fail(err, "scan kernel");
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_plan(*cfg).total;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: size outside the supported range";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
+                     moe_routing* out, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_config& c = *cfg;
+  if ((st = check_weights(c, w, false)) != MOE_OK) return st;
+  if (out == nullptr || out->topk_idx == nullptr || out->topk_gate == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route needs out->topk_idx and out->topk_gate");
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if (!aligned16(x)) return fail(MOE_ERR_INVALID_ARG, "x not 16-byte aligned");
+  const Plan p = make_plan(c);
+  if ((st = check_workspace(p, workspace, ws_bytes)) != MOE_OK) return st;
+  const Workspace ws = carve(p, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_route(c, p, ws, x, *w, out, out->topk_idx, out->topk_gate, s)) != MOE_OK) return st;
+  if (out->counts != nullptr || out->prob_sum != nullptr) {
+    if ((st = run_scan(c, p, ws, out, s)) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const moe_weights* w,
+                                   void* y, moe_routing* out, void* workspace, size_t ws_bytes,
+                                   void* stream, void* const* ev) {
+  g_last_error[0] = '\0';
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_config& c = *cfg;
+  if ((st = check_weights(c, w, true)) != MOE_OK) return st;
+  if (c.T == 0) return MOE_OK;
+  if (x == nullptr || y == nullptr) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_INVALID_ARG, "x or y not 16-byte aligned");
+  const Plan p = make_plan(c);
+  if ((st = check_workspace(p, workspace, ws_bytes)) != MOE_OK) return st;
+  const Workspace ws = carve(p, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t* idx = (out && out->topk_idx) ? out->topk_idx : ws.topk_idx;
+  float* gate = (out && out->topk_gate) ? out->topk_gate : ws.topk_gate;
+
+  mark(ev, MOE_STAGE_ROUTE, s);
+  if ((st = run_route(c, p, ws, x, *w, out, idx, gate, s)) != MOE_OK) return st;
+
+  mark(ev, MOE_STAGE_PERMUTE, s);
+  if ((st = run_scan(c, p, ws, out, s)) != MOE_OK) return st;
+  hipError_t err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts,
+                                  c.top_k, c.n_shared, ws.sorted_tok, ws.inv_row, s);
+  if (err != hipSuccess) return hip_fail(err, "scatter kernel");
+
+  mark(ev, MOE_STAGE_EXPERT_UP, s);
+  GemmArgs up{};
+  up.a = x;
+  up.gather = ws.sorted_tok;
+  up.w0 = w->w_gate;
+  up.w1 = w->w_up;
+  up.ws0 = w->ws_gate;
+  up.ws1 = w->ws_up;
+  up.offsets = ws.offsets;
+  up.tiles = ws.tiles_up;
+  up.ntiles = ws.ntiles;
+  up.out = ws.hidden;
+  up.a_rows = c.T;
+  up.n_experts = c.n_experts;
+  up.k_dim = c.d_model;
+  up.n_dim = c.d_ff;
+  up.tiles_cap = p.cap_up;
+  if ((err = launch_gemm_up(c.dtype, up, p.bm_up, s)) != hipSuccess)
+    return hip_fail(err, "gate/up GEMM");
+
+  mark(ev, MOE_STAGE_EXPERT_DOWN, s);
+  GemmArgs dn{};
+  dn.a = ws.hidden;
+  dn.gather = nullptr;
+  dn.w0 = w->w_down;
+  dn.ws0 = w->ws_down;
+  dn.offsets = ws.offsets;
+  dn.tiles = ws.tiles_down;
+  dn.ntiles = ws.ntiles + 1;
+  dn.out = ws.yperm;
+  dn.a_rows = static_cast<int>(static_cast<long>(c.T) * (c.top_k + c.n_shared));
+  dn.n_experts = c.n_experts;
+  dn.k_dim = c.d_ff;
+  dn.n_dim = c.d_model;
+  dn.tiles_cap = p.cap_down;
+  if ((err = launch_gemm_down(c.dtype, dn, p.bm_down, s)) != hipSuccess)
+    return hip_fail(err, "down GEMM");
+
+  mark(ev, MOE_STAGE_COMBINE, s);
+  if ((err = launch_combine(c.dtype, ws.yperm, ws.inv_row, gate, c.T, c.d_model, c.top_k,
+                            c.n_shared, y, s)) != hipSuccess)
+    return hip_fail(err, "combine kernel");
+  mark(ev, MOE_STAGE_COUNT, s);
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                             moe_routing* out, void* workspace, size_t ws_bytes, void* stream) {
+  return moe_layer_forward_timed(cfg, x, w, y, out, workspace, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_balance_stats(int32_t T, int32_t N, int32_t k, const int32_t* counts,
+                             const float* prob_sum, float alpha, float* f_out, float* P_out,
+                             float* aux_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (T < 0 || N <= 0 || k <= 0 || k > N) return fail(MOE_ERR_INVALID_ARG, "bad T, N or k");
+  if (N > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
+  if (counts == nullptr || prob_sum == nullptr || f_out == nullptr || P_out == nullptr ||
+      aux_out == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  hipError_t err = launch_balance(T, N, k, counts, prob_sum, alpha, f_out, P_out, aux_out,
+                                  static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "balance kernel");
+  return MOE_OK;
+}
+
+}  // extern "C"

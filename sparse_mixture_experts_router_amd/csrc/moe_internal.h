@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP translation units of libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- constants
+constexpr int kRouteTokens = 64;      // tokens per routing workgroup
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxShared = 4;
+
+// ---------------------------------------------------------------- vector types
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // one 16-byte fragment
+typedef uint16_t bf16_t;  // storage type of a bf16 element
+
+// Workspace carve-out of one forward call (every pointer is device memory).
+struct Workspace {
+  int32_t* topk_idx;   // [T, k]
+  float* topk_gate;    // [T, k]
+  int32_t* lrank;      // [T, k]     rank of the assignment inside its block
+  int32_t* blk_counts; // [B, N]
+  float* blk_psum;     // [B, N]
+  int32_t* blk_base;   // [B, N]
+  int32_t* counts;     // [N + S]
+  float* prob_sum;     // [N]
+  int32_t* offsets;    // [N + S + 1]
+  int32_t* sorted_tok; // [T k + S T]
+  int32_t* inv_row;    // [T, k]
+  int2* tiles_up;      // tile list of the gate/up GEMM
+  int2* tiles_down;    // tile list of the down GEMM
+  int32_t* ntiles;     // [2]: entries in tiles_up, tiles_down
+  void* hidden;        // [T k + S T, F]  dtype
+  void* yperm;         // [T k + S T, d]  dtype
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_route(int dtype, const void* x, const void* w_router,
+                        const float* logit_bias, const float* select_bias,
+                        int T, int d, int N, int k, float* logits_out,
+                        int32_t* topk_idx, float* topk_gate, int32_t* lrank,
+                        int32_t* blk_counts, float* blk_psum, hipStream_t s);
+
+hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
+                       int N, int k, int S, int bm_up, int cap_up, int bm_down,
+                       int cap_down, int32_t* blk_base, int32_t* counts,
+                       float* prob_sum, int32_t* user_counts,
+                       float* user_prob_sum, int32_t* offsets, int2* tiles_up,
+                       int2* tiles_down, int32_t* ntiles, hipStream_t s);
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank,
+                          const int32_t* blk_base, const int32_t* offsets,
+                          int T, int N, int k, int S, int32_t* sorted_tok,
+                          int32_t* inv_row, hipStream_t s);
+
+struct GemmArgs {
+  const void* a;             // x [T, d] (gather) or hidden [rows, F] (direct)
+  const int32_t* gather;     // sorted_tok, or NULL for direct rows
+  const void* w0;            // routed weights for expert 0 (gate or down)
+  const void* w1;            // routed up weights, gated GEMM only
+  const void* ws0;           // shared-expert weights (gate or down)
+  const void* ws1;           // shared up weights, gated GEMM only
+  const int32_t* offsets;    // [N + S + 1]
+  const int2* tiles;         // tile list
+  const int32_t* ntiles;     // device count of tiles
+  void* out;                 // [rows, n_dim]
+  int a_rows;                // rows of a (gathered indices are clamped to it)
+  int n_experts;             // routed experts N (e >= N is shared e - N)
+  int k_dim;                 // reduction length (d or F)
+  int n_dim;                 // output columns (F or d)
+  int tiles_cap;             // grid rows
+};
+
+hipError_t launch_gemm_up(int dtype, const GemmArgs& g, int bm, hipStream_t s);
+hipError_t launch_gemm_down(int dtype, const GemmArgs& g, int bm, hipStream_t s);
+int pick_bm_up(int dtype, long rows_per_expert);
+int pick_bm_down(int dtype, long rows_per_expert);
+
+hipError_t launch_combine(int dtype, const void* yperm, const int32_t* inv_row,
+                          const float* topk_gate, int T, int d, int k, int S,
+                          void* y, hipStream_t s);
+
+hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
+                          const float* prob_sum, float alpha, float* f_out,
+                          float* P_out, float* aux_out, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+}  // namespace moe

@@ -1,0 +1,184 @@
+// Grouping of the routed tokens by expert.
+//
+// The pages' layer runs each expert only on the tokens that chose it
+// ("Mixture of experts and speculative decoding", "A toy MoE layer in
+// PyTorch": an expert that no token picked does no work; "Mixture of Experts
+// and Guided Decoding", sparse-MoE passage: each expert sees the tokens whose
+// top-k contains it).  Instead of one masked pass per expert, the
+// assignments are laid out once in expert-major order:
+//
+//   counts[e]            = total assignments to e (sum of the block counts)
+//   offsets[e]           = exclusive prefix sum of counts (shared expert s
+//                          follows the routed ones with T rows)
+//   row(t, slot)         = offsets[e] + (assignments to e in earlier blocks)
+//                          + (rank of t among the block's tokens that chose e)
+//   sorted_tok[row]      = t,  inv_row[t, slot] = row
+//
+// so each expert's rows are contiguous and ordered by token.  The scan kernel
+// also writes the tile lists of the two grouped GEMMs (one entry per BM-row
+// tile of each non-empty expert), so tile scheduling needs no host round trip.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive prefix sum over v (one value per thread of a 1024-thread block);
+// returns the exclusive sum for this thread and the block total in *total.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < (kScanThreads / 64) ? s_tmp[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += o;
+    }
+    if (lane < kScanThreads / 64) s_tmp[16 + lane] = wi - w;  // exclusive per wave
+    if (lane == kScanThreads / 64 - 1) s_tmp[32] = wi;
+  }
+  __syncthreads();
+  const int res = s_tmp[16 + wave] + incl - v;
+  *total = s_tmp[32];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(
+    const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
+    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down,
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
+    int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
+    int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
+    int32_t* __restrict__ ntiles) {
+  __shared__ int s_cnt[kScanThreads];
+  __shared__ float s_ps[kScanThreads];
+  __shared__ int s_tmp[64];
+  __shared__ int s_tot[kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int B = (n_tok + kRouteTokens - 1) / kRouteTokens;
+  const int P = kScanThreads / N;  // threads per expert (N <= 512 -> P >= 2)
+  const int e = tid / P, part = tid - e * P;
+  const bool mine = e < N;
+  const int b_lo = mine ? static_cast<int>((static_cast<long>(B) * part) / P) : 0;
+  const int b_hi = mine ? static_cast<int>((static_cast<long>(B) * (part + 1)) / P) : 0;
+
+  // partial column sums over this thread's range of blocks
+  int c = 0;
+  float ps = 0.f;
+  for (int b = b_lo; b < b_hi; ++b) {
+    c += blk_counts[static_cast<size_t>(b) * N + e];
+    ps += blk_psum[static_cast<size_t>(b) * N + e];
+  }
+  s_cnt[tid] = c;
+  s_ps[tid] = ps;
+  __syncthreads();
+  if (mine && part == 0) {
+    int run = 0;
+    float pr = 0.f;
+    for (int p = 0; p < P; ++p) {
+      const int v = s_cnt[e * P + p];
+      s_cnt[e * P + p] = run;
+      run += v;
+      pr += s_ps[e * P + p];
+    }
+    s_tot[e] = run;
+    counts[e] = run;
+    prob_sum[e] = pr;
+    if (user_counts != nullptr) user_counts[e] = run;
+    if (user_prob_sum != nullptr) user_prob_sum[e] = pr;
+  }
+  __syncthreads();
+  if (mine) {
+    int run = s_cnt[tid];
+    for (int b = b_lo; b < b_hi; ++b) {
+      const size_t o = static_cast<size_t>(b) * N + e;
+      blk_base[o] = run;
+      run += blk_counts[o];
+    }
+  }
+  __syncthreads();
+
+  // offsets and tile lists over the N + S row groups
+  const int NG = N + S;
+  int cg = 0;
+  if (tid < N) cg = s_tot[tid];
+  else if (tid < NG) cg = n_tok;
+  if (tid < NG && tid >= N) counts[tid] = n_tok;
+  int total_rows;
+  const int off = block_exclusive_scan(cg, s_tmp, &total_rows);
+  if (tid < NG) offsets[tid] = off;
+  if (tid == 0) offsets[NG] = total_rows;
+
+  const int tu = tid < NG ? (cg + bm_up - 1) / bm_up : 0;
+  const int td = tid < NG ? (cg + bm_down - 1) / bm_down : 0;
+  int total_up, total_down;
+  const int base_up = block_exclusive_scan(tu, s_tmp, &total_up);
+  const int base_down = block_exclusive_scan(td, s_tmp, &total_down);
+  for (int i = 0; i < tu; ++i)
+    if (base_up + i < cap_up) tiles_up[base_up + i] = make_int2(tid, i * bm_up);
+  for (int i = 0; i < td; ++i)
+    if (base_down + i < cap_down) tiles_down[base_down + i] = make_int2(tid, i * bm_down);
+  if (tid == 0) {
+    ntiles[0] = min(total_up, cap_up);
+    ntiles[1] = min(total_down, cap_down);
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets, int n_tok, int N,
+    int k, int S, int32_t* __restrict__ sorted_tok, int32_t* __restrict__ inv_row) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const long tk = static_cast<long>(n_tok) * k;
+  if (i < tk) {
+    const int t = static_cast<int>(i / k);
+    const int e = topk_idx[i];
+    const int b = t / kRouteTokens;
+    const int row = offsets[e] + blk_base[static_cast<size_t>(b) * N + e] + lrank[i];
+    // a row outside the expert's segment would mean inconsistent routing
+    // outputs; keep every write in bounds regardless
+    const bool ok = row >= offsets[e] && row < offsets[e + 1];
+    if (ok) sorted_tok[row] = t;
+    inv_row[i] = ok ? row : offsets[e];
+  } else if (i < tk + static_cast<long>(S) * n_tok) {
+    const long j = i - tk;
+    sorted_tok[tk + j] = static_cast<int>(j % n_tok);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
+                       int S, int bm_up, int cap_up, int bm_down, int cap_down,
+                       int32_t* blk_base, int32_t* counts, float* prob_sum,
+                       int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
+                       int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
+                     k, S, bm_up, cap_up, bm_down, cap_down, blk_base, counts, prob_sum,
+                     user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank, const int32_t* blk_base,
+                          const int32_t* offsets, int T_, int N, int k, int S,
+                          int32_t* sorted_tok, int32_t* inv_row, hipStream_t s) {
+  const long n = static_cast<long>(T_) * k + static_cast<long>(S) * T_;
+  const int blocks = static_cast<int>((n + 255) / 256);
+  hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s, topk_idx, lrank, blk_base,
+                     offsets, T_, N, k, S, sorted_tok, inv_row);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                                reason="libmoe.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_layer_forward", "moe_route", "moe_balance_stats",
+                     "moe_workspace_size", "moe_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = moe.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in moe.h but not exported"
+
+
+def test_status_strings():
+    for code in range(5):
+        assert moe.moe_status_string(code).startswith("MOE_")
+    assert "unknown" in moe.moe_status_string(99)
+
+
+def test_workspace_size_validation():
+    ok = moe.make_config(64, 128, 4, 2, 256, 0, "f32")
+    n = moe.moe_workspace_size(ok)
+    assert n > 0 and n % 256 == 0
+    # grows with T, never shrinks
+    assert moe.moe_workspace_size(moe.make_config(128, 128, 4, 2, 256, 0, "f32")) > n
+    for bad in [moe.make_config(64, 100, 4, 2, 256), moe.make_config(64, 128, 4, 5, 256),
+                moe.make_config(64, 128, 600, 2, 256), moe.make_config(64, 128, 40, 17, 256),
+                moe.make_config(-1, 128, 4, 2, 256), moe.make_config(64, 128, 4, 2, 96),
+                moe.make_config(64, 128, 4, 2, 256, n_shared=5)]:
+        assert moe.moe_workspace_size(bad) == 0
+
+
+def _call_forward(cfg, weights=None, x=1 << 20, y=1 << 20, ws=None, ws_bytes=0):
+    lib = moe.lib()
+    return lib.moe_layer_forward(ctypes.byref(cfg) if cfg is not None else None, x,
+                                 ctypes.byref(weights) if weights is not None else None, y,
+                                 None, ws, ws_bytes, None)
+
+
+FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def _w(**over):
+    w = moe.MoEWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, None)
+    for k_, v in over.items():
+        setattr(w, k_, v)
+    return w
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_cfg", moe.MOE_ERR_INVALID_ARG),
+    ("k_gt_n", moe.MOE_ERR_INVALID_ARG),
+    ("zero_k", moe.MOE_ERR_INVALID_ARG),
+    ("bad_dtype", moe.MOE_ERR_INVALID_ARG),
+    ("too_many_experts", moe.MOE_ERR_UNSUPPORTED),
+    ("k_above_16", moe.MOE_ERR_UNSUPPORTED),
+    ("d_not_64", moe.MOE_ERR_UNSUPPORTED),
+    ("null_weights", moe.MOE_ERR_INVALID_ARG),
+    ("null_router", moe.MOE_ERR_INVALID_ARG),
+    ("null_expert", moe.MOE_ERR_INVALID_ARG),
+    ("shared_missing", moe.MOE_ERR_INVALID_ARG),
+    ("misaligned_weight", moe.MOE_ERR_INVALID_ARG),
+    ("null_x", moe.MOE_ERR_INVALID_ARG),
+    ("no_workspace", moe.MOE_ERR_WORKSPACE),
+    ("small_workspace", moe.MOE_ERR_WORKSPACE),
+    ("misaligned_workspace", moe.MOE_ERR_WORKSPACE),
+    ("empty_batch", moe.MOE_OK),
+])
+def test_forward_rejects_before_launch(case, expect):
+    cfg = moe.make_config(64, 128, 4, 2, 256)
+    w = _w()
+    kw = {}
+    if case == "null_cfg":
+        cfg = None
+    elif case == "k_gt_n":
+        cfg = moe.make_config(64, 128, 4, 5, 256)
+    elif case == "zero_k":
+        cfg = moe.make_config(64, 128, 4, 0, 256)
+    elif case == "bad_dtype":
+        cfg.dtype = 7
+    elif case == "too_many_experts":
+        cfg = moe.make_config(64, 128, 513, 2, 256)
+    elif case == "k_above_16":
+        cfg = moe.make_config(64, 128, 64, 17, 256)
+    elif case == "d_not_64":
+        cfg = moe.make_config(64, 96, 4, 2, 256)
+    elif case == "null_weights":
+        w = None
+    elif case == "null_router":
+        w = _w(w_router=None)
+    elif case == "null_expert":
+        w = _w(w_down=None)
+    elif case == "shared_missing":
+        cfg = moe.make_config(64, 128, 4, 2, 256, n_shared=1)
+    elif case == "misaligned_weight":
+        w = _w(w_up=FAKE + 2)
+    elif case == "null_x":
+        kw = {"x": None}
+    elif case == "no_workspace":
+        kw = {"ws": None, "ws_bytes": 10 ** 9}
+    elif case == "small_workspace":
+        kw = {"ws": FAKE, "ws_bytes": 256}
+    elif case == "misaligned_workspace":
+        kw = {"ws": FAKE + 64, "ws_bytes": 10 ** 9}
+    elif case == "empty_batch":
+        cfg = moe.make_config(0, 128, 4, 2, 256)
+        kw = {"x": None, "y": None}
+    assert _call_forward(cfg, w, **kw) == expect
+    if expect != moe.MOE_OK:
+        assert moe.lib().moe_last_error()
+
+
+def test_route_requires_outputs():
+    lib = moe.lib()
+    cfg = moe.make_config(64, 128, 4, 2, 256)
+    w = _w()
+    r = moe.MoERouting(None, None, None, None, None)
+    st = lib.moe_route(ctypes.byref(cfg), FAKE, ctypes.byref(w), ctypes.byref(r), FAKE, 10 ** 9,
+                       None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_balance_stats_validation():
+    lib = moe.lib()
+    assert lib.moe_balance_stats(10, 4, 5, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_balance_stats(10, 4, 2, None, FAKE, 0.01, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_balance_stats(10, 600, 2, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_UNSUPPORTED

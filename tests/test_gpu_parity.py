@@ -1,0 +1,144 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Element-wise on shapes the oracle finishes in seconds (several tiles, ragged
+tails, every routing variant), and on sampled tokens at the full workload
+sizes in the launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_mixture_experts_router_amd as moe
+from gpu_harness import full_parity, run_layer, sampled_parity, say, to_np
+from workloads import CONFIGS, MoEShape, make_inputs, reduced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()  # the HIP library must be built; no fallback
+
+
+def test_tiny_f32_config():
+    full_parity(CONFIGS["tiny_f32"], seed=0)
+
+
+def test_deterministic_bitwise():
+    shp = reduced(CONFIGS["deepseek_v3"], T=130, d=256, F=256, N=32)
+    inputs = make_inputs(shp, seed=5, device="cuda")
+    a = run_layer(shp, inputs)
+    b = run_layer(shp, inputs)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+REDUCED = [
+    ("mixtral_like", reduced(CONFIGS["mixtral_prefill"], T=300, d=512, F=1024)),
+    ("decode_like", reduced(CONFIGS["mixtral_decode"], T=32, d=512, F=1024)),
+    ("deepseek_like", reduced(CONFIGS["deepseek_v3"], T=200, d=512, F=256, N=64)),
+    ("qwen_like_ntail", reduced(CONFIGS["qwen3_skew"], T=333, d=256, F=192, N=128)),
+    ("max_experts_topk", MoEShape("max_experts", T=100, d=128, N=512, k=16, F=128)),
+    ("single_expert", MoEShape("single", T=70, d=128, N=1, k=1, F=64)),
+    ("f32_ragged", MoEShape("f32_ragged", T=77, d=192, N=6, k=3, F=320, dtype="f32")),
+    ("f32_shared_bias", MoEShape("f32_sb", T=65, d=128, N=8, k=2, F=128, S=2, dtype="f32",
+                                 select_bias=True)),
+    ("one_token", reduced(CONFIGS["deepseek_v3"], T=1, d=256, F=128, N=16)),
+    ("bf16_k_equals_n", MoEShape("dense", T=40, d=128, N=4, k=4, F=128)),
+]
+
+
+@pytest.mark.parametrize("label,shape", REDUCED, ids=[r[0] for r in REDUCED])
+def test_reduced_parity(label, shape):
+    full_parity(shape, seed=1, label=label)
+
+
+def test_empty_batch_is_noop():
+    shp = MoEShape("empty", T=0, d=128, N=4, k=2, F=128)
+    cfg = moe.make_config(0, 128, 4, 2, 128)
+    inputs = make_inputs(MoEShape("w", T=1, d=128, N=4, k=2, F=128), device="cuda")
+    y = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    moe.moe_layer_forward(cfg, inputs["x"][:0], inputs, y, workspace=torch.empty(
+        256, dtype=torch.uint8, device="cuda"))
+    f = torch.full((4,), 7.0, device="cuda")
+    P = torch.full((4,), 7.0, device="cuda")
+    aux = torch.full((2,), 7.0, device="cuda")
+    moe.moe_balance_stats(0, 4, 2, torch.zeros(4, dtype=torch.int32, device="cuda"),
+                          torch.zeros(4, device="cuda"), 0.01, f, P, aux)
+    torch.cuda.synchronize()
+    assert float(f.abs().sum() + P.abs().sum() + aux.abs().sum()) == 0.0
+    del shp
+
+
+def test_all_tokens_one_expert():
+    shp = MoEShape("hot", T=300, d=256, N=4, k=1, F=256)
+    inputs = make_inputs(shp, seed=2, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0.0, 0.0, 0.0, 100.0], device="cuda")
+    _, out, _ = full_parity(shp, inputs=inputs, label="all_to_expert_3")
+    assert to_np(out["counts"]).tolist() == [0, 0, 0, 300]
+
+
+def test_unchosen_expert_weights_never_read():
+    shp = MoEShape("nan_cold", T=150, d=128, N=6, k=2, F=128)
+    inputs = make_inputs(shp, seed=3, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0, 0, 0, 0, 0, -1.0e4], dtype=torch.float32,
+                                        device="cuda")
+    for name in ("w_gate", "w_up", "w_down"):
+        inputs[name][5] = float("nan")
+    _, out, _ = full_parity(shp, inputs=inputs, label="nan_in_unused_expert")
+    assert int(out["counts"][5]) == 0
+    assert bool(torch.isfinite(out["y"].float()).all())
+
+
+def test_exact_ties_go_to_lower_index():
+    # small integers make every logit an exact integer, so many keys tie exactly;
+    # experts 1 and 2 have identical router rows and always tie
+    shp = MoEShape("ties", T=256, d=128, N=8, k=3, F=128)
+    inputs = make_inputs(shp, seed=4, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    inputs["x"] = torch.randint(-2, 3, (256, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wr = torch.randint(-1, 2, (8, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wr[2] = wr[1]
+    inputs["w_router"] = wr.contiguous()
+    _, out, _ = full_parity(shp, inputs=inputs, label="exact_ties")
+    lg = to_np(out["logits"])
+    assert np.array_equal(lg[:, 1], lg[:, 2])
+    idx = to_np(out["topk_idx"])
+    both = np.sum(np.any(idx == 1, axis=1) & ~np.any(idx == 2, axis=1))
+    only2 = np.sum(np.any(idx == 2, axis=1) & ~np.any(idx == 1, axis=1))
+    say(f"[ties] tokens with 1 but not 2: {both}, with 2 but not 1: {only2}")
+    assert only2 == 0 and both > 0
+
+
+def test_route_entry_point_matches_forward():
+    shp = reduced(CONFIGS["qwen3_skew"], T=200, d=256, F=128, N=32)
+    inputs = make_inputs(shp, seed=6, device="cuda")
+    full = run_layer(shp, inputs)
+    cfg = moe.make_config(shp.T, shp.d, shp.N, shp.k, shp.F, shp.S)
+    ws = moe.alloc_workspace(cfg)
+    idx = torch.empty_like(full["topk_idx"])
+    gate = torch.empty_like(full["topk_gate"])
+    counts = torch.empty_like(full["counts"])
+    ps = torch.empty_like(full["prob_sum"])
+    lg = torch.empty_like(full["logits"])
+    moe.moe_route(cfg, inputs["x"], inputs, topk_idx=idx, topk_gate=gate, workspace=ws,
+                  logits=lg, counts=counts, prob_sum=ps)
+    torch.cuda.synchronize()
+    for a, b in ((idx, full["topk_idx"]), (gate, full["topk_gate"]), (counts, full["counts"]),
+                 (ps, full["prob_sum"]), (lg, full["logits"])):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "qwen3_skew",
+                                  "deepseek_v3"])
+def test_full_size_sampled(name):
+    out = sampled_parity(CONFIGS[name], seed=0)
+    if name == "qwen3_skew":
+        counts = to_np(out["counts"])
+        say(f"[full] qwen3_skew counts max {counts.max()} min {counts.min()} "
+            f"aux_raw {float(out['aux'][0]):.3f}")
+        assert counts.max() > 8 * counts.mean()   # the Zipf offset skews the load
+    del out
+    torch.cuda.empty_cache()
