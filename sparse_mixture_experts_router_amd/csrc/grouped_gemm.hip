@@ -203,17 +203,23 @@ hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
 
 }  // namespace
 
-int pick_bm_up(int /*dtype*/, long rows_per_expert) { return rows_per_expert <= 48 ? 32 : 128; }
-int pick_bm_down(int /*dtype*/, long rows_per_expert) { return rows_per_expert <= 48 ? 32 : 128; }
-
-hipError_t launch_gemm_up(int dtype, const GemmArgs& g, int bm, hipStream_t s) {
-  if (dtype == 1) return launch_bm<bf16_t, true>(g, bm, s);
-  return launch_bm<float, true>(g, bm, s);
+hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s) {
+  if (dtype == 1) return gated ? launch_bm<bf16_t, true>(g, bm, s) : launch_bm<bf16_t, false>(g, bm, s);
+  return gated ? launch_bm<float, true>(g, bm, s) : launch_bm<float, false>(g, bm, s);
 }
 
-hipError_t launch_gemm_down(int dtype, const GemmArgs& g, int bm, hipStream_t s) {
-  if (dtype == 1) return launch_bm<bf16_t, false>(g, bm, s);
-  return launch_bm<float, false>(g, bm, s);
+GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_bytes,
+                   size_t w_bytes) {
+  const bool small_offsets = a_bytes < (size_t{1} << 32) && w_bytes < (size_t{1} << 32);
+  if (dtype != 1 || !small_offsets) return GemmPick{0, rows_per_expert <= 48 ? 32 : 128};
+  if (rows_per_expert <= 48) return GemmPick{0, 32};
+  if (rows_per_expert >= 512) return GemmPick{1, 256};
+  return GemmPick{1, 128};
+}
+
+hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s) {
+  if (pick.variant == 1 && dtype == 1) return launch_expert_gemm(gated, pick.bm, g, s);
+  return launch_generic_gemm(dtype, gated, pick.bm, g, s);
 }
 
 }  // namespace moe

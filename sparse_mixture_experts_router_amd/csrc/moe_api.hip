@@ -1,7 +1,7 @@
 // Host side of libmoe.so: argument validation, workspace carve-out and the
 // launch sequence of the layer forward.  Every launch goes on the caller's
 // stream; nothing here allocates, frees or waits on the device.
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 #include <stdio.h>
@@ -40,6 +40,7 @@ long tile_capacity(const moe_config& c, int bm) {
 }
 
 struct Plan {
+  GemmPick up, down;
   int bm_up, bm_down;
   int cap_up, cap_down;
   size_t total;
@@ -54,8 +55,14 @@ enum {
 Plan make_plan(const moe_config& c) {
   Plan p{};
   const long rows_per_expert = static_cast<long>(c.T) * c.top_k / c.n_experts;
-  p.bm_up = pick_bm_up(c.dtype, rows_per_expert);
-  p.bm_down = pick_bm_down(c.dtype, rows_per_expert);
+  const size_t eb_ = c.dtype == MOE_BF16 ? 2 : 4;
+  const size_t rows_all = static_cast<size_t>(c.T) * (c.top_k + c.n_shared);
+  const size_t w_mat = static_cast<size_t>(c.d_model) * c.d_ff * eb_;
+  p.up = pick_gemm(c.dtype, true, rows_per_expert, static_cast<size_t>(c.T) * c.d_model * eb_,
+                   w_mat);
+  p.down = pick_gemm(c.dtype, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat);
+  p.bm_up = p.up.bm;
+  p.bm_down = p.down.bm;
   p.cap_up = static_cast<int>(tile_capacity(c, p.bm_up));
   p.cap_down = static_cast<int>(tile_capacity(c, p.bm_down));
   const size_t T = c.T, N = c.n_experts, k = c.top_k, S = c.n_shared;
@@ -274,7 +281,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   up.k_dim = c.d_model;
   up.n_dim = c.d_ff;
   up.tiles_cap = p.cap_up;
-  if ((err = launch_gemm_up(c.dtype, up, p.bm_up, s)) != hipSuccess)
+  if ((err = launch_gemm(c.dtype, true, p.up, up, s)) != hipSuccess)
     return hip_fail(err, "gate/up GEMM");
 
   mark(ev, MOE_STAGE_EXPERT_DOWN, s);
@@ -292,7 +299,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   dn.k_dim = c.d_ff;
   dn.n_dim = c.d_model;
   dn.tiles_cap = p.cap_down;
-  if ((err = launch_gemm_down(c.dtype, dn, p.bm_down, s)) != hipSuccess)
+  if ((err = launch_gemm(c.dtype, false, p.down, dn, s)) != hipSuccess)
     return hip_fail(err, "down GEMM");
 
   mark(ev, MOE_STAGE_COMBINE, s);

@@ -77,10 +77,19 @@ struct GemmArgs {
   int tiles_cap;             // grid rows
 };
 
-hipError_t launch_gemm_up(int dtype, const GemmArgs& g, int bm, hipStream_t s);
-hipError_t launch_gemm_down(int dtype, const GemmArgs& g, int bm, hipStream_t s);
-int pick_bm_up(int dtype, long rows_per_expert);
-int pick_bm_down(int dtype, long rows_per_expert);
+// Kernel choice for one grouped GEMM: variant 0 = register-staged tiles
+// (grouped_gemm.hip, fp32 and few-row shapes), 1 = large direct-to-LDS bf16
+// tiles (expert_gemm.hip); bm = rows per tile (the tile list's granularity).
+struct GemmPick {
+  int variant;
+  int bm;
+};
+// a_bytes / w_bytes: bytes of the A operand (all its rows) and of one expert's
+// weight matrix; the direct-to-LDS kernel addresses both with 32-bit offsets.
+GemmPick pick_gemm(int dtype, bool gated, long rows_per_expert, size_t a_bytes, size_t w_bytes);
+hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
+hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
+hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_combine(int dtype, const void* yperm, const int32_t* inv_row,
                           const float* topk_gate, int T, int d, int k, int S,
