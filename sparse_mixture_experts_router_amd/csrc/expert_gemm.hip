@@ -7,22 +7,25 @@
 //   plain  : Y[row, c] = (H Wd[e]^T)[row, c]
 // organised for the matrix cores and the LDS of a CDNA4 compute unit:
 //
-//  * one workgroup = 4 wavefronts owns a BM x BNE tile (BNE effective
-//    columns: for the gated pass half are gate rows and half are up rows of
-//    the same output columns, so SiLU(gate) * up is formed in registers);
-//  * operands arrive in LDS through global_load_lds_dwordx4 (16 bytes per
-//    lane straight from global memory into LDS, no register staging), two
-//    stages, one barrier per K step; each lane fetches the chunk that lands
-//    in its slot of an XOR-swizzled 128-byte row so that the ds_read_b128
-//    fragment reads of the MFMA loop are spread over all banks;
-//  * each wavefront computes a (BM / WM) x (BNE / WN) block with
-//    v_mfma_f32_16x16x32_bf16, so every 16-byte fragment read from LDS feeds
-//    BNE / WN / 16 (A) or BM / WM / 16 (B) MFMAs;
+//  * one workgroup = 4 wavefronts (2 x 2) owns a BM x BNE tile; BNE counts
+//    effective columns: for the gated pass half are gate rows and half up rows
+//    of the same output columns, so SiLU(gate) * up is formed in registers;
+//  * each wavefront accumulates a (BM/2) x (BNE/2) block with
+//    v_mfma_f32_16x16x32_bf16 into AGPRs (256 of them for a 256 x 256 tile),
+//    so each 16-byte LDS fragment feeds 8 MFMAs;
+//  * operands go global -> LDS with global_load_lds_dwordx4 (no register
+//    staging) into a ring of STAGES buffers of 32 K-elements (64 bytes of
+//    every row), with the 16-byte chunks of a row XOR-swizzled by row so the
+//    fragment reads are free of bank conflicts;
+//  * per K step a wavefront runs the first half of its MFMAs, then waits for
+//    the next stage and meets the other wavefronts at one barrier, then runs
+//    the second half while it reads the next step's fragments into a second
+//    register set, so neither the barrier nor the LDS latency leaves the
+//    matrix cores idle;
 //  * blocks are renumbered so that each of the 8 XCDs (which take workgroups
-//    round-robin) works through a contiguous range of the (row tile, column
-//    tile) order, in which consecutive tiles share a weight tile: the row
-//    tiles of one expert read the same weights while they are in that XCD's
-//    L2.
+//    round-robin) works through a contiguous range of (row tile, column tile)
+//    pairs ordered by bands of column tiles: the workgroups one XCD runs at a
+//    time share their A rows and weight rows in its L2.
 #include "mfma.h"
 
 namespace moe {
@@ -35,34 +38,71 @@ __device__ __forceinline__ void load_lds16(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)(src), (lds_void_ptr)(lds_dst), 16, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding:
+// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt untouched (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
 
-template <bool GATED, int BM, int BNE, int WM, int WN>
+// Workgroup barrier that does not drain outstanding global->LDS loads
+// (__syncthreads() would wait for all of them and serialise the ring).
+// Callers first wait for exactly the loads they need with wait_vmem<N>().
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kRowBytes = 64;  // bytes of every staged row per K step (32 bf16)
+
+// Byte offset of 16-byte chunk c (0..3) of staged row r: 64-byte rows, chunk
+// index XOR-ed with bits 1-2 of the row, so the 8 lanes of a ds_read_b128
+// group (8 consecutive rows, same logical chunk) hit 8 distinct bank groups.
+__device__ __forceinline__ int swz64(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 3)) << 4); }
+
+template <bool GATED, int BM, int BNE, int STAGES>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
-  constexpr int ROWB = 128;                 // bytes of every row per K step (64 bf16)
-  constexpr int ROWS = BM + BNE;            // rows staged per K step
-  constexpr int STAGE = ROWS * ROWB;
-  constexpr int BLOCKS = ROWS / 8;          // 1 KB LDS blocks per stage
-  constexpr int WTM = BM / WM, WTN = BNE / WN;
-  constexpr int MB = WTM / 16, NB = WTN / 16;
-  constexpr int NOUT = GATED ? NB / 2 : NB; // output column blocks per wave
-  constexpr int COLS = GATED ? BNE / 2 : BNE;   // output columns per tile
-  static_assert(WM * WN == 4 && BLOCKS % 4 == 0 && BM % 32 == 0 && BNE % 32 == 0,
-                "4 wavefronts, whole blocks");
-  static_assert(!GATED || (BNE / 2) % (BNE / 32 * 8) == 0, "a wave's B blocks are all gate or all up");
-  static_assert(!GATED || NB % 2 == 0, "gated tiles pair gate and up blocks");
+  constexpr int ROWS = BM + BNE;               // rows staged per K step
+  constexpr int STAGE = ROWS * kRowBytes;      // bytes per ring buffer
+  constexpr int WTM = BM / 2, WTN = BNE / 2;   // wavefront block
+  constexpr int MB = WTM / 16, NB = WTN / 16;  // 16 x 16 MFMA blocks
+  constexpr int NOUT = GATED ? NB / 2 : NB;    // output column blocks per wavefront
+  constexpr int COLS = GATED ? BNE / 2 : BNE;  // output columns per tile
+  constexpr int A_BPW = BM / 64, B_BPW = BNE / 64;  // 1 KB load blocks per wavefront
+  constexpr int LPS = A_BPW + B_BPW;           // loads per lane per K step
+  constexpr int NF = MB + NB;                  // fragments per K step
+  // Column tiles per band (see the header): about 32 / kBandCols row tiles of
+  // one expert run next to kBandCols weight tiles on an XCD.
+  constexpr int kBandCols = BM >= 256 ? 8 : 4;
+  static_assert(BM % 64 == 0 && BNE % 64 == 0 && STAGES >= 3 && STAGES <= 4, "tile shape");
+  static_assert(!GATED || (COLS % (B_BPW * 16) == 0 && NB % 2 == 0),
+                "a wavefront's B blocks are all gate or all up rows");
+  static_assert(2 * LPS < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   // ------------------------------------------------------- tile of this block
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
   const int lin = xcd * xq + min(xcd, xr) + (bid >> 3);
-  const int tile = lin % g.tiles_cap;
-  const int nt = lin / g.tiles_cap;
+  const int n_nt = (g.n_dim + COLS - 1) / COLS;
+  const int full_bands = n_nt / kBandCols;
+  const int band_blocks = g.tiles_cap * kBandCols;
+  int tile, nt;
+  if (lin < full_bands * band_blocks) {
+    const int band = lin / band_blocks, rem = lin - band * band_blocks;
+    tile = rem / kBandCols;
+    nt = band * kBandCols + rem % kBandCols;
+  } else {
+    const int rem = lin - full_bands * band_blocks, gn = n_nt - full_bands * kBandCols;
+    tile = rem / gn;
+    nt = full_bands * kBandCols + rem % gn;
+  }
   if (tile >= *g.ntiles) return;
   const int2 te = g.tiles[tile];
   const int e = te.x, m0 = te.y;
@@ -70,8 +110,10 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
   const int n0 = nt * COLS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform, so LDS destinations (M0) and bases live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
 
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
   const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
@@ -82,35 +124,67 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
                          : nullptr;
 
   // ------------------------------------------ this lane's global sources
-  // Staged rows: A rows 0 .. BM-1 (BM/8 blocks of 8 rows), then B rows (for
-  // the gated pass: COLS gate rows, then COLS up rows).  Each wavefront loads
-  // BM/32 A blocks and BNE/32 B blocks; lane l fills physical chunk l % 8 of
-  // row l / 8 of a block, i.e. logical chunk (l % 8) ^ (l / 8) of that row.
-  // Sources are a wave-uniform base plus a 32-bit per-lane byte offset (the
-  // host keeps every operand below 4 GiB per base).
-  constexpr int A_BPW = BM / 32, B_BPW = BNE / 32;
-  const int lchunk = (lane & 7) ^ (lane >> 3);
+  // A 1 KB load block holds 16 staged rows of 64 bytes; lane l fills physical
+  // chunk l % 4 of row l / 4 of the block, i.e. logical chunk
+  // (l % 4) ^ ((l / 8) % 4) of that row.  Staged rows: A rows 0 .. BM-1, then
+  // B rows (gated: COLS gate rows, then COLS up rows).  Wavefront w loads A
+  // blocks w*A_BPW .. and B blocks w*B_BPW ..; sources are a wave-uniform
+  // base plus a 32-bit per-lane byte offset (the host keeps every operand
+  // below 4 GiB per base).
+  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
   const char* const a_base = reinterpret_cast<const char*>(g.a);
   uint32_t a_off[A_BPW];
 #pragma unroll
   for (int j = 0; j < A_BPW; ++j) {
-    const int R = (wave * A_BPW + j) * 8 + (lane >> 3);
+    const int R = (wave * A_BPW + j) * 16 + (lane >> 2);
     const int grow = seg + m0 + min(R, mvalid - 1);
     const int srow = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
     a_off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) + lchunk * 16;
   }
-  // B blocks of this wave: rows jb0 .. jb0 + 8*B_BPW - 1 of the B part; in the
-  // gated pass waves 0-1 hold gate rows and waves 2-3 up rows.
-  const int jb0 = wave * B_BPW * 8;
+  const int jb0 = wave * B_BPW * 16;
   const bool up_rows = GATED && jb0 >= COLS;
   const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
   uint32_t b_off[B_BPW];
 #pragma unroll
   for (int j = 0; j < B_BPW; ++j) {
-    const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? COLS : 0);
+    const int jb = jb0 + j * 16 + (lane >> 2) - (up_rows ? COLS : 0);
     const int n = min(n0 + jb, g.n_dim - 1);
     b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) + lchunk * 16;
   }
+  const int a_dst = wave * A_BPW * 1024;
+  const int b_dst = BM * kRowBytes + wave * B_BPW * 1024;
+
+  const int nsteps = static_cast<int>(row_bytes / kRowBytes);  // even: K is a multiple of 64
+  // Loads of K step `step` into ring buffer step % STAGES.  Steps past the end
+  // re-read the last step (valid addresses) into a buffer nobody reads again,
+  // so every K step issues the same number of loads and the wait counts below
+  // hold without branches.
+  // load l (0 .. LPS-1) of K step `step`: A blocks first, then B blocks
+  auto issue_one = [&](int step, int l) {
+    const uint32_t koff = static_cast<uint32_t>(min(step, nsteps - 1)) * kRowBytes;
+    char* const st = smem + (step % STAGES) * STAGE;
+    if (l < A_BPW) load_lds16(a_base + (a_off[l] + koff), st + a_dst + l * 1024);
+    else load_lds16(b_base + (b_off[l - A_BPW] + koff), st + b_dst + (l - A_BPW) * 1024);
+  };
+  auto issue = [&](int step) {
+#pragma unroll
+    for (int l = 0; l < LPS; ++l) issue_one(step, l);
+  };
+
+  // LDS byte offset (inside a stage) of fragment f: A blocks 0..MB-1, then
+  // B blocks (gated: NOUT gate blocks, then NOUT up blocks of the same columns)
+  const int frow = lane & 15, fchunk = lane >> 4;
+  auto frag_off = [&](int f) {
+    int r;
+    if (f < MB) {
+      r = wm * WTM + f * 16 + frow;
+    } else {
+      const int j = f - MB;
+      if (GATED) r = BM + (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16 + frow;
+      else r = BM + wn * WTN + j * 16 + frow;
+    }
+    return swz64(r, fchunk);
+  };
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -118,52 +192,62 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // LDS row of B fragment block j for this wave
-  auto b_row = [&](int j) {
-    if (GATED) {
-      const int half = j < NOUT ? 0 : COLS;
-      const int jj = j < NOUT ? j : j - NOUT;
-      return BM + half + wn * (WTN / 2) + jj * 16 + (lane & 15);
-    }
-    return BM + wn * WTN + j * 16 + (lane & 15);
-  };
+  u32x4 fr[2][NF];  // fragments of the current and of the next K step
 
-  const int nsteps = static_cast<int>(row_bytes / ROWB);
-  char* const a_lds = smem + wave * A_BPW * 1024;
-  char* const b_lds = smem + BM * ROWB + wave * B_BPW * 1024;
-  auto issue = [&](int step, int buf) {
-    const uint32_t koff = static_cast<uint32_t>(step) * ROWB;
+  // prologue: steps 0 .. STAGES-2 in flight, step 0's fragments in fr[0]
 #pragma unroll
-    for (int j = 0; j < A_BPW; ++j)
-      load_lds16(a_base + (a_off[j] + koff), a_lds + buf * STAGE + j * 1024);
+  for (int p = 0; p < STAGES - 1; ++p) issue(p);
+  wait_vmem<(STAGES - 2) * LPS>();
+  stage_barrier();
 #pragma unroll
-    for (int j = 0; j < B_BPW; ++j)
-      load_lds16(b_base + (b_off[j] + koff), b_lds + buf * STAGE + j * 1024);
-  };
-  issue(0, 0);
+  for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f));
 
-  for (int s = 0; s < nsteps; ++s) {
-    wait_vmem_all();
-    __syncthreads();
-    if (s + 1 < nsteps) issue(s + 1, (s + 1) & 1);
-    const char* st = smem + (s & 1) * STAGE;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int ch = kc * 4 + (lane >> 4);
-      u32x4 af[MB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(st + lds_swz(wm * WTM + i * 16 + (lane & 15), ch));
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const u32x4 bf = *reinterpret_cast<const u32x4*>(st + lds_swz(b_row(j), ch));
-#pragma unroll
-        for (int i = 0; i < MB; ++i) acc[i][j] = Mfma<bf16_t>::step(af[i], bf, acc[i][j]);
-      }
-    }
+  // One K step (fr[P] holds step s's fragments): issue step s + STAGES - 1
+  // (its ring buffer was last read in step s - 1, before that step's
+  // barrier); the first half of the MFMAs; wait until step s + 1 has landed
+  // (only the STAGES - 2 younger steps may still be in flight) and meet at the
+  // barrier; the second half of the MFMAs interleaved with step s + 1's
+  // fragment reads into fr[P ^ 1].  In the last step those reads fetch data
+  // that is never used.
+  constexpr int HALF = NB / 2;
+  constexpr int PER = (MB * HALF) / NF > 0 ? (MB * HALF) / NF : 1;
+  constexpr int LPER = (MB * HALF) / LPS > 0 ? (MB * HALF) / LPS : 1;  // MFMAs per load issue
+  static_assert((MB * HALF) / LPER >= LPS, "every load of the step is issued in the first half");
+#define MOE_KSTEP(P)                                                                     \
+  {                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                   \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
+        mfma_bf16_agpr(acc[i][j], fr[P][i], fr[P][MB + j]);                              \
+        const int q = j * MB + i;                                                        \
+        if (q % LPER == 0 && q / LPER < LPS) issue_one(s + STAGES - 1, q / LPER);        \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+      }                                                                                  \
+    }                                                                                    \
+    wait_vmem<(STAGES - 2) * LPS>();                                                     \
+    stage_barrier();                                                                     \
+    const char* st = smem + ((s + 1) % STAGES) * STAGE;                                  \
+    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                  \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
+        mfma_bf16_agpr(acc[i][j], fr[P][i], fr[P][MB + j]);                              \
+        const int q = (j - HALF) * MB + i;                                               \
+        if (q % PER == PER - 1 && q / PER < NF)                                          \
+          fr[P ^ 1][q / PER] = *reinterpret_cast<const u32x4*>(st + frag_off(q / PER));  \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+      }                                                                                  \
+    }                                                                                    \
+    _Pragma("unroll") for (int r = (MB * HALF) / PER; r < NF; ++r)                       \
+      fr[P ^ 1][r] = *reinterpret_cast<const u32x4*>(st + frag_off(r));                  \
+    ++s;                                                                                 \
   }
 
+  for (int s = 0; s < nsteps;) {
+    MOE_KSTEP(0)
+    MOE_KSTEP(1)
+  }
+#undef MOE_KSTEP
+
   // -------------------------------------------------------------- epilogue
+  mfma_drain();
   bf16_t* out = static_cast<bf16_t*>(g.out);
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -179,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
         float v;
         if (GATED) {
           const float a = acc[i][j][r];
-          v = a / (1.0f + __expf(-a)) * acc[i][j + NOUT][r];
+          v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
         } else {
           v = acc[i][j][r];
         }
@@ -189,25 +273,26 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <bool GATED, int BM, int BNE, int WM, int WN>
+template <bool GATED, int BM, int BNE, int STAGES>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long n_nt = (g.n_dim + COLS - 1) / COLS;
   const long blocks = static_cast<long>(g.tiles_cap) * n_nt;
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, WM, WN>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(256), 0, s, g);
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, STAGES>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s) {
-  if (gated) {
-    if (bm == 256) return launch_v<true, 256, 256, 2, 2>(g, s);
-    return launch_v<true, 128, 256, 2, 2>(g, s);
+  if (bm == 256) {
+    if (gated) return launch_v<true, 256, 256, 4>(g, s);
+    return launch_v<false, 256, 256, 4>(g, s);
   }
-  if (bm == 256) return launch_v<false, 256, 256, 2, 2>(g, s);
-  return launch_v<false, 128, 256, 2, 2>(g, s);
+  if (bm != 128) return hipErrorInvalidValue;
+  if (gated) return launch_v<true, 128, 256, 4>(g, s);
+  return launch_v<false, 128, 256, 4>(g, s);
 }
 
 }  // namespace moe

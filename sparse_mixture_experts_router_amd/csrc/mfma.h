@@ -37,6 +37,19 @@ template <> struct Mfma<float> {
   }
 };
 
+// The same bf16 step with the accumulator pinned to AGPRs.  Used where a
+// wavefront holds 256 accumulator registers: the compiler's own MFMA form would
+// split them between VGPRs and AGPRs and copy them back and forth every
+// iteration.  Because the compiler cannot see that this asm is an MFMA, the
+// caller issues mfma_drain() before anything else reads the accumulators.
+__device__ __forceinline__ void mfma_bf16_agpr(f32x4& c, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA writing an accumulator and any other
+// instruction reading it (covers the longest 16x16x32 bf16 latency).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
