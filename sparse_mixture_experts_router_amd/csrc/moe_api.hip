@@ -23,6 +23,7 @@ moe_status hip_fail(hipError_t err, const char* where) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int R_COUNT_MAX = 32;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -41,14 +42,15 @@ long tile_capacity(const moe_config& c, int bm) {
 
 struct Plan {
   GemmPick up, down;
+  int ksplit;
   int bm_up, bm_down;
   int cap_up, cap_down;
   size_t total;
-  size_t off[17];
+  size_t off[R_COUNT_MAX];
 };
 
 enum {
-  R_IDX, R_GATE, R_LRANK, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
+  R_IDX, R_GATE, R_LRANK, R_PART, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
   R_TUP, R_TDN, R_NT, R_HID, R_YP, R_COUNT
 };
 
@@ -73,6 +75,8 @@ Plan make_plan(const moe_config& c) {
   sz[R_IDX] = T * k * 4;
   sz[R_GATE] = T * k * 4;
   sz[R_LRANK] = T * k * 4;
+  p.ksplit = route_split(c.T, c.d_model, c.dtype);
+  sz[R_PART] = p.ksplit > 1 ? static_cast<size_t>(p.ksplit) * T * N * 4 : 0;
   sz[R_BCNT] = B * N * 4;
   sz[R_BPS] = B * N * 4;
   sz[R_BBASE] = B * N * 4;
@@ -101,6 +105,7 @@ Workspace carve(const Plan& p, void* base) {
   w.topk_idx = reinterpret_cast<int32_t*>(b + p.off[R_IDX]);
   w.topk_gate = reinterpret_cast<float*>(b + p.off[R_GATE]);
   w.lrank = reinterpret_cast<int32_t*>(b + p.off[R_LRANK]);
+  w.route_partial = reinterpret_cast<float*>(b + p.off[R_PART]);
   w.blk_counts = reinterpret_cast<int32_t*>(b + p.off[R_BCNT]);
   w.blk_psum = reinterpret_cast<float*>(b + p.off[R_BPS]);
   w.blk_base = reinterpret_cast<int32_t*>(b + p.off[R_BBASE]);
@@ -171,8 +176,9 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
                      const moe_weights& w, moe_routing* out, int32_t* idx, float* gate,
                      hipStream_t s) {
   hipError_t err = launch_route(c.dtype, x, w.w_router, w.logit_bias, w.select_bias, c.T,
-                                c.d_model, c.n_experts, c.top_k, out ? out->logits : nullptr, idx,
-                                gate, ws.lrank, ws.blk_counts, ws.blk_psum, s);
+                                c.d_model, c.n_experts, c.top_k, p.ksplit, ws.route_partial,
+                                out ? out->logits : nullptr, idx, gate, ws.lrank, ws.blk_counts,
+                                ws.blk_psum, s);
   if (err != hipSuccess) return hip_fail(err, "route kernel");
   return MOE_OK;
 }

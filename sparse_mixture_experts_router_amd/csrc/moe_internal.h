@@ -24,6 +24,7 @@ struct Workspace {
   int32_t* topk_idx;   // [T, k]
   float* topk_gate;    // [T, k]
   int32_t* lrank;      // [T, k]     rank of the assignment inside its block
+  float* route_partial;// [ksplit, T, N] split-K partial logits
   int32_t* blk_counts; // [B, N]
   float* blk_psum;     // [B, N]
   int32_t* blk_base;   // [B, N]
@@ -41,11 +42,16 @@ struct Workspace {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.
+// Router GEMM + selection.  ksplit > 1 splits the reduction over workgroups
+// (few tokens): fp32 partial logits [ksplit, T, N] go to `partial` and a
+// second kernel sums them in a fixed order before the selection.
+int route_split(int T, int d, int dtype);
 hipError_t launch_route(int dtype, const void* x, const void* w_router,
                         const float* logit_bias, const float* select_bias,
-                        int T, int d, int N, int k, float* logits_out,
-                        int32_t* topk_idx, float* topk_gate, int32_t* lrank,
-                        int32_t* blk_counts, float* blk_psum, hipStream_t s);
+                        int T, int d, int N, int k, int ksplit, float* partial,
+                        float* logits_out, int32_t* topk_idx, float* topk_gate,
+                        int32_t* lrank, int32_t* blk_counts, float* blk_psum,
+                        hipStream_t s);
 
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
                        int N, int k, int S, int bm_up, int cap_up, int bm_down,

@@ -1,5 +1,4 @@
-// Routing kernel: router GEMM, top-k selection, gates and per-block statistics
-// in one launch.
+// Routing: router GEMM, top-k selection, gates and per-block statistics.
 //
 // Steps (pages: "Mixture of experts and speculative decoding", "Following one
 // token through an MoE layer" steps 1-3 and "Opening the hood: the MoE layer
@@ -15,23 +14,23 @@
 // block's assignments to the same expert (ordered by token), which the
 // grouping step turns into a row index.
 //
-// Layout: one workgroup of 4 wavefronts per 64 tokens.  Wave w computes the
-// 16 x N_pad logits of tokens 16w .. 16w+15 with 16x16 MFMA blocks; the router
-// weight slice (N_pad rows x 128 bytes) is staged once per K step in LDS and
-// shared by the 4 waves.  The logits then go through LDS so that each token's
-// N scores sit in one group of G = min(64, N_pad) lanes, where top-k runs as k
-// rounds of a butterfly arg-max over shuffles.
+// One workgroup (4 wavefronts) owns 64 tokens x N_pad experts.  The 64 x-rows
+// and the N_pad router rows stream through a global -> LDS ring (32 K-elements
+// per stage, direct 16-byte loads) into 16x16 MFMA blocks; for N_pad >= 64 the
+// wavefronts split the experts, otherwise the tokens.  With few tokens the
+// reduction dimension is split over workgroups as well (split-K): each writes
+// fp32 partial logits and a second kernel adds them in a fixed order, so the
+// logits (and hence the routing) stay deterministic.  The selection then runs
+// on the logits tile in LDS: each token's N scores sit in one group of 16
+// lanes (4 tokens per wavefront at a time), and top-k is k rounds of a
+// butterfly arg-max over __shfl_xor on a packed 64-bit (key, index) order.
+#include "lds_ring.h"
 #include "mfma.h"
 
 #include <math.h>
 
 namespace moe {
 namespace {
-
-// a before b in the selection order: higher key, equal keys -> lower index.
-__device__ __forceinline__ bool before(float ka, int ea, float kb, int eb) {
-  return ka > kb || (ka == kb && ea < eb);
-}
 
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
@@ -47,98 +46,70 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <typename T, int NB>
-__global__ __launch_bounds__(256) void route_kernel(
-    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ logit_bias,
-    const float* __restrict__ select_bias, int n_tok, int d, int N, int k,
-    float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, int32_t* __restrict__ lrank,
-    int32_t* __restrict__ blk_counts, float* __restrict__ blk_psum) {
-  constexpr int NP = NB * 16;          // experts padded to the MFMA block
-  constexpr int ROWB = 128;            // bytes of a row slice per K step
-  constexpr int G = NP < 64 ? NP : 64; // lanes per token in the selection
-  constexpr int EPL = NP / G;          // experts per lane
-  constexpr int TPW = 64 / G;          // tokens a wave selects at once
-  constexpr int LD = NP + 1;           // fp32 logits row stride in LDS
-  constexpr int TILE_BYTES = NP * ROWB;
-  constexpr int LOGIT_BYTES = kRouteTokens * LD * 4;
-  constexpr int UNION_BYTES = TILE_BYTES > LOGIT_BYTES ? TILE_BYTES : LOGIT_BYTES;
+// Compile-time layout of one routing workgroup for NB 16-expert blocks.
+template <int NB>
+struct RouteShape {
+  static constexpr int NP = NB * 16;                    // experts padded to 16
+  static constexpr int G = 16;                          // lanes per token in the selection
+  static constexpr int EPL = NP / G;                    // experts per lane (= NB)
+  static constexpr int TPW = 64 / G;                    // tokens a wave selects at once
+  static constexpr int LD = NP + 1;                     // fp32 logits row stride in LDS
+  static constexpr int WE = NB < 4 ? NB : 4;            // wavefronts across experts
+  static constexpr int WT = 4 / WE;                     // wavefronts across tokens
+  static constexpr int TB = 4 / WT;                     // 16-token blocks per wavefront
+  static constexpr int EB = NB / WE;                    // 16-expert blocks per wavefront
+  static constexpr int BLOCKS = (4 + NB + 3) / 4 * 4;   // 1 KB ring blocks per stage
+  static constexpr int LPW = BLOCKS / 4;                // loads per lane per K step
+  static constexpr int STAGES = NB >= 32 ? 3 : 4;
+  static constexpr int STAGE = BLOCKS * 1024;
+  static constexpr int RING = STAGES * STAGE;
+  static constexpr int LOGITS = kRouteTokens * LD * 4;
+  static constexpr int UNION = RING > LOGITS ? RING : LOGITS;
+  static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8 || NB == 16 || NB == 32, "NB");
+};
 
-  __shared__ __attribute__((aligned(16))) char s_union[UNION_BYTES];
-  __shared__ uint32_t s_mask[NP][2];             // tokens of the block that chose e
-  __shared__ float s_psum[4 * TPW * NP];         // per (wave, group) probability sums
-  __shared__ int32_t s_sel[kRouteTokens * kMaxTopK];
+// Selection order as one integer: higher key first, equal keys (IEEE, so the
+// key is normalised from -0 to +0) -> lower expert index first.  The fp32 key
+// is mapped to an order-preserving uint32 in the high half; the low half is
+// the complement of the index.  0 sorts below every real expert.
+__device__ __forceinline__ uint64_t order_key(float key, int e) {
+  uint32_t u = __float_as_uint(key + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int t0 = blockIdx.x * kRouteTokens;
-
-  for (int i = tid; i < NP * 2; i += 256) (&s_mask[0][0])[i] = 0u;
-
-  // ------------------------------------------------------------ router GEMM
-  const size_t row_bytes = static_cast<size_t>(d) * sizeof(T);
-  const int nsteps = static_cast<int>(row_bytes / ROWB);
-  const int ta = t0 + wave * 16 + (lane & 15);
-  const bool a_ok = ta < n_tok;
-  const char* a_row = reinterpret_cast<const char*>(x) +
-                      static_cast<size_t>(a_ok ? ta : 0) * row_bytes + 16 * (lane >> 4);
-  const char* w_bytes = reinterpret_cast<const char*>(wr);
-
-  f32x4 acc[NB];
+__device__ __forceinline__ uint64_t group16_max(uint64_t v) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int s = 0; s < nsteps; ++s) {
-    for (int c = tid; c < NP * 8; c += 256) {
-      const int row = c >> 3, ch = c & 7;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row < N)
-        v = *reinterpret_cast<const u32x4*>(w_bytes + static_cast<size_t>(row) * row_bytes +
-                                            static_cast<size_t>(s) * ROWB + ch * 16);
-      *reinterpret_cast<u32x4*>(s_union + lds_swz(row, ch)) = v;
-    }
-    u32x4 a0 = u32x4{0u, 0u, 0u, 0u}, a1 = a0;
-    if (a_ok) {
-      a0 = *reinterpret_cast<const u32x4*>(a_row + static_cast<size_t>(s) * ROWB);
-      a1 = *reinterpret_cast<const u32x4*>(a_row + static_cast<size_t>(s) * ROWB + 64);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int row = j * 16 + (lane & 15);
-      const u32x4 b0 = *reinterpret_cast<const u32x4*>(s_union + lds_swz(row, lane >> 4));
-      const u32x4 b1 = *reinterpret_cast<const u32x4*>(s_union + lds_swz(row, 4 + (lane >> 4)));
-      acc[j] = Mfma<T>::step(a0, b0, acc[j]);
-      acc[j] = Mfma<T>::step(a1, b1, acc[j]);
-    }
-    __syncthreads();
+  for (int off = 8; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
   }
+  return v;
+}
 
-  // ------------------------------------------------------- logits to LDS
-  float* s_logit = reinterpret_cast<float*>(s_union);
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int e = j * 16 + (lane & 15);
-    const float lb = (logit_bias != nullptr && e < N) ? logit_bias[e] : 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tt = wave * 16 + 4 * (lane >> 4) + r;
-      const float v = acc[j][r] + lb;
-      s_logit[tt * LD + e] = v;
-      if (logits_out != nullptr && e < N && t0 + tt < n_tok)
-        logits_out[static_cast<size_t>(t0 + tt) * N + e] = v;
-    }
-  }
-  __syncthreads();
-
-  // ------------------------------------------------------------- selection
+// ---------------------------------------------------------------- selection
+// Top-k, gates, block statistics and ranks for the 64-token tile whose fp32
+// logits (logit_bias included) are in s_logit[tt * LD + e].  A group of 16
+// lanes handles one token (4 tokens per wavefront at a time); lane gl holds
+// experts gl, gl + 16, ...
+template <int NB>
+__device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_tok, int N, int k,
+                            const float* __restrict__ select_bias, int32_t* __restrict__ topk_idx,
+                            float* __restrict__ topk_gate, int32_t* __restrict__ lrank,
+                            int32_t* __restrict__ blk_counts, float* __restrict__ blk_psum,
+                            uint32_t (*s_mask)[2], float* s_psum, int32_t* s_sel) {
+  using S = RouteShape<NB>;
+  constexpr int G = S::G, EPL = S::EPL, TPW = S::TPW, LD = S::LD, NP = S::NP;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / G;
   const int gl = lane % G;
   float psum[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) psum[i] = 0.f;
 
+#pragma unroll 1
   for (int base = 0; base < 16; base += TPW) {
     const int tt = wave * 16 + base + grp;  // token inside the block
     const int t = t0 + tt;
@@ -148,13 +119,8 @@ __global__ __launch_bounds__(256) void route_kernel(
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = gl + G * i;
-      if (e < N) {
-        r[i] = s_logit[tt * LD + e];
-        key[i] = select_bias != nullptr ? __fadd_rn(r[i], select_bias[e]) : r[i];
-      } else {
-        r[i] = -INFINITY;
-        key[i] = -INFINITY;
-      }
+      r[i] = e < N ? s_logit[tt * LD + e] : -INFINITY;
+      key[i] = (e < N && select_bias != nullptr) ? __fadd_rn(r[i], select_bias[e]) : r[i];
     }
 
     // router probabilities over all N experts (balance statistic P)
@@ -162,56 +128,42 @@ __global__ __launch_bounds__(256) void route_kernel(
 #pragma unroll
     for (int i = 0; i < EPL; ++i) m = fmaxf(m, r[i]);
     m = group_max<G>(m);
-    float ex[EPL], se = 0.f;
+    float se = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      ex[i] = (gl + G * i < N) ? expf(r[i] - m) : 0.f;
-      se += ex[i];
+      // exp2-based exponential: the statistic P tolerates its ~1e-7 relative error
+      r[i] = (gl + G * i < N) ? __expf(r[i] - m) : 0.f;  // r now holds exp(r - m)
+      se += r[i];
     }
     se = group_sum<G>(se);
     if (tok_ok) {
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) psum[i] += ex[i] / se;
+      for (int i = 0; i < EPL; ++i) psum[i] += r[i] / se;
     }
 
-    // k rounds of arg-max over the group
+    // k rounds of arg-max over the group; the owner lane marks the winner
+    // taken; lane s keeps the winner of round s
     uint32_t taken = 0u;
     int slot_e = 0;
-    float slot_r = -INFINITY;
+#pragma unroll 1
     for (int s = 0; s < k; ++s) {
-      float bk = -INFINITY;
-      int be = 0x7fffffff;
-      float br = 0.f;
+      uint64_t best = 0ull;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = gl + G * i;
-        if (e < N && !((taken >> i) & 1u) && before(key[i], e, bk, be)) {
-          bk = key[i];
-          be = e;
-          br = r[i];
-        }
+        const uint64_t o = (e < N && !((taken >> i) & 1u)) ? order_key(key[i], e) : 0ull;
+        best = o > best ? o : best;
       }
-#pragma unroll
-      for (int off = G / 2; off >= 1; off >>= 1) {
-        const float ok = __shfl_xor(bk, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        const float orr = __shfl_xor(br, off, 64);
-        if (before(ok, oe, bk, be)) {
-          bk = ok;
-          be = oe;
-          br = orr;
-        }
-      }
+      best = group16_max(best);
+      const int be = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
       if (be % G == gl) taken |= 1u << (be / G);
-      if (gl == s) {
-        slot_e = be;
-        slot_r = br;
-      }
+      if (gl == s) slot_e = be;
     }
 
     // gates: softmax over the kept (unbiased) logits, slot s held by lane s
     const bool holds = gl < k;
-    const float gm = group_max<G>(holds ? slot_r : -INFINITY);
+    const float slot_r = holds ? s_logit[tt * LD + slot_e] : -INFINITY;
+    const float gm = group_max<G>(slot_r);
     const float ge = holds ? expf(slot_r - gm) : 0.f;
     const float gs = group_sum<G>(ge);
     if (tok_ok && holds) {
@@ -223,8 +175,16 @@ __global__ __launch_bounds__(256) void route_kernel(
     }
   }
 
+  // add the 4 lane groups of the wavefront (fixed order), then one row per wave
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) s_psum[(wave * TPW + grp) * NP + gl + G * i] = psum[i];
+  for (int i = 0; i < EPL; ++i) {
+    psum[i] += __shfl_xor(psum[i], 16, 64);
+    psum[i] += __shfl_xor(psum[i], 32, 64);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s_psum[wave * NP + gl + G * i] = psum[i];
+  }
   __syncthreads();
 
   // ---------------------------------------------- block statistics and ranks
@@ -241,50 +201,251 @@ __global__ __launch_bounds__(256) void route_kernel(
     blk_counts[static_cast<size_t>(blockIdx.x) * N + e] =
         __popc(s_mask[e][0]) + __popc(s_mask[e][1]);
     float acc_p = 0.f;
-    for (int w = 0; w < 4 * TPW; ++w) acc_p += s_psum[w * NP + e];
+    for (int w = 0; w < 4; ++w) acc_p += s_psum[w * NP + e];
     blk_psum[static_cast<size_t>(blockIdx.x) * N + e] = acc_p;
   }
 }
 
+struct RouteArgs {
+  const void* x;
+  const void* wr;
+  const float* logit_bias;
+  const float* select_bias;
+  int n_tok, d, N, k;
+  int ksplit;             // workgroups along the reduction dimension
+  int steps_per_split;    // K steps (64-byte row slices) per split
+  float* partial;         // [ksplit, T, N] when ksplit > 1
+  float* logits_out;      // [T, N] or NULL
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* lrank;
+  int32_t* blk_counts;
+  float* blk_psum;
+};
+
+// Router GEMM on a global -> LDS ring; FUSED: followed by the selection.
+template <typename T, int NB, bool FUSED>
+__global__ __launch_bounds__(256) void route_gemm_kernel(RouteArgs a) {
+  using S = RouteShape<NB>;
+  constexpr int NP = S::NP, LD = S::LD, STAGES = S::STAGES, STAGE = S::STAGE, LPW = S::LPW;
+  constexpr int TB = S::TB, EB = S::EB;
+
+  __shared__ __attribute__((aligned(1024))) char s_union[S::UNION];
+  __shared__ uint32_t s_mask[NP][2];             // tokens of the block that chose e
+  __shared__ float s_psum[4 * NP];               // per-wavefront probability sums
+  __shared__ int32_t s_sel[kRouteTokens * kMaxTopK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int ks = blockIdx.y;
+  if (FUSED)
+    for (int i = tid; i < NP * 2; i += 256) (&s_mask[0][0])[i] = 0u;
+
+  // ------------------------------------------------------------ router GEMM
+  const size_t row_bytes = static_cast<size_t>(a.d) * sizeof(T);
+  const int nsteps = static_cast<int>(row_bytes / kRowBytes);
+  const int k0 = ks * a.steps_per_split;
+  const int nloc = min(a.steps_per_split, nsteps - k0);
+
+  // ring block b: rows 16b .. 16b+15 of the stage; blocks 0-3 hold the 64
+  // token rows, blocks 4 .. 4+NB-1 the router rows, the rest repeat block 0
+  const int lchunk = ring_lane_chunk(lane);
+  const char* src[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int b = wave * LPW + j;
+    const int row = (b < 4 + NB ? b : 0) * 16 + (lane >> 2);
+    const char* p;
+    if (row < 64) {
+      const int t = min(t0 + row, a.n_tok - 1);
+      p = reinterpret_cast<const char*>(a.x) + static_cast<size_t>(t) * row_bytes;
+    } else {
+      const int e = min(row - 64, a.N - 1);
+      p = reinterpret_cast<const char*>(a.wr) + static_cast<size_t>(e) * row_bytes;
+    }
+    src[j] = p + static_cast<size_t>(k0) * kRowBytes + lchunk * 16;
+  }
+  auto issue = [&](int step) {
+    const size_t koff = static_cast<size_t>(min(step, nloc - 1)) * kRowBytes;
+    char* st = s_union + (step % STAGES) * STAGE + wave * LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) load_lds16(src[j] + koff, st + j * 1024);
+  };
+
+  const int wt = wave / S::WE, we = wave % S::WE;
+  f32x4 acc[TB][EB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p) issue(p);
+  const int frow = lane & 15, fchunk = lane >> 4;
+  for (int s = 0; s < nloc; ++s) {
+    // step s has landed once only the STAGES - 2 younger steps are pending
+    wait_vmem<(STAGES - 2) * LPW>();
+    stage_barrier();
+    issue(s + STAGES - 1);  // into the buffer read in step s - 1
+    const char* st = s_union + (s % STAGES) * STAGE;
+    u32x4 af[TB], bf[EB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      af[i] = *reinterpret_cast<const u32x4*>(st + swz64((wt * TB + i) * 16 + frow, fchunk));
+#pragma unroll
+    for (int j = 0; j < EB; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(st + swz64(64 + (we * EB + j) * 16 + frow, fchunk));
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < EB; ++j) acc[i][j] = Mfma<T>::step(af[i], bf[j], acc[i][j]);
+  }
+  __syncthreads();  // drains the ring (tail re-reads included) before LDS reuse
+
+  // ----------------------------------------------- partial logits: out, done
+  if (!FUSED) {
+    float* part = a.partial + static_cast<size_t>(ks) * a.n_tok * a.N;
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int e = (we * EB + j) * 16 + frow;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + (wt * TB + i) * 16 + 4 * fchunk + r;
+          if (e < a.N && t < a.n_tok) part[static_cast<size_t>(t) * a.N + e] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
+  // ------------------------------------------------------- logits to LDS
+  float* s_logit = reinterpret_cast<float*>(s_union);
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = (we * EB + j) * 16 + frow;
+      const float lb = (a.logit_bias != nullptr && e < a.N) ? a.logit_bias[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = (wt * TB + i) * 16 + 4 * fchunk + r;
+        const float v = acc[i][j][r] + lb;
+        s_logit[tt * LD + e] = v;
+        if (a.logits_out != nullptr && e < a.N && t0 + tt < a.n_tok)
+          a.logits_out[static_cast<size_t>(t0 + tt) * a.N + e] = v;
+      }
+    }
+  __syncthreads();
+  select_tile<NB>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate, a.lrank,
+                  a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
+}
+
+// Sum of the split-K partial logits (fixed order) + logit_bias, then the
+// selection.
+template <int NB>
+__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
+  using S = RouteShape<NB>;
+  constexpr int NP = S::NP, LD = S::LD;
+  __shared__ float s_logit[kRouteTokens * LD];
+  __shared__ uint32_t s_mask[NP][2];
+  __shared__ float s_psum[4 * NP];
+  __shared__ int32_t s_sel[kRouteTokens * kMaxTopK];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouteTokens;
+  for (int i = tid; i < NP * 2; i += 256) (&s_mask[0][0])[i] = 0u;
+  for (int i = tid; i < kRouteTokens * NP; i += 256) {
+    const int tt = i / NP, e = i - tt * NP;
+    const int t = t0 + tt;
+    float v = 0.f;
+    if (t < a.n_tok && e < a.N) {
+      // loads issued in batches of 8, added in split order
+      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
+        float pv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          pv[q] = k0 + q < a.ksplit
+                      ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
+                      : 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (k0 + q < a.ksplit) v += pv[q];
+      }
+      if (a.logit_bias != nullptr) v += a.logit_bias[e];
+      if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t) * a.N + e] = v;
+    }
+    s_logit[tt * LD + e] = v;
+  }
+  __syncthreads();
+  select_tile<NB>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate, a.lrank,
+                  a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
+}
+
 template <typename T, int NB>
-hipError_t launch_route_t(const void* x, const void* w_router, const float* logit_bias,
-                          const float* select_bias, int T_, int d, int N, int k,
-                          float* logits_out, int32_t* topk_idx, float* topk_gate,
-                          int32_t* lrank, int32_t* blk_counts, float* blk_psum,
-                          hipStream_t s) {
-  const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL((route_kernel<T, NB>), dim3(blocks), dim3(256), 0, s,
-                     static_cast<const T*>(x), static_cast<const T*>(w_router), logit_bias,
-                     select_bias, T_, d, N, k, logits_out, topk_idx, topk_gate, lrank,
-                     blk_counts, blk_psum);
+hipError_t launch_nb(const RouteArgs& a, hipStream_t s) {
+  const int blocks = (a.n_tok + kRouteTokens - 1) / kRouteTokens;
+  if (a.ksplit == 1) {
+    hipLaunchKernelGGL((route_gemm_kernel<T, NB, true>), dim3(blocks, 1), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((route_gemm_kernel<T, NB, false>), dim3(blocks, a.ksplit), dim3(256), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((route_select_kernel<NB>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_route_d(int N, const void* x, const void* w_router, const float* lb,
-                          const float* sb, int T_, int d, int k, float* lo, int32_t* idx,
-                          float* gate, int32_t* lrank, int32_t* bc, float* bp,
-                          hipStream_t s) {
-  if (N <= 16) return launch_route_t<T, 1>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
-  if (N <= 32) return launch_route_t<T, 2>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
-  if (N <= 64) return launch_route_t<T, 4>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
-  if (N <= 128) return launch_route_t<T, 8>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
-  if (N <= 256) return launch_route_t<T, 16>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
-  return launch_route_t<T, 32>(x, w_router, lb, sb, T_, d, N, k, lo, idx, gate, lrank, bc, bp, s);
+hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
+  if (a.N <= 16) return launch_nb<T, 1>(a, s);
+  if (a.N <= 32) return launch_nb<T, 2>(a, s);
+  if (a.N <= 64) return launch_nb<T, 4>(a, s);
+  if (a.N <= 128) return launch_nb<T, 8>(a, s);
+  if (a.N <= 256) return launch_nb<T, 16>(a, s);
+  return launch_nb<T, 32>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_route(int dtype, const void* x, const void* w_router,
-                        const float* logit_bias, const float* select_bias, int T_, int d,
-                        int N, int k, float* logits_out, int32_t* topk_idx,
-                        float* topk_gate, int32_t* lrank, int32_t* blk_counts,
-                        float* blk_psum, hipStream_t s) {
-  if (dtype == 1)
-    return launch_route_d<bf16_t>(N, x, w_router, logit_bias, select_bias, T_, d, k, logits_out,
-                                  topk_idx, topk_gate, lrank, blk_counts, blk_psum, s);
-  return launch_route_d<float>(N, x, w_router, logit_bias, select_bias, T_, d, k, logits_out,
-                               topk_idx, topk_gate, lrank, blk_counts, blk_psum, s);
+int route_split(int T_, int d, int dtype) {
+  const int nsteps = d * (dtype == 1 ? 2 : 4) / kRowBytes;
+  const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
+  // enough workgroups to cover the GPU, at least 4 K steps each
+  int ks = (256 + blocks - 1) / blocks;
+  const int max_ks = nsteps / 4 > 0 ? nsteps / 4 : 1;
+  ks = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
+  const int per = (nsteps + ks - 1) / ks;
+  return (nsteps + per - 1) / per;  // no empty split
+}
+
+hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* logit_bias,
+                        const float* select_bias, int T_, int d, int N, int k, int ksplit,
+                        float* partial, float* logits_out, int32_t* topk_idx, float* topk_gate,
+                        int32_t* lrank, int32_t* blk_counts, float* blk_psum, hipStream_t s) {
+  RouteArgs a{};
+  a.x = x;
+  a.wr = w_router;
+  a.logit_bias = logit_bias;
+  a.select_bias = select_bias;
+  a.n_tok = T_;
+  a.d = d;
+  a.N = N;
+  a.k = k;
+  const int nsteps = d * (dtype == 1 ? 2 : 4) / kRowBytes;
+  a.ksplit = ksplit < 1 ? 1 : ksplit;
+  a.steps_per_split = (nsteps + a.ksplit - 1) / a.ksplit;
+  a.partial = partial;
+  a.logits_out = logits_out;
+  a.topk_idx = topk_idx;
+  a.topk_gate = topk_gate;
+  a.lrank = lrank;
+  a.blk_counts = blk_counts;
+  a.blk_psum = blk_psum;
+  if (a.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
+  if (dtype == 1) return launch_t<bf16_t>(a, s);
+  return launch_t<float>(a, s);
 }
 
 }  // namespace moe
