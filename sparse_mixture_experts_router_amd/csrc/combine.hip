@@ -47,8 +47,12 @@ template <> struct Vec<float> {
   }
 };
 
-template <typename T>
+// PART: the expert rows arrive as nparts fp32 partial sums (a down pass split
+// over its reduction); they are added in part order before the gate multiply.
+template <typename T, bool PART>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yperm,
+                                                      const float* __restrict__ ypart,
+                                                      int nparts, size_t part_stride,
                                                       const int32_t* __restrict__ inv_row,
                                                       const float* __restrict__ gate, int n_tok,
                                                       int d, int k, int S, T* __restrict__ y) {
@@ -70,7 +74,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yper
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int s = 0; s < k + S; ++s) {
       float v[V];
-      Vec<T>::load(yperm + static_cast<size_t>(s_row[s]) * d + c, v);
+      if (PART) {
+        const float* src = ypart + static_cast<size_t>(s_row[s]) * d + c;
+#pragma unroll
+        for (int i = 0; i < V; i += 4) Vec<float>::load(src + i, v + i);
+        for (int q = 1; q < nparts; ++q) {
+          float u[V];
+#pragma unroll
+          for (int i = 0; i < V; i += 4) Vec<float>::load(src + q * part_stride + i, u + i);
+#pragma unroll
+          for (int i = 0; i < V; ++i) v[i] += u[i];
+        }
+      } else {
+        Vec<T>::load(yperm + static_cast<size_t>(s_row[s]) * d + c, v);
+      }
       const float gs = s < k ? s_g[s] : 1.0f;
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(gs, v[i], acc[i]);
@@ -110,19 +127,31 @@ __global__ __launch_bounds__(256) void balance_kernel(int n_tok, int N, int k,
   }
 }
 
+
+template <typename T>
+void combine_t(const void* yperm, const float* ypart, int nparts, long rows,
+               const int32_t* inv_row, const float* gate, int T_, int d, int k, int S, void* y,
+               hipStream_t s) {
+  const size_t stride = static_cast<size_t>(rows) * d;
+  if (nparts > 0)
+    hipLaunchKernelGGL((combine_kernel<T, true>), dim3(T_), dim3(256), 0, s,
+                       static_cast<const T*>(yperm), ypart, nparts, stride, inv_row, gate, T_, d,
+                       k, S, static_cast<T*>(y));
+  else
+    hipLaunchKernelGGL((combine_kernel<T, false>), dim3(T_), dim3(256), 0, s,
+                       static_cast<const T*>(yperm), ypart, 0, stride, inv_row, gate, T_, d, k,
+                       S, static_cast<T*>(y));
+}
+
 }  // namespace
 
-hipError_t launch_combine(int dtype, const void* yperm, const int32_t* inv_row,
-                          const float* topk_gate, int T_, int d, int k, int S, void* y,
-                          hipStream_t s) {
+hipError_t launch_combine(int dtype, const void* yperm, const float* ypart, int nparts,
+                          long rows, const int32_t* inv_row, const float* topk_gate, int T_,
+                          int d, int k, int S, void* y, hipStream_t s) {
   if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T_), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(yperm), inv_row, topk_gate, T_, d, k, S,
-                       static_cast<bf16_t*>(y));
+    combine_t<bf16_t>(yperm, ypart, nparts, rows, inv_row, topk_gate, T_, d, k, S, y, s);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T_), dim3(256), 0, s,
-                       static_cast<const float*>(yperm), inv_row, topk_gate, T_, d, k, S,
-                       static_cast<float*>(y));
+    combine_t<float>(yperm, ypart, nparts, rows, inv_row, topk_gate, T_, d, k, S, y, s);
   return hipGetLastError();
 }
 

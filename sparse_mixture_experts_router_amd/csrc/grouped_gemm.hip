@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   const int seg = g.offsets[e];
   const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
   const int n0 = blockIdx.y * BN;
+  const bool split = !GATED && g.ksplit > 1;   // blockIdx.z: part of the reduction
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -96,7 +97,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < NBK; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 ra[A_LD], rb0[B_LD], rb1[B_LD];
-  const int nsteps = static_cast<int>(row_bytes / ROWB);
+  int nsteps = static_cast<int>(row_bytes / ROWB);
+  if (split) {  // this workgroup's share of the K steps
+    const int per = (nsteps + g.ksplit - 1) / g.ksplit;
+    const int k0 = min(static_cast<int>(blockIdx.z) * per, nsteps - 1);  // loads stay in the row
+    nsteps = max(min(per, nsteps - static_cast<int>(blockIdx.z) * per), 0);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) a_off[i] += static_cast<size_t>(k0) * ROWB;
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) b_off[i] += static_cast<size_t>(k0) * ROWB;
+  }
 
   // prologue: K step 0 into stage 0
 #pragma unroll
@@ -182,7 +192,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
         } else {
           v = acc[0][i][j][r];
         }
-        orow[col] = from_f32<T>(v);
+        if (split)
+          g.out_part[(static_cast<size_t>(blockIdx.z) * g.a_rows + seg + m0 + row) * g.n_dim + col] = v;
+        else
+          orow[col] = from_f32<T>(v);
       }
     }
   }
@@ -190,14 +203,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 
 template <typename T, bool GATED, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.tiles_cap, (g.n_dim + BN - 1) / BN);
+  dim3 grid(g.tiles_cap, (g.n_dim + BN - 1) / BN, (!GATED && g.ksplit > 1) ? g.ksplit : 1);
   hipLaunchKernelGGL((grouped_gemm_kernel<T, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 template <typename T, bool GATED>
 hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
-  if (bm == 32) return launch_t<T, GATED, 32, 128, 1, 4>(g, s);
+  if (bm == 32) return launch_t<T, GATED, 32, 64, 1, 4>(g, s);
   return launch_t<T, GATED, 128, 128, 2, 2>(g, s);
 }
 
@@ -206,6 +219,19 @@ hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s) {
   if (dtype == 1) return gated ? launch_bm<bf16_t, true>(g, bm, s) : launch_bm<bf16_t, false>(g, bm, s);
   return gated ? launch_bm<float, true>(g, bm, s) : launch_bm<float, false>(g, bm, s);
+}
+
+// Split of the down pass over workgroups for few-row (weight-streaming)
+// shapes: enough workgroups to keep several in flight per CU, each with at
+// least 16 K steps.
+int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_dim) {
+  if (pick.variant != 0 || pick.bm != 32) return 1;
+  const long blocks = static_cast<long>(tiles_cap) * ((n_dim + 63) / 64);
+  const int nsteps = static_cast<int>(static_cast<long>(k_dim) * (dtype == 1 ? 2 : 4) / 128);
+  int ks = static_cast<int>((2048 + blocks - 1) / blocks);
+  ks = ks > 8 ? 8 : ks;
+  ks = ks > nsteps / 16 ? nsteps / 16 : ks;
+  return ks < 1 ? 1 : ks;
 }
 
 GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_bytes,

@@ -42,7 +42,8 @@ long tile_capacity(const moe_config& c, int bm) {
 
 struct Plan {
   GemmPick up, down;
-  int ksplit;
+  int ksplit;  // router reduction split
+  int dsplit;  // down-pass reduction split
   int bm_up, bm_down;
   int cap_up, cap_down;
   size_t total;
@@ -51,7 +52,7 @@ struct Plan {
 
 enum {
   R_IDX, R_GATE, R_LRANK, R_PART, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
-  R_TUP, R_TDN, R_NT, R_HID, R_YP, R_COUNT
+  R_TUP, R_TDN, R_NT, R_HID, R_YP, R_YPART, R_COUNT
 };
 
 Plan make_plan(const moe_config& c) {
@@ -89,7 +90,9 @@ Plan make_plan(const moe_config& c) {
   sz[R_TDN] = static_cast<size_t>(p.cap_down) * 8;
   sz[R_NT] = 2 * 4;
   sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
-  sz[R_YP] = rows * static_cast<size_t>(c.d_model) * eb;
+  p.dsplit = down_split(c.dtype, p.down, p.cap_down, c.d_model, c.d_ff);
+  sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
+  sz[R_YPART] = p.dsplit > 1 ? static_cast<size_t>(p.dsplit) * rows * c.d_model * 4 : 0;
   size_t o = 0;
   for (int i = 0; i < R_COUNT; ++i) {
     p.off[i] = o;
@@ -119,6 +122,7 @@ Workspace carve(const Plan& p, void* base) {
   w.ntiles = reinterpret_cast<int32_t*>(b + p.off[R_NT]);
   w.hidden = b + p.off[R_HID];
   w.yperm = b + p.off[R_YP];
+  w.ypart = reinterpret_cast<float*>(b + p.off[R_YPART]);
   return w;
 }
 
@@ -305,12 +309,15 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   dn.k_dim = c.d_ff;
   dn.n_dim = c.d_model;
   dn.tiles_cap = p.cap_down;
+  dn.ksplit = p.dsplit;
+  dn.out_part = ws.ypart;
   if ((err = launch_gemm(c.dtype, false, p.down, dn, s)) != hipSuccess)
     return hip_fail(err, "down GEMM");
 
   mark(ev, MOE_STAGE_COMBINE, s);
-  if ((err = launch_combine(c.dtype, ws.yperm, ws.inv_row, gate, c.T, c.d_model, c.top_k,
-                            c.n_shared, y, s)) != hipSuccess)
+  if ((err = launch_combine(c.dtype, ws.yperm, ws.ypart, p.dsplit > 1 ? p.dsplit : 0,
+                            dn.a_rows, ws.inv_row, gate, c.T, c.d_model, c.top_k, c.n_shared,
+                            y, s)) != hipSuccess)
     return hip_fail(err, "combine kernel");
   mark(ev, MOE_STAGE_COUNT, s);
   return MOE_OK;

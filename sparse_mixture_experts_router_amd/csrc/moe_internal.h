@@ -38,6 +38,7 @@ struct Workspace {
   int32_t* ntiles;     // [2]: entries in tiles_up, tiles_down
   void* hidden;        // [T k + S T, F]  dtype
   void* yperm;         // [T k + S T, d]  dtype
+  float* ypart;        // [ksplit, T k + S T, d] fp32 split-K partials of the down pass
 };
 
 // ---------------------------------------------------------------- launchers
@@ -81,6 +82,8 @@ struct GemmArgs {
   int k_dim;                 // reduction length (d or F)
   int n_dim;                 // output columns (F or d)
   int tiles_cap;             // grid rows
+  int ksplit;                // > 1: reduction split over workgroups (plain pass only)
+  float* out_part;           // fp32 partial outputs [ksplit, a_rows, n_dim] when ksplit > 1
 };
 
 // Kernel choice for one grouped GEMM: variant 0 = register-staged tiles
@@ -97,9 +100,12 @@ hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, 
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 
-hipError_t launch_combine(int dtype, const void* yperm, const int32_t* inv_row,
-                          const float* topk_gate, int T, int d, int k, int S,
-                          void* y, hipStream_t s);
+// y from the per-expert rows: yperm (layer dtype), or, when nparts > 0, the
+// sum of nparts fp32 partial row sets ypart[nparts, rows, d] (fixed order).
+hipError_t launch_combine(int dtype, const void* yperm, const float* ypart, int nparts,
+                          long rows, const int32_t* inv_row, const float* topk_gate, int T,
+                          int d, int k, int S, void* y, hipStream_t s);
+int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_dim);
 
 hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
                           const float* prob_sum, float alpha, float* f_out,

@@ -46,6 +46,11 @@ REDUCED = [
                                  select_bias=True)),
     ("one_token", reduced(CONFIGS["deepseek_v3"], T=1, d=256, F=128, N=16)),
     ("bf16_k_equals_n", MoEShape("dense", T=40, d=128, N=4, k=4, F=128)),
+    # few rows per expert and a long reduction: the down pass splits its K
+    # steps over workgroups (39 steps -> 20 + 19; 50 steps -> 17 + 17 + 16)
+    ("decode_split_k", reduced(CONFIGS["mixtral_decode"], T=24, d=256, F=2496)),
+    ("f32_split_k_shared", MoEShape("f32_split", T=9, d=128, N=4, k=2, F=1600, S=1,
+                                    dtype="f32")),
 ]
 
 
