@@ -6,6 +6,9 @@ are resident in HBM before timing starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-tokens N]
+    python bench.py --copy-probe MIB          # counter calibration copy
+    python bench.py --summarize-profiles DIR --workload NAME
+                                              # rocprofv3 output -> profiles/
 
 Workloads (random weights of the named models' shapes, no checkpoints):
 mixtral_prefill (default), mixtral_decode, deepseek_v3, qwen3_skew, tiny_f32.
@@ -28,9 +31,15 @@ METRIC = "MoE layer tokens/sec; active TFLOP/s and HBM GB/s as % of MI355X peak"
 PEAK_BF16_TFLOPS = 2500.0     # dense MFMA bf16, MI355X
 PEAK_F32_TFLOPS = 157.3       # dense MFMA fp32
 PEAK_HBM_GBS = 8000.0         # HBM3E
-DEFAULT_CPU_TOKENS = {"mixtral_prefill": 256, "mixtral_decode": 32, "deepseek_v3": 32,
+# first CPU-oracle sample per workload; when it finishes in under CPU_MIN_S the
+# sample grows so that the reported run takes about CPU_TARGET_S
+DEFAULT_CPU_TOKENS = {"mixtral_prefill": 256, "mixtral_decode": 32, "deepseek_v3": 16,
                       "qwen3_skew": 256, "tiny_f32": 64}
-GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc", "grouped_gemm.hip")
+CPU_MIN_S, CPU_TARGET_S = 8.0, 15.0
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
+# the sources that decide the expert GEMMs' memory traffic
+GEMM_SRCS = ("expert_gemm.hip", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
+PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 1024
 
 
 def parse():
@@ -45,6 +54,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="turn the rocprofv3 runs under DIR (trace/, fetch/, write/, "
+                         "copy_fetch/, copy_write/) into profiles/ summaries and exit")
     return ap.parse_args()
 
 
@@ -73,24 +85,30 @@ def algorithmic(shape, active):
 
 
 def gemm_source_hash():
-    with open(GEMM_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in GEMM_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"expert_up_gemm_{workload}_traffic.json")
 
 
 def load_traffic(workload):
-    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary.
+    """The committed rocprofv3 --pmc record of the gate/up launch, or None.
 
-    Returns None when there is no summary or when the kernel source changed
-    since the counters were taken.
+    None also when the GEMM sources changed since the counters were taken.
     """
-    path = os.path.join(ROOT, "profiles", f"expert_up_gemm_{workload}_traffic.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
 def cpu_baseline(shape, inputs, n_tok, gpu_idx):
@@ -107,11 +125,11 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
         threads, blas = len(os.sched_getaffinity(0)), "unknown"
 
     n_tok = min(n_tok, shape.T)
-    x = inputs["x"][:n_tok].float().cpu().numpy()
+    x = inputs["x"].float().cpu().numpy()
     wr = inputs["w_router"].float().cpu().numpy()
     lb = None if inputs["logit_bias"] is None else inputs["logit_bias"].cpu().numpy()
     sb = None if inputs["select_bias"] is None else inputs["select_bias"].cpu().numpy()
-    need = sorted(set(gpu_idx[:n_tok].reshape(-1).tolist()))
+    need = sorted(set(gpu_idx[:n_tok].reshape(-1).tolist()))   # more are fetched on demand
     cache = {e: (inputs["w_gate"][e].float().cpu().numpy(), inputs["w_up"][e].float().cpu().numpy(),
                  inputs["w_down"][e].float().cpu().numpy()) for e in need}
     fetched = []
@@ -127,15 +145,186 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
     shared = None
     if shape.S:
         shared = tuple(inputs[n].float().cpu().numpy() for n in ("ws_gate", "ws_up", "ws_down"))
-    t0 = time.perf_counter()
-    ref = oracle.moe_forward(x, wr, expert, shape.k, logit_bias=lb, select_bias=sb, shared=shared,
-                             n_experts=shape.N)
-    dt = time.perf_counter() - t0
-    del ref
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"first {n_tok} of {shape.T} tokens, all their experts; NumPy float64 "
-                       f"({blas}), {dt:.1f} s; host affinity {len(os.sched_getaffinity(0))} cpus"),
-            "seconds": dt}
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.moe_forward(np.ascontiguousarray(x[:n]), wr, expert, shape.k, logit_bias=lb,
+                           select_bias=sb, shared=shared, n_experts=shape.N)
+        return time.perf_counter() - t0
+
+    dt = run(n_tok)
+    first = (n_tok, dt)
+    reps = 1
+    while dt < CPU_MIN_S and n_tok < shape.T:   # too short to time: grow the sample
+        n_tok = min(shape.T, int(np.ceil(n_tok * CPU_TARGET_S / max(dt, 1e-3))))
+        dt = run(n_tok)
+    if dt < CPU_MIN_S:                       # the whole batch is quick: repeat it
+        reps = int(np.ceil(CPU_TARGET_S / max(dt, 1e-3)))
+        dt = sum(run(n_tok) for _ in range(reps))
+    return {"value": n_tok * reps / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"first {n_tok} of {shape.T} tokens with all their experts"
+                       f"{f', {reps} runs' if reps > 1 else ''}, NumPy float64 ({blas}), "
+                       f"{dt:.1f} s in all (sized from a {first[0]}-token run of "
+                       f"{first[1]:.1f} s); host affinity {len(os.sched_getaffinity(0))} cpus"),
+            "seconds": round(dt, 2)}
+
+
+def profile_commands(d, workload):
+    """The rocprofv3 runs that --summarize-profiles reads (d: their output root)."""
+    run = f"python3 bench.py --workload {workload} --no-cpu-baseline"
+    return {
+        "trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- {run} "
+                  f"--steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} > {d}/trace_bench.json"),
+        "fetch": (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- {run} "
+                  f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
+        "write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- {run} "
+                  f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
+        "copy_fetch": (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o run -- "
+                       f"python3 bench.py --copy-probe {COPY_MIB}"),
+        "copy_write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o run -- "
+                       f"python3 bench.py --copy-probe {COPY_MIB}"),
+    }
+
+
+def is_up_gemm(name):
+    """The gate/up launch: a grouped GEMM kernel instantiated with GATED = true."""
+    return "gemm_kernel<" in name and ("<true," in name or ", true," in name)
+
+
+def short_name(name):
+    return name.replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+
+
+def read_counters(path, counter):
+    """{kernel name: [value per dispatch]} for one counter of a --pmc run (KiB)."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (f, r["Dispatch_Id"])
+                per.setdefault(key, [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+    out = {}
+    for name, v in per.values():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize_profiles(d, workload):
+    """Write profiles/expert_up_gemm_<workload>.md and the _traffic.json that
+    the bench reads, from the five rocprofv3 runs of profile_commands()."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    from workloads import CONFIGS
+
+    shape = CONFIGS[workload]
+    cmds = profile_commands("gpurun_out/prof", workload)
+    # kernel trace
+    stats = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {d}/trace")
+    rows = []
+    with open(stats[0]) as fh:
+        for r in csv.DictReader(fh):
+            if "moe::" in r["Name"]:
+                rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]),
+                             float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    up = [r for r in rows if is_up_gemm(r[0])]
+    if len(up) != 1:
+        raise SystemExit(f"expected one gate/up GEMM kernel in the trace, found {len(up)}")
+    up = up[0]
+    bench = None
+    bpath = os.path.join(d, "trace_bench.json")
+    if os.path.exists(bpath):
+        with open(bpath) as fh:
+            lines = [ln for ln in fh if ln.startswith("{")]
+        bench = json.loads(lines[-1]) if lines else None
+    # counters, calibrated on a plain copy of known size
+    copy_bytes = COPY_MIB * (1 << 20)
+
+    def copy_scale(sub, counter):
+        vals = [v for n, vs in read_counters(os.path.join(d, sub), counter).items()
+                if "copyBuffer" in n for v in vs]
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {sub}")
+        return copy_bytes / (float(np.median(vals)) * 1024.0), len(vals)
+
+    fscale, nf = copy_scale("copy_fetch", "FETCH_SIZE")
+    wscale, nw = copy_scale("copy_write", "WRITE_SIZE")
+
+    def up_kib(sub, counter):
+        vals = [v for n, vs in read_counters(os.path.join(d, sub), counter).items()
+                if is_up_gemm(short_name(n)) for v in vs]
+        if not vals:
+            raise SystemExit(f"no gate/up dispatch in {sub}")
+        return float(np.mean(vals)), len(vals)
+
+    fk, nfk = up_kib("fetch", "FETCH_SIZE")
+    wk, nwk = up_kib("write", "WRITE_SIZE")
+    fetch_b = fk * 1024.0 * fscale
+    write_b = wk * 1024.0 * wscale
+    alg = bench["roofline"]["algorithmic_bytes"] if bench else None
+    rec = {
+        "workload": workload,
+        "kernel": up[0],
+        "gemm_source_sha256_16": gemm_source_hash(),
+        "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+        "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "fetch_bytes_per_launch": int(round(fetch_b)),
+        "write_bytes_per_launch": int(round(write_b)),
+        "algorithmic_bytes_per_launch": alg,
+        "dispatches": {"fetch": nfk, "write": nwk, "copy_fetch": nf, "copy_write": nw},
+        "commands": {k: v for k, v in cmds.items() if k != "trace"},
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    md = [f"# Gate/up expert GEMM, {workload}: rocprofv3 summary", "",
+          f"Workload: {shape.describe()}.", "",
+          "Commands (run from the repository root; the summary below is",
+          f"`python3 bench.py --summarize-profiles gpurun_out/prof --workload {workload}`):", ""]
+    md += [f"    {c}" for c in cmds.values()]
+    md += ["", "## Kernel trace (--kernel-trace --stats), this library's kernels", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    md += [f"| `{n}` | {c} | {a / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} | {p:.2f} |"
+           for n, c, a, lo, hi, p in rows]
+    if bench:
+        r = bench["roofline"]
+        md += ["", f"The bench line of the traced run timed the same launch at "
+               f"{r['avg_launch_ms'] * 1e3:.1f} us on average with HIP events on its stream "
+               f"(trace: {up[2] / 1e3:.1f} us); layer {bench['ms_per_step']} ms per step, "
+               f"{bench['value']} tokens/s; roofline {r['bound']} {r['achieved']} {r['unit']} "
+               f"= {r['frac']:.3f} of peak."]
+    md += ["", "## HBM traffic of the gate/up launch (--pmc)", "",
+           "FETCH_SIZE and WRITE_SIZE are in KiB per dispatch. Each is scaled by the factor",
+           f"that makes a plain {COPY_MIB} MiB device copy read and write {COPY_MIB} MiB.", "",
+           "| quantity | value |", "|---|---:|",
+           f"| FETCH_SIZE per launch (KiB, mean of {nfk}) | {fk:.0f} |",
+           f"| WRITE_SIZE per launch (KiB, mean of {nwk}) | {wk:.0f} |",
+           f"| fetch scale (copy of {COPY_MIB} MiB) | {fscale:.3f} |",
+           f"| write scale (copy of {COPY_MIB} MiB) | {wscale:.3f} |",
+           f"| HBM bytes read per launch | {fetch_b / 1e6:.1f} MB |",
+           f"| HBM bytes written per launch | {write_b / 1e6:.1f} MB |"]
+    if alg:
+        md += [f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |",
+               f"| measured / algorithmic | {(fetch_b + write_b) / alg:.2f} |"]
+    with open(os.path.join(ROOT, "profiles", f"expert_up_gemm_{workload}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps(rec))
 
 
 def main():
@@ -148,6 +337,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
         return
 
     import numpy as np
@@ -221,7 +413,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
     roof["kernel"] = "grouped gate/up GEMM with SiLU*up (expert_up stage)"
     roof["avg_launch_ms"] = round(up_ms, 4)
-    roof["traffic"] = load_traffic(args.workload)
+    roof["algorithmic_bytes"] = ub
+    roof["algorithmic_flops"] = uf
+    rec = load_traffic(args.workload)
+    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    if rec is not None:
+        roof["traffic_source"] = os.path.relpath(traffic_path(args.workload), ROOT)
+        roof["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / ub, 3)
 
     result = {
         "metric": METRIC,
