@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   constexpr int A_BPW = BM / 64, B_BPW = BNE / 64;  // 1 KB load blocks per wavefront
   constexpr int LPS = A_BPW + B_BPW;           // loads per lane per K step
   constexpr int NF = MB + NB;                  // fragments per K step
-  // Column tiles per band (see the header): about 32 / kBandCols row tiles of
-  // one expert run next to kBandCols weight tiles on an XCD.
-  constexpr int kBandCols = BM >= 256 ? 8 : 4;
+  // Column tiles per band (see the header): the ~32 workgroups an XCD runs
+  // at once cover about 16 row tiles next to 2 weight tiles.
+  constexpr int kBandCols = 2;
   static_assert(BM % 64 == 0 && BNE % 64 == 0 && STAGES >= 3 && STAGES <= 4, "tile shape");
   static_assert(!GATED || (COLS % (B_BPW * 16) == 0 && NB % 2 == 0),
                 "a wavefront's B blocks are all gate or all up rows");
@@ -170,28 +170,34 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f));
 
-  // One K step (fr[P] holds step s's fragments): issue step s + STAGES - 1
-  // (its ring buffer was last read in step s - 1, before that step's
-  // barrier); the first half of the MFMAs; wait until step s + 1 has landed
-  // (only the STAGES - 2 younger steps may still be in flight) and meet at the
-  // barrier; the second half of the MFMAs interleaved with step s + 1's
-  // fragment reads into fr[P ^ 1].  In the last step those reads fetch data
+  // One K step (fr[P] holds step s's fragments): the first half of the
+  // MFMAs with the first L1 loads of step s + STAGES - 1 (its ring buffer was
+  // last read in step s - 1, before that step's barrier); wait until step
+  // s + 1 has landed (only the younger loads may still be in flight) and meet
+  // at the barrier; the second half of the MFMAs interleaved with step s + 1's
+  // fragment reads into fr[P ^ 1] and the remaining loads.  Spreading the
+  // loads over the whole step keeps the vector-memory queue from filling up:
+  // a wavefront issues in order, so a load stalled at issue would also hold
+  // back the MFMAs behind it.  In the last step the fragment reads fetch data
   // that is never used.
   constexpr int HALF = NB / 2;
-  constexpr int PER = (MB * HALF) / NF > 0 ? (MB * HALF) / NF : 1;
-  constexpr int LPER = (MB * HALF) / LPS > 0 ? (MB * HALF) / LPS : 1;  // MFMAs per load issue
-  static_assert((MB * HALF) / LPER >= LPS, "every load of the step is issued in the first half");
+  constexpr int QH = MB * HALF;                           // MFMAs per half step
+  constexpr int L1 = LPS / 2, L2 = LPS - L1;              // loads per half step
+  constexpr int PER = QH / NF > 0 ? QH / NF : 1;          // MFMAs per fragment read
+  constexpr int LPER1 = QH / L1 > 0 ? QH / L1 : 1;        // MFMAs per load issue
+  constexpr int LPER2 = QH / L2 > 0 ? QH / L2 : 1;
+  static_assert(QH / LPER1 >= L1 && QH / LPER2 >= L2, "every load is issued in its half step");
 #define MOE_KSTEP(P)                                                                     \
   {                                                                                      \
     _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                   \
       _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
         mfma_bf16_agpr(acc[i][j], fr[P][i], fr[P][MB + j]);                              \
         const int q = j * MB + i;                                                        \
-        if (q % LPER == 0 && q / LPER < LPS) issue_one(s + STAGES - 1, q / LPER);        \
+        if (q % LPER1 == 0 && q / LPER1 < L1) issue_one(s + STAGES - 1, q / LPER1);      \
         __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     }                                                                                    \
-    wait_vmem<(STAGES - 2) * LPS>();                                                     \
+    wait_vmem<(STAGES - 3) * LPS + L1>();                                                \
     stage_barrier();                                                                     \
     const char* st = smem + ((s + 1) % STAGES) * STAGE;                                  \
     _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                  \
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
         const int q = (j - HALF) * MB + i;                                               \
         if (q % PER == PER - 1 && q / PER < NF)                                          \
           fr[P ^ 1][q / PER] = *reinterpret_cast<const u32x4*>(st + frag_off(q / PER));  \
+        if (q % LPER2 == 0 && q / LPER2 < L2) issue_one(s + STAGES - 1, L1 + q / LPER2); \
         __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     }                                                                                    \
