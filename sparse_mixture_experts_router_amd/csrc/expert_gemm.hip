@@ -222,29 +222,50 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #undef MOE_KSTEP
 
   // -------------------------------------------------------------- epilogue
-  wait_vmem<0>();  // the tail steps' re-reads must land before the workgroup retires
+  // Each wavefront stages 64 output columns of its block at a time in LDS,
+  // row-major with rows padded by 16 bytes (the four row groups of an MFMA
+  // result then fall in distinct banks), and writes them back as whole
+  // 16-byte chunks, 8 lanes per 128-byte row segment.
+  wait_vmem<0>();   // this wavefront's last ring loads have landed
+  stage_barrier();  // and every wavefront is done with the ring
   mfma_drain();
-  bf16_t* out = static_cast<bf16_t*>(g.out);
+  constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
+  constexpr int PB = 4;                      // 16-column blocks per pass
+  constexpr int SROW = PB * 16 * 2 + 16;     // staged row bytes
+  static_assert(OC % (PB * 16) == 0 && 4 * WTM * SROW <= STAGES * STAGE, "staging space");
+  char* const stg = smem + wave * WTM * SROW;
+  bf16_t* const out = static_cast<bf16_t*>(g.out);
+  const int col0 = n0 + wn * OC;
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+  for (int pass = 0; pass < OC / (PB * 16); ++pass) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * WTM + i * 16 + 4 * (lane >> 4) + r;
-      if (row >= mvalid) continue;
-      bf16_t* orow = out + static_cast<size_t>(seg + m0 + row) * g.n_dim;
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int j = 0; j < NOUT; ++j) {
-        const int col = n0 + wn * (GATED ? WTN / 2 : WTN) + j * 16 + (lane & 15);
-        if (col >= g.n_dim) continue;
-        float v;
-        if (GATED) {
-          const float a = acc[i][j][r];
-          v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
-        } else {
-          v = acc[i][j][r];
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + 4 * (lane >> 4) + r;
+#pragma unroll
+        for (int jj = 0; jj < PB; ++jj) {
+          const int j = pass * PB + jj;
+          float v;
+          if (GATED) {
+            const float a = acc[i][j][r];
+            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
+          } else {
+            v = acc[i][j][r];
+          }
+          *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * 2) =
+              f32_to_bf16(v);
         }
-        orow[col] = f32_to_bf16(v);
       }
+    }
+    const int col = col0 + pass * PB * 16 + (lane & 7) * 8;
+#pragma unroll
+    for (int q = 0; q < WTM / 8; ++q) {
+      const int row = q * 8 + (lane >> 3);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+      const int grow = wm * WTM + row;
+      if (grow < mvalid && col < g.n_dim)
+        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(seg + m0 + grow) * g.n_dim + col) = v;
     }
   }
 }
