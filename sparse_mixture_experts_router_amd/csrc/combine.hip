@@ -47,12 +47,13 @@ template <> struct Vec<float> {
   }
 };
 
-// PART: the expert rows arrive as nparts fp32 partial sums (a down pass split
-// over its reduction); they are added in part order before the gate multiply.
-template <typename T, bool PART>
+// Rows at or past plan[kPlanRowSplit] arrive as plan[kPlanParts] fp32 partial
+// sums (a down pass split over its reduction); they are added in part order
+// before the gate multiply.
+template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yperm,
                                                       const float* __restrict__ ypart,
-                                                      int nparts, size_t part_stride,
+                                                      const int32_t* __restrict__ plan,
                                                       const int32_t* __restrict__ inv_row,
                                                       const float* __restrict__ gate, int n_tok,
                                                       int d, int k, int S, T* __restrict__ y) {
@@ -68,25 +69,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yper
     s_row[threadIdx.x] = n_tok * k + s * n_tok + t;
   }
   __syncthreads();
+  const int parts = plan[kPlanParts], row_split = plan[kPlanRowSplit];
+  const size_t pstride = static_cast<size_t>(plan[kPlanStride]) * d;
   for (int c = threadIdx.x * V; c < d; c += 256 * V) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int s = 0; s < k + S; ++s) {
+      const int row = s_row[s];
       float v[V];
-      if (PART) {
-        const float* src = ypart + static_cast<size_t>(s_row[s]) * d + c;
+      if (parts > 0 && row >= row_split) {
+        const float* src = ypart + static_cast<size_t>(row - row_split) * d + c;
 #pragma unroll
         for (int i = 0; i < V; i += 4) Vec<float>::load(src + i, v + i);
-        for (int q = 1; q < nparts; ++q) {
+        for (int q = 1; q < parts; ++q) {
           float u[V];
 #pragma unroll
-          for (int i = 0; i < V; i += 4) Vec<float>::load(src + q * part_stride + i, u + i);
+          for (int i = 0; i < V; i += 4) Vec<float>::load(src + q * pstride + i, u + i);
 #pragma unroll
           for (int i = 0; i < V; ++i) v[i] += u[i];
         }
       } else {
-        Vec<T>::load(yperm + static_cast<size_t>(s_row[s]) * d + c, v);
+        Vec<T>::load(yperm + static_cast<size_t>(row) * d + c, v);
       }
       const float gs = s < k ? s_g[s] : 1.0f;
 #pragma unroll
@@ -128,30 +132,19 @@ __global__ __launch_bounds__(256) void balance_kernel(int n_tok, int N, int k,
 }
 
 
-template <typename T>
-void combine_t(const void* yperm, const float* ypart, int nparts, long rows,
-               const int32_t* inv_row, const float* gate, int T_, int d, int k, int S, void* y,
-               hipStream_t s) {
-  const size_t stride = static_cast<size_t>(rows) * d;
-  if (nparts > 0)
-    hipLaunchKernelGGL((combine_kernel<T, true>), dim3(T_), dim3(256), 0, s,
-                       static_cast<const T*>(yperm), ypart, nparts, stride, inv_row, gate, T_, d,
-                       k, S, static_cast<T*>(y));
-  else
-    hipLaunchKernelGGL((combine_kernel<T, false>), dim3(T_), dim3(256), 0, s,
-                       static_cast<const T*>(yperm), ypart, 0, stride, inv_row, gate, T_, d, k,
-                       S, static_cast<T*>(y));
-}
-
 }  // namespace
 
-hipError_t launch_combine(int dtype, const void* yperm, const float* ypart, int nparts,
-                          long rows, const int32_t* inv_row, const float* topk_gate, int T_,
-                          int d, int k, int S, void* y, hipStream_t s) {
+hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
+                          const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
+                          int T_, int d, int k, int S, void* y, hipStream_t s) {
   if (dtype == 1)
-    combine_t<bf16_t>(yperm, ypart, nparts, rows, inv_row, topk_gate, T_, d, k, S, y, s);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T_), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(yperm), ypart, plan, inv_row, topk_gate, T_, d,
+                       k, S, static_cast<bf16_t*>(y));
   else
-    combine_t<float>(yperm, ypart, nparts, rows, inv_row, topk_gate, T_, d, k, S, y, s);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T_), dim3(256), 0, s,
+                       static_cast<const float*>(yperm), ypart, plan, inv_row, topk_gate, T_, d,
+                       k, S, static_cast<float*>(y));
   return hipGetLastError();
 }
 

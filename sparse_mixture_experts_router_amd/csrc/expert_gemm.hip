@@ -32,6 +32,92 @@
 namespace moe {
 namespace {
 
+// Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
+// passes of 128 staged bytes per row: each pass is staged row-major in LDS at
+// stg (rows padded by 16 bytes, so the four row groups of an MFMA result
+// land in distinct banks), then leaves in whole 16-byte row chunks.
+//  SBF16 : staged and written as bf16, 64 columns per pass;
+//  else  : staged as fp32, 32 columns per pass, written as bf16 (8 columns
+//          per lane) or, if out_f32, as fp32 (4 columns per lane).  The
+//          plain pass uses this one path for both of its outputs, so the
+//          accumulators have a single consumer.
+// Row i of the block goes to out[(row0 + i) * ld + col0 + ...]; rows >=
+// rows_valid and columns >= cols_valid are not written.
+template <bool GATED, bool SBF16, int MB, int NB, int WTM>
+__device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
+                                            void* out, bool out_f32, size_t ld, long row0,
+                                            int rows_valid, int col0, int cols_valid) {
+  constexpr int NOUT = GATED ? NB / 2 : NB;
+  constexpr int ES = SBF16 ? 2 : 4;      // staged element bytes
+  constexpr int PB = 128 / (16 * ES);    // 16-column blocks per pass
+  constexpr int SROW = 128 + 16;
+  static_assert(NOUT % PB == 0, "whole passes");
+#pragma unroll
+  for (int pass = 0; pass < NOUT / PB; ++pass) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + 4 * (lane >> 4) + r;
+#pragma unroll
+        for (int jj = 0; jj < PB; ++jj) {
+          const int j = pass * PB + jj;
+          float v;
+          if (GATED) {
+            const float a = acc[i][j][r];
+            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
+          } else {
+            v = acc[i][j][r];
+          }
+          if (SBF16)
+            *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) =
+                f32_to_bf16(v);
+          else
+            *reinterpret_cast<float*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) = v;
+        }
+      }
+    }
+    if (SBF16) {
+      const int col = col0 + pass * 64 + (lane & 7) * 8;
+#pragma unroll
+      for (int q = 0; q < WTM / 8; ++q) {
+        const int row = q * 8 + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    } else if (out_f32) {
+      const int col = col0 + pass * 32 + (lane & 7) * 4;
+#pragma unroll
+      for (int q = 0; q < WTM / 8; ++q) {
+        const int row = q * 8 + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    } else {
+      const int col = col0 + pass * 32 + (lane & 3) * 8;
+#pragma unroll
+      for (int q = 0; q < WTM / 16; ++q) {
+        const int row = q * 16 + (lane >> 2);
+        const char* src = stg + row * SROW + (lane & 3) * 32;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 16);
+        u32x4 v;
+        v[0] = f32_to_bf16(a[0]) | (static_cast<uint32_t>(f32_to_bf16(a[1])) << 16);
+        v[1] = f32_to_bf16(a[2]) | (static_cast<uint32_t>(f32_to_bf16(a[3])) << 16);
+        v[2] = f32_to_bf16(b[0]) | (static_cast<uint32_t>(f32_to_bf16(b[1])) << 16);
+        v[3] = f32_to_bf16(b[2]) | (static_cast<uint32_t>(f32_to_bf16(b[3])) << 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    }
+  }
+}
+
 template <bool GATED, int BM, int BNE, int STAGES>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   constexpr int ROWS = BM + BNE;               // rows staged per K step
@@ -53,25 +139,48 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
-  // ------------------------------------------------------- tile of this block
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xq = nblk >> 3, xr = nblk & 7, xcd = bid & 7;
-  const int lin = xcd * xq + min(xcd, xr) + (bid >> 3);
+  // ------------------------------------------------------- work of this block
+  // Work items: the (row tile, column tile) pairs, then (plain pass only)
+  // the pieces (part, tile, column tile) of the last `tail` row tiles when
+  // the scan split them over their reduction.  Each XCD (blocks take XCDs
+  // round-robin) gets an equal contiguous share of both lists and runs it in
+  // order; the pairs are ordered by bands of column tiles.
+  const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
   const int n_nt = (g.n_dim + COLS - 1) / COLS;
-  const int full_bands = n_nt / kBandCols;
-  const int band_blocks = g.tiles_cap * kBandCols;
-  int tile, nt;
-  if (lin < full_bands * band_blocks) {
-    const int band = lin / band_blocks, rem = lin - band * band_blocks;
-    tile = rem / kBandCols;
-    nt = band * kBandCols + rem % kBandCols;
-  } else {
-    const int rem = lin - full_bands * band_blocks, gn = n_nt - full_bands * kBandCols;
-    tile = rem / gn;
-    nt = full_bands * kBandCols + rem % gn;
+  const int ntl = *g.ntiles;
+  int tail = 0, parts = 1;
+  if (!GATED && g.plan != nullptr) {
+    tail = g.plan[kPlanTailTiles];
+    if (tail > 0) parts = g.plan[kPlanParts];
   }
-  if (tile >= *g.ntiles) return;
+  const int nrm = ntl - tail;
+  const long w_nrm = static_cast<long>(nrm) * n_nt;
+  const long w_spl = static_cast<long>(tail) * n_nt * parts;
+  const long n_lo = w_nrm * xcd / 8, n_cnt = w_nrm * (xcd + 1) / 8 - n_lo;
+  const long s_lo = w_spl * xcd / 8, s_cnt = w_spl * (xcd + 1) / 8 - s_lo;
+  int tile, nt, part = -1;
+  if (idx < n_cnt) {
+    const int lin = static_cast<int>(n_lo + idx);
+    const int full_bands = n_nt / kBandCols;
+    const int band_blocks = nrm * kBandCols;
+    if (lin < full_bands * band_blocks) {
+      const int band = lin / band_blocks, rem = lin - band * band_blocks;
+      tile = rem / kBandCols;
+      nt = band * kBandCols + rem % kBandCols;
+    } else {
+      const int rem = lin - full_bands * band_blocks, gn = n_nt - full_bands * kBandCols;
+      tile = rem / gn;
+      nt = full_bands * kBandCols + rem % gn;
+    }
+  } else if (idx - n_cnt < s_cnt) {
+    const int lin = static_cast<int>(s_lo + idx - n_cnt);
+    part = lin / (tail * n_nt);
+    const int rem = lin - part * (tail * n_nt);
+    tile = nrm + rem / n_nt;
+    nt = rem % n_nt;
+  } else {
+    return;
+  }
   const int2 te = g.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int seg = g.offsets[e];
@@ -122,7 +231,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const int a_dst = wave * A_BPW * 1024;
   const int b_dst = BM * kRowBytes + wave * B_BPW * 1024;
 
-  const int nsteps = static_cast<int>(row_bytes / kRowBytes);  // even: K is a multiple of 64
+  int nsteps = static_cast<int>(row_bytes / kRowBytes);  // even: K is a multiple of 64
+  if (part >= 0) {  // an even share of the K steps; parts <= nsteps / 16 keeps every share >= 2
+    const int per = ((nsteps + parts - 1) / parts + 1) & ~1;
+    const int k0 = part * per;
+    nsteps = min(per, nsteps - k0);
+#pragma unroll
+    for (int j = 0; j < A_BPW; ++j) a_off[j] += static_cast<uint32_t>(k0) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(k0) * kRowBytes;
+  }
   // Loads of K step `step` into ring buffer step % STAGES.  Steps past the end
   // re-read the last step (valid addresses) into a buffer nobody reads again,
   // so every K step issues the same number of loads and the wait counts below
@@ -222,51 +340,21 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #undef MOE_KSTEP
 
   // -------------------------------------------------------------- epilogue
-  // Each wavefront stages 64 output columns of its block at a time in LDS,
-  // row-major with rows padded by 16 bytes (the four row groups of an MFMA
-  // result then fall in distinct banks), and writes them back as whole
-  // 16-byte chunks, 8 lanes per 128-byte row segment.
   wait_vmem<0>();   // this wavefront's last ring loads have landed
   stage_barrier();  // and every wavefront is done with the ring
   mfma_drain();
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
-  constexpr int PB = 4;                      // 16-column blocks per pass
-  constexpr int SROW = PB * 16 * 2 + 16;     // staged row bytes
-  static_assert(OC % (PB * 16) == 0 && 4 * WTM * SROW <= STAGES * STAGE, "staging space");
-  char* const stg = smem + wave * WTM * SROW;
-  bf16_t* const out = static_cast<bf16_t*>(g.out);
+  static_assert(4 * WTM * (128 + 16) <= STAGES * STAGE, "staging space");
+  char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
-#pragma unroll
-  for (int pass = 0; pass < OC / (PB * 16); ++pass) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + 4 * (lane >> 4) + r;
-#pragma unroll
-        for (int jj = 0; jj < PB; ++jj) {
-          const int j = pass * PB + jj;
-          float v;
-          if (GATED) {
-            const float a = acc[i][j][r];
-            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
-          } else {
-            v = acc[i][j][r];
-          }
-          *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * 2) =
-              f32_to_bf16(v);
-        }
-      }
-    }
-    const int col = col0 + pass * PB * 16 + (lane & 7) * 8;
-#pragma unroll
-    for (int q = 0; q < WTM / 8; ++q) {
-      const int row = q * 8 + (lane >> 3);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
-      const int grow = wm * WTM + row;
-      if (grow < mvalid && col < g.n_dim)
-        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(seg + m0 + grow) * g.n_dim + col) = v;
-    }
+  if (part < 0) {
+    store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
+                                           seg + m0 + wm * WTM, mvalid - wm * WTM, col0, g.n_dim);
+  } else if (!GATED) {  // fp32 partial rows of a split tail tile
+    const long prow = static_cast<long>(part) * g.plan[kPlanStride] + seg + m0 -
+                      g.plan[kPlanRowSplit] + wm * WTM;
+    store_block<GATED, false, MB, NB, WTM>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
+                                           mvalid - wm * WTM, col0, g.n_dim);
   }
 }
 
@@ -274,7 +362,11 @@ template <bool GATED, int BM, int BNE, int STAGES>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long n_nt = (g.n_dim + COLS - 1) / COLS;
-  const long blocks = static_cast<long>(g.tiles_cap) * n_nt;
+  // every XCD's share of the work items fits in blocks / 8 slots (the split
+  // pieces number at most one round of g.cus workgroups)
+  const long per_xcd = (static_cast<long>(g.tiles_cap) * n_nt + 7) / 8 +
+                       (GATED ? 0 : (g.cus + 7) / 8) + 1;
+  const long blocks = 8 * per_xcd;
   hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, STAGES>),
                      dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
   return hipGetLastError();

@@ -44,6 +44,8 @@ struct Plan {
   GemmPick up, down;
   int ksplit;  // router reduction split
   int dsplit;  // down-pass reduction split
+  SplitSpec split;  // what the scan may record in the down pass's split plan
+  int cus;          // compute units of the current device
   int bm_up, bm_down;
   int cap_up, cap_down;
   size_t total;
@@ -88,11 +90,30 @@ Plan make_plan(const moe_config& c) {
   sz[R_INV] = T * k * 4;
   sz[R_TUP] = static_cast<size_t>(p.cap_up) * 8;
   sz[R_TDN] = static_cast<size_t>(p.cap_down) * 8;
-  sz[R_NT] = 2 * 4;
+  sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
   p.dsplit = down_split(c.dtype, p.down, p.cap_down, c.d_model, c.d_ff);
   sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
-  sz[R_YPART] = p.dsplit > 1 ? static_cast<size_t>(p.dsplit) * rows * c.d_model * 4 : 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  p.cus = cus > 0 ? cus : 256;
+  p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};
+  if (p.dsplit <= 1 && p.down.variant == 1) {
+    // tail split of the large-tile down GEMM (256 output columns per tile)
+    const int nnt = (c.d_model + 255) / 256;
+    const int nsteps = c.d_ff * 2 / 64;
+    p.split.tail_nnt = nnt;
+    p.split.tail_cap_rows = static_cast<long>(p.cus / nnt) * p.bm_down;
+    p.split.tail_max_parts = nsteps / 16 < 8 ? nsteps / 16 : 8;
+    if (p.split.tail_cap_rows < 2L * p.bm_down || p.split.tail_max_parts < 2) {
+      p.split.tail_nnt = 0;
+      p.split.tail_cap_rows = 0;
+    }
+  }
+  sz[R_YPART] = p.dsplit > 1 ? static_cast<size_t>(p.dsplit) * rows * c.d_model * 4
+                             : static_cast<size_t>(p.split.tail_cap_rows) * c.d_model * 4;
   size_t o = 0;
   for (int i = 0; i < R_COUNT; ++i) {
     p.off[i] = o;
@@ -190,7 +211,8 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
 moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
                     hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
-                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, ws.blk_base, ws.counts,
+                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split, ws.blk_base,
+                               ws.counts,
                                ws.prob_sum, out ? out->counts : nullptr,
                                out ? out->prob_sum : nullptr, ws.offsets, ws.tiles_up,
                                ws.tiles_down, ws.ntiles, s);
@@ -291,6 +313,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   up.k_dim = c.d_model;
   up.n_dim = c.d_ff;
   up.tiles_cap = p.cap_up;
+  up.cus = p.cus;
   if ((err = launch_gemm(c.dtype, true, p.up, up, s)) != hipSuccess)
     return hip_fail(err, "gate/up GEMM");
 
@@ -311,13 +334,14 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   dn.tiles_cap = p.cap_down;
   dn.ksplit = p.dsplit;
   dn.out_part = ws.ypart;
+  dn.plan = ws.ntiles + 2;
+  dn.cus = p.cus;
   if ((err = launch_gemm(c.dtype, false, p.down, dn, s)) != hipSuccess)
     return hip_fail(err, "down GEMM");
 
   mark(ev, MOE_STAGE_COMBINE, s);
-  if ((err = launch_combine(c.dtype, ws.yperm, ws.ypart, p.dsplit > 1 ? p.dsplit : 0,
-                            dn.a_rows, ws.inv_row, gate, c.T, c.d_model, c.top_k, c.n_shared,
-                            y, s)) != hipSuccess)
+  if ((err = launch_combine(c.dtype, ws.yperm, ws.ypart, ws.ntiles + 2, ws.inv_row, gate, c.T,
+                            c.d_model, c.top_k, c.n_shared, y, s)) != hipSuccess)
     return hip_fail(err, "combine kernel");
   mark(ev, MOE_STAGE_COUNT, s);
   return MOE_OK;

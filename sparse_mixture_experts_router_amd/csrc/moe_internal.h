@@ -35,10 +35,11 @@ struct Workspace {
   int32_t* inv_row;    // [T, k]
   int2* tiles_up;      // tile list of the gate/up GEMM
   int2* tiles_down;    // tile list of the down GEMM
-  int32_t* ntiles;     // [2]: entries in tiles_up, tiles_down
+  int32_t* ntiles;     // [kPlanInts]: entries in tiles_up, tiles_down, then the down-pass
+                       // split plan (see kPlan*)
   void* hidden;        // [T k + S T, F]  dtype
   void* yperm;         // [T k + S T, d]  dtype
-  float* ypart;        // [ksplit, T k + S T, d] fp32 split-K partials of the down pass
+  float* ypart;        // fp32 partial rows of a down pass split over its reduction
 };
 
 // ---------------------------------------------------------------- launchers
@@ -54,10 +55,20 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router,
                         int32_t* lrank, int32_t* blk_counts, float* blk_psum,
                         hipStream_t s);
 
+// Split of the down pass recorded in the plan: parts > 1 splits every row
+// (decode); otherwise tail_nnt > 0 lets the scan split the last row tiles of
+// a tail_nnt-column-tile grid that would leave cus compute units mostly idle.
+struct SplitSpec {
+  int parts;      // host split of every row (grouped_gemm.hip), or <= 1
+  int tail_nnt;   // column tiles of the down pass (0: no tail split)
+  int tail_cus;   // compute units one round of workgroups fills
+  long tail_cap_rows;  // partial rows the workspace holds over all parts
+  int tail_max_parts;  // most parts one tile may be split into
+};
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
                        int N, int k, int S, int bm_up, int cap_up, int bm_down,
-                       int cap_down, int32_t* blk_base, int32_t* counts,
-                       float* prob_sum, int32_t* user_counts,
+                       int cap_down, const SplitSpec& split, int32_t* blk_base,
+                       int32_t* counts, float* prob_sum, int32_t* user_counts,
                        float* user_prob_sum, int32_t* offsets, int2* tiles_up,
                        int2* tiles_down, int32_t* ntiles, hipStream_t s);
 
@@ -84,7 +95,17 @@ struct GemmArgs {
   int tiles_cap;             // grid rows
   int ksplit;                // > 1: reduction split over workgroups (plain pass only)
   float* out_part;           // fp32 partial outputs [ksplit, a_rows, n_dim] when ksplit > 1
+  const int32_t* plan;       // device split plan of the down pass (kPlan* entries), or null
+  int cus;                   // compute units of the device (grid sizing)
 };
+
+// Device-side plan of a down pass whose reduction is split over workgroups,
+// written by the scan kernel after ntiles[0..1]: the combine kernel adds the
+// fp32 parts of every row at or past kPlanRowSplit.
+//   decode : all rows, kPlanParts = the host's split (grouped_gemm.hip);
+//   prefill: the last kPlanTailTiles row tiles of the large-tile down GEMM,
+//            whose workgroups would otherwise run as a thin last round.
+enum { kPlanParts = 0, kPlanRowSplit = 1, kPlanStride = 2, kPlanTailTiles = 3, kPlanInts = 6 };
 
 // Kernel choice for one grouped GEMM: variant 0 = register-staged tiles
 // (grouped_gemm.hip, fp32 and few-row shapes), 1 = large direct-to-LDS bf16
@@ -100,11 +121,12 @@ hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, 
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 
-// y from the per-expert rows: yperm (layer dtype), or, when nparts > 0, the
-// sum of nparts fp32 partial row sets ypart[nparts, rows, d] (fixed order).
-hipError_t launch_combine(int dtype, const void* yperm, const float* ypart, int nparts,
-                          long rows, const int32_t* inv_row, const float* topk_gate, int T,
-                          int d, int k, int S, void* y, hipStream_t s);
+// y from the per-expert rows: yperm (layer dtype), except rows at or past
+// plan[kPlanRowSplit], which are the sum of plan[kPlanParts] fp32 partial
+// row sets ypart[part][row - row_split] (part stride plan[kPlanStride] rows).
+hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
+                          const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
+                          int T, int d, int k, int S, void* y, hipStream_t s);
 int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_dim);
 
 hipError_t launch_balance(int T, int N, int k, const int32_t* counts,

@@ -56,7 +56,7 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
-    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down,
+    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
     int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
     int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
@@ -134,6 +134,42 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     ntiles[0] = min(total_up, cap_up);
     ntiles[1] = min(total_down, cap_down);
   }
+  __syncthreads();  // tiles_down and offsets are complete
+
+  // Split plan of the down pass.  Tail split: with W = tiles x column tiles
+  // workgroups on `cus` compute units, the last round holds r = W mod cus
+  // of them.  When r is small, the last ceil(r / nnt) row tiles are instead
+  // split over their reduction into `parts` pieces, so that round runs
+  // parts times shorter.
+  if (tid == 0) {
+    int32_t* plan = ntiles + 2;
+    const int ntd = min(total_down, cap_down);
+    int parts = 0, row_split = total_rows, stride = 0, tail = 0;
+    if (split.parts > 1) {
+      parts = split.parts;
+      row_split = 0;
+      stride = total_rows;
+    } else if (split.tail_nnt > 0 && ntd > 0) {
+      const long W = static_cast<long>(ntd) * split.tail_nnt;
+      const long r = W % split.tail_cus;
+      if (r > 0) {
+        const int t = static_cast<int>((r + split.tail_nnt - 1) / split.tail_nnt);
+        int sp = split.tail_cus / (t * split.tail_nnt);
+        sp = min(sp, split.tail_max_parts);
+        if (sp >= 2 && t < ntd && static_cast<long>(t) * bm_down * sp <= split.tail_cap_rows) {
+          const int2 first = tiles_down[ntd - t];
+          parts = sp;
+          tail = t;
+          row_split = offsets[first.x] + first.y;
+          stride = t * bm_down;
+        }
+      }
+    }
+    plan[kPlanParts] = parts;
+    plan[kPlanRowSplit] = row_split;
+    plan[kPlanStride] = stride;
+    plan[kPlanTailTiles] = tail;
+  }
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
@@ -162,11 +198,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
                        int S, int bm_up, int cap_up, int bm_down, int cap_down,
-                       int32_t* blk_base, int32_t* counts, float* prob_sum,
+                       const SplitSpec& split, int32_t* blk_base, int32_t* counts, float* prob_sum,
                        int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
                        int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
-                     k, S, bm_up, cap_up, bm_down, cap_down, blk_base, counts, prob_sum,
+                     k, S, bm_up, cap_up, bm_down, cap_down, split, blk_base, counts, prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
   return hipGetLastError();
 }

@@ -84,6 +84,22 @@ def test_all_tokens_one_expert():
     assert to_np(out["counts"]).tolist() == [0, 0, 0, 300]
 
 
+@pytest.mark.parametrize("S", [0, 1])
+def test_tail_tiles_split_over_k(S):
+    """Last-round tail split of the large-tile down GEMM.
+
+    Every token goes to expert 7, so the down pass has exactly 20 row tiles of
+    128 (the last one ragged) and, with S = 1, 20 more for the shared expert;
+    16 column tiles each.  On a 256-CU device that leaves 64 (128) workgroups
+    for a last round, so the scan splits the last 4 (8) row tiles over their
+    reduction in 2 parts and the combine adds the fp32 parts."""
+    shp = MoEShape("tail", T=2510, d=4096, N=8, k=1, F=1024, S=S)
+    inputs = make_inputs(shp, seed=8, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0.0] * 7 + [100.0], device="cuda")
+    _, out, _ = full_parity(shp, inputs=inputs, label=f"tail_split_S{S}")
+    assert int(out["counts"][7]) == 2510
+
+
 def test_unchosen_expert_weights_never_read():
     shp = MoEShape("nan_cold", T=150, d=128, N=6, k=2, F=128)
     inputs = make_inputs(shp, seed=3, device="cuda")
