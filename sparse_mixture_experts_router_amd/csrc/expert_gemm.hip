@@ -14,14 +14,20 @@
 //    v_mfma_f32_16x16x32_bf16 into AGPRs (256 of them for a 256 x 256 tile),
 //    so each 16-byte LDS fragment feeds 8 MFMAs;
 //  * operands go global -> LDS with global_load_lds_dwordx4 (no register
-//    staging) into a ring of STAGES buffers of 32 K-elements (64 bytes of
-//    every row), with the 16-byte chunks of a row XOR-swizzled by row so the
+//    staging) into two buffers of 64 K-elements: 128 bytes, one whole cache
+//    line, of every row, so each load instruction asks the L2 for 8 whole
+//    lines (the L2 -> CU path serves half-line requests at about half the
+//    rate).  The 16-byte chunks of a row are XOR-swizzled by row, so the
 //    fragment reads are free of bank conflicts;
-//  * per K step a wavefront runs the first half of its MFMAs, then waits for
-//    the next stage and meets the other wavefronts at one barrier, then runs
-//    the second half while it reads the next step's fragments into a second
-//    register set, so neither the barrier nor the LDS latency leaves the
-//    matrix cores idle;
+//  * a buffer holds two K steps.  In the first a wavefront runs its MFMAs,
+//    issuing the second half of the next buffer's loads in the first half
+//    of them and reading the second step's fragments in the second half.  In
+//    the second step it runs half its MFMAs, waits for the next buffer and
+//    meets the other wavefronts at the pair's one barrier, then runs the rest
+//    while it reads the next buffer's first fragments and starts refilling
+//    the buffer it has just finished with the K steps two buffers ahead.
+//    Loads are spread over the MFMAs because a wavefront issues in order: a
+//    load stalled on a full memory queue holds back the MFMAs behind it;
 //  * blocks are renumbered so that each of the 8 XCDs (which take workgroups
 //    round-robin) works through a contiguous range of (row tile, column tile)
 //    pairs ordered by bands of column tiles: the workgroups one XCD runs at a
@@ -118,26 +124,28 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
   }
 }
 
-template <bool GATED, int BM, int BNE, int STAGES>
+template <bool GATED, int BM, int BNE>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
-  constexpr int ROWS = BM + BNE;               // rows staged per K step
-  constexpr int STAGE = ROWS * kRowBytes;      // bytes per ring buffer
+  constexpr int ROWS = BM + BNE;               // rows staged per buffer
+  constexpr int BUF = ROWS * kLineBytes;       // bytes per buffer
   constexpr int WTM = BM / 2, WTN = BNE / 2;   // wavefront block
   constexpr int MB = WTM / 16, NB = WTN / 16;  // 16 x 16 MFMA blocks
   constexpr int NOUT = GATED ? NB / 2 : NB;    // output column blocks per wavefront
   constexpr int COLS = GATED ? BNE / 2 : BNE;  // output columns per tile
-  constexpr int A_BPW = BM / 64, B_BPW = BNE / 64;  // 1 KB load blocks per wavefront
-  constexpr int LPS = A_BPW + B_BPW;           // loads per lane per K step
+  constexpr int A_BPW = BM / 32, B_BPW = BNE / 32;  // 1 KB load blocks (8 rows) per wavefront
+  constexpr int LPB = A_BPW + B_BPW;           // loads per lane per buffer
+  constexpr int LH1 = LPB / 2, LH2 = LPB - LH1;  // issued after the barrier / in the next step
   constexpr int NF = MB + NB;                  // fragments per K step
   // Column tiles per band (see the header): the ~32 workgroups an XCD runs
   // at once cover about 16 row tiles next to 2 weight tiles.
   constexpr int kBandCols = 2;
-  static_assert(BM % 64 == 0 && BNE % 64 == 0 && STAGES >= 3 && STAGES <= 4, "tile shape");
-  static_assert(!GATED || (COLS % (B_BPW * 16) == 0 && NB % 2 == 0),
+  static_assert(BM % 64 == 0 && BNE % 64 == 0, "tile shape");
+  static_assert(A_BPW % 2 == 0 && B_BPW % 2 == 0, "a load's block parity is its index parity");
+  static_assert(!GATED || (COLS % (B_BPW * 8) == 0 && NB % 2 == 0),
                 "a wavefront's B blocks are all gate or all up rows");
-  static_assert(2 * LPS < 64, "vmcnt range");
+  static_assert(LPB < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
 
   // ------------------------------------------------------- work of this block
   // Work items: the (row tile, column tile) pairs, then (plain pass only)
@@ -201,75 +209,75 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
                          : nullptr;
 
   // ------------------------------------------ this lane's global sources
-  // A 1 KB load block holds 16 staged rows of 64 bytes; lane l fills physical
-  // chunk l % 4 of row l / 4 of the block, i.e. logical chunk
-  // (l % 4) ^ ((l / 8) % 4) of that row.  Staged rows: A rows 0 .. BM-1, then
-  // B rows (gated: COLS gate rows, then COLS up rows).  Wavefront w loads A
-  // blocks w*A_BPW .. and B blocks w*B_BPW ..; sources are a wave-uniform
-  // base plus a 32-bit per-lane byte offset (the host keeps every operand
-  // below 4 GiB per base).
-  const int lchunk = ring_lane_chunk(lane);
+  // Staged rows: A rows 0 .. BM-1, then B rows (gated: COLS gate rows, then
+  // COLS up rows).  Wavefront w loads A blocks w*A_BPW .. and B blocks
+  // w*B_BPW ..; lane l of a block fetches row l / 8 of it, the chunk that
+  // line_lane_chunk assigns.  Sources are a wave-uniform base plus a 32-bit
+  // per-lane byte offset (the host keeps every operand below 4 GiB per base);
+  // rows beyond the tile are clamped to a valid row and discarded at the end.
   const char* const a_base = reinterpret_cast<const char*>(g.a);
   uint32_t a_off[A_BPW];
 #pragma unroll
   for (int j = 0; j < A_BPW; ++j) {
-    const int R = (wave * A_BPW + j) * 16 + (lane >> 2);
+    const int R = (wave * A_BPW + j) * 8 + (lane >> 3);
     const int grow = seg + m0 + min(R, mvalid - 1);
     const int srow = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
-    a_off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) + lchunk * 16;
+    a_off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) +
+               line_lane_chunk(lane, j) * 16;
   }
-  const int jb0 = wave * B_BPW * 16;
+  const int jb0 = wave * B_BPW * 8;
   const bool up_rows = GATED && jb0 >= COLS;
   const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
   uint32_t b_off[B_BPW];
 #pragma unroll
   for (int j = 0; j < B_BPW; ++j) {
-    const int jb = jb0 + j * 16 + (lane >> 2) - (up_rows ? COLS : 0);
+    const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? COLS : 0);
     const int n = min(n0 + jb, g.n_dim - 1);
-    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) + lchunk * 16;
+    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
+               line_lane_chunk(lane, j) * 16;
   }
   const int a_dst = wave * A_BPW * 1024;
-  const int b_dst = BM * kRowBytes + wave * B_BPW * 1024;
+  const int b_dst = BM * kLineBytes + wave * B_BPW * 1024;
 
-  int nsteps = static_cast<int>(row_bytes / kRowBytes);  // even: K is a multiple of 64
-  if (part >= 0) {  // an even share of the K steps; parts <= nsteps / 16 keeps every share >= 2
-    const int per = ((nsteps + parts - 1) / parts + 1) & ~1;
-    const int k0 = part * per;
-    nsteps = min(per, nsteps - k0);
+  // buffer loads ("pairs" of K steps) of this item: all, or its part's share
+  int npairs = static_cast<int>(row_bytes / kLineBytes);  // even: K is a multiple of 128
+  if (part >= 0) {
+    const int per = split_share(npairs, parts);
+    const int p0 = part * per;
+    npairs = min(per, npairs - p0);
 #pragma unroll
-    for (int j = 0; j < A_BPW; ++j) a_off[j] += static_cast<uint32_t>(k0) * kRowBytes;
+    for (int j = 0; j < A_BPW; ++j) a_off[j] += static_cast<uint32_t>(p0) * kLineBytes;
 #pragma unroll
-    for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(k0) * kRowBytes;
+    for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(p0) * kLineBytes;
   }
-  // Loads of K step `step` into ring buffer step % STAGES.  Steps past the end
-  // re-read the last step (valid addresses) into a buffer nobody reads again,
-  // so every K step issues the same number of loads and the wait counts below
-  // hold without branches.
-  // load l (0 .. LPS-1) of K step `step`: A blocks first, then B blocks
-  auto issue_one = [&](int step, int l) {
-    const uint32_t koff = static_cast<uint32_t>(min(step, nsteps - 1)) * kRowBytes;
-    char* const st = smem + (step % STAGES) * STAGE;
+  // Load l (A blocks first, then B blocks) of pair `pair` into buffer `buf`.
+  // Pairs past the end re-read the last one (valid addresses) into a buffer
+  // nobody reads again, so the loop needs no branches.
+  auto issue_one = [&](int pair, int l, int buf) {
+    const uint32_t koff = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
+    char* const st = smem + buf * BUF;
     if (l < A_BPW) load_lds16(a_base + (a_off[l] + koff), st + a_dst + l * 1024);
     else load_lds16(b_base + (b_off[l - A_BPW] + koff), st + b_dst + (l - A_BPW) * 1024);
   };
-  auto issue = [&](int step) {
-#pragma unroll
-    for (int l = 0; l < LPS; ++l) issue_one(step, l);
-  };
 
-  // LDS byte offset (inside a stage) of fragment f: A blocks 0..MB-1, then
-  // B blocks (gated: NOUT gate blocks, then NOUT up blocks of the same columns)
-  const int frow = lane & 15, fchunk = lane >> 4;
-  auto frag_off = [&](int f) {
+  // LDS byte offset (inside a buffer) of fragment f for K step t (0, 1) of
+  // the buffer: A blocks 0..MB-1, then B blocks (gated: NOUT gate blocks, then
+  // NOUT up blocks of the same columns).  Fragment rows start at multiples of
+  // 16, so the swizzle key is the lane's own.
+  const int frow = lane & 15;
+  const int fkey = swz128_key(frow);
+  const int flane0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
+  const int flane1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  auto frag_off = [&](int f, int t) {
     int r;
     if (f < MB) {
-      r = wm * WTM + f * 16 + frow;
+      r = wm * WTM + f * 16;
     } else {
       const int j = f - MB;
-      if (GATED) r = BM + (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16 + frow;
-      else r = BM + wn * WTN + j * 16 + frow;
+      if (GATED) r = BM + (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
+      else r = BM + wn * WTN + j * 16;
     }
-    return swz64(r, fchunk);
+    return r * kLineBytes + (t ? flane1 : flane0);
   };
 
   f32x4 acc[MB][NB];
@@ -278,73 +286,93 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 fr[2][NF];  // fragments of the current and of the next K step
+  u32x4 fr[2][NF];  // fragments of the two K steps of a buffer
 
-  // prologue: steps 0 .. STAGES-2 in flight, step 0's fragments in fr[0]
+  // prologue: pair 0 and the first half of pair 1 in flight; pair 0 landed;
+  // the first step's fragments in fr[0]
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p) issue(p);
-  wait_vmem<(STAGES - 2) * LPS>();
+  for (int l = 0; l < LPB; ++l) issue_one(0, l, 0);
+#pragma unroll
+  for (int l = 0; l < LH1; ++l) issue_one(1, l, 1);
+  wait_vmem<LH1>();
   stage_barrier();
 #pragma unroll
-  for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f));
+  for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f, 0));
 
-  // One K step (fr[P] holds step s's fragments): the first half of the
-  // MFMAs with the first L1 loads of step s + STAGES - 1 (its ring buffer was
-  // last read in step s - 1, before that step's barrier); wait until step
-  // s + 1 has landed (only the younger loads may still be in flight) and meet
-  // at the barrier; the second half of the MFMAs interleaved with step s + 1's
-  // fragment reads into fr[P ^ 1] and the remaining loads.  Spreading the
-  // loads over the whole step keeps the vector-memory queue from filling up:
-  // a wavefront issues in order, so a load stalled at issue would also hold
-  // back the MFMAs behind it.  In the last step the fragment reads fetch data
-  // that is never used.
+  // One buffer PB = p % 2 holds K steps 2p (fragments in fr[0]) and 2p + 1.
+  //  step 2p    : MFMAs; first half: the last LH2 loads of pair p + 1 into
+  //               PB ^ 1; second half: step 2p + 1's fragments into fr[1].
+  //  step 2p + 1: half the MFMAs; wait for pair p + 1 (the only loads in
+  //               flight) and meet at the barrier, after which nobody reads
+  //               PB again; the rest of the MFMAs while reading step 2p + 2's
+  //               fragments from PB ^ 1 into fr[0] and issuing the first LH1
+  //               loads of pair p + 2 into PB.
   constexpr int HALF = NB / 2;
-  constexpr int QH = MB * HALF;                           // MFMAs per half step
-  constexpr int L1 = LPS / 2, L2 = LPS - L1;              // loads per half step
-  constexpr int PER = QH / NF > 0 ? QH / NF : 1;          // MFMAs per fragment read
-  constexpr int LPER1 = QH / L1 > 0 ? QH / L1 : 1;        // MFMAs per load issue
-  constexpr int LPER2 = QH / L2 > 0 ? QH / L2 : 1;
-  static_assert(QH / LPER1 >= L1 && QH / LPER2 >= L2, "every load is issued in its half step");
-#define MOE_KSTEP(P)                                                                     \
-  {                                                                                      \
-    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                   \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
-        mfma_bf16_agpr(acc[i][j], fr[P][i], fr[P][MB + j]);                              \
-        const int q = j * MB + i;                                                        \
-        if (q % LPER1 == 0 && q / LPER1 < L1) issue_one(s + STAGES - 1, q / LPER1);      \
-        __builtin_amdgcn_sched_barrier(0);                                               \
-      }                                                                                  \
-    }                                                                                    \
-    wait_vmem<(STAGES - 3) * LPS + L1>();                                                \
-    stage_barrier();                                                                     \
-    const char* st = smem + ((s + 1) % STAGES) * STAGE;                                  \
-    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                  \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                   \
-        mfma_bf16_agpr(acc[i][j], fr[P][i], fr[P][MB + j]);                              \
-        const int q = (j - HALF) * MB + i;                                               \
-        if (q % PER == PER - 1 && q / PER < NF)                                          \
-          fr[P ^ 1][q / PER] = *reinterpret_cast<const u32x4*>(st + frag_off(q / PER));  \
-        if (q % LPER2 == 0 && q / LPER2 < L2) issue_one(s + STAGES - 1, L1 + q / LPER2); \
-        __builtin_amdgcn_sched_barrier(0);                                               \
-      }                                                                                  \
-    }                                                                                    \
-    _Pragma("unroll") for (int r = (MB * HALF) / PER; r < NF; ++r)                       \
-      fr[P ^ 1][r] = *reinterpret_cast<const u32x4*>(st + frag_off(r));                  \
-    ++s;                                                                                 \
+  constexpr int QH = MB * HALF;                        // MFMAs per half step
+  constexpr int PER = QH / NF > 0 ? QH / NF : 1;       // MFMAs per fragment read
+  constexpr int LP1 = QH / LH1 > 0 ? QH / LH1 : 1;     // MFMAs per load issue
+  constexpr int LP2 = QH / LH2 > 0 ? QH / LH2 : 1;
+  static_assert(QH / LP1 >= LH1 && QH / LP2 >= LH2, "every load is issued in its half step");
+#define MOE_MFMA(FR, I, J) mfma_bf16_agpr(acc[I][J], fr[FR][I], fr[FR][MB + (J)])
+#define MOE_PAIR(PB)                                                                       \
+  {                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                     \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
+        MOE_MFMA(0, i, j);                                                                 \
+        const int q = j * MB + i;                                                          \
+        if (q % LP2 == 0 && q / LP2 < LH2) issue_one(p + 1, LH1 + q / LP2, (PB) ^ 1);      \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                    \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
+        MOE_MFMA(0, i, j);                                                                 \
+        const int q = (j - HALF) * MB + i;                                                 \
+        if (q % PER == PER - 1 && q / PER < NF)                                            \
+          fr[1][q / PER] =                                                                 \
+              *reinterpret_cast<const u32x4*>(smem + (PB) * BUF + frag_off(q / PER, 1));   \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int r = QH / PER; r < NF; ++r)                                  \
+      fr[1][r] = *reinterpret_cast<const u32x4*>(smem + (PB) * BUF + frag_off(r, 1));      \
+    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                     \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
+        MOE_MFMA(1, i, j);                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+    }                                                                                      \
+    wait_vmem<0>();                                                                        \
+    stage_barrier();                                                                       \
+    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                    \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
+        MOE_MFMA(1, i, j);                                                                 \
+        const int q = (j - HALF) * MB + i;                                                 \
+        if (q % PER == PER - 1 && q / PER < NF)                                            \
+          fr[0][q / PER] = *reinterpret_cast<const u32x4*>(smem + ((PB) ^ 1) * BUF +       \
+                                                           frag_off(q / PER, 0));          \
+        if (q % LP1 == 0 && q / LP1 < LH1) issue_one(p + 2, q / LP1, PB);                  \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int r = QH / PER; r < NF; ++r)                                  \
+      fr[0][r] = *reinterpret_cast<const u32x4*>(smem + ((PB) ^ 1) * BUF + frag_off(r, 0)); \
+    ++p;                                                                                   \
   }
 
-  for (int s = 0; s < nsteps;) {
-    MOE_KSTEP(0)
-    MOE_KSTEP(1)
+  for (int p = 0; p < npairs;) {
+    MOE_PAIR(0)
+    MOE_PAIR(1)
   }
-#undef MOE_KSTEP
+#undef MOE_PAIR
+#undef MOE_MFMA
 
   // -------------------------------------------------------------- epilogue
   wait_vmem<0>();   // this wavefront's last ring loads have landed
   stage_barrier();  // and every wavefront is done with the ring
   mfma_drain();
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
-  static_assert(4 * WTM * (128 + 16) <= STAGES * STAGE, "staging space");
+  static_assert(4 * WTM * (128 + 16) <= 2 * BUF, "staging space");
   char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
   if (part < 0) {
@@ -358,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <bool GATED, int BM, int BNE, int STAGES>
+template <bool GATED, int BM, int BNE>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long n_nt = (g.n_dim + COLS - 1) / COLS;
@@ -367,21 +395,22 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   const long per_xcd = (static_cast<long>(g.tiles_cap) * n_nt + 7) / 8 +
                        (GATED ? 0 : (g.cus + 7) / 8) + 1;
   const long blocks = 8 * per_xcd;
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, STAGES>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s) {
+  if (g.k_dim % 128 != 0) return hipErrorInvalidValue;  // whole pairs of 128-byte buffers
   if (bm == 256) {
-    if (gated) return launch_v<true, 256, 256, 4>(g, s);
-    return launch_v<false, 256, 256, 4>(g, s);
+    if (gated) return launch_v<true, 256, 256>(g, s);
+    return launch_v<false, 256, 256>(g, s);
   }
   if (bm != 128) return hipErrorInvalidValue;
-  if (gated) return launch_v<true, 128, 256, 4>(g, s);
-  return launch_v<false, 128, 256, 4>(g, s);
+  if (gated) return launch_v<true, 128, 256>(g, s);
+  return launch_v<false, 128, 256>(g, s);
 }
 
 }  // namespace moe

@@ -235,9 +235,11 @@ int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_
 }
 
 GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_bytes,
-                   size_t w_bytes) {
+                   size_t w_bytes, int k_dim) {
   const bool small_offsets = a_bytes < (size_t{1} << 32) && w_bytes < (size_t{1} << 32);
-  if (dtype != 1 || !small_offsets) return GemmPick{0, rows_per_expert <= 48 ? 32 : 128};
+  // the large-tile kernel streams whole pairs of 128-byte row buffers
+  if (dtype != 1 || !small_offsets || k_dim % 128 != 0)
+    return GemmPick{0, rows_per_expert <= 48 ? 32 : 128};
   if (rows_per_expert <= 48) return GemmPick{0, 32};
   if (rows_per_expert >= 512) return GemmPick{1, 256};
   return GemmPick{1, 128};

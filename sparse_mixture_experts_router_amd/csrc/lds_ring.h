@@ -43,4 +43,22 @@ __device__ __forceinline__ int swz64(int r, int c) { return r * kRowBytes + ((c 
 // the logical chunk it must fetch so that the block matches swz64:
 __device__ __forceinline__ int ring_lane_chunk(int lane) { return (lane & 3) ^ ((lane >> 3) & 3); }
 
+// 128-byte rows: one whole cache line per row and buffer (two K steps of 32
+// bf16).  Chunk c (0..7) of row r is stored at chunk c ^ key(r), with
+// key(r) = (r mod 8) ^ (bit 3 of r): the 16 lanes of a ds_read_b128 fragment
+// group (16 consecutive rows, one logical chunk) then hit 16 distinct 16-byte
+// bank groups of a 256-byte bank row, and any 8 consecutive ones 8 distinct
+// groups of a 128-byte one.
+constexpr int kLineBytes = 128;
+__device__ __forceinline__ int swz128_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz128(int r, int c) { return r * kLineBytes + ((c ^ swz128_key(r)) << 4); }
+
+// For a 1 KB block (8 rows of 128 bytes, block index blk within the buffer)
+// written by one global_load_lds_dwordx4, lane l lands in physical chunk
+// l % 8 of row 8 blk + l / 8; the logical chunk it must fetch so that the
+// block matches swz128:
+__device__ __forceinline__ int line_lane_chunk(int lane, int blk) {
+  return (lane & 7) ^ (lane >> 3) ^ (blk & 1);
+}
+
 }  // namespace moe

@@ -64,8 +64,8 @@ Plan make_plan(const moe_config& c) {
   const size_t rows_all = static_cast<size_t>(c.T) * (c.top_k + c.n_shared);
   const size_t w_mat = static_cast<size_t>(c.d_model) * c.d_ff * eb_;
   p.up = pick_gemm(c.dtype, true, rows_per_expert, static_cast<size_t>(c.T) * c.d_model * eb_,
-                   w_mat);
-  p.down = pick_gemm(c.dtype, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat);
+                   w_mat, c.d_model);
+  p.down = pick_gemm(c.dtype, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat, c.d_ff);
   p.bm_up = p.up.bm;
   p.bm_down = p.down.bm;
   p.cap_up = static_cast<int>(tile_capacity(c, p.bm_up));
@@ -103,10 +103,9 @@ Plan make_plan(const moe_config& c) {
   if (p.dsplit <= 1 && p.down.variant == 1) {
     // tail split of the large-tile down GEMM (256 output columns per tile)
     const int nnt = (c.d_model + 255) / 256;
-    const int nsteps = c.d_ff * 2 / 64;
     p.split.tail_nnt = nnt;
     p.split.tail_cap_rows = static_cast<long>(p.cus / nnt) * p.bm_down;
-    p.split.tail_max_parts = nsteps / 16 < 8 ? nsteps / 16 : 8;
+    p.split.tail_max_parts = max_split_parts(c.d_ff * 2 / 128, 8);
     if (p.split.tail_cap_rows < 2L * p.bm_down || p.split.tail_max_parts < 2) {
       p.split.tail_nnt = 0;
       p.split.tail_cap_rows = 0;

@@ -99,6 +99,22 @@ struct GemmArgs {
   int cus;                   // compute units of the device (grid sizing)
 };
 
+// Pairs of K steps (128-byte row buffers) that each of `parts` pieces of an
+// n-pair reduction takes in the large-tile GEMM: an even count (its loop
+// runs two buffers per iteration), the last piece taking what is left.
+__host__ __device__ inline int split_share(int n, int parts) {
+  const int per = (n + parts - 1) / parts;
+  return (per + 1) & ~1;
+}
+// The most pieces (<= cap, each >= 8 pairs and none empty) an n-pair
+// reduction splits into.
+inline int max_split_parts(int n, int cap) {
+  int best = 1;
+  for (int p = 2; p <= cap; ++p)
+    if (n / p >= 8 && (p - 1) * split_share(n, p) < n) best = p;
+  return best;
+}
+
 // Device-side plan of a down pass whose reduction is split over workgroups,
 // written by the scan kernel after ntiles[0..1]: the combine kernel adds the
 // fp32 parts of every row at or past kPlanRowSplit.
@@ -116,7 +132,8 @@ struct GemmPick {
 };
 // a_bytes / w_bytes: bytes of the A operand (all its rows) and of one expert's
 // weight matrix; the direct-to-LDS kernel addresses both with 32-bit offsets.
-GemmPick pick_gemm(int dtype, bool gated, long rows_per_expert, size_t a_bytes, size_t w_bytes);
+GemmPick pick_gemm(int dtype, bool gated, long rows_per_expert, size_t a_bytes, size_t w_bytes,
+                   int k_dim);
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
