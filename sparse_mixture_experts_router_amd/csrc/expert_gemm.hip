@@ -124,7 +124,7 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
   }
 }
 
-template <bool GATED, int BM, int BNE>
+template <bool GATED, int BM, int BNE, int NBUF>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   constexpr int ROWS = BM + BNE;               // rows staged per buffer
   constexpr int BUF = ROWS * kLineBytes;       // bytes per buffer
@@ -136,23 +136,22 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   constexpr int LPB = A_BPW + B_BPW;           // loads per lane per buffer
   constexpr int LH1 = LPB / 2, LH2 = LPB - LH1;  // issued after the barrier / in the next step
   constexpr int NF = MB + NB;                  // fragments per K step
-  // Column tiles per band (see the header): the ~32 workgroups an XCD runs
-  // at once cover about 16 row tiles next to 2 weight tiles.
-  constexpr int kBandCols = 2;
   static_assert(BM % 64 == 0 && BNE % 64 == 0, "tile shape");
   static_assert(A_BPW % 2 == 0 && B_BPW % 2 == 0, "a load's block parity is its index parity");
   static_assert(!GATED || (COLS % (B_BPW * 8) == 0 && NB % 2 == 0),
                 "a wavefront's B blocks are all gate or all up rows");
-  static_assert(LPB < 64, "vmcnt range");
+  static_assert(NBUF >= 2 && (NBUF - 1) * LPB + LH1 < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
 
   // ------------------------------------------------------- work of this block
-  // Work items: the (row tile, column tile) pairs, then (plain pass only)
-  // the pieces (part, tile, column tile) of the last `tail` row tiles when
-  // the scan split them over their reduction.  Each XCD (blocks take XCDs
-  // round-robin) gets an equal contiguous share of both lists and runs it in
-  // order; the pairs are ordered by bands of column tiles.
+  // Work items: the (row tile, column tile) pairs of the scan's item list,
+  // then (plain pass only) the pieces (part, tile, column tile) of the last
+  // `tail` row tiles when the scan split them over their reduction.  Each XCD
+  // (blocks take XCDs round-robin) gets an equal contiguous share of both
+  // lists and runs it in order, so the workgroups it runs at once are one
+  // block of the list: one expert's row tiles next to a band of its weight
+  // tiles.
   const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
   const int n_nt = (g.n_dim + COLS - 1) / COLS;
   const int ntl = *g.ntiles;
@@ -168,18 +167,9 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const long s_lo = w_spl * xcd / 8, s_cnt = w_spl * (xcd + 1) / 8 - s_lo;
   int tile, nt, part = -1;
   if (idx < n_cnt) {
-    const int lin = static_cast<int>(n_lo + idx);
-    const int full_bands = n_nt / kBandCols;
-    const int band_blocks = nrm * kBandCols;
-    if (lin < full_bands * band_blocks) {
-      const int band = lin / band_blocks, rem = lin - band * band_blocks;
-      tile = rem / kBandCols;
-      nt = band * kBandCols + rem % kBandCols;
-    } else {
-      const int rem = lin - full_bands * band_blocks, gn = n_nt - full_bands * kBandCols;
-      tile = rem / gn;
-      nt = full_bands * kBandCols + rem % gn;
-    }
+    const int v = g.items[n_lo + idx];
+    tile = v >> kItemColBits;
+    nt = v & ((1 << kItemColBits) - 1);
   } else if (idx - n_cnt < s_cnt) {
     const int lin = static_cast<int>(s_lo + idx - n_cnt);
     part = lin / (tail * n_nt);
@@ -288,91 +278,100 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 
   u32x4 fr[2][NF];  // fragments of the two K steps of a buffer
 
-  // prologue: pair 0 and the first half of pair 1 in flight; pair 0 landed;
-  // the first step's fragments in fr[0]
+  // prologue: pairs 0 .. NBUF-2 and the first half of pair NBUF-1 in
+  // flight; pair 0 landed; the first step's fragments in fr[0]
 #pragma unroll
-  for (int l = 0; l < LPB; ++l) issue_one(0, l, 0);
+  for (int q = 0; q < NBUF - 1; ++q)
 #pragma unroll
-  for (int l = 0; l < LH1; ++l) issue_one(1, l, 1);
-  wait_vmem<LH1>();
+    for (int l = 0; l < LPB; ++l) issue_one(q, l, q);
+#pragma unroll
+  for (int l = 0; l < LH1; ++l) issue_one(NBUF - 1, l, NBUF - 1);
+  wait_vmem<(NBUF - 2) * LPB + LH1>();
   stage_barrier();
 #pragma unroll
   for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f, 0));
 
-  // One buffer PB = p % 2 holds K steps 2p (fragments in fr[0]) and 2p + 1.
-  //  step 2p    : MFMAs; first half: the last LH2 loads of pair p + 1 into
-  //               PB ^ 1; second half: step 2p + 1's fragments into fr[1].
-  //  step 2p + 1: half the MFMAs; wait for pair p + 1 (the only loads in
-  //               flight) and meet at the barrier, after which nobody reads
-  //               PB again; the rest of the MFMAs while reading step 2p + 2's
-  //               fragments from PB ^ 1 into fr[0] and issuing the first LH1
-  //               loads of pair p + 2 into PB.
+  // Pair p (buffer cur = p mod NBUF) = K steps 2p (fragments in fr[0]) and
+  // 2p + 1.
+  //  step 2p    : MFMAs; first half: the last LH2 loads of pair p + NBUF - 1
+  //               into buffer cur - 1 (free since the previous barrier);
+  //               second half: step 2p + 1's fragments into fr[1].
+  //  step 2p + 1: half the MFMAs; wait for pair p + 1 (pairs p + 2 ..
+  //               p + NBUF - 1 may still be in flight) and meet at the
+  //               barrier, after which nobody reads buffer cur again; the
+  //               rest of the MFMAs while reading step 2p + 2's fragments
+  //               from buffer cur + 1 into fr[0] and issuing the first LH1
+  //               loads of pair p + NBUF into buffer cur.
   constexpr int HALF = NB / 2;
   constexpr int QH = MB * HALF;                        // MFMAs per half step
   constexpr int PER = QH / NF > 0 ? QH / NF : 1;       // MFMAs per fragment read
   constexpr int LP1 = QH / LH1 > 0 ? QH / LH1 : 1;     // MFMAs per load issue
   constexpr int LP2 = QH / LH2 > 0 ? QH / LH2 : 1;
   static_assert(QH / LP1 >= LH1 && QH / LP2 >= LH2, "every load is issued in its half step");
-#define MOE_MFMA(FR, I, J) mfma_bf16_agpr(acc[I][J], fr[FR][I], fr[FR][MB + (J)])
-#define MOE_PAIR(PB)                                                                       \
-  {                                                                                        \
-    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                     \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
-        MOE_MFMA(0, i, j);                                                                 \
-        const int q = j * MB + i;                                                          \
-        if (q % LP2 == 0 && q / LP2 < LH2) issue_one(p + 1, LH1 + q / LP2, (PB) ^ 1);      \
-        __builtin_amdgcn_sched_barrier(0);                                                 \
-      }                                                                                    \
-    }                                                                                      \
-    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                    \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
-        MOE_MFMA(0, i, j);                                                                 \
-        const int q = (j - HALF) * MB + i;                                                 \
-        if (q % PER == PER - 1 && q / PER < NF)                                            \
-          fr[1][q / PER] =                                                                 \
-              *reinterpret_cast<const u32x4*>(smem + (PB) * BUF + frag_off(q / PER, 1));   \
-        __builtin_amdgcn_sched_barrier(0);                                                 \
-      }                                                                                    \
-    }                                                                                      \
-    _Pragma("unroll") for (int r = QH / PER; r < NF; ++r)                                  \
-      fr[1][r] = *reinterpret_cast<const u32x4*>(smem + (PB) * BUF + frag_off(r, 1));      \
-    _Pragma("unroll") for (int j = 0; j < HALF; ++j) {                                     \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
-        MOE_MFMA(1, i, j);                                                                 \
-        __builtin_amdgcn_sched_barrier(0);                                                 \
-      }                                                                                    \
-    }                                                                                      \
-    wait_vmem<0>();                                                                        \
-    stage_barrier();                                                                       \
-    _Pragma("unroll") for (int j = HALF; j < NB; ++j) {                                    \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                     \
-        MOE_MFMA(1, i, j);                                                                 \
-        const int q = (j - HALF) * MB + i;                                                 \
-        if (q % PER == PER - 1 && q / PER < NF)                                            \
-          fr[0][q / PER] = *reinterpret_cast<const u32x4*>(smem + ((PB) ^ 1) * BUF +       \
-                                                           frag_off(q / PER, 0));          \
-        if (q % LP1 == 0 && q / LP1 < LH1) issue_one(p + 2, q / LP1, PB);                  \
-        __builtin_amdgcn_sched_barrier(0);                                                 \
-      }                                                                                    \
-    }                                                                                      \
-    _Pragma("unroll") for (int r = QH / PER; r < NF; ++r)                                  \
-      fr[0][r] = *reinterpret_cast<const u32x4*>(smem + ((PB) ^ 1) * BUF + frag_off(r, 0)); \
-    ++p;                                                                                   \
+  int cur = 0;  // wave-uniform
+  for (int p = 0; p < npairs; ++p) {
+    const int prv = cur == 0 ? NBUF - 1 : cur - 1;
+    const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+    const char* const bcur = smem + cur * BUF;
+    const char* const bnxt = smem + nxt * BUF;
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        mfma_bf16_agpr(acc[i][j], fr[0][i], fr[0][MB + j]);
+        const int q = j * MB + i;
+        if (q % LP2 == 0 && q / LP2 < LH2) issue_one(p + NBUF - 1, LH1 + q / LP2, prv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int j = HALF; j < NB; ++j) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        mfma_bf16_agpr(acc[i][j], fr[0][i], fr[0][MB + j]);
+        const int q = (j - HALF) * MB + i;
+        if (q % PER == PER - 1 && q / PER < NF)
+          fr[1][q / PER] = *reinterpret_cast<const u32x4*>(bcur + frag_off(q / PER, 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int r = QH / PER; r < NF; ++r)
+      fr[1][r] = *reinterpret_cast<const u32x4*>(bcur + frag_off(r, 1));
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        mfma_bf16_agpr(acc[i][j], fr[1][i], fr[1][MB + j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmem<(NBUF - 2) * LPB>();
+    stage_barrier();
+#pragma unroll
+    for (int j = HALF; j < NB; ++j) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        mfma_bf16_agpr(acc[i][j], fr[1][i], fr[1][MB + j]);
+        const int q = (j - HALF) * MB + i;
+        if (q % PER == PER - 1 && q / PER < NF)
+          fr[0][q / PER] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(q / PER, 0));
+        if (q % LP1 == 0 && q / LP1 < LH1) issue_one(p + NBUF, q / LP1, cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int r = QH / PER; r < NF; ++r)
+      fr[0][r] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(r, 0));
+    cur = nxt;
   }
-
-  for (int p = 0; p < npairs;) {
-    MOE_PAIR(0)
-    MOE_PAIR(1)
-  }
-#undef MOE_PAIR
-#undef MOE_MFMA
 
   // -------------------------------------------------------------- epilogue
   wait_vmem<0>();   // this wavefront's last ring loads have landed
   stage_barrier();  // and every wavefront is done with the ring
   mfma_drain();
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
-  static_assert(4 * WTM * (128 + 16) <= 2 * BUF, "staging space");
+  static_assert(4 * WTM * (128 + 16) <= NBUF * BUF, "staging space");
   char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
   if (part < 0) {
@@ -386,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <bool GATED, int BM, int BNE>
+template <bool GATED, int BM, int BNE, int NBUF>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long n_nt = (g.n_dim + COLS - 1) / COLS;
@@ -395,7 +394,7 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   const long per_xcd = (static_cast<long>(g.tiles_cap) * n_nt + 7) / 8 +
                        (GATED ? 0 : (g.cus + 7) / 8) + 1;
   const long blocks = 8 * per_xcd;
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -404,13 +403,15 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s) {
   if (g.k_dim % 128 != 0) return hipErrorInvalidValue;  // whole pairs of 128-byte buffers
+  // buffers of 64 KB (256-row tiles: 2 fit in the LDS) or 48 KB (128-row
+  // tiles: 3 fit, keeping two pairs of K steps in flight)
   if (bm == 256) {
-    if (gated) return launch_v<true, 256, 256>(g, s);
-    return launch_v<false, 256, 256>(g, s);
+    if (gated) return launch_v<true, 256, 256, 2>(g, s);
+    return launch_v<false, 256, 256, 2>(g, s);
   }
   if (bm != 128) return hipErrorInvalidValue;
-  if (gated) return launch_v<true, 128, 256>(g, s);
-  return launch_v<false, 128, 256>(g, s);
+  if (gated) return launch_v<true, 128, 256, 3>(g, s);
+  return launch_v<false, 128, 256, 3>(g, s);
 }
 
 }  // namespace moe

@@ -45,6 +45,7 @@ struct Plan {
   int ksplit;  // router reduction split
   int dsplit;  // down-pass reduction split
   SplitSpec split;  // what the scan may record in the down pass's split plan
+  int nnt_up, nnt_down;  // column tiles of the large-tile GEMMs (0: generic kernel)
   int cus;          // compute units of the current device
   int bm_up, bm_down;
   int cap_up, cap_down;
@@ -54,7 +55,7 @@ struct Plan {
 
 enum {
   R_IDX, R_GATE, R_LRANK, R_PART, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
-  R_TUP, R_TDN, R_NT, R_HID, R_YP, R_YPART, R_COUNT
+  R_TUP, R_TDN, R_IUP, R_IDN, R_NT, R_HID, R_YP, R_YPART, R_COUNT
 };
 
 Plan make_plan(const moe_config& c) {
@@ -66,6 +67,10 @@ Plan make_plan(const moe_config& c) {
   p.up = pick_gemm(c.dtype, true, rows_per_expert, static_cast<size_t>(c.T) * c.d_model * eb_,
                    w_mat, c.d_model);
   p.down = pick_gemm(c.dtype, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat, c.d_ff);
+  // the large-tile kernel's work items hold tile indices below kItemMaxTiles
+  if (p.up.variant == 1 && tile_capacity(c, p.up.bm) >= kItemMaxTiles) p.up = GemmPick{0, 128};
+  if (p.down.variant == 1 && tile_capacity(c, p.down.bm) >= kItemMaxTiles)
+    p.down = GemmPick{0, 128};
   p.bm_up = p.up.bm;
   p.bm_down = p.down.bm;
   p.cap_up = static_cast<int>(tile_capacity(c, p.bm_up));
@@ -90,6 +95,12 @@ Plan make_plan(const moe_config& c) {
   sz[R_INV] = T * k * 4;
   sz[R_TUP] = static_cast<size_t>(p.cap_up) * 8;
   sz[R_TDN] = static_cast<size_t>(p.cap_down) * 8;
+  // work-item lists of the large-tile kernel (128 gate/up columns, 256 down
+  // columns per tile)
+  p.nnt_up = p.up.variant == 1 ? (c.d_ff + 127) / 128 : 0;
+  p.nnt_down = p.down.variant == 1 ? (c.d_model + 255) / 256 : 0;
+  sz[R_IUP] = static_cast<size_t>(p.cap_up) * p.nnt_up * 4;
+  sz[R_IDN] = static_cast<size_t>(p.cap_down) * p.nnt_down * 4;
   sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
   p.dsplit = down_split(c.dtype, p.down, p.cap_down, c.d_model, c.d_ff);
@@ -139,6 +150,8 @@ Workspace carve(const Plan& p, void* base) {
   w.inv_row = reinterpret_cast<int32_t*>(b + p.off[R_INV]);
   w.tiles_up = reinterpret_cast<int2*>(b + p.off[R_TUP]);
   w.tiles_down = reinterpret_cast<int2*>(b + p.off[R_TDN]);
+  w.items_up = reinterpret_cast<int32_t*>(b + p.off[R_IUP]);
+  w.items_down = reinterpret_cast<int32_t*>(b + p.off[R_IDN]);
   w.ntiles = reinterpret_cast<int32_t*>(b + p.off[R_NT]);
   w.hidden = b + p.off[R_HID];
   w.yperm = b + p.off[R_YP];
@@ -210,7 +223,11 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
 moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
                     hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
-                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split, ws.blk_base,
+                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
+                               ItemSpec{p.nnt_up, p.nnt_down, p.cus / 8 > 0 ? p.cus / 8 : 1,
+                                        p.nnt_up ? ws.items_up : nullptr,
+                                        p.nnt_down ? ws.items_down : nullptr},
+                               ws.blk_base,
                                ws.counts,
                                ws.prob_sum, out ? out->counts : nullptr,
                                out ? out->prob_sum : nullptr, ws.offsets, ws.tiles_up,
@@ -313,6 +330,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   up.n_dim = c.d_ff;
   up.tiles_cap = p.cap_up;
   up.cus = p.cus;
+  up.items = ws.items_up;
   if ((err = launch_gemm(c.dtype, true, p.up, up, s)) != hipSuccess)
     return hip_fail(err, "gate/up GEMM");
 
@@ -335,6 +353,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   dn.out_part = ws.ypart;
   dn.plan = ws.ntiles + 2;
   dn.cus = p.cus;
+  dn.items = ws.items_down;
   if ((err = launch_gemm(c.dtype, false, p.down, dn, s)) != hipSuccess)
     return hip_fail(err, "down GEMM");
 

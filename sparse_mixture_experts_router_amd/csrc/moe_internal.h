@@ -35,6 +35,8 @@ struct Workspace {
   int32_t* inv_row;    // [T, k]
   int2* tiles_up;      // tile list of the gate/up GEMM
   int2* tiles_down;    // tile list of the down GEMM
+  int32_t* items_up;   // work items of the large-tile gate/up GEMM (when used)
+  int32_t* items_down; // and of the large-tile down GEMM
   int32_t* ntiles;     // [kPlanInts]: entries in tiles_up, tiles_down, then the down-pass
                        // split plan (see kPlan*)
   void* hidden;        // [T k + S T, F]  dtype
@@ -58,6 +60,20 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router,
 // Split of the down pass recorded in the plan: parts > 1 splits every row
 // (decode); otherwise tail_nnt > 0 lets the scan split the last row tiles of
 // a tail_nnt-column-tile grid that would leave cus compute units mostly idle.
+// Work-item lists of the large-tile GEMMs, written by the scan kernel: for
+// every row group (expert) its row tiles x column tiles, in blocks of up to
+// 8 row tiles x (window / row tiles) column tiles, so the `window`
+// workgroups an XCD runs at once cover one expert's rows next to a band of
+// its weight tiles.  nnt = 0: no list for that pass.
+struct ItemSpec {
+  int nnt_up, nnt_down;  // column tiles of the gate/up and down passes
+  int window;            // workgroups one XCD runs at once
+  int32_t* items_up;
+  int32_t* items_down;
+};
+constexpr int kItemColBits = 12;  // column tile in the low bits of an item
+constexpr int kItemMaxTiles = 1 << 19;
+
 struct SplitSpec {
   int parts;      // host split of every row (grouped_gemm.hip), or <= 1
   int tail_nnt;   // column tiles of the down pass (0: no tail split)
@@ -67,7 +83,8 @@ struct SplitSpec {
 };
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
                        int N, int k, int S, int bm_up, int cap_up, int bm_down,
-                       int cap_down, const SplitSpec& split, int32_t* blk_base,
+                       int cap_down, const SplitSpec& split, const ItemSpec& items,
+                       int32_t* blk_base,
                        int32_t* counts, float* prob_sum, int32_t* user_counts,
                        float* user_prob_sum, int32_t* offsets, int2* tiles_up,
                        int2* tiles_down, int32_t* ntiles, hipStream_t s);
@@ -96,6 +113,7 @@ struct GemmArgs {
   int ksplit;                // > 1: reduction split over workgroups (plain pass only)
   float* out_part;           // fp32 partial outputs [ksplit, a_rows, n_dim] when ksplit > 1
   const int32_t* plan;       // device split plan of the down pass (kPlan* entries), or null
+  const int32_t* items;      // large-tile kernel: work items, (tile << 12) | column tile
   int cus;                   // compute units of the device (grid sizing)
 };
 

@@ -54,9 +54,42 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return res;
 }
 
+// Work items of a large-tile GEMM with nnt column tiles, over the row tiles
+// [0, tlimit): per row group (tile range [tb[g], tb[g + 1])) blocks of up to
+// 8 row tiles x (window / row tiles) column tiles, column by column, the
+// group's items starting at tb[g] * nnt.  The 1024 threads take items i,
+// i + 1024, ... and find the group of item i by binary search over tb
+// (ng + 1 entries, non-decreasing).
+__device__ void write_items(int32_t* __restrict__ items, int nnt, const int* tb, int ng,
+                            int tlimit, int window) {
+  if (items == nullptr || nnt <= 0) return;
+  const int total = tlimit * nnt;  // < 2^31: tiles < kItemMaxTiles, nnt < 2^kItemColBits
+  for (int i = threadIdx.x; i < total; i += kScanThreads) {
+    const int tt = i / nnt;
+    int lo = 0, hi = ng;  // largest g with tb[g] <= tt
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tb[mid] <= tt) lo = mid;
+      else hi = mid;
+    }
+    const int base = tb[lo];
+    const int T = min(tb[lo + 1], tlimit) - base;
+    const int TW = min(T, 8), CW = max(1, window / TW);
+    const int q = i - base * nnt;
+    const int b = q / (TW * nnt);
+    const int r = q - b * TW * nnt;
+    const int tw = min(TW, T - b * TW);
+    const int cbi = r / (tw * CW);
+    const int r2 = r - cbi * tw * CW;
+    const int c = cbi * CW + r2 / tw;
+    const int t = b * TW + r2 % tw;
+    items[i] = ((base + t) << kItemColBits) | c;
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
-    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split,
+    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split, ItemSpec ispec,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
     int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
     int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
@@ -65,6 +98,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __shared__ float s_ps[kScanThreads];
   __shared__ int s_tmp[64];
   __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_nrm_down;  // down-pass tiles not split over the reduction
+  __shared__ int s_tbu[kMaxExperts + kMaxShared + 1];  // first tile of each group
+  __shared__ int s_tbd[kMaxExperts + kMaxShared + 1];
 
   const int tid = threadIdx.x;
   const int B = (n_tok + kRouteTokens - 1) / kRouteTokens;
@@ -169,7 +205,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     plan[kPlanRowSplit] = row_split;
     plan[kPlanStride] = stride;
     plan[kPlanTailTiles] = tail;
+    s_nrm_down = ntd - tail;
+    s_tbu[NG] = total_up;
+    s_tbd[NG] = total_down;
   }
+  if (tid < NG) {
+    s_tbu[tid] = base_up;
+    s_tbd[tid] = base_down;
+  }
+  __syncthreads();
+  write_items(ispec.items_up, ispec.nnt_up, s_tbu, NG, min(total_up, cap_up), ispec.window);
+  write_items(ispec.items_down, ispec.nnt_down, s_tbd, NG, s_nrm_down, ispec.window);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
@@ -198,11 +244,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
                        int S, int bm_up, int cap_up, int bm_down, int cap_down,
-                       const SplitSpec& split, int32_t* blk_base, int32_t* counts, float* prob_sum,
+                       const SplitSpec& split, const ItemSpec& items, int32_t* blk_base, int32_t* counts, float* prob_sum,
                        int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
                        int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
-                     k, S, bm_up, cap_up, bm_down, cap_down, split, blk_base, counts, prob_sum,
+                     k, S, bm_up, cap_up, bm_down, cap_down, split, items, blk_base, counts,
+                     prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
   return hipGetLastError();
 }
