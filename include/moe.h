@@ -142,7 +142,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const void* x,
 /* moe_layer_forward that also records stage_events[i] (hipEvent_t, created by
  * the caller) on `stream` before stage i and stage_events[MOE_STAGE_COUNT]
  * after the last one, so the caller can time each stage.  stage_events may be
- * NULL (then identical to moe_layer_forward). */
+ * NULL (then identical to moe_layer_forward), and so may any entry (that
+ * marker is skipped: a caller timing one stage records only its two). */
 moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x,
                                    const moe_weights* w, void* y,
                                    moe_routing* out, void* workspace,

@@ -174,7 +174,8 @@ def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Option
     """Whole layer forward into ``y``; see ``moe_layer_forward`` in include/moe.h.
 
     ``stage_events``: optional list of len(STAGES) + 1 ``torch.cuda.Event``
-    (enable_timing=True) recorded before each stage and after the last.
+    (enable_timing=True) or None, recorded before each stage and after the
+    last; None entries are skipped.
     """
     dt = _TORCH_DTYPE[cfg.dtype]
     w = _weights(cfg, weights)
@@ -189,9 +190,10 @@ def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Option
         raise ValueError("need one event per stage plus one")
     s = torch.cuda.current_stream() if stream is None else stream
     for ev in stage_events:      # torch creates the HIP event on first record
-        if not ev.cuda_event:
+        if ev is not None and not ev.cuda_event:
             ev.record(s)
-    arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+    arr = (ctypes.c_void_p * len(stage_events))(
+        *[None if ev is None else ev.cuda_event for ev in stage_events])
     _check(lib().moe_layer_forward_timed(*args, arr))
 
 

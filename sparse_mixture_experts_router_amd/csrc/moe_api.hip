@@ -205,7 +205,7 @@ moe_status check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
 }
 
 void mark(void* const* ev, int i, hipStream_t s) {
-  if (ev != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+  if (ev != nullptr && ev[i] != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
 }
 
 // Shared by moe_route and moe_layer_forward: route + block statistics + scan.
