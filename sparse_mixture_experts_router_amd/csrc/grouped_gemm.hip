@@ -222,16 +222,18 @@ hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g,
 }
 
 // Split of the down pass over workgroups for few-row (weight-streaming)
-// shapes: enough workgroups to keep several in flight per CU, each with at
-// least 16 K steps.
-int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_dim) {
+// shapes: as many pieces as keep every workgroup of the pass resident at
+// once (about 4 of these 24 KB-LDS workgroups per CU), so the pass runs as
+// one round with all of its loads in flight, each piece >= 16 K steps.
+// tiles_est: row tiles the pass will have (at most its tile capacity).
+int down_split(int dtype, const GemmPick& pick, long tiles_est, int n_dim, int k_dim, int cus) {
   if (pick.variant != 0 || pick.bm != 32) return 1;
-  const long blocks = static_cast<long>(tiles_cap) * ((n_dim + 63) / 64);
+  const long blocks = tiles_est * ((n_dim + 63) / 64);
   const int nsteps = static_cast<int>(static_cast<long>(k_dim) * (dtype == 1 ? 2 : 4) / 128);
-  int ks = static_cast<int>((2048 + blocks - 1) / blocks);
+  long ks = blocks > 0 ? (4L * cus) / blocks : 1;
   ks = ks > 8 ? 8 : ks;
   ks = ks > nsteps / 16 ? nsteps / 16 : ks;
-  return ks < 1 ? 1 : ks;
+  return ks < 2 ? 1 : static_cast<int>(ks);
 }
 
 GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_bytes,

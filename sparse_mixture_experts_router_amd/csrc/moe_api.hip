@@ -103,13 +103,24 @@ Plan make_plan(const moe_config& c) {
   sz[R_IDN] = static_cast<size_t>(p.cap_down) * p.nnt_down * 4;
   sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
-  p.dsplit = down_split(c.dtype, p.down, p.cap_down, c.d_model, c.d_ff);
-  sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
+
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   p.cus = cus > 0 ? cus : 256;
+  {
+    // row tiles the down pass will have: about one per expert that gets
+    // rows (at most min(N, T k) of them) or T k / bm, whichever is more,
+    // plus the shared experts' tiles, at most the capacity
+    const long tk = static_cast<long>(T * k), bm = p.bm_down;
+    const long used = static_cast<long>(N) < tk ? static_cast<long>(N) : tk;
+    const long routed = (tk + bm - 1) / bm > used ? (tk + bm - 1) / bm : used;
+    long est = routed + static_cast<long>(S) * ((static_cast<long>(T) + bm - 1) / bm);
+    if (est > p.cap_down) est = p.cap_down;
+    p.dsplit = down_split(c.dtype, p.down, est, c.d_model, c.d_ff, p.cus);
+  }
+  sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
   p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};
   if (p.dsplit <= 1 && p.down.variant == 1) {
     // tail split of the large-tile down GEMM (256 output columns per tile)
@@ -220,14 +231,15 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
   return MOE_OK;
 }
 
+// sc.sorted_tok != nullptr: the scan kernel also writes the permutation.
 moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
-                    hipStream_t s) {
+                    const ScatterSpec& sc, hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
                                p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
                                ItemSpec{p.nnt_up, p.nnt_down, p.cus / 8 > 0 ? p.cus / 8 : 1,
                                         p.nnt_up ? ws.items_up : nullptr,
                                         p.nnt_down ? ws.items_down : nullptr},
-                               ws.blk_base,
+                               sc, ws.blk_base,
                                ws.counts,
                                ws.prob_sum, out ? out->counts : nullptr,
                                out ? out->prob_sum : nullptr, ws.offsets, ws.tiles_up,
@@ -279,7 +291,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = run_route(c, p, ws, x, *w, out, out->topk_idx, out->topk_gate, s)) != MOE_OK) return st;
   if (out->counts != nullptr || out->prob_sum != nullptr) {
-    if ((st = run_scan(c, p, ws, out, s)) != MOE_OK) return st;
+    if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
   }
   return MOE_OK;
 }
@@ -307,10 +319,18 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   if ((st = run_route(c, p, ws, x, *w, out, idx, gate, s)) != MOE_OK) return st;
 
   mark(ev, MOE_STAGE_PERMUTE, s);
-  if ((st = run_scan(c, p, ws, out, s)) != MOE_OK) return st;
-  hipError_t err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts,
-                                  c.top_k, c.n_shared, ws.sorted_tok, ws.inv_row, s);
-  if (err != hipSuccess) return hip_fail(err, "scatter kernel");
+  const long n_rows = static_cast<long>(c.T) * (c.top_k + c.n_shared);
+  hipError_t err = hipSuccess;
+  if (n_rows <= kScanScatterMaxRows) {  // one launch for scan and permutation
+    if ((st = run_scan(c, p, ws, out, ScatterSpec{idx, ws.lrank, ws.sorted_tok, ws.inv_row}, s)) !=
+        MOE_OK)
+      return st;
+  } else {
+    if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
+    err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts, c.top_k,
+                         c.n_shared, ws.sorted_tok, ws.inv_row, s);
+    if (err != hipSuccess) return hip_fail(err, "scatter kernel");
+  }
 
   mark(ev, MOE_STAGE_EXPERT_UP, s);
   GemmArgs up{};

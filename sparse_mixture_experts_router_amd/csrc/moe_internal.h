@@ -74,6 +74,16 @@ struct ItemSpec {
 constexpr int kItemColBits = 12;  // column tile in the low bits of an item
 constexpr int kItemMaxTiles = 1 << 19;
 
+// Permutation written by the scan kernel itself (sorted_tok != nullptr, for
+// small batches) instead of a separate scatter launch.
+struct ScatterSpec {
+  const int32_t* topk_idx;
+  const int32_t* lrank;
+  int32_t* sorted_tok;
+  int32_t* inv_row;
+};
+constexpr long kScanScatterMaxRows = 2048;  // two rows per scan thread
+
 struct SplitSpec {
   int parts;      // host split of every row (grouped_gemm.hip), or <= 1
   int tail_nnt;   // column tiles of the down pass (0: no tail split)
@@ -84,7 +94,7 @@ struct SplitSpec {
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
                        int N, int k, int S, int bm_up, int cap_up, int bm_down,
                        int cap_down, const SplitSpec& split, const ItemSpec& items,
-                       int32_t* blk_base,
+                       const ScatterSpec& sc, int32_t* blk_base,
                        int32_t* counts, float* prob_sum, int32_t* user_counts,
                        float* user_prob_sum, int32_t* offsets, int2* tiles_up,
                        int2* tiles_down, int32_t* ntiles, hipStream_t s);
@@ -162,7 +172,7 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
 hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
                           const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
                           int T, int d, int k, int S, void* y, hipStream_t s);
-int down_split(int dtype, const GemmPick& pick, int tiles_cap, int n_dim, int k_dim);
+int down_split(int dtype, const GemmPick& pick, long tiles_est, int n_dim, int k_dim, int cus);
 
 hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
                           const float* prob_sum, float alpha, float* f_out,

@@ -54,6 +54,31 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return res;
 }
 
+// Row i of the permutation: (token, slot) pairs first, then the shared
+// experts' rows.
+__device__ __forceinline__ void scatter_row(long i, const int32_t* __restrict__ topk_idx,
+                                            const int32_t* __restrict__ lrank,
+                                            const int32_t* __restrict__ blk_base,
+                                            const int32_t* __restrict__ offsets, int n_tok, int N,
+                                            int k, int S, int32_t* __restrict__ sorted_tok,
+                                            int32_t* __restrict__ inv_row) {
+  const long tk = static_cast<long>(n_tok) * k;
+  if (i < tk) {
+    const int t = static_cast<int>(i / k);
+    const int e = topk_idx[i];
+    const int b = t / kRouteTokens;
+    const int row = offsets[e] + blk_base[static_cast<size_t>(b) * N + e] + lrank[i];
+    // a row outside the expert's segment would mean inconsistent routing
+    // outputs; keep every write in bounds regardless
+    const bool ok = row >= offsets[e] && row < offsets[e + 1];
+    if (ok) sorted_tok[row] = t;
+    inv_row[i] = ok ? row : offsets[e];
+  } else if (i < tk + static_cast<long>(S) * n_tok) {
+    const long j = i - tk;
+    sorted_tok[tk + j] = static_cast<int>(j % n_tok);
+  }
+}
+
 // Work items of a large-tile GEMM with nnt column tiles, over the row tiles
 // [0, tlimit): per row group (tile range [tb[g], tb[g + 1])) blocks of up to
 // 8 row tiles x (window / row tiles) column tiles, column by column, the
@@ -90,6 +115,7 @@ __device__ void write_items(int32_t* __restrict__ items, int nnt, const int* tb,
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
     int k, int S, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split, ItemSpec ispec,
+    ScatterSpec sc,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
     int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
     int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
@@ -216,39 +242,34 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __syncthreads();
   write_items(ispec.items_up, ispec.nnt_up, s_tbu, NG, min(total_up, cap_up), ispec.window);
   write_items(ispec.items_down, ispec.nnt_down, s_tbd, NG, s_nrm_down, ispec.window);
+  // small batches: the permutation too (offsets and block bases are complete
+  // and visible to the workgroup since the barriers above)
+  if (sc.sorted_tok != nullptr) {
+    const long n = static_cast<long>(n_tok) * k + static_cast<long>(S) * n_tok;
+    for (long i = tid; i < n; i += kScanThreads)
+      scatter_row(i, sc.topk_idx, sc.lrank, blk_base, offsets, n_tok, N, k, S, sc.sorted_tok,
+                  sc.inv_row);
+  }
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets, int n_tok, int N,
     int k, int S, int32_t* __restrict__ sorted_tok, int32_t* __restrict__ inv_row) {
-  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  const long tk = static_cast<long>(n_tok) * k;
-  if (i < tk) {
-    const int t = static_cast<int>(i / k);
-    const int e = topk_idx[i];
-    const int b = t / kRouteTokens;
-    const int row = offsets[e] + blk_base[static_cast<size_t>(b) * N + e] + lrank[i];
-    // a row outside the expert's segment would mean inconsistent routing
-    // outputs; keep every write in bounds regardless
-    const bool ok = row >= offsets[e] && row < offsets[e + 1];
-    if (ok) sorted_tok[row] = t;
-    inv_row[i] = ok ? row : offsets[e];
-  } else if (i < tk + static_cast<long>(S) * n_tok) {
-    const long j = i - tk;
-    sorted_tok[tk + j] = static_cast<int>(j % n_tok);
-  }
+  scatter_row(static_cast<long>(blockIdx.x) * 256 + threadIdx.x, topk_idx, lrank, blk_base,
+              offsets, n_tok, N, k, S, sorted_tok, inv_row);
 }
 
 }  // namespace
 
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
                        int S, int bm_up, int cap_up, int bm_down, int cap_down,
-                       const SplitSpec& split, const ItemSpec& items, int32_t* blk_base, int32_t* counts, float* prob_sum,
+                       const SplitSpec& split, const ItemSpec& items, const ScatterSpec& sc,
+                       int32_t* blk_base, int32_t* counts, float* prob_sum,
                        int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
                        int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
-                     k, S, bm_up, cap_up, bm_down, cap_down, split, items, blk_base, counts,
+                     k, S, bm_up, cap_up, bm_down, cap_down, split, items, sc, blk_base, counts,
                      prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
   return hipGetLastError();

@@ -360,16 +360,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     const int t = t0 + tt;
     float v = 0.f;
     if (t < a.n_tok && e < a.N) {
-      // loads issued in batches of 8, added in split order
-      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
-        float pv[8];
+      // loads issued in batches of 16, added in split order
+      for (int k0 = 0; k0 < a.ksplit; k0 += 16) {
+        float pv[16];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 16; ++q)
           pv[q] = k0 + q < a.ksplit
                       ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
                       : 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 16; ++q)
           if (k0 + q < a.ksplit) v += pv[q];
       }
       if (a.logit_bias != nullptr) v += a.logit_bias[e];
