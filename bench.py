@@ -45,7 +45,7 @@ PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 10
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--seed", type=int, default=0)
@@ -413,6 +413,9 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                 for i, name in enumerate(moe.STAGES)}
+    # per-step spread (forward only, markers included) from the same pass
+    per_step = np.sort(np.array([e[0].elapsed_time(e[nst]) for e in evs]))
+    pct = {q: float(np.percentile(per_step, q)) for q in (10, 50, 90)}
 
     counts_h = counts.cpu().numpy()
     active = int(np.count_nonzero(counts_h))
@@ -462,6 +465,7 @@ def main():
                   "algorithmic_flops": lf, "algorithmic_bytes": lb,
                   "active_experts": active},
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "forward_ms_p10_p50_p90": [round(pct[10], 4), round(pct[50], 4), round(pct[90], 4)],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof,
         "cpu_baseline": None,
