@@ -35,6 +35,12 @@ What it computes, and where the pages define it:
   for i, loss = alpha * N * sum_i f_i P_i ("Keeping the experts busy", balance
   loss equation; "Mixture of Experts and Guided Decoding", routing-collapse
   passage and its auxiliary-loss equation and worked example).
+* O8 expert capacity (optional): an expert accepts at most C of a batch's
+  (token, slot) assignments; the extras are dropped ("Keeping the experts
+  busy", expert capacity).  The pages do not say which ones; here the first C
+  in token order are kept, a dropped assignment contributes nothing to y (the
+  token's other gates are not renormalised), and f, counts and P still
+  describe the router's choice before dropping.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 ties in top-k go to the lower index under IEEE comparison (+0 == -0); f_i
@@ -58,6 +64,7 @@ import numpy as np
 __all__ = [
     "router_logits",
     "selection_keys",
+    "capacity_keep",
     "topk_by_rank",
     "kept_softmax",
     "full_softmax",
@@ -201,6 +208,24 @@ def route_from_logits(r32, k: int, select_bias=None):
     return idx, kept_softmax(r32, idx)
 
 
+# --------------------------------------------------------------------------- O8
+def capacity_keep(idx, n_experts: int, capacity: int) -> np.ndarray:
+    """O8: bool [T, k], True where assignment (t, slot) is kept.
+
+    Expert e keeps the first ``capacity`` of the assignments that chose it,
+    counted in token order (a token picks an expert at most once).
+    ``capacity`` <= 0 means no limit.
+    """
+    idx = np.asarray(idx)
+    keep = np.ones(idx.shape, dtype=bool)
+    if capacity <= 0:
+        return keep
+    for e in range(n_experts):
+        tok, slot = np.nonzero(idx == e)  # row-major: ascending token
+        keep[tok[capacity:], slot[capacity:]] = False
+    return keep
+
+
 # --------------------------------------------------------------------------- O6
 def combine(gates, expert_outputs) -> np.ndarray:
     """O6 for one token: sum_j gates[j] * expert_outputs[j] (float64).
@@ -264,8 +289,9 @@ def moe_forward(
     route_logits=None,
     alpha: float = BALANCE_ALPHA,
     n_experts: Optional[int] = None,
+    capacity: int = 0,
 ):
-    """The whole layer forward, O1..O7, with the experts looped one at a time.
+    """The whole layer forward, O1..O8, with the experts looped one at a time.
 
     ``experts`` is either a tuple (W_gate [N,F,d], W_up [N,F,d], W_down [N,d,F])
     or a callable e -> (W_gate[e], W_up[e], W_down[e]) so that large layers can
@@ -276,8 +302,10 @@ def moe_forward(
     taken on those logits, which is how a caller checks another implementation's
     routing bit for bit on its own logits.
 
-    Returns a dict with y (float64 [T, d]), logits, idx, gates, counts, f, P,
-    aux_raw and aux.
+    ``capacity`` > 0 applies O8 (per-expert capacity, extras dropped).
+
+    Returns a dict with y (float64 [T, d]), logits, idx, gates, keep (the O8
+    mask), counts, f, P, aux_raw and aux.
     """
     x64 = _f64(x)
     T, d = x64.shape
@@ -289,10 +317,11 @@ def moe_forward(
     idx, g = route_from_logits(r32, k, select_bias) if T else (
         np.zeros((0, k), np.int32), np.zeros((0, k)))
     get = _expert_getter(experts)
+    keep = capacity_keep(idx, N, capacity)
 
     y = np.zeros((T, d), dtype=np.float64)
     for e in range(N):
-        tok, slot = np.nonzero(idx == e)
+        tok, slot = np.nonzero((idx == e) & keep)
         if tok.size == 0:
             continue  # an expert that no token picked does no work
         wg, wu, wd = get(e)
@@ -310,6 +339,7 @@ def moe_forward(
         "logits": r32,
         "idx": idx,
         "gates": g,
+        "keep": keep,
         "counts": counts,
         "f": f,
         "P": P,

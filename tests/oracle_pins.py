@@ -345,10 +345,69 @@ def pin_empty_batch(O):
         raise AssertionError("T = 0")
 
 
+def _brute_keep(idx, N, C):
+    """Per expert, walk the tokens in order and keep its first C assignments."""
+    T, k = idx.shape
+    keep = np.ones((T, k), dtype=bool)
+    if C <= 0:
+        return keep
+    seen = [0] * N
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            seen[e] += 1
+            if seen[e] > C:
+                keep[t, s] = False
+    return keep
+
+
+def pin_capacity_brute_force(O):
+    """Expert capacity ("Keeping the experts busy"): the first C assignments per
+    expert in token order are kept, by a plain walk over the batch."""
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        T, N = int(rng.integers(1, 13)), int(rng.integers(1, 6))
+        k = int(rng.integers(1, N + 1))
+        idx = np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
+        C = int(rng.integers(0, 5))
+        keep = O.capacity_keep(idx, N, C)
+        if not np.array_equal(keep, _brute_keep(idx, N, C)):
+            raise AssertionError(f"capacity keep mask differs (T={T} N={N} k={k} C={C})")
+        for e in range(N):
+            n_e = int(np.sum(idx == e))
+            if int(np.sum(keep & (idx == e))) != (min(n_e, C) if C > 0 else n_e):
+                raise AssertionError("kept count is not min(count, C)")
+
+
+def pin_capacity_layer(O):
+    """Capacity in the layer: no effect when C covers every count; with k = 1
+    and C = 1 each expert runs on the first token that chose it only, and the
+    dropped tokens get nothing; routing statistics ignore the capacity."""
+    rng = np.random.default_rng(23)
+    T, d, F, N = 10, 12, 16, 3
+    x, wr, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    free = O.moe_forward(x, wr, (wg, wu, wd), 2)
+    full = O.moe_forward(x, wr, (wg, wu, wd), 2, capacity=T)
+    _close(full["y"], free["y"], 0, "capacity >= every count changes nothing")
+    one = O.moe_forward(x, wr, (wg, wu, wd), 1, capacity=1)
+    idx = one["idx"][:, 0]
+    y = np.zeros((T, d))
+    for e in range(N):
+        ts = np.nonzero(idx == e)[0]
+        if ts.size:
+            t = int(ts[0])
+            y[t] = _torch_swiglu(x[t:t + 1], wg[e], wu[e], wd[e])[0]
+    _close(one["y"], y, 1e-12, "k = 1, C = 1: first token per expert only")
+    ref = O.moe_forward(x, wr, (wg, wu, wd), 1)
+    for key in ("counts", "f", "P"):
+        _close(one[key], ref[key], 0, f"{key} independent of capacity")
+
+
 ALL_PINS = [
     pin_e1_top2, pin_e2_blend, pin_e3_top2, pin_e4_dense, pin_e5_balance, pin_e6_toy_routing,
     pin_topk_brute_force, pin_select_bias_semantics, pin_swiglu_closed_form,
     pin_single_expert_is_swiglu, pin_router_linear, pin_dense_crosspath,
     pin_k_equals_n_is_dense_softmax, pin_shared_expert, pin_relabel_and_chunking, pin_stats,
-    pin_invariants, pin_unused_expert_never_read, pin_empty_batch,
+    pin_invariants, pin_unused_expert_never_read, pin_empty_batch, pin_capacity_brute_force,
+    pin_capacity_layer,
 ]

@@ -39,6 +39,12 @@ MUTATIONS = {
     "shared_dropped": ("y += swiglu_expert(x64, sg[s], su[s], sd[s])", "pass"),
     "logit_offset_dropped": ("r = r + _f64(logit_bias)[None, :]", "r = r"),
     "combine_drops_term": ("    for j in range(g.shape[0]):", "    for j in range(g.shape[0] - 1):"),
+    "capacity_keeps_last": ("keep[tok[capacity:], slot[capacity:]] = False",
+                            "keep[tok[:-capacity], slot[:-capacity]] = False"),
+    "capacity_off_by_one": ("keep[tok[capacity:], slot[capacity:]] = False",
+                            "keep[tok[capacity + 1:], slot[capacity + 1:]] = False"),
+    "capacity_ignored_in_layer": ("tok, slot = np.nonzero((idx == e) & keep)",
+                                  "tok, slot = np.nonzero(idx == e)"),
     "keys_compared_in_fp64": [
         ("return (r32 + b32[None, :]).astype(np.float32)",
          "return r32.astype(np.float64) + b32.astype(np.float64)[None, :]"),
