@@ -37,7 +37,7 @@
  *    held in the input dtype (bf16 rounding to nearest even); y is rounded once.
  *  - Results are deterministic: the same inputs give bitwise the same outputs.
  *  - Calls are thread-safe; concurrent calls must use distinct workspaces.
- *  - Supported sizes: 1 <= k <= min(N, 16), N <= 512, 0 <= S <= 4,
+ *  - Supported sizes: 1 <= k <= min(N, 16), N <= 512, 0 <= S <= 4, capacity >= 0,
  *    d and F positive multiples of 64, T >= 0 (T = 0 launches nothing and
  *    returns MOE_OK).  Other sizes return MOE_ERR_UNSUPPORTED.
  */
@@ -63,7 +63,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Layer sizes.  T tokens, d_model, N routed experts, top_k kept per token,
  * d_ff hidden size of every expert (routed and shared), n_shared always-on
- * experts, dtype a moe_dtype. */
+ * experts, dtype a moe_dtype.
+ *
+ * capacity: 0 = dropless.  C > 0 caps every routed expert at C (token, slot)
+ * assignments per call ("Mixture of experts and speculative decoding",
+ * "Keeping the experts busy": the extras are dropped).  Kept are an expert's
+ * first C assignments in token order; a dropped assignment adds nothing to y
+ * (the token's other gates are not renormalised).  topk_idx, topk_gate,
+ * counts and prob_sum still describe the router's choice before dropping. */
 typedef struct {
   int32_t T;
   int32_t d_model;
@@ -72,6 +79,7 @@ typedef struct {
   int32_t d_ff;
   int32_t n_shared;
   int32_t dtype;
+  int32_t capacity;
 } moe_config;
 
 /* Layer parameters (device pointers, caller-owned, read-only). */

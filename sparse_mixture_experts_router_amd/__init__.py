@@ -41,7 +41,7 @@ class MoEConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 class MoEWeights(ctypes.Structure):
@@ -104,10 +104,12 @@ _TORCH_DTYPE = {MOE_BF16: torch.bfloat16, MOE_F32: torch.float32}
 
 
 def make_config(T: int, d_model: int, n_experts: int, top_k: int, d_ff: int,
-                n_shared: int = 0, dtype=torch.bfloat16) -> MoEConfig:
+                n_shared: int = 0, dtype=torch.bfloat16, capacity: int = 0) -> MoEConfig:
+    """``capacity``: 0 = dropless, else the most (token, slot) assignments a
+    routed expert takes per call (the rest are dropped)."""
     code = MOE_BF16 if dtype in (torch.bfloat16, "bf16", MOE_BF16) else MOE_F32
     return MoEConfig(int(T), int(d_model), int(n_experts), int(top_k), int(d_ff),
-                     int(n_shared), code)
+                     int(n_shared), code, int(capacity))
 
 
 def moe_workspace_size(cfg: MoEConfig) -> int:

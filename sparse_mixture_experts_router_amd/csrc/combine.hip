@@ -55,8 +55,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yper
                                                       const float* __restrict__ ypart,
                                                       const int32_t* __restrict__ plan,
                                                       const int32_t* __restrict__ inv_row,
-                                                      const float* __restrict__ gate, int n_tok,
-                                                      int d, int k, int S, T* __restrict__ y) {
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ offsets, int N,
+                                                      int n_tok, int d, int k, int S,
+                                                      T* __restrict__ y) {
   constexpr int V = Vec<T>::kN;
   const int t = blockIdx.x;
   __shared__ int s_row[kMaxTopK + kMaxShared];
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yper
     s_g[threadIdx.x] = gate[static_cast<size_t>(t) * k + threadIdx.x];
   } else if (threadIdx.x < k + S) {
     const int s = threadIdx.x - k;
-    s_row[threadIdx.x] = n_tok * k + s * n_tok + t;
+    s_row[threadIdx.x] = offsets[N + s] + t;
   }
   __syncthreads();
   const int parts = plan[kPlanParts], row_split = plan[kPlanRowSplit];
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yper
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
     for (int s = 0; s < k + S; ++s) {
       const int row = s_row[s];
+      if (row < 0) continue;  // dropped by the capacity
       float v[V];
       if (parts > 0 && row >= row_split) {
         const float* src = ypart + static_cast<size_t>(row - row_split) * d + c;
@@ -136,15 +139,16 @@ __global__ __launch_bounds__(256) void balance_kernel(int n_tok, int N, int k,
 
 hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
                           const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
-                          int T_, int d, int k, int S, void* y, hipStream_t s) {
+                          const int32_t* offsets, int N, int T_, int d, int k, int S, void* y,
+                          hipStream_t s) {
   if (dtype == 1)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T_), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(yperm), ypart, plan, inv_row, topk_gate, T_, d,
-                       k, S, static_cast<bf16_t*>(y));
+                       static_cast<const bf16_t*>(yperm), ypart, plan, inv_row, topk_gate,
+                       offsets, N, T_, d, k, S, static_cast<bf16_t*>(y));
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T_), dim3(256), 0, s,
-                       static_cast<const float*>(yperm), ypart, plan, inv_row, topk_gate, T_, d,
-                       k, S, static_cast<float*>(y));
+                       static_cast<const float*>(yperm), ypart, plan, inv_row, topk_gate,
+                       offsets, N, T_, d, k, S, static_cast<float*>(y));
   return hipGetLastError();
 }
 

@@ -173,8 +173,8 @@ Workspace carve(const Plan& p, void* base) {
 moe_status check_config(const moe_config* c) {
   if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
   if (c->T < 0 || c->d_model <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->d_ff <= 0 ||
-      c->n_shared < 0)
-    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T, S >= 0)");
+      c->n_shared < 0 || c->capacity < 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T, S, capacity >= 0)");
   if (c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k > n_experts");
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad dtype");
   if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
@@ -235,7 +235,7 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
 moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
                     const ScatterSpec& sc, hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
-                               p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
+                               c.capacity, p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
                                ItemSpec{p.nnt_up, p.nnt_down, p.cus / 8 > 0 ? p.cus / 8 : 1,
                                         p.nnt_up ? ws.items_up : nullptr,
                                         p.nnt_down ? ws.items_down : nullptr},
@@ -328,7 +328,7 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   } else {
     if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
     err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts, c.top_k,
-                         c.n_shared, ws.sorted_tok, ws.inv_row, s);
+                         c.n_shared, c.capacity, ws.sorted_tok, ws.inv_row, s);
     if (err != hipSuccess) return hip_fail(err, "scatter kernel");
   }
 
@@ -378,8 +378,9 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
     return hip_fail(err, "down GEMM");
 
   mark(ev, MOE_STAGE_COMBINE, s);
-  if ((err = launch_combine(c.dtype, ws.yperm, ws.ypart, ws.ntiles + 2, ws.inv_row, gate, c.T,
-                            c.d_model, c.top_k, c.n_shared, y, s)) != hipSuccess)
+  if ((err = launch_combine(c.dtype, ws.yperm, ws.ypart, ws.ntiles + 2, ws.inv_row, gate,
+                            ws.offsets, c.n_experts, c.T, c.d_model, c.top_k, c.n_shared, y, s)) !=
+      hipSuccess)
     return hip_fail(err, "combine kernel");
   mark(ev, MOE_STAGE_COUNT, s);
   return MOE_OK;

@@ -92,7 +92,7 @@ struct SplitSpec {
   int tail_max_parts;  // most parts one tile may be split into
 };
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
-                       int N, int k, int S, int bm_up, int cap_up, int bm_down,
+                       int N, int k, int S, int capacity, int bm_up, int cap_up, int bm_down,
                        int cap_down, const SplitSpec& split, const ItemSpec& items,
                        const ScatterSpec& sc, int32_t* blk_base,
                        int32_t* counts, float* prob_sum, int32_t* user_counts,
@@ -101,8 +101,8 @@ hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank,
                           const int32_t* blk_base, const int32_t* offsets,
-                          int T, int N, int k, int S, int32_t* sorted_tok,
-                          int32_t* inv_row, hipStream_t s);
+                          int T, int N, int k, int S, int capacity,
+                          int32_t* sorted_tok, int32_t* inv_row, hipStream_t s);
 
 struct GemmArgs {
   const void* a;             // x [T, d] (gather) or hidden [rows, F] (direct)
@@ -169,9 +169,12 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
 // y from the per-expert rows: yperm (layer dtype), except rows at or past
 // plan[kPlanRowSplit], which are the sum of plan[kPlanParts] fp32 partial
 // row sets ypart[part][row - row_split] (part stride plan[kPlanStride] rows).
+// Slots with inv_row < 0 (dropped by a capacity) add nothing; shared expert
+// s's row for token t is offsets[N + s] + t.
 hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
                           const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
-                          int T, int d, int k, int S, void* y, hipStream_t s);
+                          const int32_t* offsets, int N, int T, int d, int k, int S, void* y,
+                          hipStream_t s);
 int down_split(int dtype, const GemmPick& pick, long tiles_est, int n_dim, int k_dim, int cus);
 
 hipError_t launch_balance(int T, int N, int k, const int32_t* counts,

@@ -56,18 +56,27 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 
 // Row i of the permutation: (token, slot) pairs first, then the shared
 // experts' rows.
+// An assignment whose rank (in token order) within its expert is capacity or
+// more (capacity > 0) is dropped: inv_row = -1 and no row.  Shared expert s
+// owns rows offsets[N + s] + t.
 __device__ __forceinline__ void scatter_row(long i, const int32_t* __restrict__ topk_idx,
                                             const int32_t* __restrict__ lrank,
                                             const int32_t* __restrict__ blk_base,
                                             const int32_t* __restrict__ offsets, int n_tok, int N,
-                                            int k, int S, int32_t* __restrict__ sorted_tok,
+                                            int k, int S, int capacity,
+                                            int32_t* __restrict__ sorted_tok,
                                             int32_t* __restrict__ inv_row) {
   const long tk = static_cast<long>(n_tok) * k;
   if (i < tk) {
     const int t = static_cast<int>(i / k);
     const int e = topk_idx[i];
     const int b = t / kRouteTokens;
-    const int row = offsets[e] + blk_base[static_cast<size_t>(b) * N + e] + lrank[i];
+    const int rank = blk_base[static_cast<size_t>(b) * N + e] + lrank[i];
+    if (capacity > 0 && rank >= capacity) {
+      inv_row[i] = -1;
+      return;
+    }
+    const int row = offsets[e] + rank;
     // a row outside the expert's segment would mean inconsistent routing
     // outputs; keep every write in bounds regardless
     const bool ok = row >= offsets[e] && row < offsets[e + 1];
@@ -75,7 +84,8 @@ __device__ __forceinline__ void scatter_row(long i, const int32_t* __restrict__ 
     inv_row[i] = ok ? row : offsets[e];
   } else if (i < tk + static_cast<long>(S) * n_tok) {
     const long j = i - tk;
-    sorted_tok[tk + j] = static_cast<int>(j % n_tok);
+    const int s = static_cast<int>(j / n_tok), t = static_cast<int>(j - static_cast<long>(s) * n_tok);
+    sorted_tok[offsets[N + s] + t] = t;
   }
 }
 
@@ -114,8 +124,8 @@ __device__ void write_items(int32_t* __restrict__ items, int nnt, const int* tb,
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
-    int k, int S, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split, ItemSpec ispec,
-    ScatterSpec sc,
+    int k, int S, int capacity, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split,
+    ItemSpec ispec, ScatterSpec sc,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
     int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
     int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
@@ -174,8 +184,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
   // offsets and tile lists over the N + S row groups
   const int NG = N + S;
+  // rows per group: an expert's kept assignments, every token for a shared one
   int cg = 0;
-  if (tid < N) cg = s_tot[tid];
+  if (tid < N) cg = capacity > 0 ? min(s_tot[tid], capacity) : s_tot[tid];
   else if (tid < NG) cg = n_tok;
   if (tid < NG && tid >= N) counts[tid] = n_tok;
   int total_rows;
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (split.parts > 1) {
       parts = split.parts;
       row_split = 0;
-      stride = total_rows;
+      stride = n_tok * (k + S);  // the split GEMM's partial layout: every possible row
     } else if (split.tail_nnt > 0 && ntd > 0) {
       const long W = static_cast<long>(ntd) * split.tail_nnt;
       const long r = W % split.tail_cus;
@@ -247,41 +258,41 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   if (sc.sorted_tok != nullptr) {
     const long n = static_cast<long>(n_tok) * k + static_cast<long>(S) * n_tok;
     for (long i = tid; i < n; i += kScanThreads)
-      scatter_row(i, sc.topk_idx, sc.lrank, blk_base, offsets, n_tok, N, k, S, sc.sorted_tok,
-                  sc.inv_row);
+      scatter_row(i, sc.topk_idx, sc.lrank, blk_base, offsets, n_tok, N, k, S, capacity,
+                  sc.sorted_tok, sc.inv_row);
   }
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets, int n_tok, int N,
-    int k, int S, int32_t* __restrict__ sorted_tok, int32_t* __restrict__ inv_row) {
+    int k, int S, int capacity, int32_t* __restrict__ sorted_tok, int32_t* __restrict__ inv_row) {
   scatter_row(static_cast<long>(blockIdx.x) * 256 + threadIdx.x, topk_idx, lrank, blk_base,
-              offsets, n_tok, N, k, S, sorted_tok, inv_row);
+              offsets, n_tok, N, k, S, capacity, sorted_tok, inv_row);
 }
 
 }  // namespace
 
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
-                       int S, int bm_up, int cap_up, int bm_down, int cap_down,
+                       int S, int capacity, int bm_up, int cap_up, int bm_down, int cap_down,
                        const SplitSpec& split, const ItemSpec& items, const ScatterSpec& sc,
                        int32_t* blk_base, int32_t* counts, float* prob_sum,
                        int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
                        int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
-                     k, S, bm_up, cap_up, bm_down, cap_down, split, items, sc, blk_base, counts,
-                     prob_sum,
+                     k, S, capacity, bm_up, cap_up, bm_down, cap_down, split, items, sc, blk_base,
+                     counts, prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank, const int32_t* blk_base,
-                          const int32_t* offsets, int T_, int N, int k, int S,
+                          const int32_t* offsets, int T_, int N, int k, int S, int capacity,
                           int32_t* sorted_tok, int32_t* inv_row, hipStream_t s) {
   const long n = static_cast<long>(T_) * k + static_cast<long>(S) * T_;
   const int blocks = static_cast<int>((n + 255) / 256);
   hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, s, topk_idx, lrank, blk_base,
-                     offsets, T_, N, k, S, sorted_tok, inv_row);
+                     offsets, T_, N, k, S, capacity, sorted_tok, inv_row);
   return hipGetLastError();
 }
 

@@ -39,11 +39,12 @@ def to_np(t: Optional[torch.Tensor]):
 
 
 def run_layer(shape: MoEShape, inputs: Dict[str, Optional[torch.Tensor]], alpha: float = 0.01,
-              events=None):
+              events=None, capacity: int = 0):
     """One moe_layer_forward + moe_balance_stats call; returns device outputs."""
     T = shape.T
     dev = inputs["w_gate"].device
-    cfg = moe.make_config(T, shape.d, shape.N, shape.k, shape.F, shape.S, shape.torch_dtype)
+    cfg = moe.make_config(T, shape.d, shape.N, shape.k, shape.F, shape.S, shape.torch_dtype,
+                          capacity=capacity)
     ws = moe.alloc_workspace(cfg, dev)
     out = {
         "y": torch.empty((T, shape.d), dtype=shape.torch_dtype, device=dev),
@@ -102,12 +103,13 @@ def host_inputs(inputs: Dict[str, Optional[torch.Tensor]], names: Sequence[str])
     return {n: to_np(inputs[n]) for n in names if inputs.get(n) is not None}
 
 
-def full_parity(shape: MoEShape, seed: int = 0, inputs=None, label: str = ""):
+def full_parity(shape: MoEShape, seed: int = 0, inputs=None, label: str = "",
+                capacity: int = 0):
     """Element-wise parity of the whole layer against the oracle (small shapes)."""
-    say(f"[parity] {label or shape.name}: {shape.describe()} seed={seed}")
+    say(f"[parity] {label or shape.name}: {shape.describe()} seed={seed} capacity={capacity}")
     if inputs is None:
         inputs = make_inputs(shape, seed=seed, device="cuda")
-    out = run_layer(shape, inputs)
+    out = run_layer(shape, inputs, capacity=capacity)
     gpu = {k_: to_np(v) for k_, v in out.items()}
     host = host_inputs(inputs, ["x", "w_router", "w_gate", "w_up", "w_down", "ws_gate",
                                 "ws_up", "ws_down", "logit_bias", "select_bias"])
@@ -116,7 +118,8 @@ def full_parity(shape: MoEShape, seed: int = 0, inputs=None, label: str = ""):
     ref = oracle.moe_forward(host["x"], host["w_router"],
                              (host["w_gate"], host["w_up"], host["w_down"]), shape.k,
                              select_bias=host.get("select_bias"), shared=shared,
-                             route_logits=gpu["logits"], logit_bias=host.get("logit_bias"))
+                             route_logits=gpu["logits"], logit_bias=host.get("logit_bias"),
+                             capacity=capacity)
     # the oracle's own fp64 logits agree with the GPU's to fp32 accumulation error
     own = oracle.router_logits(host["x"], host["w_router"], host.get("logit_bias"))
     if own.size:

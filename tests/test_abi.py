@@ -41,6 +41,18 @@ def test_status_strings():
     assert "unknown" in moe.moe_status_string(99)
 
 
+def test_config_struct_matches_the_header():
+    """The binding's moe_config mirrors include/moe.h field by field."""
+    import re
+    with open(os.path.join(ROOT, "include", "moe.h")) as fh:
+        hdr = fh.read()
+    body = re.search(r"typedef struct \{([^}]*)\} moe_config;", hdr).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f for f, _ in moe.MoEConfig._fields_]
+    cap = moe.make_config(64, 128, 4, 2, 256, capacity=7)
+    assert cap.capacity == 7 and moe.make_config(64, 128, 4, 2, 256).capacity == 0
+
+
 def test_workspace_size_validation():
     ok = moe.make_config(64, 128, 4, 2, 256, 0, "f32")
     n = moe.moe_workspace_size(ok)
@@ -50,7 +62,8 @@ def test_workspace_size_validation():
     for bad in [moe.make_config(64, 100, 4, 2, 256), moe.make_config(64, 128, 4, 5, 256),
                 moe.make_config(64, 128, 600, 2, 256), moe.make_config(64, 128, 40, 17, 256),
                 moe.make_config(-1, 128, 4, 2, 256), moe.make_config(64, 128, 4, 2, 96),
-                moe.make_config(64, 128, 4, 2, 256, n_shared=5)]:
+                moe.make_config(64, 128, 4, 2, 256, n_shared=5),
+                moe.make_config(64, 128, 4, 2, 256, capacity=-1)]:
         assert moe.moe_workspace_size(bad) == 0
 
 

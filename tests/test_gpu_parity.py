@@ -100,6 +100,45 @@ def test_tail_tiles_split_over_k(S):
     assert int(out["counts"][7]) == 2510
 
 
+CAPACITY_CASES = [
+    # (label, shape, capacity): mean rows per expert vs the cap
+    ("large_tiles", reduced(CONFIGS["mixtral_prefill"], T=300, d=512, F=1024), 60),
+    ("shared_and_bias", reduced(CONFIGS["deepseek_v3"], T=200, d=512, F=256, N=64), 20),
+    ("decode_split_k", reduced(CONFIGS["mixtral_decode"], T=24, d=256, F=2496), 3),
+    ("f32", MoEShape("f32_cap", T=77, d=192, N=6, k=3, F=320, dtype="f32"), 25),
+]
+
+
+@pytest.mark.parametrize("label,shape,capacity", CAPACITY_CASES,
+                         ids=[c[0] for c in CAPACITY_CASES])
+def test_capacity_parity(label, shape, capacity):
+    """Expert capacity: the first C assignments per expert in token order are
+    kept, the rest dropped (oracle O8); shared experts are untouched."""
+    _, out, ref = full_parity(shape, seed=3, label=f"capacity_{label}", capacity=capacity)
+    assert int(np.sum(~ref["keep"])) > 0, "the case should drop something"
+    # routing statistics describe the router's choice before dropping
+    assert to_np(out["counts"]).sum() == shape.T * shape.k
+
+
+def test_capacity_drops_extra_tokens_of_a_hot_expert():
+    shp = MoEShape("hot_cap", T=300, d=256, N=4, k=1, F=256)
+    inputs = make_inputs(shp, seed=2, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0.0, 0.0, 0.0, 100.0], device="cuda")
+    _, out, _ = full_parity(shp, inputs=inputs, label="hot_expert_capacity_100", capacity=100)
+    y = to_np(out["y"])
+    assert np.all(y[100:] == 0.0), "tokens past the capacity must get nothing"
+    assert np.any(y[:100] != 0.0)
+
+
+def test_capacity_at_least_every_count_is_a_no_op():
+    shp = reduced(CONFIGS["qwen3_skew"], T=200, d=256, F=128, N=32)
+    inputs = make_inputs(shp, seed=6, device="cuda")
+    free = run_layer(shp, inputs)
+    capped = run_layer(shp, inputs, capacity=shp.T)
+    for key in free:
+        assert torch.equal(free[key], capped[key]), key
+
+
 def test_unchosen_expert_weights_never_read():
     shp = MoEShape("nan_cold", T=150, d=128, N=6, k=2, F=128)
     inputs = make_inputs(shp, seed=3, device="cuda")
