@@ -417,6 +417,28 @@ def main():
     per_step = np.sort(np.array([e[0].elapsed_time(e[nst]) for e in evs]))
     pct = {q: float(np.percentile(per_step, q)) for q in (10, 50, 90)}
 
+    # The same step captured once in a HIP graph and replayed K times, as a
+    # serving loop would run it (fewer launch gaps between the kernels).
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    gs = torch.cuda.Event(enable_timing=True)
+    ge = torch.cuda.Event(enable_timing=True)
+    gs.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    ge.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = gs.elapsed_time(ge) / args.steps
+
     counts_h = counts.cpu().numpy()
     active = int(np.count_nonzero(counts_h))
     lf, lb, uf, ub = algorithmic(shape, active)
@@ -467,6 +489,9 @@ def main():
         "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "forward_ms_p10_p50_p90": [round(pct[10], 4), round(pct[50], 4), round(pct[90], 4)],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "graph_replay": {"ms_per_step": round(graph_ms, 4),
+                         "tokens_per_s": round(T / (graph_ms * 1e-3), 1),
+                         "note": "the same step captured once in a HIP graph, K replays"},
         "roofline": roof,
         "cpu_baseline": None,
     }
