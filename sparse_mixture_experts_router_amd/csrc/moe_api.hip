@@ -4,6 +4,7 @@
 #include "moe.h"
 #include "moe_internal.h"
 
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -55,7 +56,7 @@ struct Plan {
 
 enum {
   R_IDX, R_GATE, R_LRANK, R_PART, R_BCNT, R_BPS, R_BBASE, R_CNT, R_PS, R_OFF, R_SORT, R_INV,
-  R_TUP, R_TDN, R_IUP, R_IDN, R_NT, R_HID, R_YP, R_YPART, R_COUNT
+  R_TUP, R_TDN, R_IUP, R_IDN, R_TB, R_NT, R_HID, R_YP, R_YPART, R_COUNT
 };
 
 Plan make_plan(const moe_config& c) {
@@ -101,6 +102,7 @@ Plan make_plan(const moe_config& c) {
   p.nnt_down = p.down.variant == 1 ? (c.d_model + 255) / 256 : 0;
   sz[R_IUP] = static_cast<size_t>(p.cap_up) * p.nnt_up * 4;
   sz[R_IDN] = static_cast<size_t>(p.cap_down) * p.nnt_down * 4;
+  sz[R_TB] = (2 * (N + S + 1) + 2) * 4;
   sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
 
@@ -163,6 +165,7 @@ Workspace carve(const Plan& p, void* base) {
   w.tiles_down = reinterpret_cast<int2*>(b + p.off[R_TDN]);
   w.items_up = reinterpret_cast<int32_t*>(b + p.off[R_IUP]);
   w.items_down = reinterpret_cast<int32_t*>(b + p.off[R_IDN]);
+  w.tbases = reinterpret_cast<int32_t*>(b + p.off[R_TB]);
   w.ntiles = reinterpret_cast<int32_t*>(b + p.off[R_NT]);
   w.hidden = b + p.off[R_HID];
   w.yperm = b + p.off[R_YP];
@@ -231,14 +234,18 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
   return MOE_OK;
 }
 
+ItemSpec item_spec(const Plan& p, const Workspace& ws) {
+  return ItemSpec{p.nnt_up, p.nnt_down, p.cus / 8 > 0 ? p.cus / 8 : 1,
+                  p.nnt_up ? ws.items_up : nullptr, p.nnt_down ? ws.items_down : nullptr,
+                  (p.nnt_up || p.nnt_down) ? ws.tbases : nullptr};
+}
+
 // sc.sorted_tok != nullptr: the scan kernel also writes the permutation.
 moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
                     const ScatterSpec& sc, hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
                                c.capacity, p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
-                               ItemSpec{p.nnt_up, p.nnt_down, p.cus / 8 > 0 ? p.cus / 8 : 1,
-                                        p.nnt_up ? ws.items_up : nullptr,
-                                        p.nnt_down ? ws.items_down : nullptr},
+                               item_spec(p, ws),
                                sc, ws.blk_base,
                                ws.counts,
                                ws.prob_sum, out ? out->counts : nullptr,
@@ -330,6 +337,13 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
     err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts, c.top_k,
                          c.n_shared, c.capacity, ws.sorted_tok, ws.inv_row, s);
     if (err != hipSuccess) return hip_fail(err, "scatter kernel");
+  }
+  {
+    const long max_items = std::max(static_cast<long>(p.cap_up) * p.nnt_up,
+                                    static_cast<long>(p.cap_down) * p.nnt_down);
+    if ((err = launch_items(item_spec(p, ws), c.n_experts + c.n_shared, max_items, s)) !=
+        hipSuccess)
+      return hip_fail(err, "items kernel");
   }
 
   mark(ev, MOE_STAGE_EXPERT_UP, s);

@@ -37,6 +37,7 @@ struct Workspace {
   int2* tiles_down;    // tile list of the down GEMM
   int32_t* items_up;   // work items of the large-tile gate/up GEMM (when used)
   int32_t* items_down; // and of the large-tile down GEMM
+  int32_t* tbases;     // group tile bases for the items kernel (see ItemSpec)
   int32_t* ntiles;     // [kPlanInts]: entries in tiles_up, tiles_down, then the down-pass
                        // split plan (see kPlan*)
   void* hidden;        // [T k + S T, F]  dtype
@@ -60,17 +61,22 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router,
 // Split of the down pass recorded in the plan: parts > 1 splits every row
 // (decode); otherwise tail_nnt > 0 lets the scan split the last row tiles of
 // a tail_nnt-column-tile grid that would leave cus compute units mostly idle.
-// Work-item lists of the large-tile GEMMs, written by the scan kernel: for
-// every row group (expert) its row tiles x column tiles, in blocks of up to
-// 8 row tiles x (window / row tiles) column tiles, so the `window`
+// Work-item lists of the large-tile GEMMs (items kernel, after the scan):
+// for every row group (expert) its row tiles x column tiles, in blocks of up
+// to 8 row tiles x (window / row tiles) column tiles, so the `window`
 // workgroups an XCD runs at once cover one expert's rows next to a band of
-// its weight tiles.  nnt = 0: no list for that pass.
+// its weight tiles.  nnt = 0: no list for that pass.  The scan writes the
+// groups' first tiles to tbases: [0, G] gate/up (G = N + S groups, [G] =
+// their total), [G + 1, 2G + 1] down, then the tiles each list covers
+// (gate/up, down without the split tail).
 struct ItemSpec {
   int nnt_up, nnt_down;  // column tiles of the gate/up and down passes
   int window;            // workgroups one XCD runs at once
   int32_t* items_up;
   int32_t* items_down;
+  int32_t* tbases;       // [2 (G + 1) + 2], or null: the scan writes nothing
 };
+hipError_t launch_items(const ItemSpec& is, int groups, long max_items, hipStream_t s);
 constexpr int kItemColBits = 12;  // column tile in the low bits of an item
 constexpr int kItemMaxTiles = 1 << 19;
 

@@ -89,17 +89,14 @@ __device__ __forceinline__ void scatter_row(long i, const int32_t* __restrict__ 
   }
 }
 
-// Work items of a large-tile GEMM with nnt column tiles, over the row tiles
-// [0, tlimit): per row group (tile range [tb[g], tb[g + 1])) blocks of up to
-// 8 row tiles x (window / row tiles) column tiles, column by column, the
-// group's items starting at tb[g] * nnt.  The 1024 threads take items i,
-// i + 1024, ... and find the group of item i by binary search over tb
-// (ng + 1 entries, non-decreasing).
-__device__ void write_items(int32_t* __restrict__ items, int nnt, const int* tb, int ng,
-                            int tlimit, int window) {
-  if (items == nullptr || nnt <= 0) return;
-  const int total = tlimit * nnt;  // < 2^31: tiles < kItemMaxTiles, nnt < 2^kItemColBits
-  for (int i = threadIdx.x; i < total; i += kScanThreads) {
+// Item i of a large-tile GEMM's list (nnt column tiles, row tiles [0,
+// tlimit)): per row group (tile range [tb[g], tb[g + 1])) blocks of up to 8
+// row tiles x (window / row tiles) column tiles, column by column, the group's
+// items starting at tb[g] * nnt.  The group of item i is found by binary
+// search over tb (ng + 1 entries, non-decreasing).
+__device__ void write_item(int32_t* __restrict__ items, int nnt, const int* tb, int ng,
+                           int tlimit, int window, int i) {
+  {  // item i of a list of tlimit * nnt
     const int tt = i / nnt;
     int lo = 0, hi = ng;  // largest g with tb[g] <= tt
     while (hi - lo > 1) {
@@ -120,6 +117,21 @@ __device__ void write_items(int32_t* __restrict__ items, int nnt, const int* tb,
     const int t = b * TW + r2 % tw;
     items[i] = ((base + t) << kItemColBits) | c;
   }
+}
+
+// One thread per item; blockIdx.y: 0 = gate/up list, 1 = down list.
+__global__ __launch_bounds__(256) void items_kernel(ItemSpec is, int ng) {
+  __shared__ int s_tb[kMaxExperts + kMaxShared + 1];
+  const int pass = blockIdx.y;
+  const int nnt = pass == 0 ? is.nnt_up : is.nnt_down;
+  int32_t* items = pass == 0 ? is.items_up : is.items_down;
+  if (nnt <= 0 || items == nullptr) return;
+  const int32_t* tb = is.tbases + pass * (ng + 1);
+  for (int g = threadIdx.x; g <= ng; g += 256) s_tb[g] = tb[g];
+  const int tlimit = is.tbases[2 * (ng + 1) + pass];
+  __syncthreads();
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < tlimit * nnt) write_item(items, nnt, s_tb, ng, tlimit, is.window, i);
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
@@ -251,8 +263,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     s_tbd[tid] = base_down;
   }
   __syncthreads();
-  write_items(ispec.items_up, ispec.nnt_up, s_tbu, NG, min(total_up, cap_up), ispec.window);
-  write_items(ispec.items_down, ispec.nnt_down, s_tbd, NG, s_nrm_down, ispec.window);
+  // group tile bases and list lengths for the items kernel
+  if (ispec.tbases != nullptr) {
+    for (int g = tid; g <= NG; g += kScanThreads) {
+      ispec.tbases[g] = s_tbu[g];
+      ispec.tbases[NG + 1 + g] = s_tbd[g];
+    }
+    if (tid == 0) {
+      ispec.tbases[2 * (NG + 1)] = min(total_up, cap_up);
+      ispec.tbases[2 * (NG + 1) + 1] = s_nrm_down;
+    }
+  }
   // small batches: the permutation too (offsets and block bases are complete
   // and visible to the workgroup since the barriers above)
   if (sc.sorted_tok != nullptr) {
@@ -283,6 +304,13 @@ hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_,
                      k, S, capacity, bm_up, cap_up, bm_down, cap_down, split, items, sc, blk_base,
                      counts, prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_items(const ItemSpec& is, int groups, long max_items, hipStream_t s) {
+  if ((is.nnt_up <= 0 && is.nnt_down <= 0) || max_items <= 0) return hipSuccess;
+  const unsigned bx = static_cast<unsigned>((max_items + 255) / 256);
+  hipLaunchKernelGGL(items_kernel, dim3(bx, 2), dim3(256), 0, s, is, groups);
   return hipGetLastError();
 }
 
