@@ -355,27 +355,79 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kRouteTokens;
   for (int i = tid; i < NP * 2; i += 256) (&s_mask[0][0])[i] = 0u;
-  for (int i = tid; i < kRouteTokens * NP; i += 256) {
-    const int tt = i / NP, e = i - tt * NP;
-    const int t = t0 + tt;
-    float v = 0.f;
-    if (t < a.n_tok && e < a.N) {
-      // loads issued in batches of 16, added in split order
-      for (int k0 = 0; k0 < a.ksplit; k0 += 16) {
-        float pv[16];
+  const int n_here = min(kRouteTokens, a.n_tok - t0);
+  if (a.N % 4 == 0 && a.ksplit <= 8) {
+    // (many tokens, few splits) 16-byte loads of 4 experts; every (token, 4 experts) quad of the tile
+    // is a lane's, and its ksplit partials are all requested before the sum
+    // (added in split order), so the loads overlap instead of queueing
+    const int nq = a.N / 4;
+    for (int q0 = tid; q0 < kRouteTokens * nq; q0 += 256 * 4) {
+      f32x4 v[4];
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          pv[q] = k0 + q < a.ksplit
-                      ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
-                      : 0.f;
+      for (int u = 0; u < 4; ++u) v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {  // 8 splits x 4 quads in flight
+        f32x4 pv[8][4];
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (k0 + q < a.ksplit) v += pv[q];
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * 256, tt = q / nq;
+            pv[kk][u] = (k0 + kk < a.ksplit && q < kRouteTokens * nq && tt < n_here)
+                            ? *reinterpret_cast<const f32x4*>(
+                                  a.partial +
+                                  (static_cast<size_t>(k0 + kk) * a.n_tok + t0 + tt) * a.N +
+                                  (q - tt * nq) * 4)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k0 + kk < a.ksplit) v[u] += pv[kk][u];
       }
-      if (a.logit_bias != nullptr) v += a.logit_bias[e];
-      if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t) * a.N + e] = v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * 256;
+        if (q >= kRouteTokens * nq) continue;
+        const int tt = q / nq, e0 = (q - tt * nq) * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float x = v[u][c];
+          if (tt < n_here) {
+            if (a.logit_bias != nullptr) x += a.logit_bias[e0 + c];
+            if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t0 + tt) * a.N + e0 + c] = x;
+          }
+          s_logit[tt * LD + e0 + c] = tt < n_here ? x : 0.f;
+        }
+      }
     }
-    s_logit[tt * LD + e] = v;
+    for (int i = tid; i < kRouteTokens * (NP - a.N); i += 256) {  // padding experts
+      const int tt = i / (NP - a.N);
+      s_logit[tt * LD + a.N + (i - tt * (NP - a.N))] = 0.f;
+    }
+  } else {  // (few tokens, many splits) one expert per lane, 16 splits per load round
+    for (int i = tid; i < kRouteTokens * NP; i += 256) {
+      const int tt = i / NP, e = i - tt * NP;
+      const int t = t0 + tt;
+      float v = 0.f;
+      if (t < a.n_tok && e < a.N) {
+        // loads issued in batches of 16, added in split order
+        for (int k0 = 0; k0 < a.ksplit; k0 += 16) {
+          float pv[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            pv[q] = k0 + q < a.ksplit
+                        ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
+                        : 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (k0 + q < a.ksplit) v += pv[q];
+        }
+        if (a.logit_bias != nullptr) v += a.logit_bias[e];
+        if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t) * a.N + e] = v;
+      }
+      s_logit[tt * LD + e] = v;
+    }
   }
   __syncthreads();
   select_tile<NB>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate, a.lrank,
