@@ -464,8 +464,10 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
 int route_split(int T_, int d, int dtype) {
   const int nsteps = d * (dtype == 1 ? 2 : 4) / kRowBytes;
   const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
-  // enough workgroups to cover the GPU, at least 4 K steps each
-  int ks = (256 + blocks - 1) / blocks;
+  // about two workgroups per CU (a router workgroup's short reduction is
+  // latency-bound, so a second one per CU hides the first's waits), at
+  // least 4 K steps each
+  int ks = (512 + blocks - 1) / blocks;
   const int max_ks = nsteps / 4 > 0 ? nsteps / 4 : 1;
   ks = ks < 1 ? 1 : (ks > max_ks ? max_ks : ks);
   const int per = (nsteps + ks - 1) / ks;
