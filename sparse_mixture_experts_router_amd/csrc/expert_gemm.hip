@@ -38,6 +38,8 @@
 namespace moe {
 namespace {
 
+template <int N> struct CInt { static constexpr int value = N; };
+
 // Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
 // passes of 128 staged bytes per row: each pass is staged row-major in LDS at
 // stg (rows padded by 16 bytes, so the four row groups of an MFMA result
@@ -189,6 +191,9 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // wave-uniform, so LDS destinations (M0) and bases live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // 16-row blocks of this wavefront's rows that hold tile rows
+  const int mlive =
+      __builtin_amdgcn_readfirstlane(min(max((mvalid - wm * WTM + 15) / 16, 0), MB));
 
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
   const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
@@ -302,69 +307,70 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   //               rest of the MFMAs while reading step 2p + 2's fragments
   //               from buffer cur + 1 into fr[0] and issuing the first LH1
   //               loads of pair p + NBUF into buffer cur.
+  // The last row tile of a group is usually part empty: a wavefront runs the
+  // MFMAs (and reads the A fragments) of its first LIVE 16-row blocks only,
+  // LIVE the smallest of MB, MB/2, MB/4, 0 that covers its rows.  Loads and
+  // barriers are the same for every LIVE.
   constexpr int HALF = NB / 2;
-  constexpr int QH = MB * HALF;                        // MFMAs per half step
-  constexpr int PER = QH / NF > 0 ? QH / NF : 1;       // MFMAs per fragment read
-  constexpr int LP1 = QH / LH1 > 0 ? QH / LH1 : 1;     // MFMAs per load issue
-  constexpr int LP2 = QH / LH2 > 0 ? QH / LH2 : 1;
-  static_assert(QH / LP1 >= LH1 && QH / LP2 >= LH2, "every load is issued in its half step");
-  int cur = 0;  // wave-uniform
-  for (int p = 0; p < npairs; ++p) {
-    const int prv = cur == 0 ? NBUF - 1 : cur - 1;
-    const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-    const char* const bcur = smem + cur * BUF;
-    const char* const bnxt = smem + nxt * BUF;
+  // One half K step: MFMAs of column blocks J0 .. J0 + HALF - 1 on fr[S],
+  // with NL calls load(l) and NR calls read(r) spread evenly among them.
+  auto half_step = [&](auto s_, auto j0_, auto live_, auto nl_, auto nr_, auto&& load,
+                       auto&& read) {
+    constexpr int S = decltype(s_)::value, J0 = decltype(j0_)::value;
+    constexpr int LIVE = decltype(live_)::value;
+    constexpr int NL = decltype(nl_)::value, NR = decltype(nr_)::value;
+    constexpr int QH = LIVE * HALF;
+    constexpr int QS = QH > 0 ? QH : 1;
+    constexpr int LPQ = NL > 0 && QS / NL > 0 ? QS / NL : 1;  // slots per load
+    constexpr int RPQ = NR > 0 && QS / NR > 0 ? QS / NR : 1;  // slots per read
 #pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        mfma_bf16_agpr(acc[i][j], fr[0][i], fr[0][MB + j]);
-        const int q = j * MB + i;
-        if (q % LP2 == 0 && q / LP2 < LH2) issue_one(p + NBUF - 1, LH1 + q / LP2, prv);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < QS; ++q) {
+      if (q < QH) {
+        const int i = q % (LIVE > 0 ? LIVE : 1), j = J0 + q / (LIVE > 0 ? LIVE : 1);
+        mfma_bf16_agpr(acc[i][j], fr[S][i], fr[S][MB + j]);
       }
+      if (q % RPQ == RPQ - 1 && q / RPQ < NR) read(q / RPQ);
+      if (q % LPQ == 0 && q / LPQ < NL) load(q / LPQ);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = HALF; j < NB; ++j) {
+    for (int r = QS / RPQ; r < NR; ++r) read(r);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        mfma_bf16_agpr(acc[i][j], fr[0][i], fr[0][MB + j]);
-        const int q = (j - HALF) * MB + i;
-        if (q % PER == PER - 1 && q / PER < NF)
-          fr[1][q / PER] = *reinterpret_cast<const u32x4*>(bcur + frag_off(q / PER, 1));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int l = QS / LPQ; l < NL; ++l) load(l);
+  };
+  auto k_loop = [&](auto live_) {
+    constexpr int LIVE = decltype(live_)::value;
+    constexpr int NR = LIVE > 0 ? LIVE + NB : 0;  // fragments a K step reads
+    auto none = [](int) {};
+    int cur = 0;  // wave-uniform
+    for (int p = 0; p < npairs; ++p) {
+      const int prv = cur == 0 ? NBUF - 1 : cur - 1;
+      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+      const char* const bcur = smem + cur * BUF;
+      const char* const bnxt = smem + nxt * BUF;
+      auto read1 = [&](int r) {
+        const int f = r < LIVE ? r : MB + r - LIVE;
+        fr[1][f] = *reinterpret_cast<const u32x4*>(bcur + frag_off(f, 1));
+      };
+      auto read0 = [&](int r) {
+        const int f = r < LIVE ? r : MB + r - LIVE;
+        fr[0][f] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(f, 0));
+      };
+      auto load2 = [&](int l) { issue_one(p + NBUF - 1, LH1 + l, prv); };
+      auto load1 = [&](int l) { issue_one(p + NBUF, l, cur); };
+      half_step(CInt<0>{}, CInt<0>{}, live_, CInt<LH2>{}, CInt<0>{}, load2, none);
+      half_step(CInt<0>{}, CInt<HALF>{}, live_, CInt<0>{}, CInt<NR>{}, none, read1);
+      half_step(CInt<1>{}, CInt<0>{}, live_, CInt<0>{}, CInt<0>{}, none, none);
+      wait_vmem<(NBUF - 2) * LPB>();
+      stage_barrier();
+      half_step(CInt<1>{}, CInt<HALF>{}, live_, CInt<LH1>{}, CInt<NR>{}, load1, read0);
+      cur = nxt;
     }
-#pragma unroll
-    for (int r = QH / PER; r < NF; ++r)
-      fr[1][r] = *reinterpret_cast<const u32x4*>(bcur + frag_off(r, 1));
-#pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        mfma_bf16_agpr(acc[i][j], fr[1][i], fr[1][MB + j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    wait_vmem<(NBUF - 2) * LPB>();
-    stage_barrier();
-#pragma unroll
-    for (int j = HALF; j < NB; ++j) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        mfma_bf16_agpr(acc[i][j], fr[1][i], fr[1][MB + j]);
-        const int q = (j - HALF) * MB + i;
-        if (q % PER == PER - 1 && q / PER < NF)
-          fr[0][q / PER] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(q / PER, 0));
-        if (q % LP1 == 0 && q / LP1 < LH1) issue_one(p + NBUF, q / LP1, cur);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int r = QH / PER; r < NF; ++r)
-      fr[0][r] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(r, 0));
-    cur = nxt;
-  }
+  };
+  if (mlive > MB / 2) k_loop(CInt<MB>{});
+  else if (mlive > MB / 4) k_loop(CInt<MB / 2>{});
+  else if (mlive > 0) k_loop(CInt<MB / 4>{});
+  else k_loop(CInt<0>{});
 
   // -------------------------------------------------------------- epilogue
   wait_vmem<0>();   // this wavefront's last ring loads have landed
@@ -400,6 +406,11 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+int expert_gemm_cols(bool gated, int bm) {
+  (void)bm;
+  return gated ? 128 : 256;
+}
 
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s) {
   if (g.k_dim % 128 != 0) return hipErrorInvalidValue;  // whole pairs of 128-byte buffers

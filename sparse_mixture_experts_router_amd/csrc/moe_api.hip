@@ -96,10 +96,16 @@ Plan make_plan(const moe_config& c) {
   sz[R_INV] = T * k * 4;
   sz[R_TUP] = static_cast<size_t>(p.cap_up) * 8;
   sz[R_TDN] = static_cast<size_t>(p.cap_down) * 8;
-  // work-item lists of the large-tile kernel (128 gate/up columns, 256 down
-  // columns per tile)
-  p.nnt_up = p.up.variant == 1 ? (c.d_ff + 127) / 128 : 0;
-  p.nnt_down = p.down.variant == 1 ? (c.d_model + 255) / 256 : 0;
+  // work-item lists of the large-tile kernel (column tiles of the width its
+  // chosen instance computes)
+  if (p.up.variant == 1) {
+    const int cols = expert_gemm_cols(true, p.up.bm);
+    p.nnt_up = (c.d_ff + cols - 1) / cols;
+  }
+  if (p.down.variant == 1) {
+    const int cols = expert_gemm_cols(false, p.down.bm);
+    p.nnt_down = (c.d_model + cols - 1) / cols;
+  }
   sz[R_IUP] = static_cast<size_t>(p.cap_up) * p.nnt_up * 4;
   sz[R_IDN] = static_cast<size_t>(p.cap_down) * p.nnt_down * 4;
   sz[R_TB] = (2 * (N + S + 1) + 2) * 4;
@@ -126,7 +132,7 @@ Plan make_plan(const moe_config& c) {
   p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};
   if (p.dsplit <= 1 && p.down.variant == 1) {
     // tail split of the large-tile down GEMM (256 output columns per tile)
-    const int nnt = (c.d_model + 255) / 256;
+    const int nnt = p.nnt_down;
     p.split.tail_nnt = nnt;
     p.split.tail_cap_rows = static_cast<long>(p.cus / nnt) * p.bm_down;
     p.split.tail_max_parts = max_split_parts(c.d_ff * 2 / 128, 8);

@@ -171,6 +171,8 @@ GemmPick pick_gemm(int dtype, bool gated, long rows_per_expert, size_t a_bytes, 
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
+// Output columns per tile of the large-tile kernel launch_expert_gemm picks.
+int expert_gemm_cols(bool gated, int bm);
 
 // y from the per-expert rows: yperm (layer dtype), except rows at or past
 // plan[kPlanRowSplit], which are the sum of plan[kPlanParts] fp32 partial

@@ -120,6 +120,27 @@ def test_capacity_parity(label, shape, capacity):
     assert to_np(out["counts"]).sum() == shape.T * shape.k
 
 
+# Exact row counts per expert: with every expert's demand above the capacity C,
+# each gets exactly C rows, so its last row tile holds C mod BM rows.  The C
+# values put the tile's live 16-row blocks per wavefront (the large-tile
+# kernel skips the MFMAs of empty ones) into every class it distinguishes:
+# all, half, a quarter and none of a wavefront's row blocks.
+PARTIAL_TILE_CASES = (
+    [("bm256", MoEShape("part256", T=1100, d=512, N=4, k=2, F=1024), c)
+     for c in (264, 296, 356, 396, 436)] +
+    [("bm128", MoEShape("part128", T=600, d=512, N=4, k=2, F=512), c)
+     for c in (136, 158, 178, 200, 228)])
+
+
+@pytest.mark.parametrize("label,shape,capacity", PARTIAL_TILE_CASES,
+                         ids=[f"{c[0]}_C{c[2]}" for c in PARTIAL_TILE_CASES])
+def test_partial_last_tiles(label, shape, capacity):
+    _, out, ref = full_parity(shape, seed=11, label=f"partial_{label}_C{capacity}",
+                              capacity=capacity)
+    counts = to_np(out["counts"])
+    assert np.all(counts >= capacity), "every expert must be capped at exactly C rows"
+
+
 def test_capacity_drops_extra_tokens_of_a_hot_expert():
     shp = MoEShape("hot_cap", T=300, d=256, N=4, k=1, F=256)
     inputs = make_inputs(shp, seed=2, device="cuda")
