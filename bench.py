@@ -17,6 +17,7 @@ mixtral_prefill (default), mixtral_decode, deepseek_v3, qwen3_skew, tiny_f32.
 from __future__ import annotations
 
 import argparse
+import re
 import hashlib
 import json
 import os
@@ -38,7 +39,7 @@ DEFAULT_CPU_TOKENS = {"mixtral_prefill": 256, "mixtral_decode": 32, "deepseek_v3
 CPU_MIN_S, CPU_TARGET_S = 8.0, 15.0
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
 # the sources that decide the expert GEMMs' memory traffic
-GEMM_SRCS = ("expert_gemm.hip", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
+GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
 PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 1024
 
 
@@ -189,7 +190,7 @@ def profile_commands(d, workload):
 
 def is_up_gemm(name):
     """The gate/up launch: a grouped GEMM kernel instantiated with GATED = true."""
-    return "gemm_kernel<" in name and ("<true," in name or ", true," in name)
+    return re.search(r"gemm\w*_kernel<", name) is not None and ("<true," in name or ", true," in name)
 
 
 def short_name(name):

@@ -32,6 +32,7 @@
 //    round-robin) works through a contiguous range of (row tile, column tile)
 //    pairs ordered by bands of column tiles: the workgroups one XCD runs at a
 //    time share their A rows and weight rows in its L2.
+#include "expert_tile.h"
 #include "lds_ring.h"
 #include "mfma.h"
 
@@ -39,92 +40,6 @@ namespace moe {
 namespace {
 
 template <int N> struct CInt { static constexpr int value = N; };
-
-// Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
-// passes of 128 staged bytes per row: each pass is staged row-major in LDS at
-// stg (rows padded by 16 bytes, so the four row groups of an MFMA result
-// land in distinct banks), then leaves in whole 16-byte row chunks.
-//  SBF16 : staged and written as bf16, 64 columns per pass;
-//  else  : staged as fp32, 32 columns per pass, written as bf16 (8 columns
-//          per lane) or, if out_f32, as fp32 (4 columns per lane).  The
-//          plain pass uses this one path for both of its outputs, so the
-//          accumulators have a single consumer.
-// Row i of the block goes to out[(row0 + i) * ld + col0 + ...]; rows >=
-// rows_valid and columns >= cols_valid are not written.
-template <bool GATED, bool SBF16, int MB, int NB, int WTM>
-__device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
-                                            void* out, bool out_f32, size_t ld, long row0,
-                                            int rows_valid, int col0, int cols_valid) {
-  constexpr int NOUT = GATED ? NB / 2 : NB;
-  constexpr int ES = SBF16 ? 2 : 4;      // staged element bytes
-  constexpr int PB = 128 / (16 * ES);    // 16-column blocks per pass
-  constexpr int SROW = 128 + 16;
-  static_assert(NOUT % PB == 0, "whole passes");
-#pragma unroll
-  for (int pass = 0; pass < NOUT / PB; ++pass) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + 4 * (lane >> 4) + r;
-#pragma unroll
-        for (int jj = 0; jj < PB; ++jj) {
-          const int j = pass * PB + jj;
-          float v;
-          if (GATED) {
-            const float a = acc[i][j][r];
-            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
-          } else {
-            v = acc[i][j][r];
-          }
-          if (SBF16)
-            *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) =
-                f32_to_bf16(v);
-          else
-            *reinterpret_cast<float*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) = v;
-        }
-      }
-    }
-    if (SBF16) {
-      const int col = col0 + pass * 64 + (lane & 7) * 8;
-#pragma unroll
-      for (int q = 0; q < WTM / 8; ++q) {
-        const int row = q * 8 + (lane >> 3);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
-        if (row < rows_valid && col < cols_valid)
-          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
-                                    col) = v;
-      }
-    } else if (out_f32) {
-      const int col = col0 + pass * 32 + (lane & 7) * 4;
-#pragma unroll
-      for (int q = 0; q < WTM / 8; ++q) {
-        const int row = q * 8 + (lane >> 3);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
-        if (row < rows_valid && col < cols_valid)
-          *reinterpret_cast<u32x4*>(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld +
-                                    col) = v;
-      }
-    } else {
-      const int col = col0 + pass * 32 + (lane & 3) * 8;
-#pragma unroll
-      for (int q = 0; q < WTM / 16; ++q) {
-        const int row = q * 16 + (lane >> 2);
-        const char* src = stg + row * SROW + (lane & 3) * 32;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 16);
-        u32x4 v;
-        v[0] = f32_to_bf16(a[0]) | (static_cast<uint32_t>(f32_to_bf16(a[1])) << 16);
-        v[1] = f32_to_bf16(a[2]) | (static_cast<uint32_t>(f32_to_bf16(a[3])) << 16);
-        v[2] = f32_to_bf16(b[0]) | (static_cast<uint32_t>(f32_to_bf16(b[1])) << 16);
-        v[3] = f32_to_bf16(b[2]) | (static_cast<uint32_t>(f32_to_bf16(b[3])) << 16);
-        if (row < rows_valid && col < cols_valid)
-          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
-                                    col) = v;
-      }
-    }
-  }
-}
 
 template <bool GATED, int BM, int BNE, int NBUF>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
@@ -147,40 +62,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
 
   // ------------------------------------------------------- work of this block
-  // Work items: the (row tile, column tile) pairs of the scan's item list,
-  // then (plain pass only) the pieces (part, tile, column tile) of the last
-  // `tail` row tiles when the scan split them over their reduction.  Each XCD
-  // (blocks take XCDs round-robin) gets an equal contiguous share of both
-  // lists and runs it in order, so the workgroups it runs at once are one
-  // block of the list: one expert's row tiles next to a band of its weight
-  // tiles.
-  const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
-  const int n_nt = (g.n_dim + COLS - 1) / COLS;
-  const int ntl = *g.ntiles;
-  int tail = 0, parts = 1;
-  if (!GATED && g.plan != nullptr) {
-    tail = g.plan[kPlanTailTiles];
-    if (tail > 0) parts = g.plan[kPlanParts];
-  }
-  const int nrm = ntl - tail;
-  const long w_nrm = static_cast<long>(nrm) * n_nt;
-  const long w_spl = static_cast<long>(tail) * n_nt * parts;
-  const long n_lo = w_nrm * xcd / 8, n_cnt = w_nrm * (xcd + 1) / 8 - n_lo;
-  const long s_lo = w_spl * xcd / 8, s_cnt = w_spl * (xcd + 1) / 8 - s_lo;
-  int tile, nt, part = -1;
-  if (idx < n_cnt) {
-    const int v = g.items[n_lo + idx];
-    tile = v >> kItemColBits;
-    nt = v & ((1 << kItemColBits) - 1);
-  } else if (idx - n_cnt < s_cnt) {
-    const int lin = static_cast<int>(s_lo + idx - n_cnt);
-    part = lin / (tail * n_nt);
-    const int rem = lin - part * (tail * n_nt);
-    tile = nrm + rem / n_nt;
-    nt = rem % n_nt;
-  } else {
-    return;
-  }
+  int tile, nt, part, parts;
+  if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
   const int2 te = g.tiles[tile];
   const int e = te.x, m0 = te.y;
   const int seg = g.offsets[e];
@@ -321,8 +204,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     constexpr int NL = decltype(nl_)::value, NR = decltype(nr_)::value;
     constexpr int QH = LIVE * HALF;
     constexpr int QS = QH > 0 ? QH : 1;
-    constexpr int LPQ = NL > 0 && QS / NL > 0 ? QS / NL : 1;  // slots per load
-    constexpr int RPQ = NR > 0 && QS / NR > 0 ? QS / NR : 1;  // slots per read
+    constexpr int LPQ = slots_per(QS, NL);  // slots per load
+    constexpr int RPQ = slots_per(QS, NR);  // slots per read
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       if (q < QH) {
@@ -394,12 +277,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 template <bool GATED, int BM, int BNE, int NBUF>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
-  const long n_nt = (g.n_dim + COLS - 1) / COLS;
-  // every XCD's share of the work items fits in blocks / 8 slots (the split
-  // pieces number at most one round of g.cus workgroups)
-  const long per_xcd = (static_cast<long>(g.tiles_cap) * n_nt + 7) / 8 +
-                       (GATED ? 0 : (g.cus + 7) / 8) + 1;
-  const long blocks = 8 * per_xcd;
+  const long blocks = expert_grid(g, GATED, COLS);
   hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, g);
   return hipGetLastError();

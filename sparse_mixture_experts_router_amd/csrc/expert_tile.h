@@ -1,0 +1,152 @@
+// Pieces shared by the two large-tile expert GEMM kernels (expert_gemm.hip,
+// expert_gemm_ws.hip): the work decode of a workgroup and the tile epilogue.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Calls of one kind spread over `slots` MFMA slots: slots per call (>= 1).
+constexpr int slots_per(int slots, int calls) {
+  return calls > 0 && slots / calls > 0 ? slots / calls : 1;
+}
+
+// Work items: the (row tile, column tile) pairs of the scan's item list, then
+// (plain pass only) the pieces (part, tile, column tile) of the last `tail`
+// row tiles when the scan split them over their reduction.  Each XCD (blocks
+// take XCDs round-robin) gets an equal contiguous share of both lists and
+// runs it in order, so the workgroups it runs at once are one block of the
+// list: one expert's row tiles next to a band of its weight tiles.  Returns
+// false for a block with no work; part = -1 for an unsplit item, else the
+// piece's index among `parts`.
+__device__ __forceinline__ bool decode_work(const GemmArgs& g, bool gated, int cols, int& tile,
+                                            int& nt, int& part, int& parts) {
+  const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
+  const int n_nt = (g.n_dim + cols - 1) / cols;
+  const int ntl = *g.ntiles;
+  int tail = 0;
+  parts = 1;
+  if (!gated && g.plan != nullptr) {
+    tail = g.plan[kPlanTailTiles];
+    if (tail > 0) parts = g.plan[kPlanParts];
+  }
+  const int nrm = ntl - tail;
+  const long w_nrm = static_cast<long>(nrm) * n_nt;
+  const long w_spl = static_cast<long>(tail) * n_nt * parts;
+  const long n_lo = w_nrm * xcd / 8, n_cnt = w_nrm * (xcd + 1) / 8 - n_lo;
+  const long s_lo = w_spl * xcd / 8, s_cnt = w_spl * (xcd + 1) / 8 - s_lo;
+  part = -1;
+  if (idx < n_cnt) {
+    const int v = g.items[n_lo + idx];
+    tile = v >> kItemColBits;
+    nt = v & ((1 << kItemColBits) - 1);
+    return true;
+  }
+  if (idx - n_cnt < s_cnt) {
+    const int lin = static_cast<int>(s_lo + idx - n_cnt);
+    part = lin / (tail * n_nt);
+    const int rem = lin - part * (tail * n_nt);
+    tile = nrm + rem / n_nt;
+    nt = rem % n_nt;
+    return true;
+  }
+  return false;
+}
+
+// Grid of the large-tile kernels: every XCD's share of the work items fits in
+// blocks / 8 slots (the split pieces number at most one round of g.cus
+// workgroups).
+inline long expert_grid(const GemmArgs& g, bool gated, int cols) {
+  const long n_nt = (g.n_dim + cols - 1) / cols;
+  const long per_xcd = (static_cast<long>(g.tiles_cap) * n_nt + 7) / 8 +
+                       (gated ? 0 : (g.cus + 7) / 8) + 1;
+  return 8 * per_xcd;
+}
+
+// Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
+// passes of 128 staged bytes per row: each pass is staged row-major in LDS at
+// stg (rows padded by 16 bytes, so the four row groups of an MFMA result
+// land in distinct banks), then leaves in whole 16-byte row chunks.
+//  SBF16 : staged and written as bf16, 64 columns per pass;
+//  else  : staged as fp32, 32 columns per pass, written as bf16 (8 columns
+//          per lane) or, if out_f32, as fp32 (4 columns per lane).  The
+//          plain pass uses this one path for both of its outputs, so the
+//          accumulators have a single consumer.
+// Row i of the block goes to out[(row0 + i) * ld + col0 + ...]; rows >=
+// rows_valid and columns >= cols_valid are not written.
+template <bool GATED, bool SBF16, int MB, int NB, int WTM>
+__device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
+                                            void* out, bool out_f32, size_t ld, long row0,
+                                            int rows_valid, int col0, int cols_valid) {
+  constexpr int NOUT = GATED ? NB / 2 : NB;
+  constexpr int ES = SBF16 ? 2 : 4;      // staged element bytes
+  constexpr int PB = 128 / (16 * ES);    // 16-column blocks per pass
+  constexpr int SROW = 128 + 16;
+  static_assert(NOUT % PB == 0, "whole passes");
+#pragma unroll
+  for (int pass = 0; pass < NOUT / PB; ++pass) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + 4 * (lane >> 4) + r;
+#pragma unroll
+        for (int jj = 0; jj < PB; ++jj) {
+          const int j = pass * PB + jj;
+          float v;
+          if (GATED) {
+            const float a = acc[i][j][r];
+            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
+          } else {
+            v = acc[i][j][r];
+          }
+          if (SBF16)
+            *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) =
+                f32_to_bf16(v);
+          else
+            *reinterpret_cast<float*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) = v;
+        }
+      }
+    }
+    if (SBF16) {
+      const int col = col0 + pass * 64 + (lane & 7) * 8;
+#pragma unroll
+      for (int q = 0; q < WTM / 8; ++q) {
+        const int row = q * 8 + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    } else if (out_f32) {
+      const int col = col0 + pass * 32 + (lane & 7) * 4;
+#pragma unroll
+      for (int q = 0; q < WTM / 8; ++q) {
+        const int row = q * 8 + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    } else {
+      const int col = col0 + pass * 32 + (lane & 3) * 8;
+#pragma unroll
+      for (int q = 0; q < WTM / 16; ++q) {
+        const int row = q * 16 + (lane >> 2);
+        const char* src = stg + row * SROW + (lane & 3) * 32;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 16);
+        u32x4 v;
+        v[0] = f32_to_bf16(a[0]) | (static_cast<uint32_t>(f32_to_bf16(a[1])) << 16);
+        v[1] = f32_to_bf16(a[2]) | (static_cast<uint32_t>(f32_to_bf16(a[3])) << 16);
+        v[2] = f32_to_bf16(b[0]) | (static_cast<uint32_t>(f32_to_bf16(b[1])) << 16);
+        v[3] = f32_to_bf16(b[2]) | (static_cast<uint32_t>(f32_to_bf16(b[3])) << 16);
+        if (row < rows_valid && col < cols_valid)
+          *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld +
+                                    col) = v;
+      }
+    }
+  }
+}
+
+}  // namespace moe

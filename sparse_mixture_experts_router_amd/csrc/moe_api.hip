@@ -131,7 +131,7 @@ Plan make_plan(const moe_config& c) {
   sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
   p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};
   if (p.dsplit <= 1 && p.down.variant == 1) {
-    // tail split of the large-tile down GEMM (256 output columns per tile)
+    // tail split of the large-tile down GEMM
     const int nnt = p.nnt_down;
     p.split.tail_nnt = nnt;
     p.split.tail_cap_rows = static_cast<long>(p.cus / nnt) * p.bm_down;

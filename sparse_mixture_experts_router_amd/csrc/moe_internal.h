@@ -159,7 +159,8 @@ enum { kPlanParts = 0, kPlanRowSplit = 1, kPlanStride = 2, kPlanTailTiles = 3, k
 
 // Kernel choice for one grouped GEMM: variant 0 = register-staged tiles
 // (grouped_gemm.hip, fp32 and few-row shapes), 1 = large direct-to-LDS bf16
-// tiles (expert_gemm.hip); bm = rows per tile (the tile list's granularity).
+// tiles (expert_gemm.hip), which run from the scan's work-item lists; bm =
+// rows per tile (the tile list's granularity).
 struct GemmPick {
   int variant;
   int bm;

@@ -84,20 +84,28 @@ def test_all_tokens_one_expert():
     assert to_np(out["counts"]).tolist() == [0, 0, 0, 300]
 
 
-@pytest.mark.parametrize("S", [0, 1])
-def test_tail_tiles_split_over_k(S):
-    """Last-round tail split of the large-tile down GEMM.
+# (label, T, F): every token goes to expert 7, so the down pass (128-row
+# tiles, 16 column tiles of 256) has T / 128 row tiles, twice that with S = 1.
+#  base  : 20 (40) row tiles leave a last round of 64 (128) workgroups on 256
+#          CUs; the scan splits the last 4 (8) row tiles over their
+#          reduction in 2 parts (the down reduction, 1024, has 16 pairs of K
+#          steps: 8 + 8).
+#  odd_k : the same with d_ff = 1152, 18 pairs of K steps split 10 + 8.
+#  long  : 33 (66) row tiles leave 16 (32) workgroups; the last 1 (2) row
+#          tiles split in 2 parts.
+# The combine adds the fp32 parts.
+TAIL_SPLIT_CASES = [("base", 2510, 1024), ("odd_k", 2510, 1152), ("long", 4200, 1024)]
 
-    Every token goes to expert 7, so the down pass has exactly 20 row tiles of
-    128 (the last one ragged) and, with S = 1, 20 more for the shared expert;
-    16 column tiles each.  On a 256-CU device that leaves 64 (128) workgroups
-    for a last round, so the scan splits the last 4 (8) row tiles over their
-    reduction in 2 parts and the combine adds the fp32 parts."""
-    shp = MoEShape("tail", T=2510, d=4096, N=8, k=1, F=1024, S=S)
+
+@pytest.mark.parametrize("S", [0, 1])
+@pytest.mark.parametrize("label,T,F", TAIL_SPLIT_CASES, ids=[c[0] for c in TAIL_SPLIT_CASES])
+def test_tail_tiles_split_over_k(label, T, F, S):
+    """Last-round tail split of the large-tile down GEMM."""
+    shp = MoEShape("tail", T=T, d=4096, N=8, k=1, F=F, S=S)
     inputs = make_inputs(shp, seed=8, device="cuda")
     inputs["logit_bias"] = torch.tensor([0.0] * 7 + [100.0], device="cuda")
-    _, out, _ = full_parity(shp, inputs=inputs, label=f"tail_split_S{S}")
-    assert int(out["counts"][7]) == 2510
+    _, out, _ = full_parity(shp, inputs=inputs, label=f"tail_split_{label}_S{S}")
+    assert int(out["counts"][7]) == T
 
 
 CAPACITY_CASES = [
@@ -124,11 +132,15 @@ def test_capacity_parity(label, shape, capacity):
 # each gets exactly C rows, so its last row tile holds C mod BM rows.  The C
 # values put the tile's live 16-row blocks per wavefront (the large-tile
 # kernel skips the MFMAs of empty ones) into every class it distinguishes:
-# all, half, a quarter and none of a wavefront's row blocks.
+# all, half, a quarter and none of a wavefront's row blocks.  bm256: >= 512
+# rows per expert, 256-row tiles; bm128: fewer rows, 128-row tiles; odd_k:
+# the same with reductions that are odd multiples of 128.
 PARTIAL_TILE_CASES = (
     [("bm256", MoEShape("part256", T=1100, d=512, N=4, k=2, F=1024), c)
      for c in (264, 296, 356, 396, 436)] +
-    [("bm128", MoEShape("part128", T=600, d=512, N=4, k=2, F=512), c)
+    [("bm128", MoEShape("part128", T=1000, d=512, N=4, k=2, F=512), c)
+     for c in (264, 280, 296, 376, 456)] +
+    [("odd_k", MoEShape("part_odd", T=600, d=384, N=4, k=2, F=640), c)
      for c in (136, 158, 178, 200, 228)])
 
 
