@@ -42,13 +42,22 @@ What it computes, and where the pages define it:
   token's other gates are not renormalised), and f, counts and P still
   describe the router's choice before dropping.
 
+* O9 FP8 expert weights (optional): the pages size expert weights at one byte
+  per parameter in FP8 ("MoE inference: the call centre with 256 specialists
+  ...", weight-memory estimate under "Total memory") without defining the
+  format.  Here a weight is an OCP FP8 E4M3 code (sign, 4 exponent bits with
+  bias 7, 3 mantissa bits; exponent field 0 = subnormal; S.1111.111 = NaN; no
+  infinities) times a per-output-channel scale, decoded exactly to float64.
+
 Readings taken where the pages are silent (each is listed in the design notes):
 ties in top-k go to the lower index under IEEE comparison (+0 == -0); f_i
 divides by T*k so that sum f = 1 for any k; P_i uses the full N-way softmax of
 the unbiased logits; shared experts have gate 1 and count in neither k, f nor
 P; no biases inside experts or router.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+Parity status: every function here (O9 included: closed-form codes, all 256
+codes against PyTorch's float8_e4m3fn, the output-channel scale identity) is
+pinned by ``tests/test_oracle_pins.py``
 (worked examples of the pages, closed forms, brute force, library special
 cases).  SwiGLU numerics at the real layer shapes have no printed values on the
 pages; they are pinned only through the N = 1, k = 1 reduction to a library
@@ -62,6 +71,8 @@ from typing import Callable, Optional, Sequence, Tuple, Union
 import numpy as np
 
 __all__ = [
+    "e4m3_decode",
+    "dequantize",
     "router_logits",
     "selection_keys",
     "capacity_keep",
@@ -270,6 +281,28 @@ def balance(f, P, alpha: float = BALANCE_ALPHA):
 
 
 # ------------------------------------------------------------------ O1..O7
+def e4m3_decode(codes) -> np.ndarray:
+    """O9: the float64 value of each OCP FP8 E4M3 code (uint8 array).
+
+    value = (-1)^s * 2^(e - 7) * (1 + m / 8)   for exponent field e >= 1,
+            (-1)^s * 2^(-6) * (m / 8)          for e = 0 (subnormal),
+    NaN for e = 15 and m = 7.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def dequantize(codes, scale) -> np.ndarray:
+    """O9: weights [..., out, in] = e4m3_decode(codes) * scale[..., out] (one
+    scale per output channel, i.e. per row of the [out, in] matrix)."""
+    return e4m3_decode(codes) * _f64(scale)[..., :, None]
+
+
 def _expert_getter(experts: ExpertSource):
     if callable(experts):
         return experts

@@ -403,11 +403,74 @@ def pin_capacity_layer(O):
         _close(one[key], ref[key], 0, f"{key} independent of capacity")
 
 
+def pin_e4m3_closed_form(O):
+    """O9: E4M3 codes whose values follow from the format's definition alone
+    (bias 7, 3 mantissa bits, subnormals at exponent field 0, S.1111.111 NaN,
+    no infinities)."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x30: 0.5, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0,
+             0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    got = O.e4m3_decode(np.array(list(table), dtype=np.uint8))
+    _close(got, list(table.values()), 0, "E4M3 closed-form codes")
+    if not np.signbit(O.e4m3_decode(np.array([0x80], dtype=np.uint8))[0]):
+        raise AssertionError("0x80 must decode to -0.0")
+    nan = O.e4m3_decode(np.array([0x7F, 0xFF], dtype=np.uint8))
+    if not np.all(np.isnan(nan)):
+        raise AssertionError("S.1111.111 must decode to NaN")
+
+
+def pin_e4m3_library(O):
+    """O9: all 256 codes against PyTorch's float8_e4m3fn (the OCP E4M3 type),
+    widened to float64; the 127 positive finite codes strictly increase and a
+    set sign bit negates."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    if not np.array_equal(np.isnan(got), np.isnan(ref)):
+        raise AssertionError("NaN codes differ from float8_e4m3fn")
+    fin = ~np.isnan(ref)
+    _close(got[fin], ref[fin], 0, "E4M3 against float8_e4m3fn")
+    pos = got[:127]
+    if not np.all(np.diff(pos) > 0):
+        raise AssertionError("positive E4M3 codes must increase")
+    _close(got[128:255], -pos, 0, "sign bit negates")
+
+
+def pin_dequantize_per_output_channel(O):
+    """O9: a scale belongs to an output channel: x (Q s)^T = (x Q^T) s over
+    the rows n of the [out, in] matrix, for any x; a layer with FP8 weights
+    equals the layer with the decoded, scaled weights written out by the
+    library decode."""
+    rng = np.random.default_rng(31)
+    E, n_out, n_in = 2, 6, 8
+    codes = rng.integers(0, 0x7F, size=(E, n_out, n_in)).astype(np.uint8)
+    codes |= (rng.random((E, n_out, n_in)) < 0.5).astype(np.uint8) << 7
+    scale = rng.uniform(0.5, 2.0, size=(E, n_out))
+    W = O.dequantize(codes, scale)
+    x = rng.standard_normal((5, n_in))
+    q = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for e in range(E):
+        _close(x @ W[e].T, (x @ q[e].T) * scale[e][None, :], 1e-12, "scale per output channel")
+    T, d, F, N = 7, 8, 6, 2
+    xl = rng.standard_normal((T, d))
+    wr = rng.standard_normal((N, d))
+    cg = rng.integers(0, 0x7F, size=(N, F, d)).astype(np.uint8)
+    cu = rng.integers(0, 0x7F, size=(N, F, d)).astype(np.uint8)
+    cd = rng.integers(0, 0x7F, size=(N, d, F)).astype(np.uint8)
+    sg, su, sd = (rng.uniform(0.01, 0.02, size=s) for s in ((N, F), (N, F), (N, d)))
+    dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).double().numpy()
+    ref = O.moe_forward(xl, wr, (dec(cg) * sg[..., None], dec(cu) * su[..., None],
+                                 dec(cd) * sd[..., None]), 1)
+    got = O.moe_forward(xl, wr, (O.dequantize(cg, sg), O.dequantize(cu, su),
+                                 O.dequantize(cd, sd)), 1)
+    _close(got["y"], ref["y"], 1e-12, "FP8 layer")
+
+
 ALL_PINS = [
     pin_e1_top2, pin_e2_blend, pin_e3_top2, pin_e4_dense, pin_e5_balance, pin_e6_toy_routing,
     pin_topk_brute_force, pin_select_bias_semantics, pin_swiglu_closed_form,
     pin_single_expert_is_swiglu, pin_router_linear, pin_dense_crosspath,
     pin_k_equals_n_is_dense_softmax, pin_shared_expert, pin_relabel_and_chunking, pin_stats,
     pin_invariants, pin_unused_expert_never_read, pin_empty_batch, pin_capacity_brute_force,
-    pin_capacity_layer,
+    pin_capacity_layer, pin_e4m3_closed_form, pin_e4m3_library, pin_dequantize_per_output_channel,
 ]

@@ -45,6 +45,12 @@ MUTATIONS = {
                             "keep[tok[capacity + 1:], slot[capacity + 1:]] = False"),
     "capacity_ignored_in_layer": ("tok, slot = np.nonzero((idx == e) & keep)",
                                   "tok, slot = np.nonzero(idx == e)"),
+    "e4m3_bias_8": ("np.ldexp(1.0 + m / 8.0, e - 7))", "np.ldexp(1.0 + m / 8.0, e - 8))"),
+    "e4m3_subnormal_as_normal": ("mag = np.where(e == 0, np.ldexp(m / 8.0, -6),",
+                                 "mag = np.where(e < 0, np.ldexp(m / 8.0, -6),"),
+    "e4m3_no_nan": ("mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)", "pass"),
+    "scale_on_input_channel": ("return e4m3_decode(codes) * _f64(scale)[..., :, None]",
+                               "return e4m3_decode(codes) * _f64(scale)[..., None, :]"),
     "keys_compared_in_fp64": [
         ("return (r32 + b32[None, :]).astype(np.float32)",
          "return r32.astype(np.float64) + b32.astype(np.float64)[None, :]"),

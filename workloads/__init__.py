@@ -28,7 +28,7 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["MoEShape", "CONFIGS", "make_inputs", "reduced", "zipf_offsets"]
+__all__ = ["MoEShape", "CONFIGS", "make_inputs", "reduced", "zipf_offsets", "to_e4m3"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -43,6 +43,7 @@ class MoEShape:
     dtype: str = "bf16"   # "bf16" or "f32": x, all weights and y
     select_bias: bool = False   # per-expert U(-0.1, 0.1) bias on the selection key only
     zipf_s: float = 0.0         # > 0: add -s*ln(e+1) to the logits
+    fp8: bool = False           # expert weights as E4M3 codes + fp32 per-output-channel scales
 
     @property
     def torch_dtype(self):
@@ -60,6 +61,8 @@ class MoEShape:
             extra.append("selection bias U(-0.1,0.1)")
         if self.zipf_s:
             extra.append(f"Zipf(s={self.zipf_s}) logit offset")
+        if self.fp8:
+            extra.append("FP8 E4M3 expert weights, per-channel scales")
         tail = (", " + ", ".join(extra)) if extra else ""
         return (f"T={self.T} d_model={self.d} experts={self.N} top-{self.k} "
                 f"d_ff={self.F} {self.dtype}{tail}")
@@ -69,6 +72,8 @@ CONFIGS: Dict[str, MoEShape] = {
     "tiny_f32": MoEShape("tiny_f32", T=64, d=128, N=4, k=2, F=256, dtype="f32"),
     "mixtral_prefill": MoEShape("mixtral_prefill", T=4096, d=4096, N=8, k=2, F=14336),
     "mixtral_decode": MoEShape("mixtral_decode", T=32, d=4096, N=8, k=2, F=14336),
+    "mixtral_decode_fp8": MoEShape("mixtral_decode_fp8", T=32, d=4096, N=8, k=2, F=14336,
+                                   fp8=True),
     "deepseek_v3": MoEShape("deepseek_v3", T=8192, d=7168, N=256, k=8, F=2048, S=1,
                             select_bias=True),
     "qwen3_skew": MoEShape("qwen3_skew", T=16384, d=4096, N=128, k=8, F=1536,
@@ -146,4 +151,25 @@ def make_inputs(shape: MoEShape, seed: int = 0, device="cpu",
         out["select_bias"] = None
     out["logit_bias"] = (zipf_offsets(N, shape.zipf_s).to(device)
                          if shape.zipf_s > 0 else None)
+    if shape.fp8:
+        for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            codes, scale = to_e4m3(out[n]) if out[n] is not None else (None, None)
+            out[n], out[n + "_scale"] = codes, scale
     return out
+
+
+def to_e4m3(w: torch.Tensor, chunk: int = 8):
+    """Weights [E, out, in] -> (E4M3 codes as uint8 [E, out, in], fp32 scales
+    [E, out]): each output channel scaled so its largest magnitude maps to
+    448, the largest finite E4M3 value, then rounded by torch's float8_e4m3fn
+    cast.  Input preparation for the FP8 weight format, in chunks of experts."""
+    E = w.shape[0]
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scale = torch.empty(w.shape[:2], dtype=torch.float32, device=w.device)
+    for e0 in range(0, E, chunk):
+        wf = w[e0:e0 + chunk].float()
+        s = wf.abs().amax(dim=2).clamp_min(1e-30) / 448.0
+        codes[e0:e0 + chunk] = (wf / s[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scale[e0:e0 + chunk] = s
+        del wf
+    return codes, scale
