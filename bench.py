@@ -77,11 +77,14 @@ def copy_probe(mib):
 def algorithmic(shape, active):
     """Layer and gate/up-kernel algorithmic FLOPs and bytes (inputs once, outputs once)."""
     T, d, N, k, F, S, b = shape.T, shape.d, shape.N, shape.k, shape.F, shape.S, shape.elem_bytes
+    wb = 1 if shape.fp8 else b          # expert weight bytes per element
+    sb = 4 if shape.fp8 else 0          # fp32 scale bytes per output channel
     rows = T * k + S * T
     layer_flops = 2 * rows * 3 * d * F + 2 * T * d * N
-    layer_bytes = (active + S) * 3 * d * F * b + N * d * b + 2 * T * d * b + T * k * 8
+    layer_bytes = ((active + S) * (3 * d * F * wb + (2 * F + d) * sb) + N * d * b + 2 * T * d * b
+                   + T * k * 8)
     up_flops = 2 * rows * d * 2 * F
-    up_bytes = (active + S) * 2 * F * d * b + T * d * b + rows * F * b
+    up_bytes = (active + S) * 2 * F * (d * wb + sb) + T * d * b + rows * F * b
     return layer_flops, layer_bytes, up_flops, up_bytes
 
 
@@ -131,21 +134,29 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
     lb = None if inputs["logit_bias"] is None else inputs["logit_bias"].cpu().numpy()
     sb = None if inputs["select_bias"] is None else inputs["select_bias"].cpu().numpy()
     need = sorted(set(gpu_idx[:n_tok].reshape(-1).tolist()))   # more are fetched on demand
-    cache = {e: (inputs["w_gate"][e].float().cpu().numpy(), inputs["w_up"][e].float().cpu().numpy(),
-                 inputs["w_down"][e].float().cpu().numpy()) for e in need}
+
+    def weight(name, e=None):
+        w = inputs[name] if e is None else inputs[name][e]
+        if not shape.fp8:
+            return w.float().cpu().numpy()
+        sc = inputs[name + "_scale"] if e is None else inputs[name + "_scale"][e]
+        return oracle.dequantize(w.cpu().numpy(), sc.cpu().numpy())   # O9, part of the oracle
+
+    def load(e):
+        return (weight("w_gate", e), weight("w_up", e), weight("w_down", e))
+
+    cache = {e: load(e) for e in need}
     fetched = []
 
     def expert(e):
         if e not in cache:   # a selection flip against the GPU's routing: fetch on demand
             fetched.append(e)
-            cache[e] = (inputs["w_gate"][e].float().cpu().numpy(),
-                        inputs["w_up"][e].float().cpu().numpy(),
-                        inputs["w_down"][e].float().cpu().numpy())
+            cache[e] = load(e)
         return cache[e]
 
     shared = None
     if shape.S:
-        shared = tuple(inputs[n].float().cpu().numpy() for n in ("ws_gate", "ws_up", "ws_down"))
+        shared = tuple(weight(n) for n in ("ws_gate", "ws_up", "ws_down"))
 
     def run(n):
         t0 = time.perf_counter()
@@ -355,7 +366,9 @@ def main():
     print(f"[bench] drawing inputs: {shape.describe()}", file=sys.stderr, flush=True)
     inputs = make_inputs(shape, seed=args.seed, device=dev)
     T, N, k = shape.T, shape.N, shape.k
-    cfg = moe.make_config(T, shape.d, N, k, shape.F, shape.S, shape.torch_dtype)
+    cfg = moe.make_config(T, shape.d, N, k, shape.F, shape.S, shape.torch_dtype,
+                          weight_format=(moe.MOE_WEIGHTS_FP8_E4M3 if shape.fp8
+                                         else moe.MOE_WEIGHTS_DTYPE))
     ws = moe.alloc_workspace(cfg, dev)
     y = torch.empty((T, shape.d), dtype=shape.torch_dtype, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -480,6 +493,8 @@ def main():
         "config": {"workload": shape.name, "T": T, "d_model": shape.d, "n_experts": N,
                    "top_k": k, "d_ff": shape.F, "n_shared": shape.S,
                    "select_bias": shape.select_bias, "zipf_s": shape.zipf_s,
+                   "expert_weights": "fp8_e4m3 + fp32 per-channel scales" if shape.fp8
+                   else shape.dtype,
                    "parallelism": "single GPU"},
         "layer": {"tflops": round(lf / (ms_step * 1e-3) / 1e12, 2),
                   "mfma_frac": round(lf / (ms_step * 1e-3) / 1e12 / peak_flops, 4),

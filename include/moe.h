@@ -31,7 +31,8 @@
  *  - Weights use the linear layer's [out, in] layout: W_r [N, d],
  *    W_gate/W_up [N, F, d], W_down [N, d, F]; shared experts [S, F, d] and
  *    [S, d, F].  x and y are [T, d].  The element type of x, y and every weight
- *    is cfg->dtype; biases, logits, gates and statistics are fp32.
+ *    is cfg->dtype (expert weights: see moe_weight_format); biases, logits,
+ *    gates, scales and statistics are fp32.
  *  - Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32
  *    accumulation; the expert hidden activations and per-expert outputs are
  *    held in the input dtype (bf16 rounding to nearest even); y is rounded once.
@@ -39,7 +40,8 @@
  *  - Calls are thread-safe; concurrent calls must use distinct workspaces.
  *  - Supported sizes: 1 <= k <= min(N, 16), N <= 512, 0 <= S <= 4, capacity >= 0,
  *    d and F positive multiples of 64, T >= 0 (T = 0 launches nothing and
- *    returns MOE_OK).  Other sizes return MOE_ERR_UNSUPPORTED.
+ *    returns MOE_OK); FP8 expert weights with dtype MOE_BF16 only.  Other
+ *    sizes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -61,6 +63,21 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage of the expert weights (routed and shared; W_r always uses dtype).
+ * The pages size expert weights at one byte per parameter for FP8 ("MoE
+ * inference: the call centre with 256 specialists ...", the weight-memory
+ * estimate under "Total memory") but define no format; this library takes
+ * OCP FP8 E4M3 codes (bias 7, no infinities, S.1111.111 = NaN, largest
+ * finite 448) with one fp32 scale per output channel:
+ *   W[e][n][j] = decode(code[e][n][j]) * scale[e][n]
+ * (n = row of the [out, in] matrix: F rows of W_gate/W_up, d rows of W_down).
+ * Decoded values are exact in bf16; the scale multiplies each fp32 sum in
+ * the GEMM epilogue (before SiLU for gate and up).  A NaN code gives NaN. */
+typedef enum {
+  MOE_WEIGHTS_DTYPE = 0,    /* expert weights in cfg->dtype, like x and y     */
+  MOE_WEIGHTS_FP8_E4M3 = 1  /* 1-byte E4M3 codes + fp32 scales (dtype BF16)   */
+} moe_weight_format;
+
 /* Layer sizes.  T tokens, d_model, N routed experts, top_k kept per token,
  * d_ff hidden size of every expert (routed and shared), n_shared always-on
  * experts, dtype a moe_dtype.
@@ -70,7 +87,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * "Keeping the experts busy": the extras are dropped).  Kept are an expert's
  * first C assignments in token order; a dropped assignment adds nothing to y
  * (the token's other gates are not renormalised).  topk_idx, topk_gate,
- * counts and prob_sum still describe the router's choice before dropping. */
+ * counts and prob_sum still describe the router's choice before dropping.
+ *
+ * weight_format: a moe_weight_format (0 = weights in dtype). */
 typedef struct {
   int32_t T;
   int32_t d_model;
@@ -80,6 +99,7 @@ typedef struct {
   int32_t n_shared;
   int32_t dtype;
   int32_t capacity;
+  int32_t weight_format;
 } moe_config;
 
 /* Layer parameters (device pointers, caller-owned, read-only). */
@@ -96,6 +116,15 @@ typedef struct {
   const float* select_bias; /* [N] added to the selection key only (the
                                auxiliary-loss-free routing bias of "The bare
                                mechanism"), or NULL                           */
+  /* Per-output-channel scales of FP8 expert weights (MOE_WEIGHTS_FP8_E4M3;
+     ignored otherwise).  The routed ones are required by moe_layer_forward,
+     the shared ones when S > 0.                                              */
+  const float* w_gate_scale;  /* [N, F] */
+  const float* w_up_scale;    /* [N, F] */
+  const float* w_down_scale;  /* [N, d] */
+  const float* ws_gate_scale; /* [S, F] */
+  const float* ws_up_scale;   /* [S, F] */
+  const float* ws_down_scale; /* [S, d] */
 } moe_weights;
 
 /* Routing outputs (device pointers, caller-owned, written by the call).  For

@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
-    "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "STAGES", "MoEError", "MoEConfig", "MoEWeights",
+    "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "MOE_WEIGHTS_DTYPE", "MOE_WEIGHTS_FP8_E4M3", "STAGES",
+    "MoEError", "MoEConfig", "MoEWeights",
     "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
     "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
 ]
@@ -27,6 +28,9 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_FP8_E4M3 = 0, 1
+_SCALES = ("w_gate_scale", "w_up_scale", "w_down_scale", "ws_gate_scale", "ws_up_scale",
+           "ws_down_scale")
 STAGES = ("route", "permute", "expert_up", "expert_down", "combine")
 
 
@@ -41,7 +45,8 @@ class MoEConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32)]
 
 
 class MoEWeights(ctypes.Structure):
@@ -49,7 +54,7 @@ class MoEWeights(ctypes.Structure):
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p),
                 ("ws_down", ctypes.c_void_p), ("logit_bias", ctypes.c_void_p),
-                ("select_bias", ctypes.c_void_p)]
+                ("select_bias", ctypes.c_void_p)] + [(n, ctypes.c_void_p) for n in _SCALES]
 
 
 class MoERouting(ctypes.Structure):
@@ -104,12 +109,15 @@ _TORCH_DTYPE = {MOE_BF16: torch.bfloat16, MOE_F32: torch.float32}
 
 
 def make_config(T: int, d_model: int, n_experts: int, top_k: int, d_ff: int,
-                n_shared: int = 0, dtype=torch.bfloat16, capacity: int = 0) -> MoEConfig:
+                n_shared: int = 0, dtype=torch.bfloat16, capacity: int = 0,
+                weight_format: int = MOE_WEIGHTS_DTYPE) -> MoEConfig:
     """``capacity``: 0 = dropless, else the most (token, slot) assignments a
-    routed expert takes per call (the rest are dropped)."""
+    routed expert takes per call (the rest are dropped).  ``weight_format``:
+    MOE_WEIGHTS_FP8_E4M3 for expert weights given as uint8 E4M3 codes plus
+    fp32 per-output-channel scales (``*_scale`` entries of the weights)."""
     code = MOE_BF16 if dtype in (torch.bfloat16, "bf16", MOE_BF16) else MOE_F32
     return MoEConfig(int(T), int(d_model), int(n_experts), int(top_k), int(d_ff),
-                     int(n_shared), code, int(capacity))
+                     int(n_shared), code, int(capacity), int(weight_format))
 
 
 def moe_workspace_size(cfg: MoEConfig) -> int:
@@ -142,9 +150,14 @@ def _stream(stream) -> int:
 
 def _weights(cfg: MoEConfig, w: Dict[str, Optional[torch.Tensor]], experts=True) -> MoEWeights:
     dt = _TORCH_DTYPE[cfg.dtype]
-    names = ["w_router"] + (["w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"]
-                            if experts else [])
-    args = {n: _ptr(w.get(n), dt, n) for n in names}
+    fp8 = cfg.weight_format == MOE_WEIGHTS_FP8_E4M3
+    args = {"w_router": _ptr(w.get("w_router"), dt, "w_router")}
+    if experts:
+        for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            args[n] = _ptr(w.get(n), torch.uint8 if fp8 else dt, n)
+        if fp8:
+            for n in _SCALES:
+                args[n] = _ptr(w.get(n), torch.float32, n)
     args["logit_bias"] = _ptr(w.get("logit_bias"), torch.float32, "logit_bias")
     args["select_bias"] = _ptr(w.get("select_bias"), torch.float32, "select_bias")
     return MoEWeights(**args)

@@ -19,17 +19,45 @@
 // side and applies SiLU(gate) * up in the epilogue, so the gate and up
 // activations never reach memory.
 //
-// Pipeline: 4 wavefronts; per K step (128 bytes of every row) the next
+// Pipeline: 4 wavefronts; per K step (128 bytes of every A row) the next
 // tile's A and B slices are fetched into registers while the current ones
 // are multiplied out of LDS, double-buffered with one barrier per step.
+//
+// FP8 weights (TW = uint8_t: OCP E4M3 codes, one fp32 scale per output
+// channel): a K step then reads 64 bytes of every weight row, and each
+// 8-code chunk is widened to 8 bf16 (exactly) between its register and its
+// LDS slot, so the LDS layout and the MFMAs are those of bf16 weights.  The
+// scale multiplies each output channel's fp32 sum in the epilogue (before
+// SiLU in the gated pass): sum_j x_j (q_nj s_n) = s_n sum_j x_j q_nj.
+#include <type_traits>
+
 #include "mfma.h"
 
 namespace moe {
 namespace {
 
-template <typename T, bool GATED, int BM, int BN, int WM, int WN>
+// 8 E4M3 codes (bytes 0..7 of v, little endian) -> 8 bf16, one 16-byte
+// operand chunk.  Every finite E4M3 value is exact in bf16 (3 of its 7
+// mantissa bits, exponents 2^-9 .. 2^8); the conversion's scale is 1.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 v) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+  return r;
+}
+__device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
+__device__ __forceinline__ u32x4 widen(uint2 v) { return e4m3x8_to_bf16(v); }
+
+template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr bool FP8W = sizeof(TW) == 1;
+  static_assert(!FP8W || sizeof(T) == 2, "FP8 weights with bf16 activations");
+  using WReg = typename std::conditional<FP8W, uint2, u32x4>::type;
   constexpr int ROWB = 128;
+  constexpr int WROWB = FP8W ? 64 : ROWB;   // weight bytes of a row per K step
+  constexpr int WCH = FP8W ? 8 : 16;        // weight bytes per 16-byte LDS chunk
   constexpr int NMAT = GATED ? 2 : 1;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 16, NBK = WTN / 16;
@@ -56,11 +84,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
 
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * sizeof(T);
+  const size_t wrow_bytes = static_cast<size_t>(g.k_dim) * sizeof(TW);
   const size_t mat_elems = static_cast<size_t>(g.n_dim) * g.k_dim;
   const bool routed = e < g.n_experts;
   const int es = routed ? e : e - g.n_experts;
-  const char* w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_elems * sizeof(T);
-  const char* w1 = GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_elems * sizeof(T)
+  const char* w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_elems * sizeof(TW);
+  const char* w1 = GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_elems * sizeof(TW)
                          : nullptr;
 
   // per-thread global sources as byte offsets (rows beyond the tile are
@@ -84,7 +113,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
     const int c = tid + 256 * i;
     const int r = c >> 3, ch = c & 7;
     const int n = min(n0 + r, g.n_dim - 1);
-    b_off[i] = static_cast<size_t>(n) * row_bytes + ch * 16;
+    b_off[i] = static_cast<size_t>(n) * wrow_bytes + ch * WCH;
     b_dst[i] = lds_swz(r, ch);
   }
 
@@ -96,7 +125,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NBK; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[A_LD], rb0[B_LD], rb1[B_LD];
+  u32x4 ra[A_LD];
+  WReg rb0[B_LD], rb1[B_LD];
   int nsteps = static_cast<int>(row_bytes / ROWB);
   if (split) {  // this workgroup's share of the K steps
     const int per = (nsteps + g.ksplit - 1) / g.ksplit;
@@ -105,7 +135,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) a_off[i] += static_cast<size_t>(k0) * ROWB;
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) b_off[i] += static_cast<size_t>(k0) * ROWB;
+    for (int i = 0; i < B_LD; ++i) b_off[i] += static_cast<size_t>(k0) * WROWB;
   }
 
   // prologue: K step 0 into stage 0
@@ -113,15 +143,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i]);
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    rb0[i] = *reinterpret_cast<const u32x4*>(w0 + b_off[i]);
-    if (GATED) rb1[i] = *reinterpret_cast<const u32x4*>(w1 + b_off[i]);
+    rb0[i] = *reinterpret_cast<const WReg*>(w0 + b_off[i]);
+    if (GATED) rb1[i] = *reinterpret_cast<const WReg*>(w1 + b_off[i]);
   }
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(smem + a_dst[i]) = ra[i];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    *reinterpret_cast<u32x4*>(smem + A_BYTES + b_dst[i]) = rb0[i];
-    if (GATED) *reinterpret_cast<u32x4*>(smem + A_BYTES + B_BYTES + b_dst[i]) = rb1[i];
+    *reinterpret_cast<u32x4*>(smem + A_BYTES + b_dst[i]) = widen(rb0[i]);
+    if (GATED) *reinterpret_cast<u32x4*>(smem + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[i]);
   }
   __syncthreads();
 
@@ -129,12 +159,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
     const bool more = s + 1 < nsteps;
     if (more) {
       const size_t koff = static_cast<size_t>(s + 1) * ROWB;
+      const size_t kwoff = static_cast<size_t>(s + 1) * WROWB;
 #pragma unroll
       for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + koff);
 #pragma unroll
       for (int i = 0; i < B_LD; ++i) {
-        rb0[i] = *reinterpret_cast<const u32x4*>(w0 + b_off[i] + koff);
-        if (GATED) rb1[i] = *reinterpret_cast<const u32x4*>(w1 + b_off[i] + koff);
+        rb0[i] = *reinterpret_cast<const WReg*>(w0 + b_off[i] + kwoff);
+        if (GATED) rb1[i] = *reinterpret_cast<const WReg*>(w1 + b_off[i] + kwoff);
       }
     }
     const char* st = smem + (s & 1) * STAGE;
@@ -165,8 +196,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
       for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(nx + a_dst[i]) = ra[i];
 #pragma unroll
       for (int i = 0; i < B_LD; ++i) {
-        *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = rb0[i];
-        if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = rb1[i];
+        *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = widen(rb0[i]);
+        if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[i]);
       }
     }
     __syncthreads();
@@ -174,6 +205,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 
   // epilogue
   T* out = static_cast<T*>(g.out);
+  const float* scale0 = nullptr;  // FP8 weights: per-output-channel scales of this expert
+  const float* scale1 = nullptr;
+  if (FP8W) {
+    scale0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
+    if (GATED) scale1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -187,10 +224,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
         if (col >= g.n_dim) continue;
         float v;
         if (GATED) {
-          const float a = acc[0][i][j][r];
-          v = a / (1.0f + __expf(-a)) * acc[NMAT - 1][i][j][r];
+          float a = acc[0][i][j][r], b = acc[NMAT - 1][i][j][r];
+          if (FP8W) {
+            a *= scale0[col];
+            b *= scale1[col];
+          }
+          v = a / (1.0f + __expf(-a)) * b;
         } else {
           v = acc[0][i][j][r];
+          if (FP8W) v *= scale0[col];
         }
         if (split)
           g.out_part[(static_cast<size_t>(blockIdx.z) * g.a_rows + seg + m0 + row) * g.n_dim + col] = v;
@@ -201,24 +243,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename T, bool GATED, int BM, int BN, int WM, int WN>
+template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
   dim3 grid(g.tiles_cap, (g.n_dim + BN - 1) / BN, (!GATED && g.ksplit > 1) ? g.ksplit : 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, TW, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
-template <typename T, bool GATED>
+template <typename T, typename TW, bool GATED>
 hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
-  if (bm == 32) return launch_t<T, GATED, 32, 64, 1, 4>(g, s);
-  return launch_t<T, GATED, 128, 128, 2, 2>(g, s);
+  if (bm == 32) return launch_t<T, TW, GATED, 32, 64, 1, 4>(g, s);
+  return launch_t<T, TW, GATED, 128, 128, 2, 2>(g, s);
 }
 
 }  // namespace
 
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s) {
-  if (dtype == 1) return gated ? launch_bm<bf16_t, true>(g, bm, s) : launch_bm<bf16_t, false>(g, bm, s);
-  return gated ? launch_bm<float, true>(g, bm, s) : launch_bm<float, false>(g, bm, s);
+  if (dtype == 1 && g.wfp8)
+    return gated ? launch_bm<bf16_t, uint8_t, true>(g, bm, s)
+                 : launch_bm<bf16_t, uint8_t, false>(g, bm, s);
+  if (g.wfp8) return hipErrorInvalidValue;
+  if (dtype == 1)
+    return gated ? launch_bm<bf16_t, bf16_t, true>(g, bm, s) : launch_bm<bf16_t, bf16_t, false>(g, bm, s);
+  return gated ? launch_bm<float, float, true>(g, bm, s) : launch_bm<float, float, false>(g, bm, s);
 }
 
 // Split of the down pass over workgroups for few-row (weight-streaming)
@@ -236,11 +283,11 @@ int down_split(int dtype, const GemmPick& pick, long tiles_est, int n_dim, int k
   return ks < 2 ? 1 : static_cast<int>(ks);
 }
 
-GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_bytes,
+GemmPick pick_gemm(int dtype, bool fp8w, bool /*gated*/, long rows_per_expert, size_t a_bytes,
                    size_t w_bytes, int k_dim) {
   const bool small_offsets = a_bytes < (size_t{1} << 32) && w_bytes < (size_t{1} << 32);
   // the large-tile kernel streams whole pairs of 128-byte row buffers
-  if (dtype != 1 || !small_offsets || k_dim % 128 != 0)
+  if (dtype != 1 || fp8w || !small_offsets || k_dim % 128 != 0)
     return GemmPick{0, rows_per_expert <= 48 ? 32 : 128};
   if (rows_per_expert <= 48) return GemmPick{0, 32};
   if (rows_per_expert >= 512) return GemmPick{1, 256};
@@ -248,7 +295,7 @@ GemmPick pick_gemm(int dtype, bool /*gated*/, long rows_per_expert, size_t a_byt
 }
 
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s) {
-  if (pick.variant == 1 && dtype == 1) return launch_expert_gemm(gated, pick.bm, g, s);
+  if (pick.variant == 1 && dtype == 1 && !g.wfp8) return launch_expert_gemm(gated, pick.bm, g, s);
   return launch_generic_gemm(dtype, gated, pick.bm, g, s);
 }
 

@@ -63,11 +63,13 @@ Plan make_plan(const moe_config& c) {
   Plan p{};
   const long rows_per_expert = static_cast<long>(c.T) * c.top_k / c.n_experts;
   const size_t eb_ = c.dtype == MOE_BF16 ? 2 : 4;
+  const bool fp8w = c.weight_format == MOE_WEIGHTS_FP8_E4M3;
   const size_t rows_all = static_cast<size_t>(c.T) * (c.top_k + c.n_shared);
-  const size_t w_mat = static_cast<size_t>(c.d_model) * c.d_ff * eb_;
-  p.up = pick_gemm(c.dtype, true, rows_per_expert, static_cast<size_t>(c.T) * c.d_model * eb_,
-                   w_mat, c.d_model);
-  p.down = pick_gemm(c.dtype, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat, c.d_ff);
+  const size_t w_mat = static_cast<size_t>(c.d_model) * c.d_ff * (fp8w ? 1 : eb_);
+  p.up = pick_gemm(c.dtype, fp8w, true, rows_per_expert,
+                   static_cast<size_t>(c.T) * c.d_model * eb_, w_mat, c.d_model);
+  p.down = pick_gemm(c.dtype, fp8w, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat,
+                     c.d_ff);
   // the large-tile kernel's work items hold tile indices below kItemMaxTiles
   if (p.up.variant == 1 && tile_capacity(c, p.up.bm) >= kItemMaxTiles) p.up = GemmPick{0, 128};
   if (p.down.variant == 1 && tile_capacity(c, p.down.bm) >= kItemMaxTiles)
@@ -186,6 +188,10 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T, S, capacity >= 0)");
   if (c->top_k > c->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k > n_experts");
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad dtype");
+  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "bad weight_format");
+  if (c->weight_format == MOE_WEIGHTS_FP8_E4M3 && c->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 expert weights need dtype MOE_BF16");
   if (c->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
   if (c->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
   if (c->n_shared > kMaxShared) return fail(MOE_ERR_UNSUPPORTED, "n_shared > 4");
@@ -212,6 +218,13 @@ moe_status check_weights(const moe_config& c, const moe_weights* w, bool experts
       if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "shared expert weight is NULL");
       if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "shared weight not 16-byte aligned");
     }
+  }
+  if (c.weight_format == MOE_WEIGHTS_FP8_E4M3) {
+    if (w->w_gate_scale == nullptr || w->w_up_scale == nullptr || w->w_down_scale == nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "FP8 expert weight scale is NULL");
+    if (c.n_shared > 0 &&
+        (w->ws_gate_scale == nullptr || w->ws_up_scale == nullptr || w->ws_down_scale == nullptr))
+      return fail(MOE_ERR_INVALID_ARG, "FP8 shared expert weight scale is NULL");
   }
   return MOE_OK;
 }
@@ -370,6 +383,11 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   up.n_dim = c.d_ff;
   up.tiles_cap = p.cap_up;
   up.cus = p.cus;
+  up.wfp8 = c.weight_format == MOE_WEIGHTS_FP8_E4M3;
+  up.sc0 = w->w_gate_scale;
+  up.sc1 = w->w_up_scale;
+  up.ssc0 = w->ws_gate_scale;
+  up.ssc1 = w->ws_up_scale;
   up.items = ws.items_up;
   if ((err = launch_gemm(c.dtype, true, p.up, up, s)) != hipSuccess)
     return hip_fail(err, "gate/up GEMM");
@@ -393,6 +411,9 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   dn.out_part = ws.ypart;
   dn.plan = ws.ntiles + 2;
   dn.cus = p.cus;
+  dn.wfp8 = up.wfp8;
+  dn.sc0 = w->w_down_scale;
+  dn.ssc0 = w->ws_down_scale;
   dn.items = ws.items_down;
   if ((err = launch_gemm(c.dtype, false, p.down, dn, s)) != hipSuccess)
     return hip_fail(err, "down GEMM");

@@ -131,6 +131,11 @@ struct GemmArgs {
   const int32_t* plan;       // device split plan of the down pass (kPlan* entries), or null
   const int32_t* items;      // large-tile kernel: work items, (tile << 12) | column tile
   int cus;                   // compute units of the device (grid sizing)
+  bool wfp8;                 // weights are FP8 E4M3 codes with per-output-channel scales
+  const float* sc0;          // routed scales [N, n_dim] (gate or down), FP8 weights only
+  const float* sc1;          // routed up scales, gated GEMM only
+  const float* ssc0;         // shared-expert scales [S, n_dim]
+  const float* ssc1;
 };
 
 // Pairs of K steps (128-byte row buffers) that each of `parts` pieces of an
@@ -167,8 +172,10 @@ struct GemmPick {
 };
 // a_bytes / w_bytes: bytes of the A operand (all its rows) and of one expert's
 // weight matrix; the direct-to-LDS kernel addresses both with 32-bit offsets.
-GemmPick pick_gemm(int dtype, bool gated, long rows_per_expert, size_t a_bytes, size_t w_bytes,
-                   int k_dim);
+// fp8w: FP8 expert weights (register-staged kernel only: it widens them to
+// bf16 on their way into LDS).
+GemmPick pick_gemm(int dtype, bool fp8w, bool gated, long rows_per_expert, size_t a_bytes,
+                   size_t w_bytes, int k_dim);
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);

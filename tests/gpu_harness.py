@@ -44,7 +44,9 @@ def run_layer(shape: MoEShape, inputs: Dict[str, Optional[torch.Tensor]], alpha:
     T = shape.T
     dev = inputs["w_gate"].device
     cfg = moe.make_config(T, shape.d, shape.N, shape.k, shape.F, shape.S, shape.torch_dtype,
-                          capacity=capacity)
+                          capacity=capacity,
+                          weight_format=(moe.MOE_WEIGHTS_FP8_E4M3 if shape.fp8
+                                         else moe.MOE_WEIGHTS_DTYPE))
     ws = moe.alloc_workspace(cfg, dev)
     out = {
         "y": torch.empty((T, shape.d), dtype=shape.torch_dtype, device=dev),
@@ -113,6 +115,10 @@ def full_parity(shape: MoEShape, seed: int = 0, inputs=None, label: str = "",
     gpu = {k_: to_np(v) for k_, v in out.items()}
     host = host_inputs(inputs, ["x", "w_router", "w_gate", "w_up", "w_down", "ws_gate",
                                 "ws_up", "ws_down", "logit_bias", "select_bias"])
+    if shape.fp8:  # the oracle decodes the codes and applies the scales (O9)
+        for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            if host.get(n) is not None:
+                host[n] = oracle.dequantize(host[n], to_np(inputs[n + "_scale"]))
     check_routing(shape, host, gpu)
     shared = ((host["ws_gate"], host["ws_up"], host["ws_down"]) if shape.S else None)
     ref = oracle.moe_forward(host["x"], host["w_router"],
@@ -157,12 +163,19 @@ def sampled_parity(shape: MoEShape, seed: int = 0, n_samples: int = 8):
     y_s = to_np(out["y"].index_select(0, sel))
     lg_s = gpu["logits"][toks]
 
+    def weight(name, e=None):
+        w = inputs[name] if e is None else inputs[name][e]
+        if not shape.fp8:
+            return to_np(w)
+        s = inputs[name + "_scale"] if e is None else inputs[name + "_scale"][e]
+        return oracle.dequantize(to_np(w), to_np(s))
+
     def expert(e):
-        return (to_np(inputs["w_gate"][e]), to_np(inputs["w_up"][e]), to_np(inputs["w_down"][e]))
+        return (weight("w_gate", e), weight("w_up", e), weight("w_down", e))
 
     shared = None
     if shape.S:
-        shared = (to_np(inputs["ws_gate"]), to_np(inputs["ws_up"]), to_np(inputs["ws_down"]))
+        shared = (weight("ws_gate"), weight("ws_up"), weight("ws_down"))
     ref = oracle.moe_forward(x_s, None, expert, shape.k, select_bias=host.get("select_bias"),
                              shared=shared, route_logits=lg_s, n_experts=shape.N)
     err = float(np.max(np.abs(y_s - ref["y"])))

@@ -49,6 +49,10 @@ def test_config_struct_matches_the_header():
     body = re.search(r"typedef struct \{([^}]*)\} moe_config;", hdr).group(1)
     fields = re.findall(r"int32_t\s+(\w+);", body)
     assert fields == [f for f, _ in moe.MoEConfig._fields_]
+    body = re.search(r"typedef struct \{(.*?)\} moe_weights;", hdr, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    wfields = re.findall(r"const (?:void|float)\*\s+(\w+);", body)
+    assert wfields == [f for f, _ in moe.MoEWeights._fields_]
     cap = moe.make_config(64, 128, 4, 2, 256, capacity=7)
     assert cap.capacity == 7 and moe.make_config(64, 128, 4, 2, 256).capacity == 0
 
@@ -63,8 +67,13 @@ def test_workspace_size_validation():
                 moe.make_config(64, 128, 600, 2, 256), moe.make_config(64, 128, 40, 17, 256),
                 moe.make_config(-1, 128, 4, 2, 256), moe.make_config(64, 128, 4, 2, 96),
                 moe.make_config(64, 128, 4, 2, 256, n_shared=5),
-                moe.make_config(64, 128, 4, 2, 256, capacity=-1)]:
+                moe.make_config(64, 128, 4, 2, 256, capacity=-1),
+                moe.make_config(64, 128, 4, 2, 256, weight_format=2),
+                moe.make_config(64, 128, 4, 2, 256, 0, "f32",
+                                weight_format=moe.MOE_WEIGHTS_FP8_E4M3)]:
         assert moe.moe_workspace_size(bad) == 0
+    fp8 = moe.make_config(64, 128, 4, 2, 256, weight_format=moe.MOE_WEIGHTS_FP8_E4M3)
+    assert moe.moe_workspace_size(fp8) > 0
 
 
 def _call_forward(cfg, weights=None, x=1 << 20, y=1 << 20, ws=None, ws_bytes=0):
@@ -78,7 +87,8 @@ FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on the
 
 
 def _w(**over):
-    w = moe.MoEWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, None)
+    w = moe.MoEWeights(FAKE, FAKE, FAKE, FAKE, None, None, None, None, None,
+                       None, None, None, None, None, None)
     for k_, v in over.items():
         setattr(w, k_, v)
     return w
@@ -97,6 +107,9 @@ def _w(**over):
     ("null_expert", moe.MOE_ERR_INVALID_ARG),
     ("shared_missing", moe.MOE_ERR_INVALID_ARG),
     ("misaligned_weight", moe.MOE_ERR_INVALID_ARG),
+    ("fp8_scale_missing", moe.MOE_ERR_INVALID_ARG),
+    ("fp8_with_f32", moe.MOE_ERR_UNSUPPORTED),
+    ("bad_weight_format", moe.MOE_ERR_INVALID_ARG),
     ("null_x", moe.MOE_ERR_INVALID_ARG),
     ("no_workspace", moe.MOE_ERR_WORKSPACE),
     ("small_workspace", moe.MOE_ERR_WORKSPACE),
@@ -131,6 +144,14 @@ def test_forward_rejects_before_launch(case, expect):
         cfg = moe.make_config(64, 128, 4, 2, 256, n_shared=1)
     elif case == "misaligned_weight":
         w = _w(w_up=FAKE + 2)
+    elif case == "fp8_scale_missing":
+        cfg.weight_format = moe.MOE_WEIGHTS_FP8_E4M3
+        w = _w(w_gate_scale=FAKE, w_up_scale=FAKE)  # down scale missing
+    elif case == "fp8_with_f32":
+        cfg = moe.make_config(64, 128, 4, 2, 256, 0, "f32",
+                              weight_format=moe.MOE_WEIGHTS_FP8_E4M3)
+    elif case == "bad_weight_format":
+        cfg.weight_format = 5
     elif case == "null_x":
         kw = {"x": None}
     elif case == "no_workspace":

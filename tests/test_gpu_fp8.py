@@ -1,0 +1,80 @@
+"""GPU parity of FP8 (OCP E4M3) expert weights with per-output-channel scales
+against the oracle's decode (O9).  Needs an MI355X."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_router_amd as moe
+from gpu_harness import full_parity, run_layer, sampled_parity, say, to_np
+from workloads import CONFIGS, MoEShape, make_inputs, reduced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()  # the HIP library must be built; no fallback
+
+
+def test_every_finite_code_decodes_exactly():
+    """One expert, x = identity rows, gate codes all 1.0, down = identity on
+    the first F channels: y[t, n] = SiLU(1) * decode(up[n, t]), so every
+    finite code reaches the output through its own element."""
+    T = d = 256
+    F = 64
+    shp = MoEShape("fp8_codes", T=T, d=d, N=1, k=1, F=F, fp8=True)
+    inputs = make_inputs(shp, seed=3, device="cuda")
+    one = 0x38  # E4M3 1.0
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    reps = math.ceil(F * d / len(codes))
+    up = torch.tensor((codes * reps)[:F * d], dtype=torch.uint8).reshape(1, F, d)
+    down = torch.zeros((1, d, F), dtype=torch.uint8)
+    down[0, torch.arange(F), torch.arange(F)] = one
+    inputs.update({
+        "x": torch.eye(T, d, dtype=torch.bfloat16, device="cuda"),
+        "w_gate": torch.full((1, F, d), one, dtype=torch.uint8, device="cuda"),
+        "w_up": up.cuda(), "w_down": down.cuda(),
+        "w_gate_scale": torch.ones((1, F), device="cuda"),
+        "w_up_scale": torch.ones((1, F), device="cuda"),
+        "w_down_scale": torch.ones((1, d), device="cuda"),
+    })
+    out = run_layer(shp, inputs)
+    y = to_np(out["y"]).astype(np.float64)
+    ref = oracle.silu(np.ones(1))[0] * oracle.e4m3_decode(up[0].numpy()).T  # [T, F]
+    err = np.abs(y[:, :F] - ref)
+    bad = err > 2.0 ** -7 * np.abs(ref)
+    say(f"[fp8] codes: max rel err {float(np.max(err / np.maximum(np.abs(ref), 1e-30))):.3e}")
+    assert not bad.any(), f"{int(bad.sum())} codes decoded wrongly, e.g. " \
+        f"{[hex(int(up[0, n, t])) for t, n in zip(*np.nonzero(bad))][:8]}"
+    assert np.all(y[:, F:] == 0.0)
+
+
+FP8_CASES = [
+    # few rows per expert: 32-row tiles, down pass split over K (39 steps)
+    ("decode_split_k", reduced(CONFIGS["mixtral_decode_fp8"], T=24, d=256, F=2496)),
+    # prefill rows: 128-row register-staged tiles, ragged T and F
+    ("prefill", reduced(CONFIGS["mixtral_decode_fp8"], T=300, d=512, F=1088,
+                        name="fp8_prefill")),
+    # shared expert and selection bias
+    ("shared_and_bias", MoEShape("fp8_ds", T=200, d=512, N=64, k=8, F=256, S=1,
+                                 select_bias=True, fp8=True)),
+]
+
+
+@pytest.mark.parametrize("label,shape", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_parity(label, shape):
+    full_parity(shape, seed=4, label=f"fp8_{label}")
+
+
+def test_fp8_capacity():
+    shp = MoEShape("fp8_cap", T=300, d=256, N=8, k=2, F=512, fp8=True)
+    _, out, ref = full_parity(shp, seed=5, label="fp8_capacity_60", capacity=60)
+    assert int(np.sum(~ref["keep"])) > 0
+
+
+def test_fp8_full_size_sampled():
+    sampled_parity(CONFIGS["mixtral_decode_fp8"], seed=0)
