@@ -19,9 +19,10 @@
 // side and applies SiLU(gate) * up in the epilogue, so the gate and up
 // activations never reach memory.
 //
-// Pipeline: 4 wavefronts; per K step (128 bytes of every A row) the next
-// tile's A and B slices are fetched into registers while the current ones
-// are multiplied out of LDS, double-buffered with one barrier per step.
+// Pipeline: 4 wavefronts; per K step (128 bytes of every A row) the A and B
+// slices of a later step are fetched into registers while the current ones
+// are multiplied out of LDS (two LDS stages, one barrier per step that does
+// not wait for the loads in flight).
 //
 // FP8 weights (TW = uint8_t: OCP E4M3 codes, one fp32 scale per output
 // channel): a K step then reads 64 bytes of every weight row, and each
@@ -31,6 +32,7 @@
 // SiLU in the gated pass): sum_j x_j (q_nj s_n) = s_n sum_j x_j q_nj.
 #include <type_traits>
 
+#include "lds_ring.h"
 #include "mfma.h"
 
 namespace moe {
@@ -53,6 +55,7 @@ __device__ __forceinline__ u32x4 widen(uint2 v) { return e4m3x8_to_bf16(v); }
 template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   constexpr bool FP8W = sizeof(TW) == 1;
+  constexpr int PD = GATED ? 2 : 1;  // K steps of loads in flight
   static_assert(!FP8W || sizeof(T) == 2, "FP8 weights with bf16 activations");
   using WReg = typename std::conditional<FP8W, uint2, u32x4>::type;
   constexpr int ROWB = 128;
@@ -125,8 +128,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NBK; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[A_LD];
-  WReg rb0[B_LD], rb1[B_LD];
   int nsteps = static_cast<int>(row_bytes / ROWB);
   if (split) {  // this workgroup's share of the K steps
     const int per = (nsteps + g.ksplit - 1) / g.ksplit;
@@ -138,37 +139,42 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < B_LD; ++i) b_off[i] += static_cast<size_t>(k0) * WROWB;
   }
 
-  // prologue: K step 0 into stage 0
+  // PD = 2: two register slots of K-step loads; step s + 2 is loaded while
+  // step s is multiplied out of LDS and step s + 1 waits in the other slot,
+  // so two steps of loads are in flight (the gated pass, which streams two
+  // weight matrices).  PD = 1: one slot, step s + 1 loaded during step s
+  // (the plain pass: its decode split gives short K loops, where a deeper
+  // prologue measured slower).  Steps past the end re-read the last one.
+  u32x4 ra[PD][A_LD];
+  WReg rb0[PD][B_LD], rb1[PD][B_LD];
+  auto load_step = [&](int slot, int s) {
+    const int sc = min(s, nsteps - 1);
+    const size_t koff = static_cast<size_t>(sc) * ROWB;
+    const size_t kwoff = static_cast<size_t>(sc) * WROWB;
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i]);
+    for (int i = 0; i < A_LD; ++i)
+      ra[slot][i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + koff);
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    rb0[i] = *reinterpret_cast<const WReg*>(w0 + b_off[i]);
-    if (GATED) rb1[i] = *reinterpret_cast<const WReg*>(w1 + b_off[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(smem + a_dst[i]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    *reinterpret_cast<u32x4*>(smem + A_BYTES + b_dst[i]) = widen(rb0[i]);
-    if (GATED) *reinterpret_cast<u32x4*>(smem + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[i]);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      const size_t koff = static_cast<size_t>(s + 1) * ROWB;
-      const size_t kwoff = static_cast<size_t>(s + 1) * WROWB;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + koff);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        rb0[i] = *reinterpret_cast<const WReg*>(w0 + b_off[i] + kwoff);
-        if (GATED) rb1[i] = *reinterpret_cast<const WReg*>(w1 + b_off[i] + kwoff);
-      }
+    for (int i = 0; i < B_LD; ++i) {
+      rb0[slot][i] = *reinterpret_cast<const WReg*>(w0 + b_off[i] + kwoff);
+      if (GATED) rb1[slot][i] = *reinterpret_cast<const WReg*>(w1 + b_off[i] + kwoff);
     }
-    const char* st = smem + (s & 1) * STAGE;
+    // issue them here, ahead of this step's MFMAs
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto store_step = [&](int slot, int stage) {
+    char* nx = smem + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(nx + a_dst[i]) = ra[slot][i];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = widen(rb0[slot][i]);
+      if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[slot][i]);
+    }
+  };
+  auto compute = [&](int stage) {
+    const char* st = smem + stage * STAGE;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const int ch = kc * 4 + (lane >> 4);
@@ -190,17 +196,36 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
         }
       }
     }
-    if (more) {
-      char* nx = smem + ((s + 1) & 1) * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(nx + a_dst[i]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = widen(rb0[i]);
-        if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[i]);
-      }
+  };
+
+  if (nsteps > 0 && PD == 2) {
+    load_step(0, 0);
+    load_step(1, 1);
+    store_step(0, 0);
+    lds_barrier();
+    // steps s (stage 0, slot 0) and s + 1 (stage 1, slot 1)
+    for (int s = 0; s + 1 < nsteps; s += 2) {
+      load_step(0, s + 2);
+      compute(0);
+      store_step(1, 1);
+      lds_barrier();
+      load_step(1, s + 3);
+      compute(1);
+      store_step(0, 0);
+      lds_barrier();
     }
-    __syncthreads();
+    if (nsteps & 1) compute(0);  // the last (even-numbered) step sits in stage 0
+  } else if (nsteps > 0) {
+    load_step(0, 0);
+    store_step(0, 0);
+    lds_barrier();
+    for (int s = 0; s < nsteps; ++s) {
+      const bool more = s + 1 < nsteps;
+      if (more) load_step(0, s + 1);
+      compute(s & 1);
+      if (more) store_step(0, (s + 1) & 1);
+      lds_barrier();
+    }
   }
 
   // epilogue

@@ -31,6 +31,15 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier once this wavefront's LDS accesses have completed; its
+// global loads into registers keep flying (__syncthreads() would wait for
+// them too).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 constexpr int kRowBytes = 64;  // bytes of every staged row per K step (32 bf16)
 
 // Byte offset of 16-byte chunk c (0..3) of staged row r: 64-byte rows, chunk
