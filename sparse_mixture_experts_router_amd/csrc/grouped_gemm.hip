@@ -49,25 +49,22 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 v) {
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
   return r;
 }
-__device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
-__device__ __forceinline__ u32x4 widen(uint2 v) { return e4m3x8_to_bf16(v); }
 
 template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   constexpr bool FP8W = sizeof(TW) == 1;
   constexpr int PD = GATED ? 2 : 1;  // K steps of loads in flight
   static_assert(!FP8W || sizeof(T) == 2, "FP8 weights with bf16 activations");
-  using WReg = typename std::conditional<FP8W, uint2, u32x4>::type;
   constexpr int ROWB = 128;
   constexpr int WROWB = FP8W ? 64 : ROWB;   // weight bytes of a row per K step
-  constexpr int WCH = FP8W ? 8 : 16;        // weight bytes per 16-byte LDS chunk
+  constexpr int CPL = FP8W ? 2 : 1;         // 16-byte LDS chunks filled per 16-byte load
   constexpr int NMAT = GATED ? 2 : 1;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 16, NBK = WTN / 16;
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   constexpr int STAGE = A_BYTES + NMAT * B_BYTES;
   constexpr int A_LD = BM * 8 / 256;  // 16-byte chunks per thread per K step
-  constexpr int B_LD = BN * 8 / 256;
+  constexpr int B_LD = BN * 8 / 256 / CPL;  // 16-byte weight loads per thread per K step
   static_assert(WM * WN == 4, "4 wavefronts");
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
   static_assert(MB >= 1 && NBK >= 1, "wave tile below one MFMA block");
@@ -110,14 +107,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
     a_dst[i] = lds_swz(r, ch);
   }
   size_t b_off[B_LD];
-  int b_dst[B_LD];
+  int b_dst[B_LD];  // first of the CPL consecutive chunks a load fills
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int c = tid + 256 * i;
-    const int r = c >> 3, ch = c & 7;
+    const int r = c / (8 / CPL), ch = (c % (8 / CPL)) * CPL;
     const int n = min(n0 + r, g.n_dim - 1);
-    b_off[i] = static_cast<size_t>(n) * wrow_bytes + ch * WCH;
-    b_dst[i] = lds_swz(r, ch);
+    b_off[i] = static_cast<size_t>(n) * wrow_bytes + (ch / CPL) * 16;
+    b_dst[i] = r * 128 + ch;  // row and chunk, swizzled at the store
   }
 
   f32x4 acc[NMAT][MB][NBK];
@@ -146,7 +143,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   // (the plain pass: its decode split gives short K loops, where a deeper
   // prologue measured slower).  Steps past the end re-read the last one.
   u32x4 ra[PD][A_LD];
-  WReg rb0[PD][B_LD], rb1[PD][B_LD];
+  u32x4 rb0[PD][B_LD], rb1[PD][B_LD];
   auto load_step = [&](int slot, int s) {
     const int sc = min(s, nsteps - 1);
     const size_t koff = static_cast<size_t>(sc) * ROWB;
@@ -156,8 +153,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
       ra[slot][i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + koff);
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      rb0[slot][i] = *reinterpret_cast<const WReg*>(w0 + b_off[i] + kwoff);
-      if (GATED) rb1[slot][i] = *reinterpret_cast<const WReg*>(w1 + b_off[i] + kwoff);
+      rb0[slot][i] = *reinterpret_cast<const u32x4*>(w0 + b_off[i] + kwoff);
+      if (GATED) rb1[slot][i] = *reinterpret_cast<const u32x4*>(w1 + b_off[i] + kwoff);
     }
     // issue them here, ahead of this step's MFMAs
     asm volatile("" ::: "memory");
@@ -169,8 +166,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < A_LD; ++i) *reinterpret_cast<u32x4*>(nx + a_dst[i]) = ra[slot][i];
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      *reinterpret_cast<u32x4*>(nx + A_BYTES + b_dst[i]) = widen(rb0[slot][i]);
-      if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + b_dst[i]) = widen(rb1[slot][i]);
+      const int r = b_dst[i] >> 7, ch = b_dst[i] & 127;
+#pragma unroll
+      for (int h = 0; h < CPL; ++h) {
+        const int dst = lds_swz(r, ch + h);
+        if (FP8W) {
+          *reinterpret_cast<u32x4*>(nx + A_BYTES + dst) =
+              e4m3x8_to_bf16(make_uint2(rb0[slot][i][2 * h], rb0[slot][i][2 * h + 1]));
+          if (GATED)
+            *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + dst) =
+                e4m3x8_to_bf16(make_uint2(rb1[slot][i][2 * h], rb1[slot][i][2 * h + 1]));
+        } else {
+          *reinterpret_cast<u32x4*>(nx + A_BYTES + dst) = rb0[slot][i];
+          if (GATED) *reinterpret_cast<u32x4*>(nx + A_BYTES + B_BYTES + dst) = rb1[slot][i];
+        }
+      }
     }
   };
   auto compute = [&](int stage) {
