@@ -128,7 +128,7 @@ Plan make_plan(const moe_config& c) {
     const long routed = (tk + bm - 1) / bm > used ? (tk + bm - 1) / bm : used;
     long est = routed + static_cast<long>(S) * ((static_cast<long>(T) + bm - 1) / bm);
     if (est > p.cap_down) est = p.cap_down;
-    p.dsplit = down_split(c.dtype, p.down, est, c.d_model, c.d_ff, p.cus);
+    p.dsplit = down_split(c.dtype, fp8w, p.down, est, c.d_model, c.d_ff, p.cus);
   }
   sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
   p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};

@@ -191,7 +191,8 @@ hipError_t launch_combine(int dtype, const void* yperm, const float* ypart,
                           const int32_t* plan, const int32_t* inv_row, const float* topk_gate,
                           const int32_t* offsets, int N, int T, int d, int k, int S, void* y,
                           hipStream_t s);
-int down_split(int dtype, const GemmPick& pick, long tiles_est, int n_dim, int k_dim, int cus);
+int down_split(int dtype, bool fp8w, const GemmPick& pick, long tiles_est, int n_dim, int k_dim,
+               int cus);
 
 hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
                           const float* prob_sum, float alpha, float* f_out,
