@@ -41,21 +41,27 @@ namespace {
 
 template <int N> struct CInt { static constexpr int value = N; };
 
-template <bool GATED, int BM, int BNE, int NBUF>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
-  constexpr int ROWS = BM + BNE;               // rows staged per buffer
-  constexpr int BUF = ROWS * kLineBytes;       // bytes per buffer
+  // FP8W: weights are E4M3 codes; a buffer holds 64 bytes of each weight row
+  // (the same 64 K elements), read as 8-byte fragments and widened to bf16
+  // right before their MFMAs; per-column scales are applied in the epilogue.
+  constexpr int BROW = FP8W ? 64 : kLineBytes;  // staged bytes of a weight row per buffer
+  constexpr int BRPB = 1024 / BROW;             // weight rows per 1 KB load block
+  constexpr int BUF = BM * kLineBytes + BNE * BROW;  // bytes per buffer
   constexpr int WTM = BM / 2, WTN = BNE / 2;   // wavefront block
   constexpr int MB = WTM / 16, NB = WTN / 16;  // 16 x 16 MFMA blocks
   constexpr int NOUT = GATED ? NB / 2 : NB;    // output column blocks per wavefront
   constexpr int COLS = GATED ? BNE / 2 : BNE;  // output columns per tile
-  constexpr int A_BPW = BM / 32, B_BPW = BNE / 32;  // 1 KB load blocks (8 rows) per wavefront
+  constexpr int A_BPW = BM / 32;               // 1 KB A load blocks (8 rows) per wavefront
+  constexpr int B_BPW = BNE / 4 / BRPB;        // 1 KB weight load blocks per wavefront
   constexpr int LPB = A_BPW + B_BPW;           // loads per lane per buffer
   constexpr int LH1 = LPB / 2, LH2 = LPB - LH1;  // issued after the barrier / in the next step
   constexpr int NF = MB + NB;                  // fragments per K step
   static_assert(BM % 64 == 0 && BNE % 64 == 0, "tile shape");
-  static_assert(A_BPW % 2 == 0 && B_BPW % 2 == 0, "a load's block parity is its index parity");
-  static_assert(!GATED || (COLS % (B_BPW * 8) == 0 && NB % 2 == 0),
+  static_assert(A_BPW % 2 == 0 && (FP8W || B_BPW % 2 == 0),
+                "a load's block parity is its index parity");
+  static_assert(!GATED || (COLS % (B_BPW * BRPB) == 0 && NB % 2 == 0),
                 "a wavefront's B blocks are all gate or all up rows");
   static_assert(NBUF >= 2 && (NBUF - 1) * LPB + LH1 < 64, "vmcnt range");
 
@@ -79,7 +85,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_readfirstlane(min(max((mvalid - wm * WTM + 15) / 16, 0), MB));
 
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
-  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
+  const size_t wrow_bytes = static_cast<size_t>(g.k_dim) * (FP8W ? 1 : 2);
+  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * wrow_bytes;
   const bool routed = e < g.n_experts;
   const int es = routed ? e : e - g.n_experts;
   const char* w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
@@ -90,7 +97,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // Staged rows: A rows 0 .. BM-1, then B rows (gated: COLS gate rows, then
   // COLS up rows).  Wavefront w loads A blocks w*A_BPW .. and B blocks
   // w*B_BPW ..; lane l of a block fetches row l / 8 of it, the chunk that
-  // line_lane_chunk assigns.  Sources are a wave-uniform base plus a 32-bit
+  // line_lane_chunk assigns (FP8 weights: row l / 4 of a 16-row block, 16-byte
+  // chunk (l % 4) ^ (l / 16), matching the fragment reads below).  Sources are a wave-uniform base plus a 32-bit
   // per-lane byte offset (the host keeps every operand below 4 GiB per base);
   // rows beyond the tile are clamped to a valid row and discarded at the end.
   const char* const a_base = reinterpret_cast<const char*>(g.a);
@@ -103,16 +111,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     a_off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) +
                line_lane_chunk(lane, j) * 16;
   }
-  const int jb0 = wave * B_BPW * 8;
+  const int jb0 = wave * B_BPW * BRPB;
   const bool up_rows = GATED && jb0 >= COLS;
-  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
+  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * wrow_bytes;
   uint32_t b_off[B_BPW];
 #pragma unroll
   for (int j = 0; j < B_BPW; ++j) {
-    const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? COLS : 0);
+    const int jb = jb0 + j * BRPB + lane / (64 / BRPB) - (up_rows ? COLS : 0);
     const int n = min(n0 + jb, g.n_dim - 1);
-    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
-               line_lane_chunk(lane, j) * 16;
+    const int chunk = FP8W ? ((lane & 3) ^ (lane >> 4)) : line_lane_chunk(lane, j);
+    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) + chunk * 16;
   }
   const int a_dst = wave * A_BPW * 1024;
   const int b_dst = BM * kLineBytes + wave * B_BPW * 1024;
@@ -126,16 +134,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < A_BPW; ++j) a_off[j] += static_cast<uint32_t>(p0) * kLineBytes;
 #pragma unroll
-    for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(p0) * kLineBytes;
+    for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(p0) * BROW;
   }
   // Load l (A blocks first, then B blocks) of pair `pair` into buffer `buf`.
   // Pairs past the end re-read the last one (valid addresses) into a buffer
   // nobody reads again, so the loop needs no branches.
   auto issue_one = [&](int pair, int l, int buf) {
-    const uint32_t koff = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
+    const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1));
     char* const st = smem + buf * BUF;
-    if (l < A_BPW) load_lds16(a_base + (a_off[l] + koff), st + a_dst + l * 1024);
-    else load_lds16(b_base + (b_off[l - A_BPW] + koff), st + b_dst + (l - A_BPW) * 1024);
+    if (l < A_BPW) load_lds16(a_base + (a_off[l] + pc * kLineBytes), st + a_dst + l * 1024);
+    else load_lds16(b_base + (b_off[l - A_BPW] + pc * BROW), st + b_dst + (l - A_BPW) * 1024);
   };
 
   // LDS byte offset (inside a buffer) of fragment f for K step t (0, 1) of
@@ -144,8 +152,14 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // 16, so the swizzle key is the lane's own.
   const int frow = lane & 15;
   const int fkey = swz128_key(frow);
-  const int flane0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
-  const int flane1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  // K step t reads 16-byte chunk 4t + lane / 16 of each 128-byte A row; with
+  // FP8 weights chunk 2 (lane / 16) + t instead (the same elements of A and
+  // B always meet in one MFMA, in any fixed order), so that one 16-byte read
+  // of a 64-byte weight row gives a lane its codes for both steps.
+  const int ca0 = FP8W ? 2 * (lane >> 4) : (lane >> 4);
+  const int ca1 = FP8W ? 2 * (lane >> 4) + 1 : 4 + (lane >> 4);
+  const int flane0 = frow * kLineBytes + ((ca0 ^ fkey) << 4);
+  const int flane1 = frow * kLineBytes + ((ca1 ^ fkey) << 4);
   auto frag_off = [&](int f, int t) {
     int r;
     if (f < MB) {
@@ -157,6 +171,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     }
     return r * kLineBytes + (t ? flane1 : flane0);
   };
+  // FP8 weights: weight fragment j, 16 bytes of a 64-byte row (codes of K
+  // chunks 2 (lane / 16) and 2 (lane / 16) + 1: steps 0 and 1 of the buffer);
+  // the 16-byte chunks of a row are XOR-swizzled by (row mod 16) / 4, so the
+  // 16 lanes of a fragment group hit 16 distinct bank groups.
+  const int f8lane = frow * 64 + 16 * ((lane >> 4) ^ (frow >> 2));
+  auto frag8_off = [&](int j) {
+    const int rb = GATED ? (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16
+                         : wn * WTN + j * 16;
+    return BM * kLineBytes + rb * 64 + f8lane;
+  };
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -165,6 +189,13 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 fr[2][NF];  // fragments of the two K steps of a buffer
+  u32x4 fb[2][NB];  // FP8 weights: their raw weight fragments (both steps' codes)
+  // fragment f of K step t from buffer base `b` into fragment set SET
+  auto read_frag = [&](auto set_, int f, const char* b, int t) {
+    constexpr int SET = decltype(set_)::value;
+    if (FP8W && f >= MB) fb[SET][f - MB] = *reinterpret_cast<const u32x4*>(b + frag8_off(f - MB));
+    else fr[SET][f] = *reinterpret_cast<const u32x4*>(b + frag_off(f, t));
+  };
 
   // prologue: pairs 0 .. NBUF-2 and the first half of pair NBUF-1 in
   // flight; pair 0 landed; the first step's fragments in fr[0]
@@ -177,7 +208,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   wait_vmem<(NBUF - 2) * LPB + LH1>();
   stage_barrier();
 #pragma unroll
-  for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const u32x4*>(smem + frag_off(f, 0));
+  for (int f = 0; f < NF; ++f) read_frag(CInt<0>{}, f, smem, 0);
 
   // Pair p (buffer cur = p mod NBUF) = K steps 2p (fragments in fr[0]) and
   // 2p + 1.
@@ -206,11 +237,23 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     constexpr int QS = QH > 0 ? QH : 1;
     constexpr int LPQ = slots_per(QS, NL);  // slots per load
     constexpr int RPQ = slots_per(QS, NR);  // slots per read
+    u32x4 bw = {0u, 0u, 0u, 0u};  // FP8 weights: fragment j widened to bf16
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       if (q < QH) {
         const int i = q % (LIVE > 0 ? LIVE : 1), j = J0 + q / (LIVE > 0 ? LIVE : 1);
-        mfma_bf16_agpr(acc[i][j], fr[S][i], fr[S][MB + j]);
+        if (FP8W) {
+          if (i == 0) {
+            // this step's 8 codes: bytes 0-7 (step 0) or 8-15 (step 1); the
+            // first MFMA reading them waits out the VALU write
+            bw = e4m3x8_to_bf16(make_uint2(fb[S][j][2 * S], fb[S][j][2 * S + 1]));
+            mfma_bf16_agpr_after_valu(acc[i][j], fr[S][i], bw);
+          } else {
+            mfma_bf16_agpr(acc[i][j], fr[S][i], bw);
+          }
+        } else {
+          mfma_bf16_agpr(acc[i][j], fr[S][i], fr[S][MB + j]);
+        }
       }
       if (q % RPQ == RPQ - 1 && q / RPQ < NR) read(q / RPQ);
       if (q % LPQ == 0 && q / LPQ < NL) load(q / LPQ);
@@ -231,14 +274,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
       const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
       const char* const bcur = smem + cur * BUF;
       const char* const bnxt = smem + nxt * BUF;
-      auto read1 = [&](int r) {
-        const int f = r < LIVE ? r : MB + r - LIVE;
-        fr[1][f] = *reinterpret_cast<const u32x4*>(bcur + frag_off(f, 1));
-      };
-      auto read0 = [&](int r) {
-        const int f = r < LIVE ? r : MB + r - LIVE;
-        fr[0][f] = *reinterpret_cast<const u32x4*>(bnxt + frag_off(f, 0));
-      };
+      auto read1 = [&](int r) { read_frag(CInt<1>{}, r < LIVE ? r : MB + r - LIVE, bcur, 1); };
+      auto read0 = [&](int r) { read_frag(CInt<0>{}, r < LIVE ? r : MB + r - LIVE, bnxt, 0); };
       auto load2 = [&](int l) { issue_one(p + NBUF - 1, LH1 + l, prv); };
       auto load1 = [&](int l) { issue_one(p + NBUF, l, cur); };
       half_step(CInt<0>{}, CInt<0>{}, live_, CInt<LH2>{}, CInt<0>{}, load2, none);
@@ -263,22 +300,29 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   static_assert(4 * WTM * (128 + 16) <= NBUF * BUF, "staging space");
   char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
+  const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
+  const float* sc1 = nullptr;
+  if (FP8W) {
+    sc0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
+    if (GATED) sc1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
+  }
   if (part < 0) {
-    store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
-                                           seg + m0 + wm * WTM, mvalid - wm * WTM, col0, g.n_dim);
+    store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
+                                                 seg + m0 + wm * WTM, mvalid - wm * WTM, col0,
+                                                 g.n_dim, sc0, sc1);
   } else if (!GATED) {  // fp32 partial rows of a split tail tile
     const long prow = static_cast<long>(part) * g.plan[kPlanStride] + seg + m0 -
                       g.plan[kPlanRowSplit] + wm * WTM;
-    store_block<GATED, false, MB, NB, WTM>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
-                                           mvalid - wm * WTM, col0, g.n_dim);
+    store_block<GATED, false, MB, NB, WTM, FP8W>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
+                                                 mvalid - wm * WTM, col0, g.n_dim, sc0, sc1);
   }
 }
 
-template <bool GATED, int BM, int BNE, int NBUF>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W = false>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long blocks = expert_grid(g, GATED, COLS);
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF, FP8W>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -294,6 +338,17 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
   if (g.k_dim % 128 != 0) return hipErrorInvalidValue;  // whole pairs of 128-byte buffers
   // buffers of 64 KB (256-row tiles: 2 fit in the LDS) or 48 KB (128-row
   // tiles: 3 fit, keeping two pairs of K steps in flight)
+  if (g.wfp8) {
+    // FP8 weights: 48 KB (256-row tiles) or 32 KB (128-row tiles) per buffer,
+    // so one more buffer of loads fits in flight than with bf16 weights
+    if (bm == 256) {
+      if (gated) return launch_v<true, 256, 256, 3, true>(g, s);
+      return launch_v<false, 256, 256, 3, true>(g, s);
+    }
+    if (bm != 128) return hipErrorInvalidValue;
+    if (gated) return launch_v<true, 128, 256, 4, true>(g, s);
+    return launch_v<false, 128, 256, 4, true>(g, s);
+  }
   if (bm == 256) {
     if (gated) return launch_v<true, 256, 256, 2>(g, s);
     return launch_v<false, 256, 256, 2>(g, s);

@@ -74,10 +74,15 @@ inline long expert_grid(const GemmArgs& g, bool gated, int cols) {
 //          accumulators have a single consumer.
 // Row i of the block goes to out[(row0 + i) * ld + col0 + ...]; rows >=
 // rows_valid and columns >= cols_valid are not written.
-template <bool GATED, bool SBF16, int MB, int NB, int WTM>
+// SCALED (FP8 weights): each accumulator is first multiplied by its output
+// column's scale, sc0 for the gate (or plain) columns, sc1 for the up
+// columns; both indexed by the output column, col0 + ... .
+template <bool GATED, bool SBF16, int MB, int NB, int WTM, bool SCALED = false>
 __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
                                             void* out, bool out_f32, size_t ld, long row0,
-                                            int rows_valid, int col0, int cols_valid) {
+                                            int rows_valid, int col0, int cols_valid,
+                                            const float* sc0 = nullptr,
+                                            const float* sc1 = nullptr) {
   constexpr int NOUT = GATED ? NB / 2 : NB;
   constexpr int ES = SBF16 ? 2 : 4;      // staged element bytes
   constexpr int PB = 128 / (16 * ES);    // 16-column blocks per pass
@@ -85,6 +90,13 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
   static_assert(NOUT % PB == 0, "whole passes");
 #pragma unroll
   for (int pass = 0; pass < NOUT / PB; ++pass) {
+    float s0v[PB], s1v[PB];  // this pass's column scales (SCALED)
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      const int sc = min(col0 + (pass * PB + jj) * 16 + (lane & 15), cols_valid - 1);
+      s0v[jj] = SCALED ? sc0[sc] : 1.0f;
+      s1v[jj] = SCALED && GATED ? sc1[sc] : 1.0f;
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -95,10 +107,15 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
           const int j = pass * PB + jj;
           float v;
           if (GATED) {
-            const float a = acc[i][j][r];
-            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * acc[i][j + NOUT][r];
+            float a = acc[i][j][r], b = acc[i][j + NOUT][r];
+            if (SCALED) {
+              a *= s0v[jj];
+              b *= s1v[jj];
+            }
+            v = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * b;
           } else {
             v = acc[i][j][r];
+            if (SCALED) v *= s0v[jj];
           }
           if (SBF16)
             *reinterpret_cast<bf16_t*>(stg + row * SROW + (jj * 16 + (lane & 15)) * ES) =

@@ -38,17 +38,6 @@
 namespace moe {
 namespace {
 
-// 8 E4M3 codes (bytes 0..7 of v, little endian) -> 8 bf16, one 16-byte
-// operand chunk.  Every finite E4M3 value is exact in bf16 (3 of its 7
-// mantissa bits, exponents 2^-9 .. 2^8); the conversion's scale is 1.
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 v) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
-  return r;
-}
 
 template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
@@ -322,11 +311,11 @@ int down_split(int dtype, bool fp8w, const GemmPick& pick, long tiles_est, int n
   return ks < 2 ? 1 : static_cast<int>(ks);
 }
 
-GemmPick pick_gemm(int dtype, bool fp8w, bool /*gated*/, long rows_per_expert, size_t a_bytes,
+GemmPick pick_gemm(int dtype, bool /*fp8w*/, bool /*gated*/, long rows_per_expert, size_t a_bytes,
                    size_t w_bytes, int k_dim) {
   const bool small_offsets = a_bytes < (size_t{1} << 32) && w_bytes < (size_t{1} << 32);
   // the large-tile kernel streams whole pairs of 128-byte row buffers
-  if (dtype != 1 || fp8w || !small_offsets || k_dim % 128 != 0)
+  if (dtype != 1 || !small_offsets || k_dim % 128 != 0)
     return GemmPick{0, rows_per_expert <= 48 ? 32 : 128};
   if (rows_per_expert <= 48) return GemmPick{0, 32};
   if (rows_per_expert >= 512) return GemmPick{1, 256};
@@ -334,7 +323,7 @@ GemmPick pick_gemm(int dtype, bool fp8w, bool /*gated*/, long rows_per_expert, s
 }
 
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s) {
-  if (pick.variant == 1 && dtype == 1 && !g.wfp8) return launch_expert_gemm(gated, pick.bm, g, s);
+  if (pick.variant == 1 && dtype == 1) return launch_expert_gemm(gated, pick.bm, g, s);
   return launch_generic_gemm(dtype, gated, pick.bm, g, s);
 }
 

@@ -46,6 +46,26 @@ __device__ __forceinline__ void mfma_bf16_agpr(f32x4& c, u32x4 a, u32x4 b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
+// The same, for an operand that a VALU instruction may have just written (a
+// widened FP8 fragment).  CDNA3/4 need two wait states between a VALU write of
+// a VGPR and an MFMA reading it; the compiler inserts them only before MFMAs it
+// recognises, so the asm form carries its own.
+__device__ __forceinline__ void mfma_bf16_agpr_after_valu(f32x4& c, u32x4 a, u32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// 8 FP8 E4M3 codes (bytes 0..7 of v, little endian) -> 8 bf16, one 16-byte
+// MFMA operand chunk.  Every finite E4M3 value is exact in bf16 (3 of its 7
+// mantissa bits, exponents 2^-9 .. 2^8); the conversion's scale is 1.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 v) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+  return r;
+}
+
 // Wait states between the last MFMA writing an accumulator and any other
 // instruction reading it (covers the longest 16x16x32 bf16 latency).
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }

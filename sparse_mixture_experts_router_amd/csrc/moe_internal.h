@@ -172,8 +172,8 @@ struct GemmPick {
 };
 // a_bytes / w_bytes: bytes of the A operand (all its rows) and of one expert's
 // weight matrix; the direct-to-LDS kernel addresses both with 32-bit offsets.
-// fp8w: FP8 expert weights (register-staged kernel only: it widens them to
-// bf16 on their way into LDS).
+// fp8w: FP8 expert weights (both kernels take them: the register-staged one
+// widens them on their way into LDS, the large-tile one after its LDS reads).
 GemmPick pick_gemm(int dtype, bool fp8w, bool gated, long rows_per_expert, size_t a_bytes,
                    size_t w_bytes, int k_dim);
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);

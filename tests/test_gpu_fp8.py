@@ -62,6 +62,9 @@ FP8_CASES = [
     # shared expert and selection bias
     ("shared_and_bias", MoEShape("fp8_ds", T=200, d=512, N=64, k=8, F=256, S=1,
                                  select_bias=True, fp8=True)),
+    # large-tile kernel: 128-row tiles with a shared expert, 256-row tiles
+    ("large_tiles_shared", MoEShape("fp8_l128", T=600, d=512, N=8, k=2, F=512, S=1, fp8=True)),
+    ("large_tiles_256", MoEShape("fp8_l256", T=1100, d=512, N=4, k=2, F=1024, fp8=True)),
 ]
 
 
@@ -70,11 +73,33 @@ def test_fp8_parity(label, shape):
     full_parity(shape, seed=4, label=f"fp8_{label}")
 
 
+@pytest.mark.parametrize("S", [0, 1])
+def test_fp8_tail_tiles_split_over_k(S):
+    """The large-tile down pass's tail split with FP8 weights: every token on
+    expert 7, 20 (40) row tiles of 128, the last 4 (8) split in 2 parts whose
+    fp32 partial sums are scaled per part."""
+    shp = MoEShape("fp8_tail", T=2510, d=4096, N=8, k=1, F=1024, S=S, fp8=True)
+    inputs = make_inputs(shp, seed=8, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0.0] * 7 + [100.0], device="cuda")
+    _, out, _ = full_parity(shp, inputs=inputs, label=f"fp8_tail_split_S{S}")
+    assert int(out["counts"][7]) == 2510
+
+
+@pytest.mark.parametrize("shape,capacity", [
+    (MoEShape("fp8_part256", T=1100, d=512, N=4, k=2, F=1024, fp8=True), 264),
+    (MoEShape("fp8_part128", T=1000, d=512, N=4, k=2, F=512, fp8=True), 280),
+], ids=["bm256_C264", "bm128_C280"])
+def test_fp8_partial_last_tiles(shape, capacity):
+    _, out, _ = full_parity(shape, seed=11, label=f"fp8_partial_C{capacity}", capacity=capacity)
+    assert np.all(to_np(out["counts"]) >= capacity)
+
+
 def test_fp8_capacity():
     shp = MoEShape("fp8_cap", T=300, d=256, N=8, k=2, F=512, fp8=True)
     _, out, ref = full_parity(shp, seed=5, label="fp8_capacity_60", capacity=60)
     assert int(np.sum(~ref["keep"])) > 0
 
 
-def test_fp8_full_size_sampled():
-    sampled_parity(CONFIGS["mixtral_decode_fp8"], seed=0)
+@pytest.mark.parametrize("name", ["mixtral_decode_fp8", "mixtral_prefill_fp8", "deepseek_v3_fp8"])
+def test_fp8_full_size_sampled(name):
+    sampled_parity(CONFIGS[name], seed=0)

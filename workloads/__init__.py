@@ -74,6 +74,10 @@ CONFIGS: Dict[str, MoEShape] = {
     "mixtral_decode": MoEShape("mixtral_decode", T=32, d=4096, N=8, k=2, F=14336),
     "mixtral_decode_fp8": MoEShape("mixtral_decode_fp8", T=32, d=4096, N=8, k=2, F=14336,
                                    fp8=True),
+    "mixtral_prefill_fp8": MoEShape("mixtral_prefill_fp8", T=4096, d=4096, N=8, k=2, F=14336,
+                                    fp8=True),
+    "deepseek_v3_fp8": MoEShape("deepseek_v3_fp8", T=8192, d=7168, N=256, k=8, F=2048, S=1,
+                                select_bias=True, fp8=True),
     "deepseek_v3": MoEShape("deepseek_v3", T=8192, d=7168, N=256, k=8, F=2048, S=1,
                             select_bias=True),
     "qwen3_skew": MoEShape("qwen3_skew", T=16384, d=4096, N=128, k=8, F=1536,
