@@ -49,6 +49,21 @@ What it computes, and where the pages define it:
   bias 7, 3 mantissa bits; exponent field 0 = subnormal; S.1111.111 = NaN; no
   infinities) times a per-output-channel scale, decoded exactly to float64.
 
+* O10 backward (training side): the gradients of L = sum(y * dy) + c * aux
+  with respect to x, W_r, the logit offset and every expert weight, for a
+  given output gradient dy and aux-loss weight c.  The pages train the router
+  through P_i only, f_i coming from a hard choice ("Mixture of Experts and
+  Guided Decoding", routing-collapse passage after the auxiliary-loss
+  equation); everything else is the chain rule through O1..O8 with the
+  selection (O2, O3) and the capacity mask (O8) held fixed, which is the
+  derivative wherever no two keys tie.
+* O11 selection-bias update (auxiliary-loss-free routing): the pages say only
+  that the bias is adjusted as training runs to keep the experts balanced
+  ("MoE inference: the call centre with 256 specialists ...", "The bare
+  mechanism", auxiliary-loss-free variant).  Reading taken: after a batch,
+  b_i <- b_i + rate * sign(mean load - load_i), one float32 step per expert,
+  the load being the expert's count of (token, slot) assignments.
+
 Readings taken where the pages are silent (each is listed in the design notes):
 ties in top-k go to the lower index under IEEE comparison (+0 == -0); f_i
 divides by T*k so that sum f = 1 for any k; P_i uses the full N-way softmax of
@@ -56,8 +71,10 @@ the unbiased logits; shared experts have gate 1 and count in neither k, f nor
 P; no biases inside experts or router.
 
 Parity status: every function here (O9 included: closed-form codes, all 256
-codes against PyTorch's float8_e4m3fn, the output-channel scale identity) is
-pinned by ``tests/test_oracle_pins.py``
+codes against PyTorch's float8_e4m3fn, the output-channel scale identity; O10
+against central finite differences of the float64 forward and, for one expert,
+PyTorch autograd of a dense SwiGLU; O11 against its sign cases) is pinned by
+``tests/test_oracle_pins.py``
 (worked examples of the pages, closed forms, brute force, library special
 cases).  SwiGLU numerics at the real layer shapes have no printed values on the
 pages; they are pinned only through the N = 1, k = 1 reduction to a library
@@ -86,6 +103,8 @@ __all__ = [
     "stats",
     "balance",
     "moe_forward",
+    "moe_backward",
+    "update_select_bias",
     "BALANCE_ALPHA",
 ]
 
@@ -323,6 +342,7 @@ def moe_forward(
     alpha: float = BALANCE_ALPHA,
     n_experts: Optional[int] = None,
     capacity: int = 0,
+    exact_logits: bool = False,
 ):
     """The whole layer forward, O1..O8, with the experts looped one at a time.
 
@@ -337,6 +357,11 @@ def moe_forward(
 
     ``capacity`` > 0 applies O8 (per-expert capacity, extras dropped).
 
+    ``exact_logits``: gates and P take the float64 logits instead of their
+    float32 rounding (the selection still compares float32 keys), which makes
+    the output a smooth function of the weights between ties -- the function
+    whose derivative O10 is.
+
     Returns a dict with y (float64 [T, d]), logits, idx, gates, keep (the O8
     mask), counts, f, P, aux_raw and aux.
     """
@@ -346,9 +371,16 @@ def moe_forward(
         r32 = router_logits(x64, w_router, logit_bias)
     else:
         r32 = np.asarray(route_logits, dtype=np.float32)
+    r_soft = r32
+    if exact_logits and route_logits is None:
+        r_soft = x64 @ _f64(w_router).T
+        if logit_bias is not None:
+            r_soft = r_soft + _f64(logit_bias)[None, :]
     N = r32.shape[1] if n_experts is None else n_experts
     idx, g = route_from_logits(r32, k, select_bias) if T else (
         np.zeros((0, k), np.int32), np.zeros((0, k)))
+    if T and r_soft is not r32:
+        g = kept_softmax(r_soft, idx)
     get = _expert_getter(experts)
     keep = capacity_keep(idx, N, capacity)
 
@@ -365,7 +397,7 @@ def moe_forward(
         for s in range(np.asarray(sg).shape[0]):
             y += swiglu_expert(x64, sg[s], su[s], sd[s])
 
-    counts, f, P = stats(idx, r32, N)
+    counts, f, P = stats(idx, r_soft, N)
     aux_raw, aux = balance(f, P, alpha)
     return {
         "y": y,
@@ -380,3 +412,137 @@ def moe_forward(
         "aux": aux,
     }
 
+
+# -------------------------------------------------------------------------- O10
+def _sigmoid(a):
+    return 1.0 / (1.0 + np.exp(-a))
+
+
+def _swiglu_backward(X, w_gate, w_up, w_down, dout):
+    """Chain rule through one SwiGLU expert (O5) for rows X and output
+    gradient dout: returns (dX, dW_gate, dW_up, dW_down, out)."""
+    X = _f64(X)
+    wg, wu, wd = _f64(w_gate), _f64(w_up), _f64(w_down)
+    a = X @ wg.T
+    b = X @ wu.T
+    s = _sigmoid(a)
+    h = a * s * b                        # SiLU(a) * b
+    out = h @ wd.T
+    dh = dout @ wd                       # [rows, F]
+    da = dh * b * (s + a * s * (1.0 - s))  # d SiLU(a) / da = s + a s (1 - s)
+    db = dh * a * s
+    return da @ wg + db @ wu, da.T @ X, db.T @ X, dout.T @ h, out
+
+
+def moe_backward(
+    x,
+    w_router,
+    experts: Tuple[np.ndarray, np.ndarray, np.ndarray],
+    k: int,
+    dy,
+    *,
+    logit_bias=None,
+    select_bias=None,
+    shared: Optional[Sequence[np.ndarray]] = None,
+    alpha: float = BALANCE_ALPHA,
+    aux_grad: float = 1.0,
+    capacity: int = 0,
+):
+    """O10: gradients of L = sum(y * dy) + aux_grad * aux (float64).
+
+    The forward is O1..O8 with float64 logits for the gates and P (the
+    ``exact_logits`` forward); the selection is taken on the float32 keys and,
+    like the capacity mask, held fixed.  In order, reversing the forward:
+
+    * combine (O6): a kept slot j of token t passes g_tj * dy_t to its expert
+      and receives dg_tj = <dy_t, E_e(x_t)>; a shared expert gets dy_t;
+    * experts (O5): the chain rule through down, the SiLU product and gate/up,
+      giving the weight gradients and each row's contribution to dx;
+    * gates (O4): the softmax over the token's k kept logits,
+      dr_t[idx_tj] += g_tj (dg_tj - sum_l g_tl dg_tl), dropped slots included
+      with dg = 0 (their gate stays in the normalisation);
+    * balance (O7): only P depends on the weights; with c_i = aux_grad * alpha
+      * N * f_i / T, dr_t[i] += p_ti (c_i - sum_j c_j p_tj), p_t the full
+      softmax;
+    * router (O1): dW_r = dr^T x, dx += dr W_r, d logit_bias = sum_t dr_t.
+
+    Returns a dict: dx [T, d], dw_router [N, d], dlogit_bias [N], dw_gate,
+    dw_up [N, F, d], dw_down [N, d, F], and with shared experts ds_gate, ds_up,
+    ds_down; also dgate [T, k] (the gate gradients) and dlogits [T, N].
+    """
+    x64 = _f64(x)
+    T, d = x64.shape
+    wr = _f64(w_router)
+    N = wr.shape[0]
+    wg_all, wu_all, wd_all = (_f64(w) for w in experts)
+    dy = _f64(dy)
+    r = x64 @ wr.T
+    if logit_bias is not None:
+        r += _f64(logit_bias)[None, :]
+    r32 = r.astype(np.float32)
+    if T:
+        idx = topk_by_rank(selection_keys(r32, select_bias), k)
+    else:
+        idx = np.zeros((0, k), np.int32)
+    keep = capacity_keep(idx, N, capacity)
+    g = kept_softmax(r, idx)
+
+    dx = np.zeros_like(x64)
+    dwg, dwu, dwd = np.zeros_like(wg_all), np.zeros_like(wu_all), np.zeros_like(wd_all)
+    dgate = np.zeros((T, k))
+    for e in range(N):
+        tok, slot = np.nonzero(keep & (idx == e))
+        if tok.size == 0:
+            continue
+        gate = g[tok, slot][:, None]
+        dX, dWg, dWu, dWd, out = _swiglu_backward(x64[tok], wg_all[e], wu_all[e], wd_all[e],
+                                                  gate * dy[tok])
+        dgate[tok, slot] = np.sum(dy[tok] * out, axis=1)
+        dx[tok] += dX  # a token picks an expert at most once
+        dwg[e] += dWg
+        dwu[e] += dWu
+        dwd[e] += dWd
+    res = {}
+    if shared is not None:
+        sg, su, sd = (_f64(w) for w in shared)
+        ds = [np.zeros_like(sg), np.zeros_like(su), np.zeros_like(sd)]
+        for s_ in range(sg.shape[0]):
+            dX, dWg, dWu, dWd, _ = _swiglu_backward(x64, sg[s_], su[s_], sd[s_], dy)
+            dx += dX
+            ds[0][s_] += dWg
+            ds[1][s_] += dWu
+            ds[2][s_] += dWd
+        res.update(ds_gate=ds[0], ds_up=ds[1], ds_down=ds[2])
+
+    dr = np.zeros((T, N))
+    if T:
+        # kept softmax (O4)
+        dz = g * (dgate - np.sum(g * dgate, axis=1, keepdims=True))
+        np.add.at(dr, (np.repeat(np.arange(T), k), idx.reshape(-1).astype(np.int64)),
+                  dz.reshape(-1))
+        # balance loss through P (O7)
+        counts = np.bincount(idx.reshape(-1).astype(np.int64), minlength=N).astype(np.float64)
+        f = counts / float(T * k)
+        c = aux_grad * alpha * N * f / T
+        p = full_softmax(r)
+        dr += p * (c[None, :] - np.sum(p * c[None, :], axis=1, keepdims=True))
+    dx += dr @ wr
+    res.update(dx=dx, dw_router=dr.T @ x64, dlogit_bias=dr.sum(axis=0), dw_gate=dwg,
+               dw_up=dwu, dw_down=dwd, dgate=dgate, dlogits=dr, idx=idx, keep=keep)
+    return res
+
+
+# -------------------------------------------------------------------------- O11
+def update_select_bias(select_bias, counts, rate: float) -> np.ndarray:
+    """O11: b_i + rate * sign(mean(counts) - counts_i), in float32.
+
+    An expert that took more than the mean load has its selection bias
+    lowered by ``rate``, one that took less has it raised, one exactly at the
+    mean keeps it.  The mean is sum(counts) / N; the step is one float32
+    addition of +rate, -rate or 0.
+    """
+    b = np.asarray(select_bias, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.float64)
+    mean = c.sum() / c.shape[0]
+    step = np.sign(mean - c).astype(np.float32) * np.float32(rate)
+    return (b + step).astype(np.float32)

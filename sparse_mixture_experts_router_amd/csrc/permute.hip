@@ -152,7 +152,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
   const int tid = threadIdx.x;
   const int B = (n_tok + kRouteTokens - 1) / kRouteTokens;
-  const int P = kScanThreads / N;  // threads per expert (N <= 512 -> P >= 2)
+  // threads per expert (N <= 512 -> up to 2 or more), no more than there are
+  // blocks: their partial sums are added one after another below
+  const int P = min(kScanThreads / N, B > 0 ? B : 1);
   const int e = tid / P, part = tid - e * P;
   const bool mine = e < N;
   const int b_lo = mine ? static_cast<int>((static_cast<long>(B) * part) / P) : 0;

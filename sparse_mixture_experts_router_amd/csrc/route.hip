@@ -405,27 +405,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
       const int tt = i / (NP - a.N);
       s_logit[tt * LD + a.N + (i - tt * (NP - a.N))] = 0.f;
     }
-  } else {  // (few tokens, many splits) one expert per lane, 16 splits per load round
-    for (int i = tid; i < kRouteTokens * NP; i += 256) {
+  } else {  // (few tokens, many splits) one (token, expert) pair per lane
+    for (int i = tid; i < kRouteTokens * NP; i += 256) {  // padding tokens and experts
       const int tt = i / NP, e = i - tt * NP;
+      if (tt >= n_here || e >= a.N) s_logit[tt * LD + e] = 0.f;
+    }
+    for (int i = tid; i < n_here * a.N; i += 256) {
+      const int tt = i / a.N, e = i - tt * a.N;
       const int t = t0 + tt;
+      // up to 32 partials requested before the first is added (in split order)
       float v = 0.f;
-      if (t < a.n_tok && e < a.N) {
-        // loads issued in batches of 16, added in split order
-        for (int k0 = 0; k0 < a.ksplit; k0 += 16) {
-          float pv[16];
+      for (int k0 = 0; k0 < a.ksplit; k0 += 32) {
+        float pv[32];
 #pragma unroll
-          for (int q = 0; q < 16; ++q)
-            pv[q] = k0 + q < a.ksplit
-                        ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
-                        : 0.f;
+        for (int q = 0; q < 32; ++q)
+          pv[q] = k0 + q < a.ksplit
+                      ? a.partial[(static_cast<size_t>(k0 + q) * a.n_tok + t) * a.N + e]
+                      : 0.f;
 #pragma unroll
-          for (int q = 0; q < 16; ++q)
-            if (k0 + q < a.ksplit) v += pv[q];
-        }
-        if (a.logit_bias != nullptr) v += a.logit_bias[e];
-        if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t) * a.N + e] = v;
+        for (int q = 0; q < 32; ++q)
+          if (k0 + q < a.ksplit) v += pv[q];
       }
+      if (a.logit_bias != nullptr) v += a.logit_bias[e];
+      if (a.logits_out != nullptr) a.logits_out[static_cast<size_t>(t) * a.N + e] = v;
       s_logit[tt * LD + e] = v;
     }
   }

@@ -466,6 +466,110 @@ def pin_dequantize_per_output_channel(O):
     _close(got["y"], ref["y"], 1e-12, "FP8 layer")
 
 
+# ------------------------------------------------------------------ backward
+def _fd_grad(fun, arrays, h=1e-6):
+    """Central differences of the scalar fun(*arrays) w.r.t. every element."""
+    grads = []
+    for a_i, a in enumerate(arrays):
+        g = np.zeros_like(a)
+        for pos in np.ndindex(a.shape):
+            old = a[pos]
+            a[pos] = old + h
+            up = fun(*arrays)
+            a[pos] = old - h
+            dn = fun(*arrays)
+            a[pos] = old
+            g[pos] = (up - dn) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def pin_backward_finite_differences(O):
+    """O10 against central differences of the exact-logit forward: every
+    gradient (x, W_r, logit offset, routed and shared expert weights), with a
+    selection bias, a shared expert, an aux-loss weight and a capacity."""
+    rng = np.random.default_rng(41)
+    T, d, F, N, k = 7, 5, 3, 4, 2
+    x, wr, (wg, wu, wd), sh = _layer(rng, T, d, F, N, S=1)
+    wr = wr * 3.0
+    lb = rng.standard_normal(N) * 0.3
+    sb = (rng.standard_normal(N) * 0.3).astype(np.float32)
+    dy = rng.standard_normal((T, d))
+    alpha, aux_grad = 0.3, 2.5
+    for cap in (0, 3):
+        B = O.moe_backward(x, wr, (wg, wu, wd), k, dy, logit_bias=lb, select_bias=sb,
+                           shared=sh, alpha=alpha, aux_grad=aux_grad, capacity=cap)
+        if cap and B["keep"].all():
+            raise AssertionError("capacity case drops nothing")
+
+        def loss(x_, wr_, lb_, wg_, wu_, wd_, sg_, su_, sd_):
+            out = O.moe_forward(x_, wr_, (wg_, wu_, wd_), k, logit_bias=lb_, select_bias=sb,
+                                shared=(sg_, su_, sd_), alpha=alpha, capacity=cap,
+                                exact_logits=True)
+            if not np.array_equal(out["idx"], B["idx"]):
+                raise AssertionError("finite-difference step changed the routing")
+            return float(np.sum(out["y"] * dy)) + aux_grad * out["aux"]
+
+        arrays = [x.copy(), wr.copy(), lb.copy(), wg.copy(), wu.copy(), wd.copy(),
+                  sh[0].copy(), sh[1].copy(), sh[2].copy()]
+        fd = _fd_grad(loss, arrays)
+        names = ["dx", "dw_router", "dlogit_bias", "dw_gate", "dw_up", "dw_down",
+                 "ds_gate", "ds_up", "ds_down"]
+        for name, ref in zip(names, fd):
+            _close(B[name], ref, 1e-6, f"{name} vs finite differences (capacity {cap})")
+
+
+def pin_backward_one_expert_is_swiglu_autograd(O):
+    """N = 1, k = 1: the layer is a dense SwiGLU with gate 1 and a constant
+    balance loss, so the expert gradients are PyTorch autograd's and the
+    router gets exactly zero."""
+    rng = np.random.default_rng(43)
+    x, wr, (wg, wu, wd), _ = _layer(rng, 9, 6, 8, 1)
+    dy = rng.standard_normal((9, 6))
+    B = O.moe_backward(x, wr, (wg, wu, wd), 1, dy)
+    X, Wg, Wu, Wd = (torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+                     for a in (x, wg[0], wu[0], wd[0]))
+    y = Fnn.linear(Fnn.silu(Fnn.linear(X, Wg)) * Fnn.linear(X, Wu), Wd)
+    (y * torch.as_tensor(dy)).sum().backward()
+    _close(B["dx"], X.grad.numpy(), 1e-12, "one expert dx vs autograd")
+    _close(B["dw_gate"][0], Wg.grad.numpy(), 1e-12, "one expert dW_gate vs autograd")
+    _close(B["dw_up"][0], Wu.grad.numpy(), 1e-12, "one expert dW_up vs autograd")
+    _close(B["dw_down"][0], Wd.grad.numpy(), 1e-12, "one expert dW_down vs autograd")
+    _close(B["dw_router"], np.zeros_like(wr), 0, "one expert router gradient")
+
+
+def pin_backward_uniform_router_balance(O):
+    """W_r = 0 and dy = 0: every logit is 0, the selection takes experts
+    0..k-1 (ties to the lower index), p = 1/N, and the only gradient is the
+    balance loss's: dr[t, j] = (c_j - mean c) / N with c_j = aux_grad alpha N
+    f_j / T, f_j = 1/k for j < k."""
+    rng = np.random.default_rng(47)
+    T, d, F, N, k = 5, 4, 3, 6, 2
+    x, _, (wg, wu, wd), _ = _layer(rng, T, d, F, N)
+    wr = np.zeros((N, d))
+    alpha, aux_grad = 0.01, 3.0
+    B = O.moe_backward(x, wr, (wg, wu, wd), k, np.zeros((T, d)), alpha=alpha,
+                       aux_grad=aux_grad)
+    f = np.array([1.0 / k] * k + [0.0] * (N - k))
+    c = aux_grad * alpha * N * f / T
+    dr = np.tile((c - c.mean()) / N, (T, 1))
+    _close(B["dlogits"], dr, 1e-15, "balance-loss logit gradient")
+    _close(B["dw_router"], dr.T @ x, 1e-14, "router weight gradient")
+    _close(B["dx"], np.zeros((T, d)), 0, "dx with W_r = 0 and dy = 0")
+
+
+def pin_select_bias_update(O):
+    """O11 sign cases: above the mean load -> bias - rate, below -> + rate,
+    at the mean -> unchanged; one float32 addition (1 + 1e-8 stays 1)."""
+    got = O.update_select_bias([0.0, 0.5, -1.0, 1e-8], [10, 2, 6, 6], 0.25)
+    exp = np.array([-0.25, 0.75, -1.0, 1e-8], dtype=np.float32)
+    if got.dtype != np.float32 or not np.array_equal(got, exp):
+        raise AssertionError(f"bias update {got} expected {exp}")
+    got = O.update_select_bias([1.0, 1.0], [0, 4], 1e-8)
+    if not np.array_equal(got, np.array([1.0, 1.0], np.float32)):
+        raise AssertionError("bias update must be a float32 addition")
+
+
 ALL_PINS = [
     pin_e1_top2, pin_e2_blend, pin_e3_top2, pin_e4_dense, pin_e5_balance, pin_e6_toy_routing,
     pin_topk_brute_force, pin_select_bias_semantics, pin_swiglu_closed_form,
@@ -473,4 +577,6 @@ ALL_PINS = [
     pin_k_equals_n_is_dense_softmax, pin_shared_expert, pin_relabel_and_chunking, pin_stats,
     pin_invariants, pin_unused_expert_never_read, pin_empty_batch, pin_capacity_brute_force,
     pin_capacity_layer, pin_e4m3_closed_form, pin_e4m3_library, pin_dequantize_per_output_channel,
+    pin_backward_finite_differences, pin_backward_one_expert_is_swiglu_autograd,
+    pin_backward_uniform_router_balance, pin_select_bias_update,
 ]

@@ -51,6 +51,24 @@ MUTATIONS = {
     "e4m3_no_nan": ("mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)", "pass"),
     "scale_on_input_channel": ("return e4m3_decode(codes) * _f64(scale)[..., :, None]",
                                "return e4m3_decode(codes) * _f64(scale)[..., None, :]"),
+    "bwd_silu_derivative": ("da = dh * b * (s + a * s * (1.0 - s))", "da = dh * b * s"),
+    "bwd_gate_not_applied": ("wd_all[e],\n                                                  gate * dy[tok])",
+                             "wd_all[e],\n                                                  dy[tok])"),
+    "bwd_gate_gradient_wrong": ("dgate[tok, slot] = np.sum(dy[tok] * out, axis=1)",
+                                "dgate[tok, slot] = np.sum(dy[tok], axis=1)"),
+    "bwd_softmax_not_centred": ("dz = g * (dgate - np.sum(g * dgate, axis=1, keepdims=True))",
+                                "dz = g * dgate"),
+    "bwd_balance_sign": ("dr += p * (c[None, :] - np.sum(p * c[None, :], axis=1, keepdims=True))",
+                         "dr -= p * (c[None, :] - np.sum(p * c[None, :], axis=1, keepdims=True))"),
+    "bwd_balance_not_over_T": ("c = aux_grad * alpha * N * f / T", "c = aux_grad * alpha * N * f"),
+    "bwd_router_term_missing": ("    dx += dr @ wr\n", "    pass\n"),
+    "bwd_shared_dx_dropped": ("            dx += dX\n            ds[0][s_] += dWg",
+                              "            ds[0][s_] += dWg"),
+    "bwd_capacity_ignored": ("tok, slot = np.nonzero(keep & (idx == e))",
+                             "tok, slot = np.nonzero(idx == e)"),
+    "bwd_down_grad_transposed": ("return da @ wg + db @ wu, da.T @ X, db.T @ X, dout.T @ h, out",
+                                 "return da @ wg + db @ wu, da.T @ X, db.T @ X, (h.T @ dout).T[::-1], out"),
+    "bias_update_sign": ("step = np.sign(mean - c)", "step = np.sign(c - mean)"),
     "keys_compared_in_fp64": [
         ("return (r32 + b32[None, :]).astype(np.float32)",
          "return r32.astype(np.float64) + b32.astype(np.float64)[None, :]"),
