@@ -1,6 +1,6 @@
 /*
- * moe.h -- C ABI of libmoe.so, a sparse mixture-of-experts layer forward for
- * AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of libmoe.so, a sparse mixture-of-experts layer (forward,
+ * and the backward of its training pass) for AMD Instinct MI355X (gfx950).
  *
  * The layer (defined on "Mixture of experts and speculative decoding", section
  * "Opening the hood: the MoE layer precisely", and on "MoE inference: the call
@@ -40,8 +40,9 @@
  *  - Calls are thread-safe; concurrent calls must use distinct workspaces.
  *  - Supported sizes: 1 <= k <= min(N, 16), N <= 512, 0 <= S <= 4, capacity >= 0,
  *    d and F positive multiples of 64, T >= 0 (T = 0 launches nothing and
- *    returns MOE_OK); FP8 expert weights with dtype MOE_BF16 only.  Other
- *    sizes return MOE_ERR_UNSUPPORTED.
+ *    returns MOE_OK, except that moe_layer_backward writes zero weight
+ *    gradients); FP8 expert weights with dtype MOE_BF16 only.  Other sizes
+ *    return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -195,6 +196,72 @@ moe_status moe_balance_stats(int32_t T, int32_t N, int32_t k,
                              const int32_t* counts, const float* prob_sum,
                              float alpha, float* f_out, float* P_out,
                              float* aux_out, void* stream);
+
+/* ------------------------------------------------------------- backward
+ *
+ * Gradients of  L = sum(y * dy) + aux_grad * alpha * N * sum_e f_e P_e  with
+ * respect to x and every parameter, through the forward above.  The balance
+ * loss reaches the router through P only: f comes from a hard choice and is
+ * a constant ("Mixture of Experts and Guided Decoding", routing-collapse
+ * passage after the auxiliary-loss equation).  The selection (top-k on the
+ * keys) and the capacity mask are held fixed; select_bias gets no gradient.
+ *
+ *   kept slot j of token t:  d(expert input) = g_tj dy_t,
+ *                            dg_tj = <dy_t, E_e(x_t)>
+ *   gates (kept softmax):    dr_t[idx_tj] += g_tj (dg_tj - sum_l g_tl dg_tl)
+ *   balance loss:            dr_t[e] += p_te (c_e - sum_j c_j p_tj),
+ *                            c_e = aux_grad alpha N f_e / T, p_t = softmax(r_t)
+ *   router:                  dW_r = dr^T x, dx += dr W_r,
+ *                            d logit_bias = sum_t dr_t
+ * plus the chain rule through every SwiGLU expert for dx, dW_gate, dW_up and
+ * dW_down (shared experts with gate 1).
+ *
+ * The call recomputes the routing and the gate/up projections from x (it
+ * takes no state from a forward call).  Arithmetic: bf16 operands on the
+ * matrix cores with fp32 accumulation; the intermediate per-row tensors (gate
+ * and up projections, dy W_down, the SwiGLU gradients, each row's dx
+ * contribution) are held in dtype; the router gradient and every reduction
+ * are fp32; each output is rounded once to its type.  Deterministic.
+ * Expert weights must be in dtype (MOE_WEIGHTS_DTYPE): FP8 codes have no
+ * gradient, so MOE_ERR_UNSUPPORTED.  T = 0 writes zero weight gradients. */
+typedef struct {
+  void* dx;           /* [T, d]     dtype, required when T > 0                  */
+  void* dw_router;    /* [N, d]     dtype, required                             */
+  float* dlogit_bias; /* [N]        fp32, or NULL                               */
+  void* dw_gate;      /* [N, F, d]  dtype, required (experts no token chose: 0) */
+  void* dw_up;        /* [N, F, d]  dtype, required                             */
+  void* dw_down;      /* [N, d, F]  dtype, required                             */
+  void* dws_gate;     /* [S, F, d]  dtype, required when S > 0                  */
+  void* dws_up;       /* [S, F, d]                                              */
+  void* dws_down;     /* [S, d, F]                                              */
+} moe_grads;
+
+/* Bytes of device workspace moe_layer_backward needs for `cfg` (a multiple
+ * of 256; it holds transposed copies of the expert weights, so it is about
+ * three times their size plus per-row activations).  0 for an invalid cfg. */
+size_t moe_backward_workspace_size(const moe_config* cfg);
+
+/* Layer backward: x [T, d] and weights as for moe_layer_forward, dy [T, d]
+ * the gradient of L with respect to y (dtype), alpha the balance-loss
+ * coefficient and aux_grad the weight of that loss in L.  Writes every
+ * gradient of `grads` (caller-owned device arrays, 16-byte aligned).
+ * `workspace` holds moe_backward_workspace_size(cfg) bytes, 256-byte
+ * aligned; its contents are scratch. */
+moe_status moe_layer_backward(const moe_config* cfg, const void* x,
+                              const moe_weights* w, const void* dy, float alpha,
+                              float aux_grad, moe_grads* grads, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* Auxiliary-loss-free balancing ("MoE inference: the call centre with 256
+ * specialists ...", "The bare mechanism": a routing bias adjusted during
+ * training keeps the experts balanced without a loss term).  The pages give
+ * no rule; this library's reading is one step toward the mean load:
+ *   select_bias[e] += rate * sign(mean_j counts[j] - counts[e])
+ * (fp32 addition; the sign is taken exactly on the integer counts), counts
+ * being the (token, slot) assignments per routed expert of a batch
+ * (moe_routing.counts).  N <= 512; device arrays; enqueued on `stream`. */
+moe_status moe_update_select_bias(int32_t N, const int32_t* counts, float rate,
+                                  float* select_bias, void* stream);
 
 #ifdef __cplusplus
 }

@@ -447,6 +447,7 @@ def moe_backward(
     alpha: float = BALANCE_ALPHA,
     aux_grad: float = 1.0,
     capacity: int = 0,
+    route_idx=None,
 ):
     """O10: gradients of L = sum(y * dy) + aux_grad * aux (float64).
 
@@ -466,6 +467,11 @@ def moe_backward(
       softmax;
     * router (O1): dW_r = dr^T x, dx += dr W_r, d logit_bias = sum_t dr_t.
 
+    ``route_idx`` (int [T, k]) replaces the selection when given, which is how
+    a caller checks another implementation's backward on that
+    implementation's own choice of experts (near-ties in the logits may be
+    taken either way by two correct implementations).
+
     Returns a dict: dx [T, d], dw_router [N, d], dlogit_bias [N], dw_gate,
     dw_up [N, F, d], dw_down [N, d, F], and with shared experts ds_gate, ds_up,
     ds_down; also dgate [T, k] (the gate gradients) and dlogits [T, N].
@@ -480,7 +486,9 @@ def moe_backward(
     if logit_bias is not None:
         r += _f64(logit_bias)[None, :]
     r32 = r.astype(np.float32)
-    if T:
+    if route_idx is not None:
+        idx = np.asarray(route_idx).astype(np.int32).reshape(T, k)
+    elif T:
         idx = topk_by_rank(selection_keys(r32, select_bias), k)
     else:
         idx = np.zeros((0, k), np.int32)

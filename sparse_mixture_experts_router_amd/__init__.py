@@ -1,4 +1,4 @@
-"""Sparse mixture-of-experts layer forward on AMD MI355X (gfx950).
+"""Sparse mixture-of-experts layer (forward and backward) on AMD MI355X (gfx950).
 
 A thin ctypes binding of ``libmoe.so``: every function below only marshals
 PyTorch tensors (device memory) and the current HIP stream into the C ABI
@@ -21,6 +21,8 @@ __all__ = [
     "MoEError", "MoEConfig", "MoEWeights",
     "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
     "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
+    "MoEGrads", "moe_backward_workspace_size", "alloc_backward_workspace", "moe_layer_backward",
+    "moe_update_select_bias",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +65,14 @@ class MoERouting(ctypes.Structure):
                 ("prob_sum", ctypes.c_void_p)]
 
 
+class MoEGrads(ctypes.Structure):
+    _fields_ = [("dx", ctypes.c_void_p), ("dw_router", ctypes.c_void_p),
+                ("dlogit_bias", ctypes.c_void_p), ("dw_gate", ctypes.c_void_p),
+                ("dw_up", ctypes.c_void_p), ("dw_down", ctypes.c_void_p),
+                ("dws_gate", ctypes.c_void_p), ("dws_up", ctypes.c_void_p),
+                ("dws_down", ctypes.c_void_p)]
+
+
 _LIB = None
 
 
@@ -92,6 +102,13 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward_timed.restype = ctypes.c_int
         L.moe_balance_stats.argtypes = [i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         L.moe_balance_stats.restype = ctypes.c_int
+        L.moe_backward_workspace_size.argtypes = [cfgp]
+        L.moe_backward_workspace_size.restype = sz
+        L.moe_layer_backward.argtypes = [cfgp, vp, wp, vp, ctypes.c_float, ctypes.c_float,
+                                         ctypes.POINTER(MoEGrads), vp, sz, vp]
+        L.moe_layer_backward.restype = ctypes.c_int
+        L.moe_update_select_bias.argtypes = [i32, vp, ctypes.c_float, vp, vp]
+        L.moe_update_select_bias.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -220,6 +237,46 @@ def moe_balance_stats(T: int, N: int, k: int, counts: torch.Tensor, prob_sum: to
         int(T), int(N), int(k), _ptr(counts, torch.int32, "counts"),
         _ptr(prob_sum, torch.float32, "prob_sum"), float(alpha), _ptr(f, torch.float32, "f"),
         _ptr(P, torch.float32, "P"), _ptr(aux, torch.float32, "aux"), _stream(stream)))
+
+
+def moe_backward_workspace_size(cfg: MoEConfig) -> int:
+    return int(lib().moe_backward_workspace_size(ctypes.byref(cfg)))
+
+
+def alloc_backward_workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
+    n = moe_backward_workspace_size(cfg)
+    if n == 0:
+        raise MoEError(MOE_ERR_INVALID_ARG, "configuration rejected")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+_GRADS = ("dx", "dw_router", "dlogit_bias", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up",
+          "dws_down")
+
+
+def moe_layer_backward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]],
+                       dy: torch.Tensor, grads: Dict[str, Optional[torch.Tensor]], *,
+                       workspace: torch.Tensor, alpha: float = 0.01, aux_grad: float = 1.0,
+                       stream=None) -> None:
+    """Gradients of sum(y * dy) + aux_grad * aux into ``grads`` (keys dx,
+    dw_router, dlogit_bias, dw_gate, dw_up, dw_down, dws_*); see
+    ``moe_layer_backward`` in include/moe.h."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    w = _weights(cfg, weights)
+    g = MoEGrads(**{n: _ptr(grads.get(n), torch.float32 if n == "dlogit_bias" else dt, n)
+                    for n in _GRADS})
+    _check(lib().moe_layer_backward(
+        ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(dy, dt, "dy"), float(alpha),
+        float(aux_grad), ctypes.byref(g), _ptr(workspace, None, "workspace"), workspace.numel(),
+        _stream(stream)))
+
+
+def moe_update_select_bias(counts: torch.Tensor, rate: float, select_bias: torch.Tensor,
+                           stream=None) -> None:
+    """select_bias += rate * sign(mean(counts) - counts), in place (fp32)."""
+    _check(lib().moe_update_select_bias(
+        int(counts.numel()), _ptr(counts, torch.int32, "counts"), float(rate),
+        _ptr(select_bias, torch.float32, "select_bias"), _stream(stream)))
 
 
 class MoELayer:

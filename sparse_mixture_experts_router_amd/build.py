@@ -20,7 +20,7 @@ OBJ_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "expert_gemm.hip", "combine.hip",
-           "moe_api.hip"]
+           "backward.hip", "moe_api.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -59,17 +59,28 @@ enum {
   R_TUP, R_TDN, R_IUP, R_IDN, R_TB, R_NT, R_HID, R_YP, R_YPART, R_COUNT
 };
 
-Plan make_plan(const moe_config& c) {
+// bwd: the plan of the backward's routing and plain GEMMs instead: the "up"
+// tile list serves the passes with F output columns and K = d (G, U, D), the
+// "down" list the pass with d output columns and K = 2F (dXp); no split of
+// any reduction, and no forward activations.
+Plan make_plan(const moe_config& c, bool bwd = false) {
   Plan p{};
   const long rows_per_expert = static_cast<long>(c.T) * c.top_k / c.n_experts;
   const size_t eb_ = c.dtype == MOE_BF16 ? 2 : 4;
   const bool fp8w = c.weight_format == MOE_WEIGHTS_FP8_E4M3;
   const size_t rows_all = static_cast<size_t>(c.T) * (c.top_k + c.n_shared);
   const size_t w_mat = static_cast<size_t>(c.d_model) * c.d_ff * (fp8w ? 1 : eb_);
-  p.up = pick_gemm(c.dtype, fp8w, true, rows_per_expert,
-                   static_cast<size_t>(c.T) * c.d_model * eb_, w_mat, c.d_model);
-  p.down = pick_gemm(c.dtype, fp8w, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat,
-                     c.d_ff);
+  if (bwd) {
+    p.up = pick_gemm(c.dtype, false, false, rows_per_expert,
+                     static_cast<size_t>(c.T) * c.d_model * eb_, w_mat, c.d_model);
+    p.down = pick_gemm(c.dtype, false, false, rows_per_expert, rows_all * 2 * c.d_ff * eb_,
+                       2 * w_mat, 2 * c.d_ff);
+  } else {
+    p.up = pick_gemm(c.dtype, fp8w, true, rows_per_expert,
+                     static_cast<size_t>(c.T) * c.d_model * eb_, w_mat, c.d_model);
+    p.down = pick_gemm(c.dtype, fp8w, false, rows_per_expert, rows_all * c.d_ff * eb_, w_mat,
+                       c.d_ff);
+  }
   // the large-tile kernel's work items hold tile indices below kItemMaxTiles
   if (p.up.variant == 1 && tile_capacity(c, p.up.bm) >= kItemMaxTiles) p.up = GemmPick{0, 128};
   if (p.down.variant == 1 && tile_capacity(c, p.down.bm) >= kItemMaxTiles)
@@ -101,7 +112,7 @@ Plan make_plan(const moe_config& c) {
   // work-item lists of the large-tile kernel (column tiles of the width its
   // chosen instance computes)
   if (p.up.variant == 1) {
-    const int cols = expert_gemm_cols(true, p.up.bm);
+    const int cols = expert_gemm_cols(!bwd, p.up.bm);
     p.nnt_up = (c.d_ff + cols - 1) / cols;
   }
   if (p.down.variant == 1) {
@@ -112,7 +123,7 @@ Plan make_plan(const moe_config& c) {
   sz[R_IDN] = static_cast<size_t>(p.cap_down) * p.nnt_down * 4;
   sz[R_TB] = (2 * (N + S + 1) + 2) * 4;
   sz[R_NT] = kPlanInts * 4;
-  sz[R_HID] = rows * static_cast<size_t>(c.d_ff) * eb;
+  sz[R_HID] = bwd ? 0 : rows * static_cast<size_t>(c.d_ff) * eb;
 
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -128,11 +139,11 @@ Plan make_plan(const moe_config& c) {
     const long routed = (tk + bm - 1) / bm > used ? (tk + bm - 1) / bm : used;
     long est = routed + static_cast<long>(S) * ((static_cast<long>(T) + bm - 1) / bm);
     if (est > p.cap_down) est = p.cap_down;
-    p.dsplit = down_split(c.dtype, fp8w, p.down, est, c.d_model, c.d_ff, p.cus);
+    p.dsplit = bwd ? 1 : down_split(c.dtype, fp8w, p.down, est, c.d_model, c.d_ff, p.cus);
   }
-  sz[R_YP] = p.dsplit > 1 ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
+  sz[R_YP] = (p.dsplit > 1 || bwd) ? 0 : rows * static_cast<size_t>(c.d_model) * eb;
   p.split = SplitSpec{p.dsplit, 0, p.cus, 0, 1};
-  if (p.dsplit <= 1 && p.down.variant == 1) {
+  if (p.dsplit <= 1 && p.down.variant == 1 && !bwd) {
     // tail split of the large-tile down GEMM
     const int nnt = p.nnt_down;
     p.split.tail_nnt = nnt;
@@ -274,6 +285,116 @@ moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe
   return MOE_OK;
 }
 
+// Offsets, tile lists, the permutation (sorted_tok, inv_row) and the
+// large-tile GEMMs' work items, from the routing in idx and the block sums.
+moe_status run_permute(const moe_config& c, const Plan& p, const Workspace& ws, moe_routing* out,
+                       const int32_t* idx, hipStream_t s) {
+  moe_status st;
+  const long n_rows = static_cast<long>(c.T) * (c.top_k + c.n_shared);
+  hipError_t err = hipSuccess;
+  if (n_rows <= kScanScatterMaxRows) {  // one launch for scan and permutation
+    if ((st = run_scan(c, p, ws, out, ScatterSpec{idx, ws.lrank, ws.sorted_tok, ws.inv_row}, s)) !=
+        MOE_OK)
+      return st;
+  } else {
+    if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
+    err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts, c.top_k,
+                         c.n_shared, c.capacity, ws.sorted_tok, ws.inv_row, s);
+    if (err != hipSuccess) return hip_fail(err, "scatter kernel");
+  }
+  const long max_items = std::max(static_cast<long>(p.cap_up) * p.nnt_up,
+                                  static_cast<long>(p.cap_down) * p.nnt_down);
+  if ((err = launch_items(item_spec(p, ws), c.n_experts + c.n_shared, max_items, s)) != hipSuccess)
+    return hip_fail(err, "items kernel");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- backward
+// Workspace of moe_layer_backward: the regions of make_plan(c, true) (routing,
+// scan, tile lists), then the backward's own.
+enum {
+  B_LOGITS, B_G, B_U, B_D, B_H, B_DAB, B_DXP, B_RGATE, B_DG, B_DR, B_DR32, B_DXR, B_WDT,
+  B_WDT_S, B_WCAT, B_WCAT_S, B_WRT, B_KBASE, B_DOT, B_HT, B_DABT, B_XT, B_XTF, B_DRT, B_COUNT
+};
+
+struct BwdPlan {
+  Plan p;
+  size_t off[B_COUNT];
+  size_t total;
+  long rows;  // T (k + S): every permuted row the forward may have
+  long kseg;  // columns of the transposed segments: sum over groups of rows rounded up to 64
+  int Kr;     // N rounded up to 64
+  int Tp;     // T rounded up to 64
+};
+
+BwdPlan make_bwd_plan(const moe_config& c) {
+  BwdPlan b{};
+  b.p = make_plan(c, true);
+  const size_t T = c.T, d = c.d_model, F = c.d_ff, N = c.n_experts, S = c.n_shared;
+  const size_t G = N + S;
+  const size_t eb = c.dtype == MOE_BF16 ? 2 : 4;
+  b.rows = static_cast<long>(T) * (c.top_k + c.n_shared);
+  b.kseg = (b.rows + 63 * static_cast<long>(G) + 63) / 64 * 64;
+  b.Kr = static_cast<int>((N + 63) / 64 * 64);
+  b.Tp = static_cast<int>((T + 63) / 64 * 64);
+  const size_t rows = b.rows, ks = b.kseg, Kr = b.Kr, Tp = b.Tp;
+  size_t sz[B_COUNT];
+  sz[B_LOGITS] = T * N * 4;
+  sz[B_G] = sz[B_U] = sz[B_D] = sz[B_H] = rows * F * eb;
+  sz[B_DAB] = rows * 2 * F * eb;
+  sz[B_DXP] = rows * d * eb;
+  sz[B_RGATE] = sz[B_DG] = rows * 4;
+  sz[B_DR] = T * Kr * eb;
+  sz[B_DR32] = T * N * 4;
+  sz[B_DXR] = T * d * 4;
+  sz[B_WDT] = N * F * d * eb;
+  sz[B_WDT_S] = S * F * d * eb;
+  sz[B_WCAT] = N * d * 2 * F * eb;
+  sz[B_WCAT_S] = S * d * 2 * F * eb;
+  sz[B_WRT] = d * Kr * eb;
+  sz[B_KBASE] = (G + 1) * 4;
+  sz[B_DOT] = d * ks * eb;
+  sz[B_HT] = F * ks * eb;
+  sz[B_DABT] = 2 * F * ks * eb;
+  sz[B_XT] = d * ks * eb;
+  sz[B_XTF] = d * Tp * eb;
+  sz[B_DRT] = Kr * Tp * eb;
+  size_t o = b.p.total;
+  for (int i = 0; i < B_COUNT; ++i) {
+    b.off[i] = o;
+    o += align_up(sz[i] ? sz[i] : 1);
+  }
+  b.total = o;
+  return b;
+}
+
+// One plain (no SiLU) grouped pass of the forward's GEMMs over the permuted
+// rows: out[row] = A[row or gather[row]] W_e^T with W_e [n_dim, k_dim].
+GemmArgs plain_pass(const moe_config& c, const Plan& p, const Workspace& ws, bool up_list,
+                    const void* a, const int32_t* gather, int a_rows, const void* w0,
+                    const void* ws0, int k_dim, int n_dim, void* out) {
+  GemmArgs g{};
+  g.a = a;
+  g.gather = gather;
+  g.w0 = w0;
+  g.ws0 = ws0;
+  g.offsets = ws.offsets;
+  g.tiles = up_list ? ws.tiles_up : ws.tiles_down;
+  g.ntiles = up_list ? ws.ntiles : ws.ntiles + 1;
+  g.out = out;
+  g.a_rows = a_rows;
+  g.n_experts = c.n_experts;
+  g.k_dim = k_dim;
+  g.n_dim = n_dim;
+  g.tiles_cap = up_list ? p.cap_up : p.cap_down;
+  g.ksplit = 1;
+  g.out_part = nullptr;
+  g.plan = nullptr;
+  g.items = up_list ? ws.items_up : ws.items_down;
+  g.cus = p.cus;
+  return g;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -345,25 +466,8 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
   if ((st = run_route(c, p, ws, x, *w, out, idx, gate, s)) != MOE_OK) return st;
 
   mark(ev, MOE_STAGE_PERMUTE, s);
-  const long n_rows = static_cast<long>(c.T) * (c.top_k + c.n_shared);
+  if ((st = run_permute(c, p, ws, out, idx, s)) != MOE_OK) return st;
   hipError_t err = hipSuccess;
-  if (n_rows <= kScanScatterMaxRows) {  // one launch for scan and permutation
-    if ((st = run_scan(c, p, ws, out, ScatterSpec{idx, ws.lrank, ws.sorted_tok, ws.inv_row}, s)) !=
-        MOE_OK)
-      return st;
-  } else {
-    if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
-    err = launch_scatter(idx, ws.lrank, ws.blk_base, ws.offsets, c.T, c.n_experts, c.top_k,
-                         c.n_shared, c.capacity, ws.sorted_tok, ws.inv_row, s);
-    if (err != hipSuccess) return hip_fail(err, "scatter kernel");
-  }
-  {
-    const long max_items = std::max(static_cast<long>(p.cap_up) * p.nnt_up,
-                                    static_cast<long>(p.cap_down) * p.nnt_down);
-    if ((err = launch_items(item_spec(p, ws), c.n_experts + c.n_shared, max_items, s)) !=
-        hipSuccess)
-      return hip_fail(err, "items kernel");
-  }
 
   mark(ev, MOE_STAGE_EXPERT_UP, s);
   GemmArgs up{};
@@ -444,6 +548,177 @@ moe_status moe_balance_stats(int32_t T, int32_t N, int32_t k, const int32_t* cou
   hipError_t err = launch_balance(T, N, k, counts, prob_sum, alpha, f_out, P_out, aux_out,
                                   static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "balance kernel");
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  return make_bwd_plan(*cfg).total;
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_weights* w,
+                              const void* dy, float alpha, float aux_grad, moe_grads* gr,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const moe_config& c = *cfg;
+  if (c.weight_format != MOE_WEIGHTS_DTYPE)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward needs expert weights in dtype");
+  if ((st = check_weights(c, w, true)) != MOE_OK) return st;
+  if (gr == nullptr) return fail(MOE_ERR_INVALID_ARG, "grads is NULL");
+  {
+    const void* req[5] = {c.T > 0 ? gr->dx : gr->dw_router, gr->dw_router, gr->dw_gate,
+                          gr->dw_up, gr->dw_down};
+    for (const void* q : req) {
+      if (q == nullptr) return fail(MOE_ERR_INVALID_ARG, "required gradient is NULL");
+      if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "gradient not 16-byte aligned");
+    }
+    if (c.n_shared > 0) {
+      const void* sh[3] = {gr->dws_gate, gr->dws_up, gr->dws_down};
+      for (const void* q : sh) {
+        if (q == nullptr) return fail(MOE_ERR_INVALID_ARG, "shared expert gradient is NULL");
+        if (!aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "gradient not 16-byte aligned");
+      }
+    }
+  }
+  if (c.T > 0) {
+    if (x == nullptr || dy == nullptr) return fail(MOE_ERR_INVALID_ARG, "x or dy is NULL");
+    if (!aligned16(x) || !aligned16(dy))
+      return fail(MOE_ERR_INVALID_ARG, "x or dy not 16-byte aligned");
+  }
+  const BwdPlan b = make_bwd_plan(c);
+  const Plan& p = b.p;
+  if ((st = check_workspace(p, workspace, ws_bytes)) != MOE_OK) return st;
+  if (ws_bytes < b.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_backward_workspace_size");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = c.dtype, T = c.T, d = c.d_model, F = c.d_ff, N = c.n_experts, k = c.top_k,
+            S = c.n_shared, G = N + S;
+  const size_t eb = dt == MOE_BF16 ? 2 : 4;
+  hipError_t err = hipSuccess;
+  if (T == 0) {  // no rows: every weight gradient is zero
+    if ((err = launch_kgemm(dt, false, nullptr, 0, nullptr, 0, d, F, G, nullptr, 0, gr->dw_down,
+                            gr->dws_down, N, s)) != hipSuccess ||
+        (err = launch_kgemm(dt, false, nullptr, 0, nullptr, 0, F, d, G, nullptr, 0, gr->dw_gate,
+                            gr->dws_gate, N, s)) != hipSuccess ||
+        (err = launch_kgemm(dt, false, nullptr, 0, nullptr, 0, F, d, G, nullptr, 0, gr->dw_up,
+                            gr->dws_up, N, s)) != hipSuccess ||
+        (err = launch_kgemm(dt, false, nullptr, 0, nullptr, 0, N, d, 1, nullptr, 0,
+                            gr->dw_router, nullptr, 1, s)) != hipSuccess)
+      return hip_fail(err, "zero gradients");
+    if (gr->dlogit_bias != nullptr &&
+        (err = launch_colsum(nullptr, 0, N, gr->dlogit_bias, s)) != hipSuccess)
+      return hip_fail(err, "zero gradients");
+    return MOE_OK;
+  }
+  const Workspace ws = carve(p, workspace);
+  char* base = static_cast<char*>(workspace);
+  auto at = [&](int r) { return static_cast<void*>(base + b.off[r]); };
+  float* logits = static_cast<float*>(at(B_LOGITS));
+  float* rgate = static_cast<float*>(at(B_RGATE));
+  float* dg_row = static_cast<float*>(at(B_DG));
+  float* dr32 = static_cast<float*>(at(B_DR32));
+  float* dxr = static_cast<float*>(at(B_DXR));
+  int32_t* kbase = static_cast<int32_t*>(at(B_KBASE));
+  const int rows = static_cast<int>(b.rows);
+
+  // routing and grouping, as in the forward
+  err = launch_route(dt, x, w->w_router, w->logit_bias, w->select_bias, T, d, N, k, p.ksplit,
+                     ws.route_partial, logits, ws.topk_idx, ws.topk_gate, ws.lrank, ws.blk_counts,
+                     ws.blk_psum, s);
+  if (err != hipSuccess) return hip_fail(err, "route kernel");
+  if ((st = run_permute(c, p, ws, nullptr, ws.topk_idx, s)) != MOE_OK) return st;
+
+  // weights transposed: W_down -> [N, F, d]; [W_gate | W_up] -> [N, d, 2F]; W_r -> [d, Kr]
+  const long fd = static_cast<long>(F) * d;
+  if ((err = launch_transpose(dt, w->w_down, d, F, fd, at(B_WDT), d, 0, d, fd, N, s)) != hipSuccess ||
+      (err = launch_transpose(dt, w->w_gate, F, d, fd, at(B_WCAT), 2 * F, 0, F, 2 * fd, N, s)) !=
+          hipSuccess ||
+      (err = launch_transpose(dt, w->w_up, F, d, fd, at(B_WCAT), 2 * F, F, F, 2 * fd, N, s)) !=
+          hipSuccess ||
+      (err = launch_transpose(dt, w->w_router, N, d, 0, at(B_WRT), b.Kr, 0, b.Kr, 0, 1, s)) !=
+          hipSuccess)
+    return hip_fail(err, "weight transpose");
+  if (S > 0 &&
+      ((err = launch_transpose(dt, w->ws_down, d, F, fd, at(B_WDT_S), d, 0, d, fd, S, s)) !=
+           hipSuccess ||
+       (err = launch_transpose(dt, w->ws_gate, F, d, fd, at(B_WCAT_S), 2 * F, 0, F, 2 * fd, S, s)) !=
+           hipSuccess ||
+       (err = launch_transpose(dt, w->ws_up, F, d, fd, at(B_WCAT_S), 2 * F, F, F, 2 * fd, S, s)) !=
+           hipSuccess))
+    return hip_fail(err, "weight transpose");
+
+  // G, U (recomputed) and D = dy W_down, all [rows, F]
+  GemmArgs ga = plain_pass(c, p, ws, true, x, ws.sorted_tok, T, w->w_gate, w->ws_gate, d, F, at(B_G));
+  if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "G GEMM");
+  ga = plain_pass(c, p, ws, true, x, ws.sorted_tok, T, w->w_up, w->ws_up, d, F, at(B_U));
+  if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "U GEMM");
+  ga = plain_pass(c, p, ws, true, dy, ws.sorted_tok, T, at(B_WDT), S > 0 ? at(B_WDT_S) : nullptr,
+                  d, F, at(B_D));
+  if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "D GEMM");
+
+  // gates per row, SwiGLU backward, then dXp = [dA dB] [W_gate; W_up]
+  if ((err = launch_row_gate(ws.inv_row, ws.topk_gate, ws.offsets, T, k, N, S, rgate, s)) !=
+          hipSuccess ||
+      (err = launch_swiglu_bwd(dt, at(B_G), at(B_U), at(B_D), rgate, ws.offsets, G, F, rows,
+                               at(B_H), at(B_DAB), dg_row, s)) != hipSuccess)
+    return hip_fail(err, "SwiGLU backward");
+  ga = plain_pass(c, p, ws, false, at(B_DAB), nullptr, rows, at(B_WCAT),
+                  S > 0 ? at(B_WCAT_S) : nullptr, 2 * F, d, at(B_DXP));
+  if ((err = launch_gemm(dt, false, p.down, ga, s)) != hipSuccess) return hip_fail(err, "dX GEMM");
+
+  // router: dr, d logit_bias, dx = dr W_r + the rows' dXp
+  if ((err = launch_router_bwd(dt, logits, ws.topk_idx, ws.topk_gate, ws.inv_row, dg_row,
+                               ws.counts, T, N, k, alpha, aux_grad, b.Kr, at(B_DR), dr32, s)) !=
+      hipSuccess)
+    return hip_fail(err, "router backward");
+  if (gr->dlogit_bias != nullptr &&
+      (err = launch_colsum(dr32, T, N, gr->dlogit_bias, s)) != hipSuccess)
+    return hip_fail(err, "logit-bias gradient");
+  if ((err = launch_kgemm(dt, true, at(B_DR), b.Kr, at(B_WRT), b.Kr, T, d, 1, nullptr, b.Kr, dxr,
+                          nullptr, 1, s)) != hipSuccess ||
+      (err = launch_dx_combine(dt, at(B_DXP), dxr, ws.inv_row, ws.offsets, T, N, k, S, d, gr->dx,
+                               s)) != hipSuccess)
+    return hip_fail(err, "dx");
+
+  // weight gradients over each group's rows
+  const long ks = b.kseg;
+  if ((err = launch_kbase(ws.offsets, G, kbase, s)) != hipSuccess ||
+      (err = launch_segment_transpose(dt, dy, d, T, ws.sorted_tok, rgate, ws.offsets, kbase, G, ks,
+                                      at(B_DOT), ks, s)) != hipSuccess ||
+      (err = launch_segment_transpose(dt, at(B_H), F, rows, nullptr, nullptr, ws.offsets, kbase, G,
+                                      ks, at(B_HT), ks, s)) != hipSuccess ||
+      (err = launch_segment_transpose(dt, at(B_DAB), 2 * F, rows, nullptr, nullptr, ws.offsets,
+                                      kbase, G, ks, at(B_DABT), ks, s)) != hipSuccess ||
+      (err = launch_segment_transpose(dt, x, d, T, ws.sorted_tok, nullptr, ws.offsets, kbase, G, ks,
+                                      at(B_XT), ks, s)) != hipSuccess)
+    return hip_fail(err, "segment transpose");
+  const char* dabt = static_cast<const char*>(at(B_DABT));
+  if ((err = launch_kgemm(dt, false, at(B_DOT), ks, at(B_HT), ks, d, F, G, kbase, 0, gr->dw_down,
+                          gr->dws_down, N, s)) != hipSuccess ||
+      (err = launch_kgemm(dt, false, dabt, ks, at(B_XT), ks, F, d, G, kbase, 0, gr->dw_gate,
+                          gr->dws_gate, N, s)) != hipSuccess ||
+      (err = launch_kgemm(dt, false, dabt + static_cast<size_t>(F) * ks * eb, ks, at(B_XT), ks, F,
+                          d, G, kbase, 0, gr->dw_up, gr->dws_up, N, s)) != hipSuccess)
+    return hip_fail(err, "expert weight gradients");
+  if ((err = launch_transpose(dt, x, T, d, 0, at(B_XTF), b.Tp, 0, b.Tp, 0, 1, s)) != hipSuccess ||
+      (err = launch_transpose(dt, at(B_DR), T, b.Kr, 0, at(B_DRT), b.Tp, 0, b.Tp, 0, 1, s)) !=
+          hipSuccess ||
+      (err = launch_kgemm(dt, false, at(B_DRT), b.Tp, at(B_XTF), b.Tp, N, d, 1, nullptr, b.Tp,
+                          gr->dw_router, nullptr, 1, s)) != hipSuccess)
+    return hip_fail(err, "router weight gradient");
+  return MOE_OK;
+}
+
+moe_status moe_update_select_bias(int32_t N, const int32_t* counts, float rate,
+                                  float* select_bias, void* stream) {
+  g_last_error[0] = '\0';
+  if (N <= 0) return fail(MOE_ERR_INVALID_ARG, "N must be positive");
+  if (N > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
+  if (counts == nullptr || select_bias == nullptr) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  hipError_t err = launch_bias_update(counts, N, rate, select_bias, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "bias update kernel");
   return MOE_OK;
 }
 

@@ -198,6 +198,43 @@ hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
                           const float* prob_sum, float alpha, float* f_out,
                           float* P_out, float* aux_out, hipStream_t s);
 
+// ---------------------------------------------------------------- backward (backward.hip)
+// dtype: 1 = bf16, 0 = fp32 (the layer type of every operand but the fp32
+// ones named).
+// dst[b][c][col0 + r] = src[b][r][c] (r < R), 0 for R <= r < rpad.
+hipError_t launch_transpose(int dtype, const void* src, int R, int C, long src_batch, void* dst,
+                            long ldd, int col0, int rpad, long dst_batch, int batch,
+                            hipStream_t s);
+// kbase[g + 1] = kbase[g] + (offsets[g + 1] - offsets[g] rounded up to 64).
+hipError_t launch_kbase(const int32_t* offsets, int G, int32_t* kbase, hipStream_t s);
+// Group g's rows (source row gather[r] or r, times rscale[r] when given) into
+// columns kbase[g] .. of dst [C, ldd]; padding columns 0.  kmax: a multiple
+// of 64 at least kbase[G].
+hipError_t launch_segment_transpose(int dtype, const void* src, int C, int src_rows,
+                                    const int32_t* gather, const float* rscale,
+                                    const int32_t* offsets, const int32_t* kbase, int G,
+                                    long kmax, void* dst, long ldd, hipStream_t s);
+hipError_t launch_row_gate(const int32_t* inv_row, const float* gate, const int32_t* offsets,
+                           int T, int k, int N, int S, float* rgate, hipStream_t s);
+hipError_t launch_swiglu_bwd(int dtype, const void* G_, const void* U, const void* D,
+                             const float* rgate, const int32_t* offsets, int G, int F,
+                             long rows_max, void* H, void* dAB, float* dg_row, hipStream_t s);
+hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
+                             const float* gate, const int32_t* inv_row, const float* dg_row,
+                             const int32_t* counts, int T, int N, int k, float alpha,
+                             float aux_grad, int Kr, void* dr_pad, float* dr32, hipStream_t s);
+hipError_t launch_colsum(const float* dr32, int T, int N, float* out, hipStream_t s);
+hipError_t launch_dx_combine(int dtype, const void* dXp, const float* dxr, const int32_t* inv_row,
+                             const int32_t* offsets, int T, int N, int k, int S, int d, void* dx,
+                             hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, int N, float rate, float* bias,
+                              hipStream_t s);
+// C_g[m][n] = sum over kbase[g] <= j < kbase[g + 1] (or 0 <= j < k_all when
+// kbase is null) of a[m][j] b[n][j]; groups >= alt_from write to c_alt.
+hipError_t launch_kgemm(int dtype, bool out_f32, const void* a, long lda, const void* b, long ldb,
+                        int M, int N, int groups, const int32_t* kbase, int k_all, void* c,
+                        void* c_alt, int alt_from, hipStream_t s);
+
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);

@@ -466,6 +466,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
 int route_split(int T_, int d, int dtype) {
   const int nsteps = d * (dtype == 1 ? 2 : 4) / kRowBytes;
   const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
+  if (blocks <= 0) return 1;  // no tokens: nothing to split
   // about two workgroups per CU (a router workgroup's short reduction is
   // latency-bound, so a second one per CU hides the first's waits), at
   // least 4 K steps each

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("moe_layer_forward", "moe_route", "moe_balance_stats",
-                     "moe_workspace_size", "moe_status_string"):
+                     "moe_workspace_size", "moe_status_string", "moe_layer_backward",
+                     "moe_backward_workspace_size", "moe_update_select_bias"):
         assert required in names
 
 
@@ -186,3 +187,95 @@ def test_balance_stats_validation():
         moe.MOE_ERR_INVALID_ARG
     assert lib.moe_balance_stats(10, 600, 2, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None) == \
         moe.MOE_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------- backward
+def test_grads_struct_matches_the_header():
+    with open(HEADER) as fh:
+        hdr = fh.read()
+    body = re.search(r"typedef struct \{([^}]*)\} moe_grads;", hdr).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:void|float)\*\s+(\w+);", body)
+    assert fields == [f for f, _ in moe.MoEGrads._fields_]
+
+
+def test_backward_workspace_size():
+    lib = moe.lib()
+    cfg = moe.make_config(64, 128, 4, 2, 256, n_shared=1)
+    fwd = lib.moe_workspace_size(ctypes.byref(cfg))
+    bwd = lib.moe_backward_workspace_size(ctypes.byref(cfg))
+    # at least the transposed expert weights: 3 matrices of F x d per expert
+    assert bwd % 256 == 0 and bwd >= 3 * 5 * 256 * 128 * 2 and bwd > fwd
+    bad = moe.make_config(64, 96, 4, 2, 256)
+    assert lib.moe_backward_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_workspace_sizes_of_an_empty_batch():
+    """T = 0 is a valid size: both queries answer (and do not divide by the
+    number of token blocks)."""
+    lib = moe.lib()
+    cfg = moe.make_config(0, 128, 4, 2, 256, n_shared=1)
+    assert lib.moe_workspace_size(ctypes.byref(cfg)) > 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(cfg)) > 0
+
+
+def _grads(**over):
+    g = {n: FAKE for n, _ in moe.MoEGrads._fields_}
+    g.update(over)
+    return moe.MoEGrads(**g)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_grads", moe.MOE_ERR_INVALID_ARG),
+    ("null_dx", moe.MOE_ERR_INVALID_ARG),
+    ("null_dw_down", moe.MOE_ERR_INVALID_ARG),
+    ("misaligned_grad", moe.MOE_ERR_INVALID_ARG),
+    ("shared_grad_missing", moe.MOE_ERR_INVALID_ARG),
+    ("fp8_weights", moe.MOE_ERR_UNSUPPORTED),
+    ("null_dy", moe.MOE_ERR_INVALID_ARG),
+    ("small_workspace", moe.MOE_ERR_WORKSPACE),
+    ("forward_sized_workspace", moe.MOE_ERR_WORKSPACE),
+    ("bad_cfg", moe.MOE_ERR_UNSUPPORTED),
+])
+def test_backward_rejects_before_launch(case, expect):
+    lib = moe.lib()
+    cfg = moe.make_config(64, 128, 4, 2, 256)
+    w = _w()
+    g = _grads()
+    x = dy = FAKE
+    ws, ws_bytes = FAKE, 10 ** 12
+    if case == "null_grads":
+        g = None
+    elif case == "null_dx":
+        g = _grads(dx=None)
+    elif case == "null_dw_down":
+        g = _grads(dw_down=None)
+    elif case == "misaligned_grad":
+        g = _grads(dw_up=FAKE + 4)
+    elif case == "shared_grad_missing":
+        cfg = moe.make_config(64, 128, 4, 2, 256, n_shared=1)
+        w = _w(ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE)
+        g = _grads(dws_up=None)
+    elif case == "fp8_weights":
+        cfg.weight_format = moe.MOE_WEIGHTS_FP8_E4M3
+        w = _w(w_gate_scale=FAKE, w_up_scale=FAKE, w_down_scale=FAKE)
+    elif case == "null_dy":
+        dy = None
+    elif case == "small_workspace":
+        ws_bytes = 256
+    elif case == "forward_sized_workspace":
+        ws_bytes = lib.moe_workspace_size(ctypes.byref(cfg))
+    elif case == "bad_cfg":
+        cfg = moe.make_config(64, 96, 4, 2, 256)
+    st = lib.moe_layer_backward(ctypes.byref(cfg), x, ctypes.byref(w), dy, 0.01, 1.0,
+                                None if g is None else ctypes.byref(g), ws, ws_bytes, None)
+    assert st == expect
+    assert lib.moe_last_error()
+
+
+def test_select_bias_update_validation():
+    lib = moe.lib()
+    assert lib.moe_update_select_bias(0, FAKE, 0.1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_select_bias(4, None, 0.1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_select_bias(4, FAKE, 0.1, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_update_select_bias(513, FAKE, 0.1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
