@@ -6,6 +6,8 @@ are resident in HBM before timing starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-tokens N]
+    python bench.py --pass backward [--workload NAME] ...
+                                              # the layer backward, its own JSON line
     python bench.py --copy-probe MIB          # counter calibration copy
     python bench.py --summarize-profiles DIR --workload NAME
                                               # rocprofv3 output -> profiles/
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+                    help="backward: time moe_layer_backward instead (one JSON line of its own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0)
@@ -339,6 +343,175 @@ def summarize_profiles(d, workload):
     print(json.dumps(rec))
 
 
+BWD_CPU_MAX_F64_BYTES = 32 << 30   # oracle backward baseline only when its fp64 weights and
+                                   # weight gradients fit in this much host memory
+
+
+def backward_flops(shape):
+    """Algorithmic FLOPs of one backward call per stage (GEMM stages only) and in all."""
+    T, d, N, k, F, S = shape.T, shape.d, shape.N, shape.k, shape.F, shape.S
+    rows = T * k + S * T
+    stage = {"recompute": 4 * rows * d * F, "grad_h": 2 * rows * d * F,
+             "grad_x": 4 * rows * d * F + 2 * T * N * d, "grad_w": 6 * rows * d * F,
+             "grad_wr": 2 * T * N * d}
+    total = sum(stage.values()) + 2 * T * N * d  # + the recomputed router GEMM
+    return stage, total
+
+
+def cpu_backward_baseline(shape, inputs, dy, idx_all, n_tok):
+    """The oracle's backward (O10), as it stands, on the first n tokens (with the
+    GPU's choice of experts for them), grown until one call takes >= CPU_MIN_S."""
+    import numpy as np
+    import torch
+
+    import oracle
+    if shape.fp8 or shape.dtype != "bf16" and shape.dtype != "f32":
+        return None
+    wbytes = 3 * shape.N * shape.F * shape.d * 8
+    if 2 * wbytes > BWD_CPU_MAX_F64_BYTES:
+        return {"skipped": f"float64 weights and gradients would take {2 * wbytes / 2**30:.0f} GiB"}
+    host = {n: inputs[n].float().cpu().numpy().astype(np.float64) for n in
+            ("w_router", "w_gate", "w_up", "w_down") if inputs.get(n) is not None}
+    shared = None
+    if shape.S:
+        shared = tuple(inputs[n].float().cpu().numpy().astype(np.float64)
+                       for n in ("ws_gate", "ws_up", "ws_down"))
+    lb = inputs["logit_bias"].cpu().numpy() if inputs.get("logit_bias") is not None else None
+    sb = inputs["select_bias"].cpu().numpy() if inputs.get("select_bias") is not None else None
+    threads = torch.get_num_threads()
+
+    def run(n):
+        x = inputs["x"][:n].float().cpu().numpy().astype(np.float64)
+        g = dy[:n].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.moe_backward(x, host["w_router"], (host["w_gate"], host["w_up"], host["w_down"]),
+                            shape.k, g, logit_bias=lb, select_bias=sb, shared=shared,
+                            route_idx=idx_all[:n])
+        return time.perf_counter() - t0
+
+    n = min(n_tok, shape.T)
+    el = run(n)
+    while el < CPU_MIN_S and n < shape.T:
+        n = min(shape.T, max(n + 1, int(n * min(8.0, CPU_TARGET_S / max(el, 1e-3)))))
+        el = run(n)
+    return {"value": round(n / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle backward (float64 NumPy) on the first {n} of {shape.T} tokens, "
+                      f"one call, {el:.1f} s, the GPU's expert choice for those tokens"}
+
+
+def bench_backward(args, shape):
+    """One step = one moe_layer_backward call (routing and gate/up recomputed,
+    every gradient written) on resident inputs; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_router_amd as moe
+    from workloads import make_inputs
+
+    if shape.fp8:
+        print("bench.py: the backward takes expert weights in the layer dtype", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    print(f"[bench] backward, drawing inputs: {shape.describe()}", file=sys.stderr, flush=True)
+    inputs = make_inputs(shape, seed=args.seed, device=dev)
+    T, d, N, k, F, S = shape.T, shape.d, shape.N, shape.k, shape.F, shape.S
+    dt = shape.torch_dtype
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed * 7919 + 17)
+    dy = torch.randn((T, d), generator=gen, device=dev).to(dt)
+    cfg = moe.make_config(T, d, N, k, F, S, dt)
+    ws = moe.alloc_backward_workspace(cfg, dev)
+    g = {"dx": torch.empty((T, d), dtype=dt, device=dev),
+         "dw_router": torch.empty((N, d), dtype=dt, device=dev),
+         "dlogit_bias": torch.empty(N, dtype=torch.float32, device=dev),
+         "dw_gate": torch.empty((N, F, d), dtype=dt, device=dev),
+         "dw_up": torch.empty((N, F, d), dtype=dt, device=dev),
+         "dw_down": torch.empty((N, d, F), dtype=dt, device=dev)}
+    if S:
+        g.update(dws_gate=torch.empty((S, F, d), dtype=dt, device=dev),
+                 dws_up=torch.empty((S, F, d), dtype=dt, device=dev),
+                 dws_down=torch.empty((S, d, F), dtype=dt, device=dev))
+    stream = torch.cuda.current_stream()
+    nst = len(moe.BACKWARD_STAGES)
+
+    def step(events=None):
+        moe.moe_layer_backward(cfg, inputs["x"], inputs, dy, g, workspace=ws,
+                               stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = start.elapsed_time(end) / args.steps
+    # per-stage breakdown from K more steps with every marker (HIP events on
+    # the library's stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, name in enumerate(moe.BACKWARD_STAGES)}
+    sflops, total = backward_flops(shape)
+    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    dom = max(sflops, key=lambda n_: stage_ms[n_])
+    launches = {"recompute": 2, "grad_h": 1, "grad_x": 1, "grad_w": 3, "grad_wr": 1}[dom]
+    achieved = sflops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    kernels = {"recompute": "grouped GEMMs of the gate and up projections (2 launches)",
+               "grad_h": "grouped GEMM dy W_down + SwiGLU backward",
+               "grad_x": "grouped GEMM [dA dB][W_gate; W_up] + router backward + dx",
+               "grad_w": "weight-gradient grouped GEMMs, reduction per expert (3 launches)",
+               "grad_wr": "router weight gradient"}[dom]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernels,
+            "stage": dom, "avg_launch_ms": round(stage_ms[dom] / launches, 4),
+            "algorithmic_flops": sflops[dom] // launches,
+            "note": "stage time (HIP events on the library's stream) over its launches"}
+    result = {
+        "metric": "MoE layer backward tokens/sec; GEMM TFLOP/s as % of MI355X peak",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens and dy, N(0,0.02^2) random weights)",
+        "config": {"workload": shape.name + "_backward", "T": T, "d_model": d, "n_experts": N,
+                   "top_k": k, "d_ff": F, "n_shared": S, "parallelism": "single GPU"},
+        "layer": {"tflops": round(total / (ms_step * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(total / (ms_step * 1e-3) / 1e12 / peak, 4),
+                  "algorithmic_flops": total},
+        "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        fws = moe.alloc_workspace(cfg, dev)
+        y = torch.empty((T, d), dtype=dt, device=dev)
+        moe.moe_layer_forward(cfg, inputs["x"], inputs, y, workspace=fws, topk_idx=idx)
+        n = args.cpu_tokens or 32
+        print(f"[bench] CPU oracle backward from {n} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_backward_baseline(shape, inputs, dy, idx.cpu().numpy(), n)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -361,6 +534,9 @@ def main():
     from workloads import CONFIGS, make_inputs
 
     shape = CONFIGS[args.workload]
+    if args.pass_ == "backward":
+        bench_backward(args, shape)
+        return
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     print(f"[bench] drawing inputs: {shape.describe()}", file=sys.stderr, flush=True)

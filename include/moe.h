@@ -252,6 +252,29 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x,
                               float aux_grad, moe_grads* grads, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* Stage markers for moe_layer_backward_timed. */
+enum {
+  MOE_BSTAGE_ROUTE = 0,       /* routing and grouping, recomputed               */
+  MOE_BSTAGE_TRANSPOSE_W = 1, /* W_down, [W_gate | W_up] and W_r transposed      */
+  MOE_BSTAGE_RECOMPUTE = 2,   /* gate and up projections of the rows (2 GEMMs)   */
+  MOE_BSTAGE_GRAD_H = 3,      /* dy W_down (GEMM), then the SwiGLU backward      */
+  MOE_BSTAGE_GRAD_X = 4,      /* [dA dB] [W_gate; W_up] (GEMM), router, dx       */
+  MOE_BSTAGE_SEGMENTS = 5,    /* per-expert operands of the weight gradients     */
+  MOE_BSTAGE_GRAD_W = 6,      /* dW_down, dW_gate, dW_up (3 grouped GEMMs)       */
+  MOE_BSTAGE_GRAD_WR = 7,     /* dW_r                                            */
+  MOE_BSTAGE_COUNT = 8
+};
+
+/* moe_layer_backward that also records stage_events[i] (hipEvent_t, created
+ * by the caller) on `stream` before stage i and stage_events[MOE_BSTAGE_COUNT]
+ * after the last; NULL array or NULL entries are skipped, as for
+ * moe_layer_forward_timed.  With T = 0 no marker is recorded. */
+moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x,
+                                    const moe_weights* w, const void* dy,
+                                    float alpha, float aux_grad, moe_grads* grads,
+                                    void* workspace, size_t ws_bytes, void* stream,
+                                    void* const* stage_events);
+
 /* Auxiliary-loss-free balancing ("MoE inference: the call centre with 256
  * specialists ...", "The bare mechanism": a routing bias adjusted during
  * training keeps the experts balanced without a loss term).  The pages give

@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
-    "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "MOE_WEIGHTS_DTYPE", "MOE_WEIGHTS_FP8_E4M3", "STAGES",
+    "MOE_ERR_HIP", "MOE_F32", "MOE_BF16", "MOE_WEIGHTS_DTYPE", "MOE_WEIGHTS_FP8_E4M3", "STAGES", "BACKWARD_STAGES",
     "MoEError", "MoEConfig", "MoEWeights",
     "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
     "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
@@ -34,6 +34,8 @@ MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_FP8_E4M3 = 0, 1
 _SCALES = ("w_gate_scale", "w_up_scale", "w_down_scale", "ws_gate_scale", "ws_up_scale",
            "ws_down_scale")
 STAGES = ("route", "permute", "expert_up", "expert_down", "combine")
+BACKWARD_STAGES = ("route", "transpose_w", "recompute", "grad_h", "grad_x", "segments", "grad_w",
+                   "grad_wr")
 
 
 class MoEError(RuntimeError):
@@ -107,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_backward.argtypes = [cfgp, vp, wp, vp, ctypes.c_float, ctypes.c_float,
                                          ctypes.POINTER(MoEGrads), vp, sz, vp]
         L.moe_layer_backward.restype = ctypes.c_int
+        L.moe_layer_backward_timed.argtypes = L.moe_layer_backward.argtypes + [ctypes.POINTER(vp)]
+        L.moe_layer_backward_timed.restype = ctypes.c_int
         L.moe_update_select_bias.argtypes = [i32, vp, ctypes.c_float, vp, vp]
         L.moe_update_select_bias.restype = ctypes.c_int
         _LIB = L
@@ -254,21 +258,38 @@ _GRADS = ("dx", "dw_router", "dlogit_bias", "dw_gate", "dw_up", "dw_down", "dws_
           "dws_down")
 
 
+def _event_array(stage_events, n, stream):
+    if len(stage_events) != n + 1:
+        raise ValueError("need one event per stage plus one")
+    s = torch.cuda.current_stream() if stream is None else stream
+    for ev in stage_events:      # torch creates the HIP event on first record
+        if ev is not None and not ev.cuda_event:
+            ev.record(s)
+    return (ctypes.c_void_p * len(stage_events))(
+        *[None if ev is None else ev.cuda_event for ev in stage_events])
+
+
 def moe_layer_backward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]],
                        dy: torch.Tensor, grads: Dict[str, Optional[torch.Tensor]], *,
                        workspace: torch.Tensor, alpha: float = 0.01, aux_grad: float = 1.0,
-                       stream=None) -> None:
+                       stream=None,
+                       stage_events: Optional[Sequence[torch.cuda.Event]] = None) -> None:
     """Gradients of sum(y * dy) + aux_grad * aux into ``grads`` (keys dx,
     dw_router, dlogit_bias, dw_gate, dw_up, dw_down, dws_*); see
-    ``moe_layer_backward`` in include/moe.h."""
+    ``moe_layer_backward`` in include/moe.h.  ``stage_events``: as for
+    moe_layer_forward, one per BACKWARD_STAGES entry plus one."""
     dt = _TORCH_DTYPE[cfg.dtype]
     w = _weights(cfg, weights)
     g = MoEGrads(**{n: _ptr(grads.get(n), torch.float32 if n == "dlogit_bias" else dt, n)
                     for n in _GRADS})
-    _check(lib().moe_layer_backward(
-        ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(dy, dt, "dy"), float(alpha),
-        float(aux_grad), ctypes.byref(g), _ptr(workspace, None, "workspace"), workspace.numel(),
-        _stream(stream)))
+    args = (ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(dy, dt, "dy"),
+            float(alpha), float(aux_grad), ctypes.byref(g), _ptr(workspace, None, "workspace"),
+            workspace.numel(), _stream(stream))
+    if stage_events is None:
+        _check(lib().moe_layer_backward(*args))
+    else:
+        _check(lib().moe_layer_backward_timed(
+            *args, _event_array(stage_events, len(BACKWARD_STAGES), stream)))
 
 
 def moe_update_select_bias(counts: torch.Tensor, rate: float, select_bias: torch.Tensor,

@@ -556,9 +556,10 @@ size_t moe_backward_workspace_size(const moe_config* cfg) {
   return make_bwd_plan(*cfg).total;
 }
 
-moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_weights* w,
-                              const void* dy, float alpha, float aux_grad, moe_grads* gr,
-                              void* workspace, size_t ws_bytes, void* stream) {
+moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const moe_weights* w,
+                                    const void* dy, float alpha, float aux_grad, moe_grads* gr,
+                                    void* workspace, size_t ws_bytes, void* stream,
+                                    void* const* ev) {
   g_last_error[0] = '\0';
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
@@ -624,6 +625,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
   const int rows = static_cast<int>(b.rows);
 
   // routing and grouping, as in the forward
+  mark(ev, MOE_BSTAGE_ROUTE, s);
   err = launch_route(dt, x, w->w_router, w->logit_bias, w->select_bias, T, d, N, k, p.ksplit,
                      ws.route_partial, logits, ws.topk_idx, ws.topk_gate, ws.lrank, ws.blk_counts,
                      ws.blk_psum, s);
@@ -631,6 +633,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
   if ((st = run_permute(c, p, ws, nullptr, ws.topk_idx, s)) != MOE_OK) return st;
 
   // weights transposed: W_down -> [N, F, d]; [W_gate | W_up] -> [N, d, 2F]; W_r -> [d, Kr]
+  mark(ev, MOE_BSTAGE_TRANSPOSE_W, s);
   const long fd = static_cast<long>(F) * d;
   if ((err = launch_transpose(dt, w->w_down, d, F, fd, at(B_WDT), d, 0, d, fd, N, s)) != hipSuccess ||
       (err = launch_transpose(dt, w->w_gate, F, d, fd, at(B_WCAT), 2 * F, 0, F, 2 * fd, N, s)) !=
@@ -650,10 +653,12 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
     return hip_fail(err, "weight transpose");
 
   // G, U (recomputed) and D = dy W_down, all [rows, F]
+  mark(ev, MOE_BSTAGE_RECOMPUTE, s);
   GemmArgs ga = plain_pass(c, p, ws, true, x, ws.sorted_tok, T, w->w_gate, w->ws_gate, d, F, at(B_G));
   if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "G GEMM");
   ga = plain_pass(c, p, ws, true, x, ws.sorted_tok, T, w->w_up, w->ws_up, d, F, at(B_U));
   if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "U GEMM");
+  mark(ev, MOE_BSTAGE_GRAD_H, s);
   ga = plain_pass(c, p, ws, true, dy, ws.sorted_tok, T, at(B_WDT), S > 0 ? at(B_WDT_S) : nullptr,
                   d, F, at(B_D));
   if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "D GEMM");
@@ -664,6 +669,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
       (err = launch_swiglu_bwd(dt, at(B_G), at(B_U), at(B_D), rgate, ws.offsets, G, F, rows,
                                at(B_H), at(B_DAB), dg_row, s)) != hipSuccess)
     return hip_fail(err, "SwiGLU backward");
+  mark(ev, MOE_BSTAGE_GRAD_X, s);
   ga = plain_pass(c, p, ws, false, at(B_DAB), nullptr, rows, at(B_WCAT),
                   S > 0 ? at(B_WCAT_S) : nullptr, 2 * F, d, at(B_DXP));
   if ((err = launch_gemm(dt, false, p.down, ga, s)) != hipSuccess) return hip_fail(err, "dX GEMM");
@@ -683,6 +689,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
     return hip_fail(err, "dx");
 
   // weight gradients over each group's rows
+  mark(ev, MOE_BSTAGE_SEGMENTS, s);
   const long ks = b.kseg;
   if ((err = launch_kbase(ws.offsets, G, kbase, s)) != hipSuccess ||
       (err = launch_segment_transpose(dt, dy, d, T, ws.sorted_tok, rgate, ws.offsets, kbase, G, ks,
@@ -695,6 +702,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
                                       at(B_XT), ks, s)) != hipSuccess)
     return hip_fail(err, "segment transpose");
   const char* dabt = static_cast<const char*>(at(B_DABT));
+  mark(ev, MOE_BSTAGE_GRAD_W, s);
   if ((err = launch_kgemm(dt, false, at(B_DOT), ks, at(B_HT), ks, d, F, G, kbase, 0, gr->dw_down,
                           gr->dws_down, N, s)) != hipSuccess ||
       (err = launch_kgemm(dt, false, dabt, ks, at(B_XT), ks, F, d, G, kbase, 0, gr->dw_gate,
@@ -702,13 +710,22 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_we
       (err = launch_kgemm(dt, false, dabt + static_cast<size_t>(F) * ks * eb, ks, at(B_XT), ks, F,
                           d, G, kbase, 0, gr->dw_up, gr->dws_up, N, s)) != hipSuccess)
     return hip_fail(err, "expert weight gradients");
+  mark(ev, MOE_BSTAGE_GRAD_WR, s);
   if ((err = launch_transpose(dt, x, T, d, 0, at(B_XTF), b.Tp, 0, b.Tp, 0, 1, s)) != hipSuccess ||
       (err = launch_transpose(dt, at(B_DR), T, b.Kr, 0, at(B_DRT), b.Tp, 0, b.Tp, 0, 1, s)) !=
           hipSuccess ||
       (err = launch_kgemm(dt, false, at(B_DRT), b.Tp, at(B_XTF), b.Tp, N, d, 1, nullptr, b.Tp,
                           gr->dw_router, nullptr, 1, s)) != hipSuccess)
     return hip_fail(err, "router weight gradient");
+  mark(ev, MOE_BSTAGE_COUNT, s);
   return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const void* x, const moe_weights* w,
+                              const void* dy, float alpha, float aux_grad, moe_grads* gr,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return moe_layer_backward_timed(cfg, x, w, dy, alpha, aux_grad, gr, workspace, ws_bytes, stream,
+                                  nullptr);
 }
 
 moe_status moe_update_select_bias(int32_t N, const int32_t* counts, float rate,
