@@ -24,11 +24,13 @@
 //
 // The weight gradients reduce over rows.  Their operands are first transposed
 // into K-major segments, one per expert, each padded with zero columns to a
-// multiple of 64, so that one grouped GEMM (kgemm_kernel) with a reduction
+// multiple of 128, so that one grouped GEMM (kgemm_kernel) with a reduction
 // length per group computes every expert's gradient.
+#include "lds_ring.h"
 #include "vec.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -38,36 +40,58 @@ template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return b
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 
 // ------------------------------------------------------------- transposes
-// dst[b][c][col0 + r] = src[b][r][c] for r < R, 0 for R <= r < rpad; 64 x 64
-// tiles through LDS.  Grid (ceil(rpad / 64), ceil(C / 64), batch).
+// 64 x 64 tiles through LDS with 16-byte global accesses on both sides: a
+// thread moves V = 16 / sizeof(T) consecutive elements of a source row in,
+// and V consecutive elements of a destination row out.  Callers keep C,
+// col0 and ldd multiples of 64 (every row length here is), so no 16-byte
+// access straddles the end of a row.
+template <typename T> struct alignas(16) Chunk {
+  static constexpr int V = 16 / static_cast<int>(sizeof(T));
+  T v[V];
+};
+
+// dst[b][c][col0 + r] = src[b][r][c] for r < R, 0 for R <= r < rpad.
+// Grid (ceil(rpad / 64), C / 64, batch).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int R, int C,
                                                         long src_batch, T* __restrict__ dst,
                                                         long ldd, int col0, int rpad,
                                                         long dst_batch) {
-  __shared__ T tile[64][65];
+  constexpr int V = Chunk<T>::V, CPR = 64 / V, RPP = 256 / CPR;
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + V];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const T* s = src + blockIdx.z * src_batch;
   T* d = dst + blockIdx.z * dst_batch;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? s[static_cast<long>(r) * C + c] : T(0);
+  const int t = threadIdx.x, ch = (t % CPR) * V;
+  for (int i = t / CPR; i < 64; i += RPP) {
+    const int r = r0 + i, c = c0 + ch;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(s + static_cast<long>(r) * C + c);
+    *reinterpret_cast<u32x4*>(&tile[i][ch]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < rpad) d[static_cast<long>(c) * ldd + col0 + r] = tile[tx][i];
+  for (int j = t / CPR; j < 64; j += RPP) {
+    const int c = c0 + j, r = r0 + ch;
+    if (c >= C || r >= rpad) continue;
+    Chunk<T> out;
+#pragma unroll
+    for (int q = 0; q < V; ++q) out.v[q] = tile[ch + q][j];
+    T* o = d + static_cast<long>(c) * ldd + col0 + r;
+    if (r + V <= rpad) {
+      *reinterpret_cast<Chunk<T>*>(o) = out;
+    } else {
+      for (int q = 0; q < V && r + q < rpad; ++q) o[q] = out.v[q];
+    }
   }
 }
 
 // Segment starts: kbase[0] = 0, kbase[g + 1] = kbase[g] + (rows of group g
-// rounded up to 64).  One workgroup; groups <= 1024.
+// rounded up to 128).  One workgroup; groups <= 1024.
 __global__ __launch_bounds__(1024) void kbase_kernel(const int32_t* __restrict__ offsets, int G,
                                                      int32_t* __restrict__ kbase) {
   __shared__ int s[1024];
   const int t = threadIdx.x;
-  s[t] = t < G ? ((offsets[t + 1] - offsets[t] + 63) & ~63) : 0;
+  s[t] = t < G ? ((offsets[t + 1] - offsets[t] + 127) & ~127) : 0;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int add = t >= off ? s[t - off] : 0;
@@ -82,15 +106,16 @@ __global__ __launch_bounds__(1024) void kbase_kernel(const int32_t* __restrict__
 // Rows of every group, transposed into its segment: for group g's j-th row
 // (permuted row offsets[g] + j; source row gather[that] or that row itself),
 // dst[c][kbase[g] + j] = scale * src[source row][c], with scale = rscale[row]
-// (or 1); columns of the padding are 0.  Grid (kmax / 64, ceil(C / 64)); a
+// (or 1); columns of the padding are 0.  Grid (kmax / 64, C / 64); a
 // 64-column block lies inside one segment, so it finds its group by binary
-// search over kbase.
+// search over kbase.  16-byte accesses as in transpose_kernel.
 template <typename T>
 __global__ __launch_bounds__(256) void segment_transpose_kernel(
     const T* __restrict__ src, int C, int src_rows, const int32_t* __restrict__ gather,
     const float* __restrict__ rscale, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ kbase, int G, T* __restrict__ dst, long ldd) {
-  __shared__ T tile[64][65];
+  constexpr int V = Chunk<T>::V, CPR = 64 / V, RPP = 256 / CPR;
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + V];
   __shared__ int s_row[64];
   __shared__ float s_sc[64];
   const int k0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
@@ -103,9 +128,9 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(
   }
   const int j0 = k0 - kbase[lo];
   const int off = offsets[lo], cnt = offsets[lo + 1] - off;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int j = j0 + tid;
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int j = j0 + t;
     int row = -1;
     float sc = 0.f;
     if (j < cnt) {
@@ -113,21 +138,35 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(
       row = min(max(row, 0), src_rows - 1);
       sc = rscale != nullptr ? rscale[off + j] : 1.f;
     }
-    s_row[tid] = row;
-    s_sc[tid] = sc;
+    s_row[t] = row;
+    s_sc[t] = sc;
   }
   __syncthreads();
-  const int tx = tid & 63, ty = tid >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int row = s_row[i], c = c0 + tx;
-    float v = 0.f;
-    if (row >= 0 && c < C) v = s_sc[i] * to_f32<T>(src[static_cast<long>(row) * C + c]);
-    tile[i][tx] = from_f32<T>(v);
+  const int ch = (t % CPR) * V;
+  for (int i = t / CPR; i < 64; i += RPP) {
+    const int row = s_row[i], c = c0 + ch;
+    Chunk<T> v;
+    if (row >= 0 && c < C) {
+      v = *reinterpret_cast<const Chunk<T>*>(src + static_cast<long>(row) * C + c);
+      if (rscale != nullptr) {
+        const float sc = s_sc[i];
+#pragma unroll
+        for (int q = 0; q < V; ++q) v.v[q] = from_f32<T>(sc * to_f32<T>(v.v[q]));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < V; ++q) v.v[q] = T(0);
+    }
+    *reinterpret_cast<Chunk<T>*>(&tile[i][ch]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i;
-    if (c < C) dst[static_cast<long>(c) * ldd + k0 + tx] = tile[tx][i];
+  for (int j = t / CPR; j < 64; j += RPP) {
+    const int c = c0 + j;
+    if (c >= C) continue;
+    Chunk<T> out;
+#pragma unroll
+    for (int q = 0; q < V; ++q) out.v[q] = tile[ch + q][j];
+    *reinterpret_cast<Chunk<T>*>(dst + static_cast<long>(c) * ldd + k0 + ch) = out;
   }
 }
 
@@ -344,9 +383,14 @@ __global__ __launch_bounds__(512) void bias_update_kernel(const int32_t* __restr
 // Grouped GEMM with a reduction length per group (the weight gradients):
 //   C_g[m][n] = sum_{kk in [kbase[g], kbase[g+1])} A[m][kk] B[n][kk]
 // for m < M, n < N; A, B row-major with pitches lda, ldb (elements), every
-// segment a multiple of 64 elements (zero padded).  Groups >= alt_from write
-// to c_alt instead (shared experts).  128 x 128 tiles, 4 wavefronts of
-// 64 x 64, K steps of 128 bytes per row staged through two LDS buffers.
+// segment a multiple of 128 elements (zero padded), so the K steps of 128
+// bytes per row come in pairs.  N is a multiple of 64.  Groups >= alt_from
+// write to c_alt instead (shared experts).  128 x 128 tiles, 4 wavefronts of
+// 64 x 64.  Each thread stages its 16-byte slices of a K step in registers:
+// the loads of step s + 2 are issued while step s is multiplied out of one
+// LDS buffer and step s + 1 is stored into the other, and the barrier that
+// ends a step waits only for LDS traffic.  The epilogue stages each
+// wavefront's block through LDS and writes whole 16-byte row chunks.
 struct KgArgs {
   const void* a;
   const void* b;
@@ -359,15 +403,26 @@ struct KgArgs {
   int alt_from;
 };
 
+template <typename TO>
+constexpr int kgemm_lds_bytes() {
+  // two buffers of A and B tiles (128 rows x 128 bytes), or the epilogue's
+  // four staged 64 x 64 blocks, whichever is larger
+  return 4 * 128 * 128 > 4 * 64 * (64 * static_cast<int>(sizeof(TO)) + 16)
+             ? 4 * 128 * 128
+             : 4 * 64 * (64 * static_cast<int>(sizeof(TO)) + 16);
+}
+
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
-  __shared__ __attribute__((aligned(16))) char lds[2][2][128 * 128];
+  __shared__ __attribute__((aligned(16))) char lds_raw[kgemm_lds_bytes<TO>()];
+  // buffer P, operand X (0 = A, 1 = B)
+  auto buf = [&](int P, int X) { return lds_raw + (P * 2 + X) * 128 * 128; };
   const int grp = blockIdx.y;
   const int ntn = (g.N + 127) / 128;
   const int m0 = (blockIdx.x / ntn) * 128, n0 = (blockIdx.x % ntn) * 128;
   const long kb = g.kbase != nullptr ? g.kbase[grp] : 0;
   const long ke = g.kbase != nullptr ? g.kbase[grp + 1] : g.k_all;
-  const int nsteps = static_cast<int>((ke - kb) * static_cast<long>(sizeof(T)) / 128);
+  const int nsteps = static_cast<int>((ke - kb) * static_cast<long>(sizeof(T)) / 128);  // even
   const char* A = static_cast<const char*>(g.a) + kb * static_cast<long>(sizeof(T));
   const char* B = static_cast<const char*>(g.b) + kb * static_cast<long>(sizeof(T));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -384,19 +439,23 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
     pb[i] = B + br * g.ldb * static_cast<long>(sizeof(T)) + ch * 16;
     lo[i] = lds_swz(row, ch);
   }
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int s) {
+  u32x4 ra[2][4], rb[2][4];
+  // loads of step s (clamped into the segment) into register slot P
+  auto gload = [&](auto slot, int s) {
+    constexpr int P = decltype(slot)::value;
+    const long off = static_cast<long>(min(s, nsteps - 1)) * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + static_cast<long>(s) * 128);
-      rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + static_cast<long>(s) * 128);
+      ra[P][i] = *reinterpret_cast<const u32x4*>(pa[i] + off);
+      rb[P][i] = *reinterpret_cast<const u32x4*>(pb[i] + off);
     }
   };
-  auto sstore = [&](int st) {
+  auto sstore = [&](auto slot) {
+    constexpr int P = decltype(slot)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(lds[st][0] + lo[i]) = ra[i];
-      *reinterpret_cast<u32x4*>(lds[st][1] + lo[i]) = rb[i];
+      *reinterpret_cast<u32x4*>(buf(P, 0) + lo[i]) = ra[P][i];
+      *reinterpret_cast<u32x4*>(buf(P, 1) + lo[i]) = rb[P][i];
     }
   };
 
@@ -406,46 +465,78 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nsteps > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int st = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+  auto compute = [&](auto stage) {
+    constexpr int P = decltype(stage)::value;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         af[i] = *reinterpret_cast<const u32x4*>(
-            lds[st][0] + lds_swz(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
+            buf(P, 0) + lds_swz(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
         bf[i] = *reinterpret_cast<const u32x4*>(
-            lds[st][1] + lds_swz(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
+            buf(P, 1) + lds_swz(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::step(af[i], bf[j], acc[i][j]);
     }
-    if (s + 1 < nsteps) sstore(st ^ 1);
-    __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (nsteps > 0) {
+    gload(S0{}, 0);
+    gload(S1{}, 1);
+    sstore(S0{});
+    lds_barrier();
+    // (the scheduling barriers keep each step's loads ahead of its MFMAs:
+    // issued late, they would leave one step of latency hiding instead of two)
+    for (int s = 0; s < nsteps; s += 2) {
+      // step s from LDS buffer 0; step s + 1 waits in register slot 1
+      gload(S0{}, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(S0{});
+      sstore(S1{});
+      lds_barrier();
+      // step s + 1 from buffer 1; step s + 2 waits in slot 0
+      gload(S1{}, s + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(S1{});
+      sstore(S0{});
+      lds_barrier();
+    }
   }
 
-  const bool alt = grp >= g.alt_from;
-  TO* C = static_cast<TO*>(alt ? g.c_alt : g.c) +
-          static_cast<long>(alt ? grp - g.alt_from : grp) * g.M * g.N;
+  // epilogue: the wavefront's 64 x 64 block through LDS (rows of 64 outputs
+  // padded by 16 bytes), then 16-byte row chunks
+  constexpr int V = 16 / static_cast<int>(sizeof(TO));
+  constexpr int RB = 64 * static_cast<int>(sizeof(TO)) + 16;  // staged row bytes
+  char* stg = lds_raw + wave * 64 * RB;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (row < g.M && col < g.N) C[static_cast<long>(row) * g.N + col] = from_f32<TO>(acc[i][j][r]);
+        const int row = i * 16 + 4 * (lane >> 4) + r, col = j * 16 + (lane & 15);
+        *reinterpret_cast<TO*>(stg + row * RB + col * static_cast<int>(sizeof(TO))) =
+            from_f32<TO>(acc[i][j][r]);
       }
+  lds_barrier();
+  const bool alt = grp >= g.alt_from;
+  TO* C = static_cast<TO*>(alt ? g.c_alt : g.c) +
+          static_cast<long>(alt ? grp - g.alt_from : grp) * g.M * g.N;
+  constexpr int CPR = 64 / V;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int it = 0; it < 64 * CPR / 64; ++it) {
+    const int q = lane + 64 * it, row = q / CPR, c = (q % CPR) * V;
+    const int grow = m0 + wm * 64 + row, gcol = n0 + wn * 64 + c;
+    if (grow < g.M && gcol < g.N)
+      *reinterpret_cast<u32x4*>(C + static_cast<long>(grow) * g.N + gcol) =
+          *reinterpret_cast<const u32x4*>(stg + row * RB + c * static_cast<int>(sizeof(TO)));
+  }
 }
 
 }  // namespace
@@ -454,7 +545,7 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
 template <typename T>
 static hipError_t transpose_t(const void* src, int R, int C, long src_batch, void* dst, long ldd,
                               int col0, int rpad, long dst_batch, int batch, hipStream_t s) {
-  if (R <= 0 && rpad <= 0) return hipSuccess;
+  if (rpad <= 0 || C <= 0 || batch <= 0) return hipSuccess;
   const dim3 grid((rpad + 63) / 64, (C + 63) / 64, batch);
   hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, static_cast<const T*>(src), R, C,
                      src_batch, static_cast<T*>(dst), ldd, col0, rpad, dst_batch);

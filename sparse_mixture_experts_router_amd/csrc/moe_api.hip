@@ -322,9 +322,9 @@ struct BwdPlan {
   size_t off[B_COUNT];
   size_t total;
   long rows;  // T (k + S): every permuted row the forward may have
-  long kseg;  // columns of the transposed segments: sum over groups of rows rounded up to 64
-  int Kr;     // N rounded up to 64
-  int Tp;     // T rounded up to 64
+  long kseg;  // columns of the transposed segments: sum over groups of rows rounded up to 128
+  int Kr;     // N rounded up to 128
+  int Tp;     // T rounded up to 128
 };
 
 BwdPlan make_bwd_plan(const moe_config& c) {
@@ -334,9 +334,11 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   const size_t G = N + S;
   const size_t eb = c.dtype == MOE_BF16 ? 2 : 4;
   b.rows = static_cast<long>(T) * (c.top_k + c.n_shared);
-  b.kseg = (b.rows + 63 * static_cast<long>(G) + 63) / 64 * 64;
-  b.Kr = static_cast<int>((N + 63) / 64 * 64);
-  b.Tp = static_cast<int>((T + 63) / 64 * 64);
+  // the weight-gradient GEMM takes its reduction in pairs of 128-byte steps:
+  // segments, Kr and Tp are multiples of 128 elements
+  b.kseg = (b.rows + 127 * static_cast<long>(G) + 127) / 128 * 128;
+  b.Kr = static_cast<int>((N + 127) / 128 * 128);
+  b.Tp = static_cast<int>((T + 127) / 128 * 128);
   const size_t rows = b.rows, ks = b.kseg, Kr = b.Kr, Tp = b.Tp;
   size_t sz[B_COUNT];
   sz[B_LOGITS] = T * N * 4;

@@ -205,7 +205,7 @@ hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
 hipError_t launch_transpose(int dtype, const void* src, int R, int C, long src_batch, void* dst,
                             long ldd, int col0, int rpad, long dst_batch, int batch,
                             hipStream_t s);
-// kbase[g + 1] = kbase[g] + (offsets[g + 1] - offsets[g] rounded up to 64).
+// kbase[g + 1] = kbase[g] + (offsets[g + 1] - offsets[g] rounded up to 128).
 hipError_t launch_kbase(const int32_t* offsets, int G, int32_t* kbase, hipStream_t s);
 // Group g's rows (source row gather[r] or r, times rscale[r] when given) into
 // columns kbase[g] .. of dst [C, ldd]; padding columns 0.  kmax: a multiple
@@ -231,6 +231,7 @@ hipError_t launch_bias_update(const int32_t* counts, int N, float rate, float* b
                               hipStream_t s);
 // C_g[m][n] = sum over kbase[g] <= j < kbase[g + 1] (or 0 <= j < k_all when
 // kbase is null) of a[m][j] b[n][j]; groups >= alt_from write to c_alt.
+// Every segment (and k_all) a multiple of 128 elements; N a multiple of 64.
 hipError_t launch_kgemm(int dtype, bool out_f32, const void* a, long lda, const void* b, long ldb,
                         int M, int N, int groups, const int32_t* kbase, int k_all, void* c,
                         void* c_alt, int alt_from, hipStream_t s);
