@@ -318,14 +318,26 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
   }
 }
 
-// d logit_bias[e] = sum_t dr32[t, e], tokens in order.
+// d logit_bias[e] = sum_t dr32[t, e]: one workgroup per expert; thread i
+// adds tokens i, i + 256, ... (eight loads in flight), then the fixed-order
+// workgroup sum.
 __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ dr32, int n_tok,
                                                      int N, float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= N) return;
+  __shared__ float s_red[4];
+  const int e = blockIdx.x;
   float acc = 0.f;
-  for (int t = 0; t < n_tok; ++t) acc += dr32[static_cast<long>(t) * N + e];
-  out[e] = acc;
+  for (int t0 = threadIdx.x; t0 < n_tok; t0 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 256 * u;
+      v[u] = t < n_tok ? dr32[static_cast<long>(t) * N + e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  const float tot = block_sum256(acc, s_red);
+  if (threadIdx.x == 0) out[e] = tot;
 }
 
 // dx[t] = dxr[t] + the token's kept routed rows of dXp (slot order) + its
@@ -623,7 +635,7 @@ hipError_t launch_router_bwd(int dtype, const float* logits, const int32_t* idx,
 }
 
 hipError_t launch_colsum(const float* dr32, int T_, int N, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((N + 255) / 256), dim3(256), 0, s, dr32, T_, N, out);
+  hipLaunchKernelGGL(colsum_kernel, dim3(N), dim3(256), 0, s, dr32, T_, N, out);
   return hipGetLastError();
 }
 
