@@ -181,3 +181,37 @@ def test_select_bias_update_exact(N):
     torch.cuda.synchronize()
     got = b.cpu().numpy()
     assert np.array_equal(got, exp), f"max diff {np.max(np.abs(got - exp))}"
+
+
+def test_backward_full_size_mixtral_prefill():
+    """The bench's backward workload at full size (T = 4096, d = 4096, 8 experts,
+    top-2, d_ff = 14336, bf16), every gradient element against the oracle's
+    float64 backward (about 9 TFLOP of NumPy on the host, ~10-30 s)."""
+    import time
+    from workloads import CONFIGS
+    t0 = time.time()
+    shape = CONFIGS["mixtral_prefill"]
+    inputs = make_inputs(shape, seed=0, device="cuda")
+    dy = draw_dy(shape, 0)
+    fwd = forward_routing(shape, inputs)
+    say(f"[bwd-full] {shape.describe()}: forward done {time.time() - t0:.1f}s")
+    check_routing(shape, {}, fwd)
+    g = run_backward(shape, inputs, dy)
+    say(f"[bwd-full] backward done {time.time() - t0:.1f}s")
+    host = {n: inputs[n].float().cpu().numpy().astype(np.float64)
+            for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    ref = oracle.moe_backward(host["x"], host["w_router"],
+                              (host["w_gate"], host["w_up"], host["w_down"]), shape.k,
+                              dy.float().cpu().numpy().astype(np.float64), alpha=ALPHA,
+                              aux_grad=AUX_GRAD, route_idx=fwd["topk_idx"])
+    del host
+    say(f"[bwd-full] oracle done {time.time() - t0:.1f}s")
+    for n in GRADS:
+        got = g[n].float().cpu().numpy()
+        exp = ref[n]
+        assert np.all(np.isfinite(got)), f"{n}: non-finite values"
+        scale = float(np.max(np.abs(exp)))
+        err = float(np.max(np.abs(got - exp)))
+        say(f"[bwd-full]   {n:12s} max|ref| {scale:.3e} max|err| {err:.3e} ({err / scale:.2e})")
+        assert err <= 2.0 ** -6 * scale, f"{n}: error {err} > 2^-6 * {scale}"
+        del got
