@@ -398,7 +398,10 @@ __global__ __launch_bounds__(512) void bias_update_kernel(const int32_t* __restr
 // segment a multiple of 128 elements (zero padded), so the K steps of 128
 // bytes per row come in pairs.  N is a multiple of 64.  Groups >= alt_from
 // write to c_alt instead (shared experts).  128 x 128 tiles, 4 wavefronts of
-// 64 x 64.  Each thread stages its 16-byte slices of a K step in registers:
+// 64 x 64.  Rows of 128 bytes in LDS, their 16-byte chunks XOR-swizzled by
+// (row mod 8) ^ (row bit 3), so the 16 rows of a fragment read land in 16
+// different bank groups.  Each thread stages its 16-byte slices of a K step
+// in registers:
 // the loads of step s + 2 are issued while step s is multiplied out of one
 // LDS buffer and step s + 1 is stored into the other, and the barrier that
 // ends a step waits only for LDS traffic.  The epilogue stages each
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
     const long ar = min(m0 + row, g.M - 1), br = min(n0 + row, g.N - 1);
     pa[i] = A + ar * g.lda * static_cast<long>(sizeof(T)) + ch * 16;
     pb[i] = B + br * g.ldb * static_cast<long>(sizeof(T)) + ch * 16;
-    lo[i] = lds_swz(row, ch);
+    lo[i] = swz128(row, ch);
   }
   u32x4 ra[2][4], rb[2][4];
   // loads of step s (clamped into the segment) into register slot P
@@ -485,9 +488,9 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KgArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         af[i] = *reinterpret_cast<const u32x4*>(
-            buf(P, 0) + lds_swz(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
+            buf(P, 0) + swz128(wm * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
         bf[i] = *reinterpret_cast<const u32x4*>(
-            buf(P, 1) + lds_swz(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
+            buf(P, 1) + swz128(wn * 64 + i * 16 + (lane & 15), kk * 4 + (lane >> 4)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
