@@ -2,7 +2,9 @@
 
 One step = one whole layer forward (route, grouping, gate/up experts, down
 experts, combine) plus the balance statistics, on seeded synthetic inputs that
-are resident in HBM before timing starts.  Prints ONE JSON line.
+are resident in HBM before timing starts.  Prints ONE JSON line; its
+"backward" object times the layer's backward on the same inputs (bf16/fp32
+expert weights).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--cpu-tokens N]
@@ -55,6 +57,8 @@ def parse():
                     help="backward: time moe_layer_backward instead (one JSON line of its own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="forward line without its compact backward measurement")
     ap.add_argument("--cpu-tokens", type=int, default=0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (calibrates "
@@ -399,6 +403,57 @@ def cpu_backward_baseline(shape, inputs, dy, idx_all, n_tok):
                       f"one call, {el:.1f} s, the GPU's expert choice for those tokens"}
 
 
+def time_backward(shape, inputs, steps, warmup, seed=0):
+    """K timed moe_layer_backward calls on resident inputs (dy seeded): the
+    backward's ms per step, tokens/s and GEMM rate, for the forward's line."""
+    import torch
+
+    import sparse_mixture_experts_router_amd as moe
+    dev = inputs["x"].device
+    T, d, N, k, F, S = shape.T, shape.d, shape.N, shape.k, shape.F, shape.S
+    dt = shape.torch_dtype
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 7919 + 17)
+    dy = torch.randn((T, d), generator=gen, device=dev).to(dt)
+    cfg = moe.make_config(T, d, N, k, F, S, dt)
+    ws = moe.alloc_backward_workspace(cfg, dev)
+    g = {"dx": torch.empty((T, d), dtype=dt, device=dev),
+         "dw_router": torch.empty((N, d), dtype=dt, device=dev),
+         "dlogit_bias": torch.empty(N, dtype=torch.float32, device=dev),
+         "dw_gate": torch.empty((N, F, d), dtype=dt, device=dev),
+         "dw_up": torch.empty((N, F, d), dtype=dt, device=dev),
+         "dw_down": torch.empty((N, d, F), dtype=dt, device=dev)}
+    if S:
+        g.update(dws_gate=torch.empty((S, F, d), dtype=dt, device=dev),
+                 dws_up=torch.empty((S, F, d), dtype=dt, device=dev),
+                 dws_down=torch.empty((S, d, F), dtype=dt, device=dev))
+
+    def step():
+        moe.moe_layer_backward(cfg, inputs["x"], inputs, dy, g, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    _, total = backward_flops(shape)
+    peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    del ws, g
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "tflops": round(total / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(total / (ms * 1e-3) / 1e12 / peak, 4), "steps": steps,
+            "note": "moe_layer_backward on the same inputs (seeded dy): routing and gate/up "
+                    "recomputed, every gradient written; details: bench.py --pass backward"}
+
+
 def bench_backward(args, shape):
     """One step = one moe_layer_backward call (routing and gate/up recomputed,
     every gradient written) on resident inputs; prints one JSON line."""
@@ -687,6 +742,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if not args.no_backward and not shape.fp8:
+        print("[bench] backward of the same layer", file=sys.stderr, flush=True)
+        result["backward"] = time_backward(shape, inputs, min(args.steps, 20),
+                                           min(args.warmup, 3), args.seed)
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or DEFAULT_CPU_TOKENS.get(args.workload, 64)
         print(f"[bench] CPU oracle on {n} tokens", file=sys.stderr, flush=True)
