@@ -249,7 +249,7 @@ def summarize_profiles(d, workload):
     from workloads import CONFIGS
 
     shape = CONFIGS[workload]
-    cmds = profile_commands("gpurun_out/prof", workload)
+    cmds = profile_commands(d.rstrip("/"), workload)
     # kernel trace
     stats = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
@@ -315,7 +315,7 @@ def summarize_profiles(d, workload):
     md = [f"# Gate/up expert GEMM, {workload}: rocprofv3 summary", "",
           f"Workload: {shape.describe()}.", "",
           "Commands (run from the repository root; the summary below is",
-          f"`python3 bench.py --summarize-profiles gpurun_out/prof --workload {workload}`):", ""]
+          f"`python3 bench.py --summarize-profiles {d.rstrip('/')} --workload {workload}`):", ""]
     md += [f"    {c}" for c in cmds.values()]
     md += ["", "## Kernel trace (--kernel-trace --stats), this library's kernels", "",
            "| kernel | calls | avg us | min us | max us | % of GPU time |",
@@ -570,8 +570,8 @@ def bench_backward(args, shape):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards over tokens or experts, but no multi-GPU path is built)",
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards over tokens or experts, but no multi-GPU path exists)",
               file=sys.stderr)
         sys.exit(2)
 
