@@ -347,6 +347,23 @@ def summarize_profiles(d, workload):
     print(json.dumps(rec))
 
 
+def backward_traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"kgemm_backward_{workload}_traffic.json")
+
+
+def load_backward_traffic(workload):
+    """The committed rocprofv3 --pmc record of the weight-gradient GEMM
+    launches, or None (also when backward.hip changed since it was taken)."""
+    path = backward_traffic_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    with open(os.path.join(CSRC, "backward.hip"), "rb") as fh:
+        h = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return rec if rec.get("backward_source_sha256_16") == h else None
+
+
 BWD_CPU_MAX_F64_BYTES = 32 << 30   # oracle backward baseline only when its fp64 weights and
                                    # weight gradients fit in this much host memory
 
@@ -533,6 +550,18 @@ def bench_backward(args, shape):
             "stage": dom, "avg_launch_ms": round(stage_ms[dom] / launches, 4),
             "algorithmic_flops": sflops[dom] // launches,
             "note": "stage time (HIP events on the library's stream) over its launches"}
+    if dom == "grad_w":
+        # per launch: the two transposed operands (rows x (d + F)) in, one
+        # weight gradient per expert out
+        rows = T * k + S * T
+        b = shape.elem_bytes
+        roof["algorithmic_bytes"] = rows * (d + F) * b + (N + S) * d * F * b
+        rec = load_backward_traffic(shape.name)
+        if rec is not None:
+            roof["traffic"] = rec["hbm_bytes_per_launch_mean"]
+            roof["traffic_source"] = os.path.relpath(backward_traffic_path(shape.name), ROOT)
+            roof["traffic_over_algorithmic"] = round(
+                rec["hbm_bytes_per_launch_mean"] / roof["algorithmic_bytes"], 3)
     result = {
         "metric": "MoE layer backward tokens/sec; GEMM TFLOP/s as % of MI355X peak",
         "value": round(T / (ms_step * 1e-3), 1),
