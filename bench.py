@@ -1,7 +1,8 @@
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
 One step = one whole layer forward (route, grouping, gate/up experts, down
-experts, combine) plus the balance statistics, on seeded synthetic inputs that
+experts, combine, and the balance statistics written by the grouping step), on
+seeded synthetic inputs that
 are resident in HBM before timing starts.  Prints ONE JSON line; its
 "backward" object times the layer's backward on the same inputs (bf16/fp32
 expert weights).
@@ -641,10 +642,11 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(events=None):
+        # the forward also writes the balance statistics (f, P, aux) from its
+        # grouping step, so one call covers the whole path
         moe.moe_layer_forward(cfg, inputs["x"], inputs, y, workspace=ws, topk_idx=idx,
-                              topk_gate=gate, counts=counts, prob_sum=psum,
-                              stage_events=events)
-        moe.moe_balance_stats(T, N, k, counts, psum, 0.01, f, P, aux)
+                              topk_gate=gate, counts=counts, prob_sum=psum, f=f, P=P, aux=aux,
+                              alpha=0.01, stage_events=events)
 
     for _ in range(args.warmup):
         step()

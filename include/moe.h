@@ -130,13 +130,19 @@ typedef struct {
 
 /* Routing outputs (device pointers, caller-owned, written by the call).  For
  * moe_layer_forward every field is optional (NULL = not wanted); moe_route
- * requires topk_idx and topk_gate. */
+ * requires topk_idx and topk_gate.  f, P and aux are the balance statistics
+ * moe_balance_stats computes (bitwise the same values), produced inside the
+ * call's grouping step instead of a launch of their own. */
 typedef struct {
   float* logits;      /* [T, N]  r including logit_bias                       */
   int32_t* topk_idx;  /* [T, k]  chosen experts, slot 0 = largest key          */
   float* topk_gate;   /* [T, k]  softmax over the kept unbiased logits        */
   int32_t* counts;    /* [N]     (token, slot) assignments per routed expert  */
   float* prob_sum;    /* [N]     sum over tokens of softmax(r_t) over all N   */
+  float* f;           /* [N]     counts / (T k)                               */
+  float* P;           /* [N]     prob_sum / T                                 */
+  float* aux;         /* [2]     N sum_e f_e P_e, then balance_alpha times it */
+  float balance_alpha;/*         coefficient of aux[1] (not a pointer)        */
 } moe_routing;
 
 /* Stage markers for moe_layer_forward_timed. */

@@ -64,7 +64,8 @@ class MoEWeights(ctypes.Structure):
 class MoERouting(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
                 ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
-                ("prob_sum", ctypes.c_void_p)]
+                ("prob_sum", ctypes.c_void_p), ("f", ctypes.c_void_p), ("P", ctypes.c_void_p),
+                ("aux", ctypes.c_void_p), ("balance_alpha", ctypes.c_float)]
 
 
 class MoEGrads(ctypes.Structure):
@@ -184,20 +185,24 @@ def _weights(cfg: MoEConfig, w: Dict[str, Optional[torch.Tensor]], experts=True)
     return MoEWeights(**args)
 
 
-def _routing(logits=None, topk_idx=None, topk_gate=None, counts=None, prob_sum=None):
+def _routing(logits=None, topk_idx=None, topk_gate=None, counts=None, prob_sum=None, f=None,
+             P=None, aux=None, alpha=0.01):
     return MoERouting(_ptr(logits, torch.float32, "logits"),
                       _ptr(topk_idx, torch.int32, "topk_idx"),
                       _ptr(topk_gate, torch.float32, "topk_gate"),
                       _ptr(counts, torch.int32, "counts"),
-                      _ptr(prob_sum, torch.float32, "prob_sum"))
+                      _ptr(prob_sum, torch.float32, "prob_sum"),
+                      _ptr(f, torch.float32, "f"), _ptr(P, torch.float32, "P"),
+                      _ptr(aux, torch.float32, "aux"), float(alpha))
 
 
 def moe_route(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]], *,
               topk_idx: torch.Tensor, topk_gate: torch.Tensor, workspace: torch.Tensor,
-              logits=None, counts=None, prob_sum=None, stream=None) -> None:
+              logits=None, counts=None, prob_sum=None, f=None, P=None, aux=None, alpha=0.01,
+              stream=None) -> None:
     """Routing only; see ``moe_route`` in include/moe.h."""
     w = _weights(cfg, weights, experts=False)
-    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum)
+    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
     _check(lib().moe_route(ctypes.byref(cfg), _ptr(x, _TORCH_DTYPE[cfg.dtype], "x"),
                            ctypes.byref(w), ctypes.byref(r), _ptr(workspace, None, "workspace"),
                            workspace.numel(), _stream(stream)))
@@ -205,17 +210,20 @@ def moe_route(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch
 
 def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]],
                       y: torch.Tensor, *, workspace: torch.Tensor, logits=None, topk_idx=None,
-                      topk_gate=None, counts=None, prob_sum=None, stream=None,
+                      topk_gate=None, counts=None, prob_sum=None, f=None, P=None, aux=None,
+                      alpha=0.01, stream=None,
                       stage_events: Optional[Sequence[torch.cuda.Event]] = None) -> None:
     """Whole layer forward into ``y``; see ``moe_layer_forward`` in include/moe.h.
 
+    ``f``, ``P``, ``aux``: optional balance statistics written by the same
+    call (``aux`` = [N sum f P, alpha N sum f P]).
     ``stage_events``: optional list of len(STAGES) + 1 ``torch.cuda.Event``
     (enable_timing=True) or None, recorded before each stage and after the
     last; None entries are skipped.
     """
     dt = _TORCH_DTYPE[cfg.dtype]
     w = _weights(cfg, weights)
-    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum)
+    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
     args = (ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(y, dt, "y"),
             ctypes.byref(r), _ptr(workspace, None, "workspace"), workspace.numel(),
             _stream(stream))
@@ -304,7 +312,7 @@ class MoELayer:
     """Convenience holder: config, device weights and a workspace sized once.
 
     ``forward(x)`` allocates the outputs with torch (device memory only) and
-    calls ``moe_layer_forward`` followed by ``moe_balance_stats``.
+    calls ``moe_layer_forward``, which also writes the balance statistics.
     """
 
     def __init__(self, weights: Dict[str, Optional[torch.Tensor]], top_k: int,
@@ -344,7 +352,6 @@ class MoELayer:
         moe_layer_forward(cfg, x, self.weights, out["y"], workspace=self._ws,
                           logits=out["logits"], topk_idx=out["topk_idx"],
                           topk_gate=out["topk_gate"], counts=out["counts"],
-                          prob_sum=out["prob_sum"])
-        moe_balance_stats(T, self.N, self.k, out["counts"], out["prob_sum"], self.alpha,
-                          out["f"], out["P"], out["aux"])
+                          prob_sum=out["prob_sum"], f=out["f"], P=out["P"], aux=out["aux"],
+                          alpha=self.alpha)
         return out

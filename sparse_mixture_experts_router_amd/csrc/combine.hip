@@ -12,6 +12,7 @@
 //   f_e = counts_e / (T k), P_e = prob_sum_e / T, loss = alpha N sum_e f_e P_e.
 #include "mfma.h"
 #include "vec.h"
+#include "balance.h"
 
 namespace moe {
 namespace {
@@ -79,30 +80,8 @@ __global__ __launch_bounds__(256) void balance_kernel(int n_tok, int N, int k,
                                                       float* __restrict__ P_out,
                                                       float* __restrict__ aux_out) {
   __shared__ float s_part[256];
-  float part = 0.f;
-  for (int e = threadIdx.x; e < N; e += 256) {
-    float f = 0.f, p = 0.f;
-    if (n_tok > 0) {
-      f = static_cast<float>(counts[e]) / (static_cast<float>(n_tok) * static_cast<float>(k));
-      p = prob_sum[e] / static_cast<float>(n_tok);
-    }
-    f_out[e] = f;
-    P_out[e] = p;
-    part = fmaf(f, p, part);
-  }
-  s_part[threadIdx.x] = part;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) s_part[threadIdx.x] += s_part[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const float raw = static_cast<float>(N) * s_part[0];
-    aux_out[0] = raw;
-    aux_out[1] = alpha * raw;
-  }
+  balance_block(n_tok, N, k, counts, prob_sum, alpha, f_out, P_out, aux_out, s_part);
 }
-
 
 }  // namespace
 

@@ -275,8 +275,10 @@ moe_status run_scan(const moe_config& c, const Plan& p, const Workspace& ws, moe
                     const ScatterSpec& sc, hipStream_t s) {
   hipError_t err = launch_scan(ws.blk_counts, ws.blk_psum, c.T, c.n_experts, c.top_k, c.n_shared,
                                c.capacity, p.bm_up, p.cap_up, p.bm_down, p.cap_down, p.split,
-                               item_spec(p, ws),
-                               sc, ws.blk_base,
+                               item_spec(p, ws), sc,
+                               out ? BalanceSpec{out->f, out->P, out->aux, out->balance_alpha}
+                                   : BalanceSpec{nullptr, nullptr, nullptr, 0.f},
+                               ws.blk_base,
                                ws.counts,
                                ws.prob_sum, out ? out->counts : nullptr,
                                out ? out->prob_sum : nullptr, ws.offsets, ws.tiles_up,
@@ -439,7 +441,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
   const Workspace ws = carve(p, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = run_route(c, p, ws, x, *w, out, out->topk_idx, out->topk_gate, s)) != MOE_OK) return st;
-  if (out->counts != nullptr || out->prob_sum != nullptr) {
+  if (out->counts != nullptr || out->prob_sum != nullptr || out->f != nullptr ||
+      out->P != nullptr || out->aux != nullptr) {
     if ((st = run_scan(c, p, ws, out, ScatterSpec{}, s)) != MOE_OK) return st;
   }
   return MOE_OK;

@@ -90,6 +90,15 @@ struct ScatterSpec {
 };
 constexpr long kScanScatterMaxRows = 2048;  // two rows per scan thread
 
+// Balance statistics the scan kernel writes as well (each pointer may be
+// null): f [N], P [N], aux [2] = [N sum f P, alpha N sum f P].
+struct BalanceSpec {
+  float* f;
+  float* P;
+  float* aux;
+  float alpha;
+};
+
 struct SplitSpec {
   int parts;      // host split of every row (grouped_gemm.hip), or <= 1
   int tail_nnt;   // column tiles of the down pass (0: no tail split)
@@ -100,7 +109,7 @@ struct SplitSpec {
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T,
                        int N, int k, int S, int capacity, int bm_up, int cap_up, int bm_down,
                        int cap_down, const SplitSpec& split, const ItemSpec& items,
-                       const ScatterSpec& sc, int32_t* blk_base,
+                       const ScatterSpec& sc, const BalanceSpec& bal, int32_t* blk_base,
                        int32_t* counts, float* prob_sum, int32_t* user_counts,
                        float* user_prob_sum, int32_t* offsets, int2* tiles_up,
                        int2* tiles_down, int32_t* ntiles, hipStream_t s);

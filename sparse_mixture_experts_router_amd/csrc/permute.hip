@@ -17,6 +17,7 @@
 // so each expert's rows are contiguous and ordered by token.  The scan kernel
 // also writes the tile lists of the two grouped GEMMs (one entry per BM-row
 // tile of each non-empty expert), so tile scheduling needs no host round trip.
+#include "balance.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void items_kernel(ItemSpec is, int ng) {
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t* __restrict__ blk_counts, const float* __restrict__ blk_psum, int n_tok, int N,
     int k, int S, int capacity, int bm_up, int cap_up, int bm_down, int cap_down, SplitSpec split,
-    ItemSpec ispec, ScatterSpec sc,
+    ItemSpec ispec, ScatterSpec sc, BalanceSpec bal,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts, float* __restrict__ prob_sum,
     int32_t* __restrict__ user_counts, float* __restrict__ user_prob_sum,
     int32_t* __restrict__ offsets, int2* __restrict__ tiles_up, int2* __restrict__ tiles_down,
@@ -284,6 +285,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       scatter_row(i, sc.topk_idx, sc.lrank, blk_base, offsets, n_tok, N, k, S, capacity,
                   sc.sorted_tok, sc.inv_row);
   }
+  // balance statistics from the totals above (counts and prob_sum are
+  // complete and visible to the workgroup since the barriers above)
+  if (bal.f != nullptr || bal.P != nullptr || bal.aux != nullptr) {
+    __shared__ float s_bal[256];
+    balance_block(n_tok, N, k, counts, prob_sum, bal.alpha, bal.f, bal.P, bal.aux, s_bal);
+  }
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
@@ -299,11 +306,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 hipError_t launch_scan(const int32_t* blk_counts, const float* blk_psum, int T_, int N, int k,
                        int S, int capacity, int bm_up, int cap_up, int bm_down, int cap_down,
                        const SplitSpec& split, const ItemSpec& items, const ScatterSpec& sc,
-                       int32_t* blk_base, int32_t* counts, float* prob_sum,
+                       const BalanceSpec& bal, int32_t* blk_base, int32_t* counts, float* prob_sum,
                        int32_t* user_counts, float* user_prob_sum, int32_t* offsets,
                        int2* tiles_up, int2* tiles_down, int32_t* ntiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk_counts, blk_psum, T_, N,
-                     k, S, capacity, bm_up, cap_up, bm_down, cap_down, split, items, sc, blk_base,
+                     k, S, capacity, bm_up, cap_up, bm_down, cap_down, split, items, sc, bal,
+                     blk_base,
                      counts, prob_sum,
                      user_counts, user_prob_sum, offsets, tiles_up, tiles_down, ntiles);
   return hipGetLastError();

@@ -169,6 +169,15 @@ def test_forward_rejects_before_launch(case, expect):
         assert moe.lib().moe_last_error()
 
 
+def test_routing_struct_matches_the_header():
+    with open(HEADER) as fh:
+        hdr = fh.read()
+    body = re.search(r"typedef struct \{([^}]*)\} moe_routing;", hdr).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(?:float|int32_t)\*?\s+(\w+);", body)
+    assert fields == [f for f, _ in moe.MoERouting._fields_]
+
+
 def test_route_requires_outputs():
     lib = moe.lib()
     cfg = moe.make_config(64, 128, 4, 2, 256)

@@ -224,6 +224,39 @@ def test_route_entry_point_matches_forward():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shape", [
+    reduced(CONFIGS["mixtral_decode"], T=24, d=256, F=256),
+    reduced(CONFIGS["qwen3_skew"], T=1000, d=256, F=128, N=128),
+    MoEShape("n512", T=70, d=128, N=512, k=4, F=64),
+], ids=["decode", "qwen_skew", "N512"])
+def test_balance_outputs_of_the_forward(shape):
+    """f, P and aux written by the forward's grouping step are bitwise the
+    values moe_balance_stats computes from the same counts and sums, and the
+    same again from moe_route."""
+    inputs = make_inputs(shape, seed=4, device="cuda")
+    out = run_layer(shape, inputs, alpha=0.03)
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S)
+    ws = moe.alloc_workspace(cfg)
+    N = shape.N
+    f, P = (torch.empty(N, device="cuda") for _ in range(2))
+    aux = torch.empty(2, device="cuda")
+    y = torch.empty_like(inputs["x"])
+    moe.moe_layer_forward(cfg, inputs["x"], inputs, y, workspace=ws, f=f, P=P, aux=aux,
+                          alpha=0.03)
+    torch.cuda.synchronize()
+    for a, b in ((f, out["f"]), (P, out["P"]), (aux, out["aux"])):
+        assert torch.equal(a, b)
+    idx = torch.empty_like(out["topk_idx"])
+    gate = torch.empty_like(out["topk_gate"])
+    f2, P2 = (torch.empty(N, device="cuda") for _ in range(2))
+    aux2 = torch.empty(2, device="cuda")
+    moe.moe_route(cfg, inputs["x"], inputs, topk_idx=idx, topk_gate=gate, workspace=ws, f=f2,
+                  P=P2, aux=aux2, alpha=0.03)
+    torch.cuda.synchronize()
+    for a, b in ((f2, out["f"]), (P2, out["P"]), (aux2, out["aux"])):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "qwen3_skew",
                                   "deepseek_v3"])
 def test_full_size_sampled(name):
