@@ -1,0 +1,51 @@
+"""Seeded random layer shapes inside the supported envelope (needs an MI355X):
+the forward element by element against the oracle (full_parity), and for some
+of them the backward (check_backward).  The shapes mix ragged T, d and F that
+are multiples of 64 but not of 128 or 256, odd expert counts, k up to 8,
+shared experts, capacities that drop, both biases and both dtypes, so that
+every GEMM path (32-row decode tiles, register-staged tiles, 128- and
+256-row large tiles) meets sizes the hand-picked cases do not.
+"""
+import numpy as np
+import pytest
+
+from gpu_harness import full_parity, say
+from test_gpu_backward import check_backward
+from workloads import MoEShape
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(seed=2024, n=14):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "f32" if i % 5 == 4 else "bf16"
+        N = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 33, 64]))
+        k = int(rng.integers(1, min(N, 8) + 1))
+        d = int(rng.choice([64, 128, 192, 320, 512]))
+        F = int(rng.choice([64, 128, 192, 320, 576]))
+        S = int(rng.choice([0, 0, 1, 2]))
+        T = int(rng.choice([1, 5, 63, 64, 65, 130, 257, 700, 1100]))
+        cap = 0
+        if N > 1 and rng.random() < 0.3:
+            cap = max(1, int(T * k / N * 0.7))
+        shape = MoEShape(f"rand{i}", T=T, d=d, N=N, k=k, F=F, S=S, dtype=dtype,
+                         select_bias=bool(rng.random() < 0.4),
+                         zipf_s=float(rng.choice([0.0, 0.0, 1.2])))
+        out.append((shape, cap))
+    return out
+
+
+SHAPES = _shapes()
+
+
+@pytest.mark.parametrize("shape,cap", SHAPES, ids=[s.name for s, _ in SHAPES])
+def test_random_shape_forward(shape, cap):
+    full_parity(shape, seed=100 + int(shape.name[4:]), capacity=cap, label=shape.name)
+
+
+@pytest.mark.parametrize("shape,cap", SHAPES[::2], ids=[s.name for s, _ in SHAPES[::2]])
+def test_random_shape_backward(shape, cap):
+    say(f"[rand-bwd] {shape.name} capacity={cap}")
+    check_backward(shape, seed=3, capacity=cap, label=shape.name)
