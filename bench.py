@@ -193,7 +193,7 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
 
 def profile_commands(d, workload):
     """The rocprofv3 runs that --summarize-profiles reads (d: their output root)."""
-    run = f"python3 bench.py --workload {workload} --no-cpu-baseline"
+    run = f"python3 bench.py --workload {workload} --no-cpu-baseline --no-backward"
     return {
         "trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- {run} "
                   f"--steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} > {d}/trace_bench.json"),
