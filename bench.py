@@ -214,9 +214,28 @@ def profile_commands(d, workload):
     }
 
 
+def gemm_template_args(name):
+    """(kernel, [template arguments]) of a grouped GEMM kernel name, or None."""
+    m = re.search(r"(expert_gemm_kernel|grouped_gemm_kernel)<([^>]*)>", name)
+    return None if m is None else (m.group(1), [a.strip() for a in m.group(2).split(",")])
+
+
 def is_up_gemm(name):
-    """The gate/up launch: a grouped GEMM kernel instantiated with GATED = true."""
-    return re.search(r"gemm\w*_kernel<", name) is not None and ("<true," in name or ", true," in name)
+    """The gate/up launch: a grouped GEMM kernel instantiated with GATED = true
+    (expert_gemm_kernel's first template argument, grouped_gemm_kernel's third)."""
+    ka = gemm_template_args(name)
+    if ka is None:
+        return False
+    kern, args = ka
+    i = 0 if kern == "expert_gemm_kernel" else 2
+    return len(args) > i and args[i] == "true"
+
+
+def is_grad_w_gemm(name):
+    """The weight-gradient launches: expert_gemm_kernel with KMAJ (its sixth
+    template argument) = true."""
+    ka = gemm_template_args(name)
+    return ka is not None and ka[0] == "expert_gemm_kernel" and len(ka[1]) == 6 and ka[1][5] == "true"
 
 
 def short_name(name):
@@ -354,21 +373,175 @@ def summarize_profiles(d, workload):
     print(json.dumps(rec))
 
 
+def backward_profile_commands(d, workload):
+    """The rocprofv3 runs that --summarize-profiles --pass backward reads."""
+    run = f"python3 bench.py --pass backward --workload {workload} --no-cpu-baseline"
+    return {
+        "trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/btrace -o run -- "
+                  f"{run} --steps 10 --warmup 2 > {d}/btrace_bench.json"),
+        "fetch": (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/bfetch -o run -- {run} "
+                  f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
+        "write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/bwrite -o run -- {run} "
+                  f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
+        "copy_fetch": (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o run -- "
+                       f"python3 bench.py --copy-probe {COPY_MIB}"),
+        "copy_write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o run -- "
+                       f"python3 bench.py --copy-probe {COPY_MIB}"),
+    }
+
+
+def read_counters_ordered(path, counter, keep):
+    """Values (KiB) of one counter for the dispatches whose kernel name passes
+    keep(), in dispatch order."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and keep(short_name(r["Kernel_Name"])):
+                    key = int(r["Dispatch_Id"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def summarize_backward_profiles(d, workload):
+    """Write profiles/grad_w_gemm_backward_<workload>.md and the _traffic.json
+    that the backward bench reads, from backward_profile_commands()' runs."""
+    import csv
+    import glob
+
+    import numpy as np
+
+    from workloads import CONFIGS
+
+    shape = CONFIGS[workload]
+    cmds = backward_profile_commands(d.rstrip("/"), workload)
+    stats = glob.glob(os.path.join(d, "btrace", "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {d}/btrace")
+    rows = []
+    with open(stats[0]) as fh:
+        for r in csv.DictReader(fh):
+            if "moe::" in r["Name"]:
+                rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]),
+                             float(r["MinNs"]), float(r["MaxNs"]), float(r["Percentage"])))
+    gw = [r for r in rows if is_grad_w_gemm(r[0])]
+    if len(gw) != 1:
+        raise SystemExit(f"expected one weight-gradient GEMM kernel in the trace, found {len(gw)}")
+    gw = gw[0]
+    bench = None
+    bpath = os.path.join(d, "btrace_bench.json")
+    if os.path.exists(bpath):
+        with open(bpath) as fh:
+            lines = [ln for ln in fh if ln.startswith("{")]
+        bench = json.loads(lines[-1]) if lines else None
+    copy_bytes = COPY_MIB * (1 << 20)
+
+    def copy_scale(sub, counter):
+        vals = [v for n, vs in read_counters(os.path.join(d, sub), counter).items()
+                if "copyBuffer" in n for v in vs]
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {sub}")
+        return copy_bytes / (float(np.median(vals)) * 1024.0)
+
+    fscale = copy_scale("copy_fetch", "FETCH_SIZE")
+    wscale = copy_scale("copy_write", "WRITE_SIZE")
+    roles = ("dW_down", "dW_gate", "dW_up")  # launch order inside a backward call
+
+    def by_role(sub, counter):
+        vals = read_counters_ordered(os.path.join(d, sub), counter, is_grad_w_gemm)
+        if not vals or len(vals) % 3:
+            raise SystemExit(f"{sub}: {len(vals)} weight-gradient dispatches, not 3 per call")
+        return [float(np.mean(vals[i::3])) for i in range(3)], len(vals)
+
+    fk, nf = by_role("bfetch", "FETCH_SIZE")
+    wk, nw = by_role("bwrite", "WRITE_SIZE")
+    hbm = [fk[i] * 1024.0 * fscale + wk[i] * 1024.0 * wscale for i in range(3)]
+    roof = bench["roofline"] if bench else {}
+    alg = roof.get("algorithmic_bytes")
+    rec = {
+        "workload": workload,
+        "kernel": gw[0] + " (" + ", ".join(roles) + ")",
+        "backward_source_sha256_16": backward_source_hash(),
+        "fetch_kib_per_launch": [round(v, 1) for v in fk],
+        "write_kib_per_launch": [round(v, 1) for v in wk],
+        "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+        "hbm_bytes_per_launch": [int(round(v)) for v in hbm],
+        "hbm_bytes_per_launch_mean": int(round(float(np.mean(hbm)))),
+        "algorithmic_bytes_per_launch": alg,
+        "dispatches": {"fetch": nf, "write": nw},
+        "commands": {k: v for k, v in cmds.items() if k != "trace"},
+    }
+    with open(backward_traffic_path(workload), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    md = [f"# Weight-gradient GEMMs of the layer backward, {workload}: rocprofv3 summary", "",
+          f"Workload: {shape.describe()}; one `moe_layer_backward` per step (routing and "
+          "gate/up recomputed, every gradient written).", "",
+          "Commands (run from the repository root; the summary below is",
+          f"`python3 bench.py --summarize-profiles {d.rstrip('/')} --workload {workload} "
+          "--pass backward`):", ""]
+    md += [f"    {c}" for c in cmds.values()]
+    md += ["", "## Kernel trace (--kernel-trace --stats), this library's kernels", "",
+           "| kernel | calls | avg us | min us | max us | % of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    md += [f"| `{n}` | {c} | {a / 1e3:.1f} | {lo / 1e3:.1f} | {hi / 1e3:.1f} | {p:.2f} |"
+           for n, c, a, lo, hi, p in rows]
+    md += ["", f"`{gw[0]}` is the three weight-gradient launches of every call "
+           f"({', '.join(roles)}); the trace averages them ({gw[2] / 1e3:.1f} us)."]
+    if bench:
+        st = ", ".join(f"{k} {v:.3f}" for k, v in bench["stages_ms"].items())
+        md += ["", f"The bench line of the traced run: {bench['ms_per_step']} ms per backward step, "
+               f"{bench['value']} tokens/s. Stages (ms, HIP events on the library's stream, "
+               f"markers included): {st}. Slowest GEMM stage {roof.get('stage')}: "
+               f"{roof.get('avg_launch_ms', 0) * 1e3:.1f} us per launch, {roof.get('achieved')} "
+               f"TFLOP/s = {roof.get('frac', 0):.3f} of peak."]
+    md += ["", "## HBM traffic of the weight-gradient launches (--pmc)", "",
+           "FETCH_SIZE and WRITE_SIZE are in KiB per dispatch (means over the calls of the",
+           f"runs: {nf // 3} and {nw // 3}). Each is scaled by the factor that makes a plain "
+           f"{COPY_MIB} MiB device", f"copy read and write {COPY_MIB} MiB (fetch "
+           f"{fscale:.3f}, write {wscale:.3f}).", "",
+           "| launch | FETCH_SIZE (KiB) | HBM read (GB) | WRITE_SIZE (KiB) | HBM written (GB) |",
+           "|---|---:|---:|---:|---:|"]
+    md += [f"| {roles[i]} | {fk[i]:,.0f} | {fk[i] * 1024 * fscale / 1e9:.2f} | {wk[i]:,.0f} | "
+           f"{wk[i] * 1024 * wscale / 1e9:.2f} |" for i in range(3)]
+    if alg:
+        md += ["", f"Algorithmic bytes per launch (both transposed operands in, one weight "
+               f"gradient per expert out): {alg / 1e9:.2f} GB; measured / algorithmic "
+               f"{float(np.mean(hbm)) / alg:.2f} (mean over the three launches)."]
+    with open(os.path.join(ROOT, "profiles", f"grad_w_gemm_backward_{workload}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps(rec))
+
+
 def backward_traffic_path(workload):
-    return os.path.join(ROOT, "profiles", f"kgemm_backward_{workload}_traffic.json")
+    return os.path.join(ROOT, "profiles", f"grad_w_gemm_backward_{workload}_traffic.json")
+
+
+def backward_source_hash():
+    """Hash of the sources of the weight-gradient launches (the backward's
+    host code and the large-tile GEMM it runs them on)."""
+    h = hashlib.sha256()
+    for name in ("backward.hip",) + GEMM_SRCS:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def load_backward_traffic(workload):
     """The committed rocprofv3 --pmc record of the weight-gradient GEMM
-    launches, or None (also when backward.hip changed since it was taken)."""
+    launches, or None (also when their sources changed since it was taken)."""
     path = backward_traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    with open(os.path.join(CSRC, "backward.hip"), "rb") as fh:
-        h = hashlib.sha256(fh.read()).hexdigest()[:16]
-    return rec if rec.get("backward_source_sha256_16") == h else None
+    return rec if rec.get("backward_source_sha256_16") == backward_source_hash() else None
 
 
 BWD_CPU_MAX_F64_BYTES = 32 << 30   # oracle backward baseline only when its fp64 weights and
@@ -615,7 +788,10 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, args.workload)
+        if args.pass_ == "backward":
+            summarize_backward_profiles(args.summarize_profiles, args.workload)
+        else:
+            summarize_profiles(args.summarize_profiles, args.workload)
         return
 
     import numpy as np

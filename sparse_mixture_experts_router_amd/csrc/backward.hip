@@ -667,6 +667,22 @@ hipError_t launch_kgemm(int dtype, bool out_f32, const void* a, long lda, const 
                         int M, int N, int groups, const int32_t* kbase, int k_all, void* c,
                         void* c_alt, int alt_from, hipStream_t s) {
   if (M <= 0 || N <= 0 || groups <= 0) return hipSuccess;
+  if (dtype == 1 && !out_f32 && kbase != nullptr && lda == ldb) {
+    // grouped bf16 products on the forward's 256 x 256 LDS-DMA kernel
+    GemmArgs ga{};
+    ga.a = a;
+    ga.w0 = b;
+    ga.a_rows = M;
+    ga.n_dim = N;
+    ga.k_dim = static_cast<int>(lda);
+    ga.kbase = kbase;
+    ga.groups = groups;
+    ga.out = c;
+    ga.out_alt = c_alt;
+    ga.alt_from = alt_from;
+    const hipError_t e = launch_kmajor_gemm(ga, s);
+    if (e != hipErrorInvalidValue) return e;  // else: operands it does not take
+  }
   KgArgs g{a, b, lda, ldb, M, N, kbase, k_all, c, c_alt, alt_from};
   const dim3 grid(static_cast<unsigned>(((M + 127) / 128) * ((N + 127) / 128)), groups);
   if (dtype == 1) {

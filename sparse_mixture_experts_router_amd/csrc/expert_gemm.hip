@@ -41,8 +41,12 @@ namespace {
 
 template <int N> struct CInt { static constexpr int value = N; };
 
-template <bool GATED, int BM, int BNE, int NBUF, bool FP8W>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
+  // KMAJ: the weight-gradient products C_g = A_g B_g^T (GemmArgs' kbase
+  // fields): A rows are rows of a, B rows rows of w0, both starting at
+  // column kbase[g], and the reduction runs over that group's columns only.
+  static_assert(!KMAJ || (!GATED && !FP8W), "weight-gradient mode: plain bf16");
   // FP8W: weights are E4M3 codes; a buffer holds 64 bytes of each weight row
   // (the same 64 K elements), read as 8-byte fragments and widened to bf16
   // right before their MFMAs; per-column scales are applied in the epilogue.
@@ -68,13 +72,22 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
 
   // ------------------------------------------------------- work of this block
-  int tile, nt, part, parts;
-  if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
-  const int2 te = g.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int seg = g.offsets[e];
-  const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
-  const int n0 = nt * COLS;
+  int part = -1, parts = 1, e = 0, m0 = 0, seg = 0, mvalid = 0, n0 = 0;
+  long kb = 0;  // KMAJ: first reduction column of the group
+  if constexpr (KMAJ) {
+    if (!decode_kwork(g, BM, COLS, e, m0, n0)) return;
+    mvalid = min(BM, g.a_rows - m0);
+    kb = g.kbase[e];
+  } else {
+    int tile, nt;
+    if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
+    const int2 te = g.tiles[tile];
+    e = te.x;
+    m0 = te.y;
+    seg = g.offsets[e];
+    mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+    n0 = nt * COLS;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform, so LDS destinations (M0) and bases live in scalar registers
@@ -89,7 +102,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const size_t mat_bytes = static_cast<size_t>(g.n_dim) * wrow_bytes;
   const bool routed = e < g.n_experts;
   const int es = routed ? e : e - g.n_experts;
-  const char* w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
+  const char* w0 = KMAJ ? reinterpret_cast<const char*>(g.w0) + kb * 2
+                        : reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
   const char* w1 = GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_bytes
                          : nullptr;
 
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // chunk (l % 4) ^ (l / 16), matching the fragment reads below).  Sources are a wave-uniform base plus a 32-bit
   // per-lane byte offset (the host keeps every operand below 4 GiB per base);
   // rows beyond the tile are clamped to a valid row and discarded at the end.
-  const char* const a_base = reinterpret_cast<const char*>(g.a);
+  const char* const a_base = reinterpret_cast<const char*>(g.a) + kb * 2;
   uint32_t a_off[A_BPW];
 #pragma unroll
   for (int j = 0; j < A_BPW; ++j) {
@@ -126,7 +140,9 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const int b_dst = BM * kLineBytes + wave * B_BPW * 1024;
 
   // buffer loads ("pairs" of K steps) of this item: all, or its part's share
-  int npairs = static_cast<int>(row_bytes / kLineBytes);  // even: K is a multiple of 128
+  // even: K is a multiple of 128 (KMAJ: so is every group's share)
+  int npairs = KMAJ ? static_cast<int>((g.kbase[e + 1] - kb) * 2 / kLineBytes)
+                    : static_cast<int>(row_bytes / kLineBytes);
   if (part >= 0) {
     const int per = split_share(npairs, parts);
     const int p0 = part * per;
@@ -198,7 +214,9 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   };
 
   // prologue: pairs 0 .. NBUF-2 and the first half of pair NBUF-1 in
-  // flight; pair 0 landed; the first step's fragments in fr[0]
+  // flight; pair 0 landed; the first step's fragments in fr[0].  A group
+  // with nothing to reduce (KMAJ) skips to the epilogue and writes zeros.
+  if (npairs > 0) {
 #pragma unroll
   for (int q = 0; q < NBUF - 1; ++q)
 #pragma unroll
@@ -291,6 +309,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   else if (mlive > MB / 4) k_loop(CInt<MB / 2>{});
   else if (mlive > 0) k_loop(CInt<MB / 4>{});
   else k_loop(CInt<0>{});
+  }  // npairs > 0
 
   // -------------------------------------------------------------- epilogue
   wait_vmem<0>();   // this wavefront's last ring loads have landed
@@ -306,7 +325,17 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     sc0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
     if (GATED) sc1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
   }
-  if (part < 0) {
+  if constexpr (KMAJ) {
+    const size_t cmat = static_cast<size_t>(g.a_rows) * g.n_dim;
+    bf16_t* const c = e < g.alt_from
+                          ? static_cast<bf16_t*>(g.out) + static_cast<size_t>(e) * cmat
+                          : static_cast<bf16_t*>(g.out_alt) + static_cast<size_t>(e - g.alt_from) * cmat;
+    // staged as bf16: 64 columns, whole 128-byte lines of a row, per pass
+    // (32 fp32 columns per pass left half lines, and the weight gradients
+    // wrote 1.37 GB for 0.94 GB)
+    store_block<false, true, MB, NB, WTM>(acc, stg, lane, c, false, g.n_dim, m0 + wm * WTM,
+                                          mvalid - wm * WTM, col0, g.n_dim);
+  } else if (part < 0) {
     store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
                                                  seg + m0 + wm * WTM, mvalid - wm * WTM, col0,
                                                  g.n_dim, sc0, sc1);
@@ -328,6 +357,19 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s) {
+  // whole 128-byte buffers from 16-byte aligned rows, 32-bit lane offsets
+  if (g.k_dim % 64 != 0 || g.n_dim % 8 != 0 ||
+      static_cast<size_t>(g.a_rows) * g.k_dim * 2 >= (size_t{1} << 32) ||
+      static_cast<size_t>(g.n_dim) * g.k_dim * 2 >= (size_t{1} << 32))
+    return hipErrorInvalidValue;
+  const long blocks = kmajor_grid(g, 256, 256);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((expert_gemm_kernel<false, 256, 256, 2, false, true>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
 
 int expert_gemm_cols(bool gated, int bm) {
   (void)bm;

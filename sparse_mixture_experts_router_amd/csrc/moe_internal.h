@@ -145,6 +145,15 @@ struct GemmArgs {
   const float* sc1;          // routed up scales, gated GEMM only
   const float* ssc0;         // shared-expert scales [S, n_dim]
   const float* ssc1;
+  // Weight-gradient mode of the large-tile kernel (launch_kmajor_gemm):
+  // C_g = A_g B_g^T for groups g, A [a_rows, ...] and B [n_dim, ...] both
+  // with row stride k_dim elements, group g reducing over columns
+  // kbase[g] .. kbase[g + 1]; C_g is [a_rows, n_dim], written to out (g <
+  // alt_from) or out_alt (g >= alt_from).
+  const int32_t* kbase;
+  void* out_alt;
+  int groups;
+  int alt_from;
 };
 
 // Pairs of K steps (128-byte row buffers) that each of `parts` pieces of an
@@ -186,6 +195,9 @@ struct GemmPick {
 GemmPick pick_gemm(int dtype, bool fp8w, bool gated, long rows_per_expert, size_t a_bytes,
                    size_t w_bytes, int k_dim);
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
+// bf16 weight-gradient products on the large-tile kernel (GemmArgs' kbase
+// fields); hipErrorInvalidValue when the operands do not fit it.
+hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 // Output columns per tile of the large-tile kernel launch_expert_gemm picks.
