@@ -235,7 +235,7 @@ def is_grad_w_gemm(name):
     """The weight-gradient launches: expert_gemm_kernel with KMAJ (its sixth
     template argument) = true."""
     ka = gemm_template_args(name)
-    return ka is not None and ka[0] == "expert_gemm_kernel" and len(ka[1]) == 6 and ka[1][5] == "true"
+    return ka is not None and ka[0] == "expert_gemm_kernel" and len(ka[1]) >= 6 and ka[1][5] == "true"
 
 
 def short_name(name):

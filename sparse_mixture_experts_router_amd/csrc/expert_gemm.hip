@@ -41,12 +41,27 @@ namespace {
 
 template <int N> struct CInt { static constexpr int value = N; };
 
-template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false>
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// BT: physical 16-byte chunk of logical chunk c in K-row kk of the staged B
+// tile is c ^ bt_key(kk).  A transpose read of one wavefront touches the 16
+// rows 8 g + 4 h + r (g, r < 4) of a K step; the key gives them 16 distinct
+// chunk offsets, spreading the reads over the LDS banks.
+__device__ __forceinline__ int bt_key(int kk) { return 2 * ((kk & 3) + 4 * ((kk >> 3) & 3)); }
+
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false, bool BT = false>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // KMAJ: the weight-gradient products C_g = A_g B_g^T (GemmArgs' kbase
   // fields): A rows are rows of a, B rows rows of w0, both starting at
   // column kbase[g], and the reduction runs over that group's columns only.
   static_assert(!KMAJ || (!GATED && !FP8W), "weight-gradient mode: plain bf16");
+  // BT: weights as K-rows ([k_dim, n_dim] per expert, rows split between w0
+  // and w1 at bt_rows0).  A buffer stages 64 K-rows x 256 columns (512
+  // contiguous bytes of each row, whole cache lines), and a B fragment is
+  // two ds_read_b64_tr_b16: in a group of 16 lanes, lane j points at 4
+  // columns (4 (j % 4) ..) of K-row k0 + j / 4 and lane i receives column i
+  // of rows k0 .. k0 + 3, i.e. 4 consecutive K values of one column.
+  static_assert(!BT || (!GATED && !FP8W && !KMAJ && BNE == 256), "B-row mode: plain bf16, 256 columns");
   // FP8W: weights are E4M3 codes; a buffer holds 64 bytes of each weight row
   // (the same 64 K elements), read as 8-byte fragments and widened to bf16
   // right before their MFMAs; per-column scales are applied in the epilogue.
@@ -127,14 +142,37 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
   const int jb0 = wave * B_BPW * BRPB;
   const bool up_rows = GATED && jb0 >= COLS;
-  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * wrow_bytes;
+  const char* b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * wrow_bytes;
+  const char* b_base1 = nullptr;  // BT: the weights of K-rows bt_rows0 ..
+  const uint32_t ldb = static_cast<uint32_t>(g.n_dim) * 2;  // BT: bytes per K-row
+  const int bt_pairs0 = BT ? g.bt_rows0 / 64 : 0;          // BT: buffers taken from w0
   uint32_t b_off[B_BPW];
+  if constexpr (BT) {
+    const char* const w0r = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) +
+                            static_cast<size_t>(es) * g.bt_rows0 * ldb;
+    const char* const w1r = reinterpret_cast<const char*>(routed ? g.w1 : g.ws1);
+    b_base = w0r + static_cast<size_t>(n0) * 2;
+    b_base1 = w1r == nullptr ? b_base
+                             : w1r + static_cast<size_t>(es) * (g.k_dim - g.bt_rows0) * ldb +
+                                   static_cast<size_t>(n0) * 2;
+    // block j of wavefront w: K-rows 2 (w B_BPW + j) and + 1, 32 lanes each;
+    // lane l writes physical chunk l % 32 of its row and fetches the logical
+    // chunk the key maps there (columns past n_dim are clamped to a valid
+    // chunk; their results are discarded)
 #pragma unroll
-  for (int j = 0; j < B_BPW; ++j) {
-    const int jb = jb0 + j * BRPB + lane / (64 / BRPB) - (up_rows ? COLS : 0);
-    const int n = min(n0 + jb, g.n_dim - 1);
-    const int chunk = FP8W ? ((lane & 3) ^ (lane >> 4)) : line_lane_chunk(lane, j);
-    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) + chunk * 16;
+    for (int j = 0; j < B_BPW; ++j) {
+      const int kk = 2 * (wave * B_BPW + j) + (lane >> 5);
+      const int col = min(n0 + 8 * ((lane & 31) ^ bt_key(kk)), g.n_dim - 8);
+      b_off[j] = static_cast<uint32_t>(kk) * ldb + static_cast<uint32_t>(col - n0) * 2;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < B_BPW; ++j) {
+      const int jb = jb0 + j * BRPB + lane / (64 / BRPB) - (up_rows ? COLS : 0);
+      const int n = min(n0 + jb, g.n_dim - 1);
+      const int chunk = FP8W ? ((lane & 3) ^ (lane >> 4)) : line_lane_chunk(lane, j);
+      b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) + chunk * 16;
+    }
   }
   const int a_dst = wave * A_BPW * 1024;
   const int b_dst = BM * kLineBytes + wave * B_BPW * 1024;
@@ -158,8 +196,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   auto issue_one = [&](int pair, int l, int buf) {
     const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1));
     char* const st = smem + buf * BUF;
-    if (l < A_BPW) load_lds16(a_base + (a_off[l] + pc * kLineBytes), st + a_dst + l * 1024);
-    else load_lds16(b_base + (b_off[l - A_BPW] + pc * BROW), st + b_dst + (l - A_BPW) * 1024);
+    if (l < A_BPW) {
+      load_lds16(a_base + (a_off[l] + pc * kLineBytes), st + a_dst + l * 1024);
+    } else if constexpr (BT) {
+      const bool second = static_cast<int>(pc) >= bt_pairs0;
+      const uint32_t prow = (second ? pc - bt_pairs0 : pc) * 64u * ldb;
+      load_lds16((second ? b_base1 : b_base) + (b_off[l - A_BPW] + prow),
+                 st + b_dst + (l - A_BPW) * 1024);
+    } else {
+      load_lds16(b_base + (b_off[l - A_BPW] + pc * BROW), st + b_dst + (l - A_BPW) * 1024);
+    }
   };
 
   // LDS byte offset (inside a buffer) of fragment f for K step t (0, 1) of
@@ -207,10 +253,30 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   u32x4 fr[2][NF];  // fragments of the two K steps of a buffer
   u32x4 fb[2][NB];  // FP8 weights: their raw weight fragments (both steps' codes)
   // fragment f of K step t from buffer base `b` into fragment set SET
+  // BT: lane constants of the transpose reads (row 8 (lane / 16) + (lane %
+  // 16) / 4 of a K step, columns 4 (lane % 4) .. of the fragment's 16)
+  const int bt_lane = (8 * (lane >> 4) + ((lane & 15) >> 2)) * 512 + ((lane & 3) >> 1) * 16 +
+                      (lane & 1) * 8;
+  const int bt_s = bt_key(8 * (lane >> 4) + ((lane & 15) >> 2));
   auto read_frag = [&](auto set_, int f, const char* b, int t) {
     constexpr int SET = decltype(set_)::value;
-    if (FP8W && f >= MB) fb[SET][f - MB] = *reinterpret_cast<const u32x4*>(b + frag8_off(f - MB));
-    else fr[SET][f] = *reinterpret_cast<const u32x4*>(b + frag_off(f, t));
+    if (FP8W && f >= MB) {
+      fb[SET][f - MB] = *reinterpret_cast<const u32x4*>(b + frag8_off(f - MB));
+    } else if (BT && f >= MB) {
+      const int nl = wn * WTN + (f - MB) * 16;  // first local column of the fragment
+      const char* p = b + BM * kLineBytes + t * 32 * 512 + bt_lane + (((nl >> 3) ^ bt_s) << 4);
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+      u32x4 v;
+      v[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1));
+      v[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3));
+      v[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1));
+      v[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
+      fr[SET][f] = v;
+    } else {
+      fr[SET][f] = *reinterpret_cast<const u32x4*>(b + frag_off(f, t));
+    }
   };
 
   // prologue: pairs 0 .. NBUF-2 and the first half of pair NBUF-1 in
@@ -347,11 +413,11 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <bool GATED, int BM, int BNE, int NBUF, bool FP8W = false>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W = false, bool BT = false>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long blocks = expert_grid(g, GATED, COLS);
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF, FP8W>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF, FP8W, false, BT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -369,6 +435,24 @@ hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s) {
   hipLaunchKernelGGL((expert_gemm_kernel<false, 256, 256, 2, false, true>),
                      dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
   return hipGetLastError();
+}
+
+bool expert_gemm_bt_fits(int bm, int k_dim, int n_dim, int rows0, long a_rows) {
+  // whole pairs of 64-row buffers, each from one weight matrix; 16-byte
+  // aligned K-rows; 32-bit offsets inside one expert's matrices and into A
+  return (bm == 128 || bm == 256) && k_dim % 128 == 0 && rows0 > 0 && rows0 % 64 == 0 &&
+         rows0 <= k_dim && n_dim % 8 == 0 && n_dim >= 8 &&
+         static_cast<size_t>(k_dim) * n_dim * 2 < (size_t{1} << 32) &&
+         static_cast<size_t>(a_rows) * k_dim * 2 < (size_t{1} << 32);
+}
+
+hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s) {
+  if (!expert_gemm_bt_fits(bm, g.k_dim, g.n_dim, g.bt_rows0, g.a_rows) ||
+      (g.bt_rows0 < g.k_dim && g.w1 == nullptr))
+    return hipErrorInvalidValue;
+  if (bm == 256) return launch_v<false, 256, 256, 2, false, true>(g, s);
+  if (bm == 128) return launch_v<false, 128, 256, 3, false, true>(g, s);
+  return hipErrorInvalidValue;
 }
 
 int expert_gemm_cols(bool gated, int bm) {

@@ -637,24 +637,41 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
   if (err != hipSuccess) return hip_fail(err, "route kernel");
   if ((st = run_permute(c, p, ws, nullptr, ws.topk_idx, s)) != MOE_OK) return st;
 
-  // weights transposed: W_down -> [N, F, d]; [W_gate | W_up] -> [N, d, 2F]; W_r -> [d, Kr]
+  // D = dy W_down and dXp = [dA dB] [W_gate; W_up] either read the weights
+  // as K-rows on the large-tile kernel (bf16) or run on transposed copies:
+  // W_down -> [N, F, d], [W_gate | W_up] -> [N, d, 2F].  The K-row reads
+  // made those two GEMMs 1.7-2.1x slower, while a transpose costs in
+  // proportion to the weight bytes, so the K-row path is taken when a weight
+  // matrix serves few rows (< 384 per group on average: DeepSeek-V3-shaped
+  // backward 37.0 -> 34.6 ms; Mixtral-shaped, 1024 rows, 9.3 -> 11.4 ms had
+  // it been taken).  W_r -> [d, Kr] always.
+  const bool few_rows = rows < 384L * G;
+  const bool bt_h = dt == 1 && few_rows && p.up.variant == 1 &&
+                    expert_gemm_bt_fits(p.up.bm, d, F, d, T);
+  const bool bt_x = dt == 1 && few_rows && p.down.variant == 1 &&
+                    expert_gemm_bt_fits(p.down.bm, 2 * F, d, F, rows);
   mark(ev, MOE_BSTAGE_TRANSPOSE_W, s);
   const long fd = static_cast<long>(F) * d;
-  if ((err = launch_transpose(dt, w->w_down, d, F, fd, at(B_WDT), d, 0, d, fd, N, s)) != hipSuccess ||
-      (err = launch_transpose(dt, w->w_gate, F, d, fd, at(B_WCAT), 2 * F, 0, F, 2 * fd, N, s)) !=
-          hipSuccess ||
-      (err = launch_transpose(dt, w->w_up, F, d, fd, at(B_WCAT), 2 * F, F, F, 2 * fd, N, s)) !=
-          hipSuccess ||
+  if ((!bt_h &&
+       (err = launch_transpose(dt, w->w_down, d, F, fd, at(B_WDT), d, 0, d, fd, N, s)) !=
+           hipSuccess) ||
+      (!bt_x &&
+       ((err = launch_transpose(dt, w->w_gate, F, d, fd, at(B_WCAT), 2 * F, 0, F, 2 * fd, N, s)) !=
+            hipSuccess ||
+        (err = launch_transpose(dt, w->w_up, F, d, fd, at(B_WCAT), 2 * F, F, F, 2 * fd, N, s)) !=
+            hipSuccess)) ||
       (err = launch_transpose(dt, w->w_router, N, d, 0, at(B_WRT), b.Kr, 0, b.Kr, 0, 1, s)) !=
           hipSuccess)
     return hip_fail(err, "weight transpose");
   if (S > 0 &&
-      ((err = launch_transpose(dt, w->ws_down, d, F, fd, at(B_WDT_S), d, 0, d, fd, S, s)) !=
-           hipSuccess ||
-       (err = launch_transpose(dt, w->ws_gate, F, d, fd, at(B_WCAT_S), 2 * F, 0, F, 2 * fd, S, s)) !=
-           hipSuccess ||
-       (err = launch_transpose(dt, w->ws_up, F, d, fd, at(B_WCAT_S), 2 * F, F, F, 2 * fd, S, s)) !=
-           hipSuccess))
+      ((!bt_h &&
+        (err = launch_transpose(dt, w->ws_down, d, F, fd, at(B_WDT_S), d, 0, d, fd, S, s)) !=
+            hipSuccess) ||
+       (!bt_x &&
+        ((err = launch_transpose(dt, w->ws_gate, F, d, fd, at(B_WCAT_S), 2 * F, 0, F, 2 * fd, S,
+                                 s)) != hipSuccess ||
+         (err = launch_transpose(dt, w->ws_up, F, d, fd, at(B_WCAT_S), 2 * F, F, F, 2 * fd, S,
+                                 s)) != hipSuccess))))
     return hip_fail(err, "weight transpose");
 
   // G, U (recomputed) and D = dy W_down, all [rows, F]
@@ -664,9 +681,16 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
   ga = plain_pass(c, p, ws, true, x, ws.sorted_tok, T, w->w_up, w->ws_up, d, F, at(B_U));
   if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "U GEMM");
   mark(ev, MOE_BSTAGE_GRAD_H, s);
-  ga = plain_pass(c, p, ws, true, dy, ws.sorted_tok, T, at(B_WDT), S > 0 ? at(B_WDT_S) : nullptr,
-                  d, F, at(B_D));
-  if ((err = launch_gemm(dt, false, p.up, ga, s)) != hipSuccess) return hip_fail(err, "D GEMM");
+  if (bt_h) {
+    ga = plain_pass(c, p, ws, true, dy, ws.sorted_tok, T, w->w_down, w->ws_down, d, F, at(B_D));
+    ga.bt_rows0 = d;
+    err = launch_expert_gemm_bt(p.up.bm, ga, s);
+  } else {
+    ga = plain_pass(c, p, ws, true, dy, ws.sorted_tok, T, at(B_WDT),
+                    S > 0 ? at(B_WDT_S) : nullptr, d, F, at(B_D));
+    err = launch_gemm(dt, false, p.up, ga, s);
+  }
+  if (err != hipSuccess) return hip_fail(err, "D GEMM");
 
   // gates per row, SwiGLU backward, then dXp = [dA dB] [W_gate; W_up]
   if ((err = launch_row_gate(ws.inv_row, ws.topk_gate, ws.offsets, T, k, N, S, rgate, s)) !=
@@ -675,9 +699,19 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
                                at(B_H), at(B_DAB), dg_row, s)) != hipSuccess)
     return hip_fail(err, "SwiGLU backward");
   mark(ev, MOE_BSTAGE_GRAD_X, s);
-  ga = plain_pass(c, p, ws, false, at(B_DAB), nullptr, rows, at(B_WCAT),
-                  S > 0 ? at(B_WCAT_S) : nullptr, 2 * F, d, at(B_DXP));
-  if ((err = launch_gemm(dt, false, p.down, ga, s)) != hipSuccess) return hip_fail(err, "dX GEMM");
+  if (bt_x) {
+    ga = plain_pass(c, p, ws, false, at(B_DAB), nullptr, rows, w->w_gate, w->ws_gate, 2 * F, d,
+                    at(B_DXP));
+    ga.w1 = w->w_up;
+    ga.ws1 = w->ws_up;
+    ga.bt_rows0 = F;
+    err = launch_expert_gemm_bt(p.down.bm, ga, s);
+  } else {
+    ga = plain_pass(c, p, ws, false, at(B_DAB), nullptr, rows, at(B_WCAT),
+                    S > 0 ? at(B_WCAT_S) : nullptr, 2 * F, d, at(B_DXP));
+    err = launch_gemm(dt, false, p.down, ga, s);
+  }
+  if (err != hipSuccess) return hip_fail(err, "dX GEMM");
 
   // router: dr, d logit_bias, dx = dr W_r + the rows' dXp
   if ((err = launch_router_bwd(dt, logits, ws.topk_idx, ws.topk_gate, ws.inv_row, dg_row,

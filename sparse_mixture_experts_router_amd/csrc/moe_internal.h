@@ -154,6 +154,12 @@ struct GemmArgs {
   void* out_alt;
   int groups;
   int alt_from;
+  // B-row mode of the large-tile kernel (launch_expert_gemm_bt): the plain
+  // pass with weights given as [k_dim, n_dim] per expert (K-rows, n_dim
+  // contiguous) instead of [n_dim, k_dim].  Rows 0 .. bt_rows0 - 1 of the
+  // reduction come from w0 / ws0 (expert stride bt_rows0 x n_dim), the rest
+  // from w1 / ws1 (stride (k_dim - bt_rows0) x n_dim).
+  int bt_rows0;
 };
 
 // Pairs of K steps (128-byte row buffers) that each of `parts` pieces of an
@@ -198,6 +204,10 @@ hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, 
 // bf16 weight-gradient products on the large-tile kernel (GemmArgs' kbase
 // fields); hipErrorInvalidValue when the operands do not fit it.
 hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s);
+// The plain grouped GEMM on the large-tile kernel with B given as K-rows
+// (GemmArgs' bt_rows0); hipErrorInvalidValue when the shape does not fit it.
+hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s);
+bool expert_gemm_bt_fits(int bm, int k_dim, int n_dim, int rows0, long a_rows);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 // Output columns per tile of the large-tile kernel launch_expert_gemm picks.
