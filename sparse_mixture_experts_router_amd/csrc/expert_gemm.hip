@@ -447,8 +447,10 @@ bool expert_gemm_bt_fits(int bm, int k_dim, int n_dim, int rows0, long a_rows) {
 }
 
 hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s) {
+  // no split plan: the pieces of a split reduction shift their B offsets
+  // along [n_dim, k_dim] rows, which this mode's K-row staging does not do
   if (!expert_gemm_bt_fits(bm, g.k_dim, g.n_dim, g.bt_rows0, g.a_rows) ||
-      (g.bt_rows0 < g.k_dim && g.w1 == nullptr))
+      (g.bt_rows0 < g.k_dim && g.w1 == nullptr) || g.plan != nullptr)
     return hipErrorInvalidValue;
   if (bm == 256) return launch_v<false, 256, 256, 2, false, true>(g, s);
   if (bm == 128) return launch_v<false, 128, 256, 3, false, true>(g, s);
