@@ -125,6 +125,10 @@ BACKWARD_CASES = [
     # experts no token chose: their weight gradients are exactly zero
     ("unused_experts", MoEShape("bwd_unused", T=6, d=128, N=32, k=1, F=128)),
     ("fp32", MoEShape("bwd_f32", T=96, d=128, N=4, k=2, F=256, S=1, dtype="f32")),
+    # few rows per weight matrix (128 per expert): D and dXp read the weights
+    # as K-rows on the large-tile kernel; dXp's 768-long reduction takes 6
+    # buffers from W_gate, then 6 from W_up; D's 384 columns end in a part tile
+    ("kmajor_rows", MoEShape("bwd_krows", T=512, d=512, N=16, k=4, F=384, S=1)),
     # DeepSeek-V3's routing structure: 256 experts, top-8, shared expert and
     # selection bias (257 segments, most a few rows long or empty)
     ("many_experts", MoEShape("bwd_many", T=100, d=128, N=256, k=8, F=128, S=1,
