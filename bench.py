@@ -16,7 +16,10 @@ expert weights).
                                               # rocprofv3 output -> profiles/
 
 Workloads (random weights of the named models' shapes, no checkpoints):
-mixtral_prefill (default), mixtral_decode, deepseek_v3, qwen3_skew, tiny_f32.
+deepseek_v3 (default: the largest single-GPU workload), mixtral_prefill,
+mixtral_decode, qwen3_skew, tiny_f32, and FP8-weight variants.  The default run
+also times mixtral_prefill, mixtral_decode and qwen3_skew on the same GPU and
+reports them under "other_workloads" (--also "" turns that off).
 """
 
 from __future__ import annotations
@@ -39,13 +42,22 @@ PEAK_F32_TFLOPS = 157.3       # dense MFMA fp32
 PEAK_HBM_GBS = 8000.0         # HBM3E
 # first CPU-oracle sample per workload; when it finishes in under CPU_MIN_S the
 # sample grows so that the reported run takes about CPU_TARGET_S
-DEFAULT_CPU_TOKENS = {"mixtral_prefill": 256, "mixtral_decode": 32, "deepseek_v3": 16,
+DEFAULT_CPU_TOKENS = {"mixtral_prefill": 256, "mixtral_decode": 32, "deepseek_v3": 8,
                       "qwen3_skew": 256, "tiny_f32": 64}
 CPU_MIN_S, CPU_TARGET_S = 8.0, 15.0
+# host memory the CPU baseline may fill with float64 expert weights; past it the
+# token sample stops growing and is repeated instead
+CPU_F64_WEIGHT_BUDGET = 40 << 30
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
 # the sources that decide the expert GEMMs' memory traffic
 GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
 PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 1024
+# matrix-core counters of the expert GEMMs, one --pmc pass (3 SQ + 1 GRBM):
+# busy cycles of the MFMA units summed over the SIMDs, MFMA bf16 operations / 512,
+# and the GPU's active cycles summed over the 8 XCDs
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CU_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+SIMDS, XCDS = 1024, 8
 
 
 def parse():
@@ -53,7 +65,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--workload", default="deepseek_v3")
+    ap.add_argument("--also", default="mixtral_prefill,mixtral_decode,qwen3_skew",
+                    help="comma-separated workloads timed after the headline one "
+                         "(compact entries under other_workloads; empty: none)")
     ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
                     help="backward: time moe_layer_backward instead (one JSON line of its own)")
     ap.add_argument("--seed", type=int, default=0)
@@ -130,8 +145,31 @@ def load_traffic(workload):
     return rec
 
 
+def mfma_path(workload):
+    return os.path.join(ROOT, "profiles", f"expert_gemm_{workload}_mfma.json")
+
+
+def load_mfma(workload):
+    """The committed rocprofv3 --pmc record of the expert GEMMs' matrix-core
+    counters, or None (also when the GEMM sources changed since)."""
+    path = mfma_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return rec
+
+
 def cpu_baseline(shape, inputs, n_tok, gpu_idx):
-    """The CPU oracle, as it stands, on the first n_tok tokens of the same batch."""
+    """The CPU oracle, as it stands, on the first n_tok tokens of the same batch.
+
+    The experts those tokens use are widened to float64 on the host before the
+    timed runs (widening the inputs' bits is not the oracle's arithmetic), so
+    each run times the oracle's forward alone.  The sample grows until one run
+    takes CPU_MIN_S, while the float64 weights it needs fit
+    CPU_F64_WEIGHT_BUDGET; past that the sample is repeated instead."""
     import numpy as np
 
     import oracle
@@ -143,24 +181,36 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
     except Exception:  # threadpoolctl missing: report the affinity set
         threads, blas = len(os.sched_getaffinity(0)), "unknown"
 
+    def f64(t):
+        return t.double().cpu().numpy()
+
     n_tok = min(n_tok, shape.T)
-    x = inputs["x"].float().cpu().numpy()
-    wr = inputs["w_router"].float().cpu().numpy()
+    x = f64(inputs["x"])
+    wr = f64(inputs["w_router"])
     lb = None if inputs["logit_bias"] is None else inputs["logit_bias"].cpu().numpy()
     sb = None if inputs["select_bias"] is None else inputs["select_bias"].cpu().numpy()
-    need = sorted(set(gpu_idx[:n_tok].reshape(-1).tolist()))   # more are fetched on demand
 
     def weight(name, e=None):
         w = inputs[name] if e is None else inputs[name][e]
         if not shape.fp8:
-            return w.float().cpu().numpy()
+            return f64(w)
         sc = inputs[name + "_scale"] if e is None else inputs[name + "_scale"][e]
         return oracle.dequantize(w.cpu().numpy(), sc.cpu().numpy())   # O9, part of the oracle
 
     def load(e):
         return (weight("w_gate", e), weight("w_up", e), weight("w_down", e))
 
-    cache = {e: load(e) for e in need}
+    per_expert = 3 * shape.d * shape.F * 8
+    cache = {}
+
+    def need(n):
+        return sorted(set(gpu_idx[:n].reshape(-1).tolist()))
+
+    def prepare(n):
+        for e in need(n):
+            if e not in cache:
+                cache[e] = load(e)
+
     fetched = []
 
     def expert(e):
@@ -175,25 +225,35 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
 
     def run(n):
         t0 = time.perf_counter()
-        oracle.moe_forward(np.ascontiguousarray(x[:n]), wr, expert, shape.k, logit_bias=lb,
+        oracle.moe_forward(x[:n], wr, expert, shape.k, logit_bias=lb,
                            select_bias=sb, shared=shared, n_experts=shape.N)
         return time.perf_counter() - t0
 
+    prepare(n_tok)
     dt = run(n_tok)
     first = (n_tok, dt)
     reps = 1
     while dt < CPU_MIN_S and n_tok < shape.T:   # too short to time: grow the sample
-        n_tok = min(shape.T, int(np.ceil(n_tok * CPU_TARGET_S / max(dt, 1e-3))))
+        nxt = min(shape.T, int(np.ceil(n_tok * CPU_TARGET_S / max(dt, 1e-3))))
+        if len(need(nxt)) * per_expert > CPU_F64_WEIGHT_BUDGET:
+            break
+        n_tok = nxt
+        prepare(n_tok)
         dt = run(n_tok)
-    if dt < CPU_MIN_S:                       # the whole batch is quick: repeat it
-        reps = int(np.ceil(CPU_TARGET_S / max(dt, 1e-3)))
-        dt = sum(run(n_tok) for _ in range(reps))
+    if dt < CPU_MIN_S:                       # quick (or capped) sample: repeat it
+        reps, dt = 0, 0.0
+        while dt < CPU_TARGET_S:
+            dt += run(n_tok)
+            reps += 1
     return {"value": n_tok * reps / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"first {n_tok} of {shape.T} tokens with all their experts"
                        f"{f', {reps} runs' if reps > 1 else ''}, NumPy float64 ({blas}), "
                        f"{dt:.1f} s in all (sized from a {first[0]}-token run of "
-                       f"{first[1]:.1f} s); host affinity {len(os.sched_getaffinity(0))} cpus"),
+                       f"{first[1]:.1f} s); weights widened to float64 before timing "
+                       f"({len(cache)} experts); host affinity "
+                       f"{len(os.sched_getaffinity(0))} cpus"
+                       f"{f'; {len(fetched)} experts fetched during timing' if fetched else ''}"),
             "seconds": round(dt, 2)}
 
 
@@ -207,6 +267,8 @@ def profile_commands(d, workload):
                   f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
         "write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- {run} "
                   f"--steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
+        "mfma": (f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d {d}/mfma "
+                 f"-o run -- {run} --steps {PMC_STEPS} --warmup {PMC_WARMUP}"),
         "copy_fetch": (f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o run -- "
                        f"python3 bench.py --copy-probe {COPY_MIB}"),
         "copy_write": (f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o run -- "
@@ -236,6 +298,18 @@ def is_grad_w_gemm(name):
     template argument) = true."""
     ka = gemm_template_args(name)
     return ka is not None and ka[0] == "expert_gemm_kernel" and len(ka[1]) >= 6 and ka[1][5] == "true"
+
+
+def is_down_gemm(name):
+    """The down launch: a forward grouped GEMM kernel with GATED = false (and,
+    for the large-tile kernel, neither the weight-gradient nor the K-row mode)."""
+    ka = gemm_template_args(name)
+    if ka is None:
+        return False
+    kern, args = ka
+    if kern == "expert_gemm_kernel":
+        return args[0] == "false" and all(a == "false" for a in args[5:])
+    return len(args) > 2 and args[2] == "false"
 
 
 def short_name(name):
@@ -338,6 +412,41 @@ def summarize_profiles(d, workload):
     with open(traffic_path(workload), "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
+    # matrix-core counters of both expert GEMMs (bf16 layers only)
+    mrec = None
+    if os.path.isdir(os.path.join(d, "mfma")) and shape.dtype == "bf16":
+        rows_all = shape.T * (shape.k + shape.S)
+        alg_flops = {"up": 4 * rows_all * shape.d * shape.F, "down": 2 * rows_all * shape.d * shape.F}
+        trace_us = {"up": up[2] / 1e3}
+        dn = [r_ for r_ in rows if is_down_gemm(r_[0])]
+        if len(dn) == 1:
+            trace_us["down"] = dn[0][2] / 1e3
+        mrec = {"workload": workload, "gemm_source_sha256_16": gemm_source_hash(),
+                "counters": list(MFMA_COUNTERS), "command": cmds["mfma"]}
+        for role, pick in (("up", is_up_gemm), ("down", is_down_gemm)):
+            vals = {}
+            for c in MFMA_COUNTERS:
+                v = [x_ for n_, xs in read_counters(os.path.join(d, "mfma"), c).items()
+                     if pick(short_name(n_)) for x_ in xs]
+                if not v:
+                    raise SystemExit(f"no {role} dispatch with {c} in {d}/mfma")
+                vals[c] = float(np.mean(v))
+            cycles = vals["GRBM_GUI_ACTIVE"] / XCDS
+            issued = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            ent = {"kernel": (up[0] if role == "up" else (dn[0][0] if len(dn) == 1 else None)),
+                   "gpu_active_cycles": round(cycles),
+                   "mfma_busy_frac": round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS), 4),
+                   "cu_busy_frac": round(vals["SQ_BUSY_CU_CYCLES"] * 4 / (cycles * 256), 4),
+                   "mfma_flops_issued": int(issued),
+                   "algorithmic_flops": alg_flops[role],
+                   "issued_over_algorithmic": round(issued / alg_flops[role], 4)}
+            if role in trace_us:
+                ent["trace_avg_us"] = round(trace_us[role], 1)
+                ent["clock_ghz"] = round(cycles / (trace_us[role] * 1e3), 3)
+            mrec[role] = ent
+        with open(mfma_path(workload), "w") as fh:
+            json.dump(mrec, fh, indent=1)
+            fh.write("\n")
     md = [f"# Gate/up expert GEMM, {workload}: rocprofv3 summary", "",
           f"Workload: {shape.describe()}.", "",
           "Commands (run from the repository root; the summary below is",
@@ -368,6 +477,21 @@ def summarize_profiles(d, workload):
     if alg:
         md += [f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |",
                f"| measured / algorithmic | {(fetch_b + write_b) / alg:.2f} |"]
+    if mrec is not None:
+        md += ["", "## Matrix-core counters of the expert GEMMs (--pmc)", "",
+               f"Counters {', '.join(MFMA_COUNTERS)}, one pass. MFMA busy = "
+               f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs); CU busy ="
+               " SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x 256 CUs); issued FLOPs ="
+               " SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against the algorithmic"
+               " 4 rows d F (gate/up) or 2 rows d F (down); clock = active cycles per XCD over"
+               " the kernel trace's mean duration.", "",
+               "| launch | MFMA busy | CU busy | issued / algorithmic FLOPs | clock (GHz) |",
+               "|---|---:|---:|---:|---:|"]
+        for role in ("up", "down"):
+            e_ = mrec[role]
+            md.append(f"| {role} `{e_['kernel']}` | {e_['mfma_busy_frac']:.3f} | "
+                      f"{e_['cu_busy_frac']:.3f} | {e_['issued_over_algorithmic']:.3f} | "
+                      f"{e_.get('clock_ghz', float('nan')):.2f} |")
     with open(os.path.join(ROOT, "profiles", f"expert_up_gemm_{workload}.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps(rec))
@@ -776,6 +900,167 @@ def bench_backward(args, shape):
     print(json.dumps(result), flush=True)
 
 
+def time_forward(moe, shape, inputs, steps, warmup, extras=True):
+    """Time `steps` layer forwards after `warmup`, inputs resident in HBM.
+
+    The timed region is bracketed by HIP events on the library's stream (and
+    the wall clock).  Inside it, one step in mark_stride(steps) also records
+    events around the gate/up and the down launches, so their durations are
+    measured live in the timed region.  With `extras`, K more (untimed) steps
+    with every stage marker give the stage breakdown and the per-step spread,
+    and the step is replayed K times from a HIP graph."""
+    import numpy as np
+    import torch
+
+    dev = inputs["x"].device
+    T, N, k = shape.T, shape.N, shape.k
+    cfg = moe.make_config(T, shape.d, N, k, shape.F, shape.S, shape.torch_dtype,
+                          weight_format=(moe.MOE_WEIGHTS_FP8_E4M3 if shape.fp8
+                                         else moe.MOE_WEIGHTS_DTYPE))
+    ws = moe.alloc_workspace(cfg, dev)
+    y = torch.empty((T, shape.d), dtype=shape.torch_dtype, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(N, dtype=torch.int32, device=dev)
+    psum = torch.empty(N, dtype=torch.float32, device=dev)
+    f = torch.empty(N, dtype=torch.float32, device=dev)
+    P = torch.empty(N, dtype=torch.float32, device=dev)
+    aux = torch.empty(2, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        # the forward also writes the balance statistics (f, P, aux) from its
+        # grouping step, so one call covers the whole path
+        moe.moe_layer_forward(cfg, inputs["x"], inputs, y, workspace=ws, topk_idx=idx,
+                              topk_gate=gate, counts=counts, prob_sum=psum, f=f, P=P, aux=aux,
+                              alpha=0.01, stage_events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {shape.name}: warmup {warmup} done; timing {steps} steps", file=sys.stderr,
+          flush=True)
+    nst = len(moe.STAGES)
+    iu, idn = moe.STAGES.index("expert_up"), moe.STAGES.index("expert_down")
+
+    def gemm_events():
+        evs_ = [None] * (nst + 1)
+        for i in (iu, iu + 1, idn + 1):
+            evs_[i] = torch.cuda.Event(enable_timing=True)
+        return evs_
+
+    every = mark_stride(steps)
+    marked = list(range(every // 2, steps, every))
+    tevs = {i: gemm_events() for i in marked}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(tevs.get(i))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = start.elapsed_time(end) / steps
+    up_ms = sum(e[iu].elapsed_time(e[iu + 1]) for e in tevs.values()) / len(tevs)
+    dn_ms = sum(e[idn].elapsed_time(e[idn + 1]) for e in tevs.values()) / len(tevs)
+    res = {"cfg": cfg, "ms_step": ms_step, "wall_ms": wall * 1e3 / steps, "up_ms": up_ms,
+           "down_ms": dn_ms, "marked": len(tevs), "every": every, "idx": idx,
+           "counts": counts.cpu().numpy()}
+    if extras:
+        # per-stage breakdown from K more (untimed) steps with every marker
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+               for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        res["stage_ms"] = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps
+                           for i, name in enumerate(moe.STAGES)}
+        per_step = np.sort(np.array([e[0].elapsed_time(e[nst]) for e in evs]))
+        res["pct"] = {q: float(np.percentile(per_step, q)) for q in (10, 50, 90)}
+        # the same step captured once in a HIP graph and replayed K times, as a
+        # serving loop would run it
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.Event(enable_timing=True)
+        ge = torch.cuda.Event(enable_timing=True)
+        gs.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        res["graph_ms"] = gs.elapsed_time(ge) / steps
+        del graph
+    del ws
+    return res
+
+
+def roofline_of(shape, active, up_ms, workload):
+    """The gate/up launch against both roofs.  `bound` is the roof that binds
+    at its arithmetic intensity (time at the MFMA peak against time at the HBM
+    peak); achieved and frac are in that roof's unit, and both fractions are
+    reported."""
+    _, _, uf, ub = algorithmic(shape, active)
+    peak_flops = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_mfma = uf / (peak_flops * 1e12)
+    t_hbm = ub / (PEAK_HBM_GBS * 1e9)
+    tflops = uf / (up_ms * 1e-3) / 1e12
+    gbs = ub / (up_ms * 1e-3) / 1e9
+    if t_hbm > t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
+    roof["mfma_frac"] = round(tflops / peak_flops, 4)
+    roof["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+    roof["arithmetic_intensity"] = round(uf / ub, 1)
+    roof["kernel"] = "grouped gate/up GEMM with SiLU*up (expert_up stage)"
+    roof["avg_launch_ms"] = round(up_ms, 4)
+    roof["algorithmic_bytes"] = ub
+    roof["algorithmic_flops"] = uf
+    rec = load_traffic(workload)
+    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
+    if rec is not None:
+        roof["traffic_source"] = os.path.relpath(traffic_path(workload), ROOT)
+        roof["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / ub, 3)
+    mrec = load_mfma(workload)
+    if mrec is not None:
+        roof["mfma_busy"] = mrec["up"]["mfma_busy_frac"]
+        roof["mfma_flops_issued_over_algorithmic"] = mrec["up"]["issued_over_algorithmic"]
+        roof["mfma_source"] = os.path.relpath(mfma_path(workload), ROOT)
+    return roof
+
+
+def layer_of(shape, active, ms_step):
+    lf, lb, _, _ = algorithmic(shape, active)
+    peak_flops = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    tflops = lf / (ms_step * 1e-3) / 1e12
+    gbs = lb / (ms_step * 1e-3) / 1e9
+    return {"tflops": round(tflops, 2), "mfma_frac": round(tflops / peak_flops, 4),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline_ms": round(max(lf / (peak_flops * 1e12), lb / (PEAK_HBM_GBS * 1e9)) * 1e3, 4),
+            "algorithmic_flops": lf, "algorithmic_bytes": lb, "active_experts": active}
+
+
+def config_of(shape):
+    return {"workload": shape.name, "T": shape.T, "d_model": shape.d, "n_experts": shape.N,
+            "top_k": shape.k, "d_ff": shape.F, "n_shared": shape.S,
+            "select_bias": shape.select_bias, "zipf_s": shape.zipf_s,
+            "expert_weights": "fp8_e4m3 + fp32 per-channel scales" if shape.fp8 else shape.dtype,
+            "parallelism": "single GPU"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -808,126 +1093,16 @@ def main():
     dev = torch.device("cuda:0")
     print(f"[bench] drawing inputs: {shape.describe()}", file=sys.stderr, flush=True)
     inputs = make_inputs(shape, seed=args.seed, device=dev)
-    T, N, k = shape.T, shape.N, shape.k
-    cfg = moe.make_config(T, shape.d, N, k, shape.F, shape.S, shape.torch_dtype,
-                          weight_format=(moe.MOE_WEIGHTS_FP8_E4M3 if shape.fp8
-                                         else moe.MOE_WEIGHTS_DTYPE))
-    ws = moe.alloc_workspace(cfg, dev)
-    y = torch.empty((T, shape.d), dtype=shape.torch_dtype, device=dev)
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(N, dtype=torch.int32, device=dev)
-    psum = torch.empty(N, dtype=torch.float32, device=dev)
-    f = torch.empty(N, dtype=torch.float32, device=dev)
-    P = torch.empty(N, dtype=torch.float32, device=dev)
-    aux = torch.empty(2, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(events=None):
-        # the forward also writes the balance statistics (f, P, aux) from its
-        # grouping step, so one call covers the whole path
-        moe.moe_layer_forward(cfg, inputs["x"], inputs, y, workspace=ws, topk_idx=idx,
-                              topk_gate=gate, counts=counts, prob_sum=psum, f=f, P=P, aux=aux,
-                              alpha=0.01, stage_events=events)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
-          flush=True)
-
-    # Timed region: K steps.  HIP events on the library's stream bracket the
-    # dominant launch (the gate/up GEMM) in one step of every MARK_EVERY, so
-    # its duration is measured live inside the region while the markers (a
-    # few microseconds each between kernels) stay out of most steps.
-    nst = len(moe.STAGES)
-    iu = moe.STAGES.index("expert_up")
-
-    def up_events():
-        evs_ = [None] * (nst + 1)
-        evs_[iu] = torch.cuda.Event(enable_timing=True)
-        evs_[iu + 1] = torch.cuda.Event(enable_timing=True)
-        return evs_
-
-    every = mark_stride(args.steps)
-    marked = list(range(every // 2, args.steps, every))
-    tevs = {i: up_events() for i in marked}
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(tevs.get(i))
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    up_ms = sum(e[iu].elapsed_time(e[iu + 1]) for e in tevs.values()) / len(tevs)
-
-    # Per-stage breakdown from K more (untimed) steps with every marker.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    stage_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                for i, name in enumerate(moe.STAGES)}
-    # per-step spread (forward only, markers included) from the same pass
-    per_step = np.sort(np.array([e[0].elapsed_time(e[nst]) for e in evs]))
-    pct = {q: float(np.percentile(per_step, q)) for q in (10, 50, 90)}
-
-    # The same step captured once in a HIP graph and replayed K times, as a
-    # serving loop would run it (fewer launch gaps between the kernels).
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    graph.replay()
-    torch.cuda.synchronize()
-    gs = torch.cuda.Event(enable_timing=True)
-    ge = torch.cuda.Event(enable_timing=True)
-    gs.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    ge.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = gs.elapsed_time(ge) / args.steps
-
-    counts_h = counts.cpu().numpy()
-    active = int(np.count_nonzero(counts_h))
-    lf, lb, uf, ub = algorithmic(shape, active)
-    tok_s = T / (ms_step * 1e-3)
-    peak_flops = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
-    decode_like = (T * k) / max(1, active) < 64
-    if decode_like:
-        achieved = ub / (up_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = uf / (up_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
-                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4)}
-    roof["kernel"] = "grouped gate/up GEMM with SiLU*up (expert_up stage)"
-    roof["avg_launch_ms"] = round(up_ms, 4)
-    roof["timed_launches"] = f"{len(tevs)} of the {args.steps} timed steps (one in {every})"
-    roof["algorithmic_bytes"] = ub
-    roof["algorithmic_flops"] = uf
-    rec = load_traffic(args.workload)
-    roof["traffic"] = None if rec is None else rec["hbm_bytes_per_launch"]
-    if rec is not None:
-        roof["traffic_source"] = os.path.relpath(traffic_path(args.workload), ROOT)
-        roof["traffic_over_algorithmic"] = round(rec["hbm_bytes_per_launch"] / ub, 3)
-
+    T = shape.T
+    r = time_forward(moe, shape, inputs, args.steps, args.warmup)
+    ms_step = r["ms_step"]
+    active = int(np.count_nonzero(r["counts"]))
+    roof = roofline_of(shape, active, r["up_ms"], args.workload)
+    roof["timed_launches"] = (f"{r['marked']} of the {args.steps} timed steps "
+                              f"(one in {r['every']})")
     result = {
         "metric": METRIC,
-        "value": round(tok_s, 1),
+        "value": round(T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -938,23 +1113,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) random weights of the model's shape)",
-        "config": {"workload": shape.name, "T": T, "d_model": shape.d, "n_experts": N,
-                   "top_k": k, "d_ff": shape.F, "n_shared": shape.S,
-                   "select_bias": shape.select_bias, "zipf_s": shape.zipf_s,
-                   "expert_weights": "fp8_e4m3 + fp32 per-channel scales" if shape.fp8
-                   else shape.dtype,
-                   "parallelism": "single GPU"},
-        "layer": {"tflops": round(lf / (ms_step * 1e-3) / 1e12, 2),
-                  "mfma_frac": round(lf / (ms_step * 1e-3) / 1e12 / peak_flops, 4),
-                  "hbm_gbs": round(lb / (ms_step * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(lb / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                  "algorithmic_flops": lf, "algorithmic_bytes": lb,
-                  "active_experts": active},
-        "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
-        "forward_ms_p10_p50_p90": [round(pct[10], 4), round(pct[50], 4), round(pct[90], 4)],
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "graph_replay": {"ms_per_step": round(graph_ms, 4),
-                         "tokens_per_s": round(T / (graph_ms * 1e-3), 1),
+        "config": config_of(shape),
+        "layer": layer_of(shape, active, ms_step),
+        "stages_ms": {k_: round(v, 4) for k_, v in r["stage_ms"].items()},
+        "down_launch_ms": round(r["down_ms"], 4),
+        "forward_ms_p10_p50_p90": [round(r["pct"][q], 4) for q in (10, 50, 90)],
+        "wall_ms_per_step": round(r["wall_ms"], 4),
+        "graph_replay": {"ms_per_step": round(r["graph_ms"], 4),
+                         "tokens_per_s": round(T / (r["graph_ms"] * 1e-3), 1),
                          "note": "the same step captured once in a HIP graph, K replays"},
         "roofline": roof,
         "cpu_baseline": None,
@@ -966,7 +1132,38 @@ def main():
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or DEFAULT_CPU_TOKENS.get(args.workload, 64)
         print(f"[bench] CPU oracle on {n} tokens", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(shape, inputs, n, idx.cpu().numpy())
+        result["cpu_baseline"] = cpu_baseline(shape, inputs, n, r["idx"].cpu().numpy())
+    del inputs, r
+    torch.cuda.empty_cache()
+
+    also = [w for w in args.also.split(",") if w and w != args.workload]
+    if also:
+        others = {}
+        for name in also:
+            shp = CONFIGS[name]
+            print(f"[bench] also: drawing inputs of {name}: {shp.describe()}", file=sys.stderr,
+                  flush=True)
+            inp = make_inputs(shp, seed=args.seed, device=dev)
+            o = time_forward(moe, shp, inp, args.steps, args.warmup, extras=False)
+            act = int(np.count_nonzero(o["counts"]))
+            rf = roofline_of(shp, act, o["up_ms"], name)
+            others[name] = {
+                "ms_per_step": round(o["ms_step"], 4),
+                "tokens_per_s": round(shp.T / (o["ms_step"] * 1e-3), 1),
+                "layer": {k_: v for k_, v in layer_of(shp, act, o["ms_step"]).items()
+                          if k_ in ("tflops", "mfma_frac", "hbm_gbs", "hbm_frac", "roofline_ms")},
+                "gate_up": {k_: rf[k_] for k_ in ("bound", "achieved", "unit", "frac", "mfma_frac",
+                                                  "hbm_frac", "avg_launch_ms")},
+                "down_launch_ms": round(o["down_ms"], 4),
+                "config": {k_: v for k_, v in config_of(shp).items() if k_ != "parallelism"},
+            }
+            del inp, o
+            torch.cuda.empty_cache()
+        result["other_workloads"] = {
+            "note": ("timed in the same run, same protocol (warm-up, K steps between HIP "
+                     "events; gate/up and down launches from markers in one step in "
+                     f"{mark_stride(args.steps)})"),
+            **others}
     print(json.dumps(result), flush=True)
 
 

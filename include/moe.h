@@ -159,6 +159,39 @@ enum {
  * (a multiple of 256).  Returns 0 for an invalid or unsupported cfg. */
 size_t moe_workspace_size(const moe_config* cfg);
 
+/* How moe_layer_forward runs `cfg` on the current device (kernel choices and
+ * reduction splits, all decided on the host from cfg and the device's
+ * compute-unit count), for tests and profiling.  The kernels and splits do
+ * not change the results' definition; they only change where the work runs.
+ *   up_kernel / down_kernel: 0 = register-staged tiles (fp32 layers and
+ *     batches of few rows per expert), 1 = large-tile kernel (bf16 prefill);
+ *   up_tile_rows / down_tile_rows: rows per tile of each grouped GEMM;
+ *   route_split: workgroups the router GEMM's reduction is split over
+ *     (1 = the router GEMM and the selection run in one kernel);
+ *   down_split: pieces every row of the down pass is split into over its
+ *     reduction (decode shapes), else 1;
+ *   tail_split_cols: column tiles of the down pass when its last row tiles
+ *     may be split over the reduction (0 = never);
+ *   split_plan_offset: byte offset in the workspace of the split plan each
+ *     forward writes there on the device, int32 [4] = {pieces, first split
+ *     row, rows per piece, split row tiles} (pieces = 0: nothing split);
+ *   workspace_bytes: moe_workspace_size(cfg).
+ * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for a bad cfg or NULL out. */
+typedef struct {
+  int32_t up_kernel;
+  int32_t up_tile_rows;
+  int32_t down_kernel;
+  int32_t down_tile_rows;
+  int32_t route_split;
+  int32_t down_split;
+  int32_t tail_split_cols;
+  int32_t compute_units;
+  uint64_t split_plan_offset;
+  uint64_t workspace_bytes;
+} moe_plan_info;
+
+moe_status moe_forward_plan(const moe_config* cfg, moe_plan_info* out);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* moe_status_string(int status);
 

@@ -22,7 +22,7 @@ __all__ = [
     "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
     "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
     "MoEGrads", "moe_backward_workspace_size", "alloc_backward_workspace", "moe_layer_backward",
-    "moe_update_select_bias",
+    "moe_update_select_bias", "MoEPlanInfo", "moe_forward_plan"
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,14 @@ class MoERouting(ctypes.Structure):
                 ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("prob_sum", ctypes.c_void_p), ("f", ctypes.c_void_p), ("P", ctypes.c_void_p),
                 ("aux", ctypes.c_void_p), ("balance_alpha", ctypes.c_float)]
+
+
+class MoEPlanInfo(ctypes.Structure):
+    _fields_ = [("up_kernel", ctypes.c_int32), ("up_tile_rows", ctypes.c_int32),
+                ("down_kernel", ctypes.c_int32), ("down_tile_rows", ctypes.c_int32),
+                ("route_split", ctypes.c_int32), ("down_split", ctypes.c_int32),
+                ("tail_split_cols", ctypes.c_int32), ("compute_units", ctypes.c_int32),
+                ("split_plan_offset", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 
 
 class MoEGrads(ctypes.Structure):
@@ -114,6 +122,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_backward_timed.restype = ctypes.c_int
         L.moe_update_select_bias.argtypes = [i32, vp, ctypes.c_float, vp, vp]
         L.moe_update_select_bias.restype = ctypes.c_int
+        L.moe_forward_plan.argtypes = [cfgp, ctypes.POINTER(MoEPlanInfo)]
+        L.moe_forward_plan.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -153,7 +163,20 @@ def alloc_workspace(cfg: MoEConfig, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
+def moe_forward_plan(cfg: MoEConfig) -> Dict[str, int]:
+    """How moe_layer_forward runs ``cfg`` on the current device (kernel
+    choices, tile rows, reduction splits, and the workspace offset of the
+    device-side split plan); see ``moe_forward_plan`` in include/moe.h."""
+    info = MoEPlanInfo()
+    _check(lib().moe_forward_plan(ctypes.byref(cfg), ctypes.byref(info)))
+    return {name: int(getattr(info, name)) for name, _ in MoEPlanInfo._fields_}
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor",
+         numel: Optional[int] = None) -> Optional[int]:
+    """Device address of ``t`` after checking placement, layout, dtype and,
+    when ``numel`` is given, its element count: the C ABI sees only pointers,
+    so a tensor of the wrong size would be read or written out of bounds."""
     if t is None:
         return None
     if not t.is_cuda:
@@ -162,6 +185,8 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the configuration needs {numel}")
     return t.data_ptr()
 
 
@@ -170,30 +195,43 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _weight_numels(cfg: MoEConfig) -> Dict[str, int]:
+    """Element count of every weight, bias and scale that ``cfg`` implies."""
+    N, d, F, S = cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.n_shared
+    return {"w_router": N * d, "w_gate": N * F * d, "w_up": N * F * d, "w_down": N * d * F,
+            "ws_gate": S * F * d, "ws_up": S * F * d, "ws_down": S * d * F,
+            "logit_bias": N, "select_bias": N,
+            "w_gate_scale": N * F, "w_up_scale": N * F, "w_down_scale": N * d,
+            "ws_gate_scale": S * F, "ws_up_scale": S * F, "ws_down_scale": S * d}
+
+
 def _weights(cfg: MoEConfig, w: Dict[str, Optional[torch.Tensor]], experts=True) -> MoEWeights:
     dt = _TORCH_DTYPE[cfg.dtype]
     fp8 = cfg.weight_format == MOE_WEIGHTS_FP8_E4M3
-    args = {"w_router": _ptr(w.get("w_router"), dt, "w_router")}
+    n = _weight_numels(cfg)
+    args = {"w_router": _ptr(w.get("w_router"), dt, "w_router", n["w_router"])}
     if experts:
-        for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
-            args[n] = _ptr(w.get(n), torch.uint8 if fp8 else dt, n)
+        for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            args[name] = _ptr(w.get(name), torch.uint8 if fp8 else dt, name, n[name])
         if fp8:
-            for n in _SCALES:
-                args[n] = _ptr(w.get(n), torch.float32, n)
-    args["logit_bias"] = _ptr(w.get("logit_bias"), torch.float32, "logit_bias")
-    args["select_bias"] = _ptr(w.get("select_bias"), torch.float32, "select_bias")
+            for name in _SCALES:
+                args[name] = _ptr(w.get(name), torch.float32, name, n[name])
+    args["logit_bias"] = _ptr(w.get("logit_bias"), torch.float32, "logit_bias", n["logit_bias"])
+    args["select_bias"] = _ptr(w.get("select_bias"), torch.float32, "select_bias",
+                               n["select_bias"])
     return MoEWeights(**args)
 
 
-def _routing(logits=None, topk_idx=None, topk_gate=None, counts=None, prob_sum=None, f=None,
-             P=None, aux=None, alpha=0.01):
-    return MoERouting(_ptr(logits, torch.float32, "logits"),
-                      _ptr(topk_idx, torch.int32, "topk_idx"),
-                      _ptr(topk_gate, torch.float32, "topk_gate"),
-                      _ptr(counts, torch.int32, "counts"),
-                      _ptr(prob_sum, torch.float32, "prob_sum"),
-                      _ptr(f, torch.float32, "f"), _ptr(P, torch.float32, "P"),
-                      _ptr(aux, torch.float32, "aux"), float(alpha))
+def _routing(cfg: MoEConfig, logits=None, topk_idx=None, topk_gate=None, counts=None,
+             prob_sum=None, f=None, P=None, aux=None, alpha=0.01):
+    T, N, k = cfg.T, cfg.n_experts, cfg.top_k
+    return MoERouting(_ptr(logits, torch.float32, "logits", T * N),
+                      _ptr(topk_idx, torch.int32, "topk_idx", T * k),
+                      _ptr(topk_gate, torch.float32, "topk_gate", T * k),
+                      _ptr(counts, torch.int32, "counts", N),
+                      _ptr(prob_sum, torch.float32, "prob_sum", N),
+                      _ptr(f, torch.float32, "f", N), _ptr(P, torch.float32, "P", N),
+                      _ptr(aux, torch.float32, "aux", 2), float(alpha))
 
 
 def moe_route(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch.Tensor]], *,
@@ -202,8 +240,9 @@ def moe_route(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optional[torch
               stream=None) -> None:
     """Routing only; see ``moe_route`` in include/moe.h."""
     w = _weights(cfg, weights, experts=False)
-    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
-    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x, _TORCH_DTYPE[cfg.dtype], "x"),
+    r = _routing(cfg, logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
+    _check(lib().moe_route(ctypes.byref(cfg),
+                           _ptr(x, _TORCH_DTYPE[cfg.dtype], "x", cfg.T * cfg.d_model),
                            ctypes.byref(w), ctypes.byref(r), _ptr(workspace, None, "workspace"),
                            workspace.numel(), _stream(stream)))
 
@@ -223,8 +262,9 @@ def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Option
     """
     dt = _TORCH_DTYPE[cfg.dtype]
     w = _weights(cfg, weights)
-    r = _routing(logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
-    args = (ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(y, dt, "y"),
+    r = _routing(cfg, logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
+    td = cfg.T * cfg.d_model
+    args = (ctypes.byref(cfg), _ptr(x, dt, "x", td), ctypes.byref(w), _ptr(y, dt, "y", td),
             ctypes.byref(r), _ptr(workspace, None, "workspace"), workspace.numel(),
             _stream(stream))
     if stage_events is None:
@@ -246,9 +286,10 @@ def moe_balance_stats(T: int, N: int, k: int, counts: torch.Tensor, prob_sum: to
                       stream=None) -> None:
     """f = counts / (T k), P = prob_sum / T, aux = [N sum f P, alpha N sum f P]."""
     _check(lib().moe_balance_stats(
-        int(T), int(N), int(k), _ptr(counts, torch.int32, "counts"),
-        _ptr(prob_sum, torch.float32, "prob_sum"), float(alpha), _ptr(f, torch.float32, "f"),
-        _ptr(P, torch.float32, "P"), _ptr(aux, torch.float32, "aux"), _stream(stream)))
+        int(T), int(N), int(k), _ptr(counts, torch.int32, "counts", N),
+        _ptr(prob_sum, torch.float32, "prob_sum", N), float(alpha),
+        _ptr(f, torch.float32, "f", N), _ptr(P, torch.float32, "P", N),
+        _ptr(aux, torch.float32, "aux", 2), _stream(stream)))
 
 
 def moe_backward_workspace_size(cfg: MoEConfig) -> int:
@@ -288,9 +329,14 @@ def moe_layer_backward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optio
     moe_layer_forward, one per BACKWARD_STAGES entry plus one."""
     dt = _TORCH_DTYPE[cfg.dtype]
     w = _weights(cfg, weights)
-    g = MoEGrads(**{n: _ptr(grads.get(n), torch.float32 if n == "dlogit_bias" else dt, n)
+    wn = _weight_numels(cfg)
+    td = cfg.T * cfg.d_model
+    gn = {"dx": td, "dw_router": wn["w_router"], "dlogit_bias": cfg.n_experts,
+          "dw_gate": wn["w_gate"], "dw_up": wn["w_up"], "dw_down": wn["w_down"],
+          "dws_gate": wn["ws_gate"], "dws_up": wn["ws_up"], "dws_down": wn["ws_down"]}
+    g = MoEGrads(**{n: _ptr(grads.get(n), torch.float32 if n == "dlogit_bias" else dt, n, gn[n])
                     for n in _GRADS})
-    args = (ctypes.byref(cfg), _ptr(x, dt, "x"), ctypes.byref(w), _ptr(dy, dt, "dy"),
+    args = (ctypes.byref(cfg), _ptr(x, dt, "x", td), ctypes.byref(w), _ptr(dy, dt, "dy", td),
             float(alpha), float(aux_grad), ctypes.byref(g), _ptr(workspace, None, "workspace"),
             workspace.numel(), _stream(stream))
     if stage_events is None:
@@ -303,9 +349,10 @@ def moe_layer_backward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Optio
 def moe_update_select_bias(counts: torch.Tensor, rate: float, select_bias: torch.Tensor,
                            stream=None) -> None:
     """select_bias += rate * sign(mean(counts) - counts), in place (fp32)."""
+    n = int(counts.numel())
     _check(lib().moe_update_select_bias(
-        int(counts.numel()), _ptr(counts, torch.int32, "counts"), float(rate),
-        _ptr(select_bias, torch.float32, "select_bias"), _stream(stream)))
+        n, _ptr(counts, torch.int32, "counts"), float(rate),
+        _ptr(select_bias, torch.float32, "select_bias", n), _stream(stream)))
 
 
 class MoELayer:

@@ -1,5 +1,5 @@
-// Pieces shared by the two large-tile expert GEMM kernels (expert_gemm.hip,
-// expert_gemm_ws.hip): the work decode of a workgroup and the tile epilogue.
+// Pieces of the large-tile expert GEMM kernel (expert_gemm.hip): the work
+// decode of a workgroup in each of its modes and the tile epilogue.
 #pragma once
 
 #include "moe_internal.h"

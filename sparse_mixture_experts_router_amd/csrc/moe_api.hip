@@ -5,6 +5,7 @@
 #include "moe_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -29,6 +30,27 @@ constexpr int R_COUNT_MAX = 32;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, asked of the runtime once per device:
+// the attribute query costs a host round trip that every decode step would
+// otherwise pay.  Devices past the table are asked on every call.
+constexpr int kCuCacheDevices = 64;
+std::atomic<int> g_cus[kCuCacheDevices];  // 0: not asked yet
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kCuCacheDevices) {
+    const int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < kCuCacheDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 // Row tiles that a grouped GEMM with `bm`-row tiles can need in the worst
 // case: each routed expert with c_e > 0 rows needs ceil(c_e / bm) tiles, and
@@ -125,11 +147,7 @@ Plan make_plan(const moe_config& c, bool bwd = false) {
   sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = bwd ? 0 : rows * static_cast<size_t>(c.d_ff) * eb;
 
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  p.cus = cus > 0 ? cus : 256;
+  p.cus = device_cus();
   {
     // row tiles the down pass will have: about one per expert that gets
     // rows (at most min(N, T k) of them) or T k / bm, whichever is more,
@@ -423,6 +441,25 @@ const char* moe_status_string(int status) {
 }
 
 const char* moe_last_error(void) { return g_last_error; }
+
+moe_status moe_forward_plan(const moe_config* cfg, moe_plan_info* out) {
+  g_last_error[0] = '\0';
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  const Plan p = make_plan(*cfg);
+  out->up_kernel = p.up.variant;
+  out->up_tile_rows = p.up.bm;
+  out->down_kernel = p.down.variant;
+  out->down_tile_rows = p.down.bm;
+  out->route_split = p.ksplit;
+  out->down_split = p.dsplit;
+  out->tail_split_cols = p.split.tail_nnt;
+  out->compute_units = p.cus;
+  out->split_plan_offset = p.off[R_NT] + 2 * sizeof(int32_t);
+  out->workspace_bytes = p.total;
+  return MOE_OK;
+}
 
 moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
                      moe_routing* out, void* workspace, size_t ws_bytes, void* stream) {

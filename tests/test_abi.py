@@ -288,3 +288,23 @@ def test_select_bias_update_validation():
     assert lib.moe_update_select_bias(4, None, 0.1, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_update_select_bias(4, FAKE, 0.1, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_update_select_bias(513, FAKE, 0.1, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_forward_plan_reports_the_path():
+    """moe_forward_plan: kernel choices, tile rows and splits of the benchmark
+    shapes, consistent with the workspace size (no GPU needed)."""
+    pre = moe.make_config(4096, 4096, 8, 2, 14336)
+    info = moe.moe_forward_plan(pre)
+    assert (info["up_kernel"], info["up_tile_rows"]) == (1, 256)
+    assert (info["down_kernel"], info["down_tile_rows"]) == (1, 256)
+    assert info["down_split"] == 1 and info["tail_split_cols"] == 4096 // 256
+    assert info["workspace_bytes"] == moe.moe_workspace_size(pre)
+    off = info["split_plan_offset"]
+    assert off % 4 == 0 and off + 16 <= info["workspace_bytes"]
+    dec = moe.moe_forward_plan(moe.make_config(32, 4096, 8, 2, 14336))
+    assert (dec["up_kernel"], dec["up_tile_rows"]) == (0, 32) and dec["down_split"] >= 2
+    f32 = moe.moe_forward_plan(moe.make_config(64, 128, 4, 2, 256, 0, "f32"))
+    assert f32["up_kernel"] == 0 and f32["tail_split_cols"] == 0
+    with pytest.raises(moe.MoEError):
+        moe.moe_forward_plan(moe.make_config(64, 100, 4, 2, 256))
+    assert moe.lib().moe_forward_plan(ctypes.byref(pre), None) == moe.MOE_ERR_INVALID_ARG

@@ -167,6 +167,7 @@ def test_backward_empty_batch_zero_gradients():
     shape = MoEShape("bwd_empty", T=0, d=128, N=4, k=2, F=128, S=1)
     inputs = make_inputs(MoEShape("bwd_w", T=1, d=128, N=4, k=2, F=128, S=1), seed=1,
                          device="cuda")
+    inputs["x"] = inputs["x"][:0]
     dy = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
     g = run_backward(shape, inputs, dy)
     for n, v in g.items():

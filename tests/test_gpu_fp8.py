@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import sparse_mixture_experts_router_amd as moe
-from gpu_harness import full_parity, run_layer, sampled_parity, say, to_np
+from gpu_harness import full_parity, full_size_parity, run_layer, say, to_np
 from workloads import CONFIGS, MoEShape, make_inputs, reduced
 
 pytestmark = pytest.mark.gpu
@@ -76,13 +76,19 @@ def test_fp8_parity(label, shape):
 @pytest.mark.parametrize("S", [0, 1])
 def test_fp8_tail_tiles_split_over_k(S):
     """The large-tile down pass's tail split with FP8 weights: every token on
-    expert 7, 20 (40) row tiles of 128, the last 4 (8) split in 2 parts whose
-    fp32 partial sums are scaled per part."""
-    shp = MoEShape("fp8_tail", T=2510, d=4096, N=8, k=1, F=1024, S=S, fp8=True)
+    expert 7, 20 (40) row tiles of 256, the last 4 (8) split in 2 pieces
+    (on 256 compute units) whose fp32 partial sums are scaled per piece."""
+    shp = MoEShape("fp8_tail", T=5000, d=4096, N=8, k=1, F=1024, S=S, fp8=True)
     inputs = make_inputs(shp, seed=8, device="cuda")
     inputs["logit_bias"] = torch.tensor([0.0] * 7 + [100.0], device="cuda")
     _, out, _ = full_parity(shp, inputs=inputs, label=f"fp8_tail_split_S{S}")
-    assert int(out["counts"][7]) == 2510
+    assert int(out["counts"][7]) == 5000
+    pieces, _, _, tail = to_np(out["split_plan"]).tolist()
+    assert pieces >= 2 and tail >= 1, "the tail split was not taken"
+    cfg = moe.make_config(5000, 4096, 8, 1, 1024, S,
+                          weight_format=moe.MOE_WEIGHTS_FP8_E4M3)
+    if moe.moe_forward_plan(cfg)["compute_units"] == 256:
+        assert (pieces, tail) == ((2, 4) if S == 0 else (2, 8))
 
 
 @pytest.mark.parametrize("shape,capacity", [
@@ -100,6 +106,7 @@ def test_fp8_capacity():
     assert int(np.sum(~ref["keep"])) > 0
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["mixtral_decode_fp8", "mixtral_prefill_fp8", "deepseek_v3_fp8"])
-def test_fp8_full_size_sampled(name):
-    sampled_parity(CONFIGS[name], seed=0)
+def test_fp8_full_size_every_element(name):
+    full_size_parity(CONFIGS[name], seed=0)

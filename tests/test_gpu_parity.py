@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import sparse_mixture_experts_router_amd as moe
-from gpu_harness import full_parity, run_layer, sampled_parity, say, to_np
+from gpu_harness import full_parity, full_size_parity, run_layer, say, to_np
 from workloads import CONFIGS, MoEShape, make_inputs, reduced
 
 pytestmark = pytest.mark.gpu
@@ -84,28 +84,44 @@ def test_all_tokens_one_expert():
     assert to_np(out["counts"]).tolist() == [0, 0, 0, 300]
 
 
-# (label, T, F): every token goes to expert 7, so the down pass (128-row
-# tiles, 16 column tiles of 256) has T / 128 row tiles, twice that with S = 1.
-#  base  : 20 (40) row tiles leave a last round of 64 (128) workgroups on 256
-#          CUs; the scan splits the last 4 (8) row tiles over their
-#          reduction in 2 parts (the down reduction, 1024, has 16 pairs of K
-#          steps: 8 + 8).
-#  odd_k : the same with d_ff = 1152, 18 pairs of K steps split 10 + 8.
-#  long  : 33 (66) row tiles leave 16 (32) workgroups; the last 1 (2) row
-#          tiles split in 2 parts.
-# The combine adds the fp32 parts.
-TAIL_SPLIT_CASES = [("base", 2510, 1024), ("odd_k", 2510, 1152), ("long", 4200, 1024)]
+# (label, T, F, {S: (pieces, split row tiles)} on 256 compute units): every
+# token goes to expert 7, so the down pass (256-row tiles, 16 column tiles of
+# 256) has ceil(T / 256) row tiles, twice that with S = 1, i.e. W = 16 x tiles
+# workgroups.  The last round holds r = W mod 256 of them; the scan splits the
+# last ceil(r / 16) row tiles over their reduction into min(256 / (16 x those
+# tiles), the most pieces the reduction allows) pieces, each at least 8 pairs
+# of K steps:
+#  base  : T = 5000, 20 (40) row tiles: r = 64 (128), the last 4 (8) row tiles
+#          split in 2 pieces (d_ff = 1024: 16 pairs of K steps, 8 + 8).
+#  odd_k : the same with d_ff = 1152, 18 pairs split 10 + 8.
+#  long  : T = 4200, d_ff = 4096, 17 (34) row tiles: r = 16 (32), the last 1
+#          (2) row tiles split in 8 pieces of 8 pairs.
+# The combine adds the fp32 pieces.
+TAIL_SPLIT_CASES = [("base", 5000, 1024, {0: (2, 4), 1: (2, 8)}),
+                    ("odd_k", 5000, 1152, {0: (2, 4), 1: (2, 8)}),
+                    ("long", 4200, 4096, {0: (8, 1), 1: (8, 2)})]
 
 
 @pytest.mark.parametrize("S", [0, 1])
-@pytest.mark.parametrize("label,T,F", TAIL_SPLIT_CASES, ids=[c[0] for c in TAIL_SPLIT_CASES])
-def test_tail_tiles_split_over_k(label, T, F, S):
-    """Last-round tail split of the large-tile down GEMM."""
+@pytest.mark.parametrize("label,T,F,plan", TAIL_SPLIT_CASES, ids=[c[0] for c in TAIL_SPLIT_CASES])
+def test_tail_tiles_split_over_k(label, T, F, plan, S):
+    """Last-round tail split of the large-tile down GEMM, and that the scan
+    actually took it."""
     shp = MoEShape("tail", T=T, d=4096, N=8, k=1, F=F, S=S)
+    cfg = moe.make_config(T, 4096, 8, 1, F, S)
+    info = moe.moe_forward_plan(cfg)
+    assert info["down_kernel"] == 1 and info["down_tile_rows"] == 256
     inputs = make_inputs(shp, seed=8, device="cuda")
     inputs["logit_bias"] = torch.tensor([0.0] * 7 + [100.0], device="cuda")
     _, out, _ = full_parity(shp, inputs=inputs, label=f"tail_split_{label}_S{S}")
     assert int(out["counts"][7]) == T
+    pieces, first_row, stride, tail = to_np(out["split_plan"]).tolist()
+    say(f"[tail] {label} S={S}: {pieces} pieces over the last {tail} row tiles from row "
+        f"{first_row} ({info['compute_units']} CUs)")
+    assert pieces >= 2 and tail >= 1, "the tail split was not taken"
+    assert stride == tail * 256
+    if info["compute_units"] == 256:
+        assert (pieces, tail) == plan[S]
 
 
 CAPACITY_CASES = [
@@ -257,10 +273,11 @@ def test_balance_outputs_of_the_forward(shape):
         assert torch.equal(a, b)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "qwen3_skew",
                                   "deepseek_v3"])
-def test_full_size_sampled(name):
-    out = sampled_parity(CONFIGS[name], seed=0)
+def test_full_size_every_element(name):
+    out = full_size_parity(CONFIGS[name], seed=0)
     if name == "qwen3_skew":
         counts = to_np(out["counts"])
         say(f"[full] qwen3_skew counts max {counts.max()} min {counts.min()} "
