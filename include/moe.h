@@ -227,6 +227,28 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x,
                                    size_t ws_bytes, void* stream,
                                    void* const* stage_events);
 
+/* Bytes of the device array that moe_layer_forward_noalloc uses as its
+ * workspace: one array per GPU the library runs on, held until the process
+ * ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as moe_layer_forward, but
+ * no workspace argument: the workspace is a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES on the current GPU, so the call never allocates.
+ * A cfg whose workspace (moe_workspace_size) exceeds that returns
+ * MOE_ERR_WORKSPACE and launches nothing: decode batches and small prefill
+ * batches fit (the Mixtral-shaped layer at 32 tokens needs 4 MB), large
+ * prefill batches do not.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (the forward reads nothing from its
+ * workspace that it has not written in the same call): calls that overlap
+ * on one GPU (concurrent streams, or threads) race and must be serialised
+ * by the caller. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x,
+                                     const moe_weights* w, void* y,
+                                     moe_routing* out, void* stream);
+
 /* Balance statistics from the routing sums of T tokens, N experts, top-k:
  * f_out[e] = counts[e] / (T k), P_out[e] = prob_sum[e] / T,
  * aux_out[0] = N * sum_e f_e P_e, aux_out[1] = alpha * aux_out[0]

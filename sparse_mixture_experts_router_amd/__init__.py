@@ -22,7 +22,8 @@ __all__ = [
     "MoERouting", "lib", "make_config", "moe_workspace_size", "moe_status_string",
     "alloc_workspace", "moe_route", "moe_layer_forward", "moe_balance_stats", "MoELayer",
     "MoEGrads", "moe_backward_workspace_size", "alloc_backward_workspace", "moe_layer_backward",
-    "moe_update_select_bias", "MoEPlanInfo", "moe_forward_plan"
+    "moe_update_select_bias", "MoEPlanInfo", "moe_forward_plan", "moe_layer_forward_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_FP8_E4M3 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 _SCALES = ("w_gate_scale", "w_up_scale", "w_down_scale", "ws_gate_scale", "ws_up_scale",
            "ws_down_scale")
 STAGES = ("route", "permute", "expert_up", "expert_down", "combine")
@@ -124,6 +126,8 @@ def lib() -> ctypes.CDLL:
         L.moe_update_select_bias.restype = ctypes.c_int
         L.moe_forward_plan.argtypes = [cfgp, ctypes.POINTER(MoEPlanInfo)]
         L.moe_forward_plan.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [cfgp, vp, wp, vp, rp, vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -279,6 +283,25 @@ def moe_layer_forward(cfg: MoEConfig, x: torch.Tensor, weights: Dict[str, Option
     arr = (ctypes.c_void_p * len(stage_events))(
         *[None if ev is None else ev.cuda_event for ev in stage_events])
     _check(lib().moe_layer_forward_timed(*args, arr))
+
+
+def moe_layer_forward_noalloc(cfg: MoEConfig, x: torch.Tensor,
+                              weights: Dict[str, Optional[torch.Tensor]], y: torch.Tensor, *,
+                              logits=None, topk_idx=None, topk_gate=None, counts=None,
+                              prob_sum=None, f=None, P=None, aux=None, alpha=0.01,
+                              stream=None) -> None:
+    """moe_layer_forward without a workspace argument: the library's own
+    per-GPU device array of NOALLOC_SCRATCH_BYTES serves as the workspace, so
+    the call allocates nothing; see ``moe_layer_forward_noalloc`` in
+    include/moe.h (larger configurations raise MOE_ERR_WORKSPACE; calls that
+    overlap on one GPU race)."""
+    dt = _TORCH_DTYPE[cfg.dtype]
+    w = _weights(cfg, weights)
+    r = _routing(cfg, logits, topk_idx, topk_gate, counts, prob_sum, f, P, aux, alpha)
+    td = cfg.T * cfg.d_model
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), _ptr(x, dt, "x", td),
+                                           ctypes.byref(w), _ptr(y, dt, "y", td),
+                                           ctypes.byref(r), _stream(stream)))
 
 
 def moe_balance_stats(T: int, N: int, k: int, counts: torch.Tensor, prob_sum: torch.Tensor,

@@ -81,6 +81,32 @@ enum {
   R_TUP, R_TDN, R_IUP, R_IDN, R_TB, R_NT, R_HID, R_YP, R_YPART, R_COUNT
 };
 
+// Workspace of moe_layer_forward_noalloc: a file-scope device array, one copy
+// per GPU (the runtime allocates it when it loads this library's code object
+// on that GPU and keeps it until the process ends).  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is asked
+// of the runtime once per device, with that device current, and only that
+// address is ever handed to kernels.
+__device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kCuCacheDevices];  // device address per device, or null
+
+moe_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev < 0 || dev >= kCuCacheDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device index past the scratch address table");
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return MOE_OK;
+}
+
 // bwd: the plan of the backward's routing and plain GEMMs instead: the "up"
 // tile list serves the passes with F output columns and K = d (G, U, D), the
 // "down" list the pass with d output columns and K = 2F (dXp); no split of
@@ -576,6 +602,26 @@ moe_status moe_layer_forward_timed(const moe_config* cfg, const void* x, const m
 moe_status moe_layer_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                              moe_routing* out, void* workspace, size_t ws_bytes, void* stream) {
   return moe_layer_forward_timed(cfg, x, w, y, out, workspace, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w,
+                                     void* y, moe_routing* out, void* stream) {
+  g_last_error[0] = '\0';
+  const moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const size_t need = make_plan(*cfg).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "the configuration needs %zu bytes of workspace; moe_layer_forward_noalloc holds "
+             "%zu (MOE_NOALLOC_SCRATCH_BYTES)",
+             need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+    return MOE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const moe_status sa = scratch_address(&ws);
+  if (sa != MOE_OK) return sa;
+  return moe_layer_forward_timed(cfg, x, w, y, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
+                                 nullptr);
 }
 
 moe_status moe_balance_stats(int32_t T, int32_t N, int32_t k, const int32_t* counts,
