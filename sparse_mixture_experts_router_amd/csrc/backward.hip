@@ -399,7 +399,7 @@ __global__ __launch_bounds__(512) void bias_update_kernel(const int32_t* __restr
 // bytes per row come in pairs.  N is a multiple of 64.  Groups >= alt_from
 // write to c_alt instead (shared experts).  128 x 128 tiles, 4 wavefronts of
 // 64 x 64.  Rows of 128 bytes in LDS, their 16-byte chunks XOR-swizzled by
-// (row mod 8) ^ (row bit 3), so the 16 rows of a fragment read land in 16
+// row mod 8 (swz128), so each 16-lane phase of a fragment read lands in 16
 // different bank groups.  Each thread stages its 16-byte slices of a K step
 // in registers:
 // the loads of step s + 2 are issued while step s is multiplied out of one

@@ -49,7 +49,8 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 // chunk offsets, spreading the reads over the LDS banks.
 __device__ __forceinline__ int bt_key(int kk) { return 2 * ((kk & 3) + 4 * ((kk >> 3) & 3)); }
 
-template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false, bool BT = false>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false, bool BT = false,
+          bool TRIPB = false>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // KMAJ: the weight-gradient products C_g = A_g B_g^T (GemmArgs' kbase
   // fields): A rows are rows of a, B rows rows of w0, both starting at
@@ -67,7 +68,16 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   // right before their MFMAs; per-column scales are applied in the epilogue.
   constexpr int BROW = FP8W ? 64 : kLineBytes;  // staged bytes of a weight row per buffer
   constexpr int BRPB = 1024 / BROW;             // weight rows per 1 KB load block
-  constexpr int BUF = BM * kLineBytes + BNE * BROW;  // bytes per buffer
+  constexpr int ABUF = BM * kLineBytes;           // bytes of the A rows of a buffer
+  constexpr int BBUF = BNE * BROW;                // bytes of the weight rows of a buffer
+  constexpr int BUF = ABUF + BBUF;                // bytes per buffer
+  // TRIPB: the A rows keep NBUF = 2 buffers and the weight rows get a third,
+  // so each pair's weight loads are issued a whole pair earlier than its A
+  // loads (weights come from HBM, the gathered A rows mostly from L2, which
+  // a tile's column tiles share).  2 x 32 KB + 3 x 32 KB = the whole 160 KB.
+  static_assert(!TRIPB || (NBUF == 2 && !FP8W && !BT && !KMAJ), "TRIPB: bf16 forward, 2 A buffers");
+  constexpr int NBB = TRIPB ? 3 : NBUF;           // weight-row buffers
+  constexpr int SMEM = TRIPB ? NBUF * ABUF + NBB * BBUF : NBUF * BUF;
   constexpr int WTM = BM / 2, WTN = BNE / 2;   // wavefront block
   constexpr int MB = WTM / 16, NB = WTN / 16;  // 16 x 16 MFMA blocks
   constexpr int NOUT = GATED ? NB / 2 : NB;    // output column blocks per wavefront
@@ -84,7 +94,12 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
                 "a wavefront's B blocks are all gate or all up rows");
   static_assert(NBUF >= 2 && (NBUF - 1) * LPB + LH1 < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF];
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  // base of the A rows / weight rows of buffer q (TRIPB: separate rings)
+  auto abuf = [&](int q) -> char* { return TRIPB ? smem + q * ABUF : smem + q * BUF; };
+  auto bbuf = [&](int q) -> char* {
+    return TRIPB ? smem + NBUF * ABUF + q * BBUF : smem + q * BUF + ABUF;
+  };
 
   // ------------------------------------------------------- work of this block
   int part = -1, parts = 1, e = 0, m0 = 0, seg = 0, mvalid = 0, n0 = 0;
@@ -174,8 +189,8 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
       b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) + chunk * 16;
     }
   }
-  const int a_dst = wave * A_BPW * 1024;
-  const int b_dst = BM * kLineBytes + wave * B_BPW * 1024;
+  const int a_dst = wave * A_BPW * 1024;  // inside the A rows of a buffer
+  const int b_dst = wave * B_BPW * 1024;  // inside its weight rows
 
   // buffer loads ("pairs" of K steps) of this item: all, or its part's share
   // even: K is a multiple of 128 (KMAJ: so is every group's share)
@@ -190,21 +205,21 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < B_BPW; ++j) b_off[j] += static_cast<uint32_t>(p0) * BROW;
   }
-  // Load l (A blocks first, then B blocks) of pair `pair` into buffer `buf`.
-  // Pairs past the end re-read the last one (valid addresses) into a buffer
-  // nobody reads again, so the loop needs no branches.
-  auto issue_one = [&](int pair, int l, int buf) {
+  // Load l (A blocks first, then B blocks) of pair `pair` into A buffer `ab`
+  // or weight buffer `bb`.  Pairs past the end re-read the last one (valid
+  // addresses) into a buffer nobody reads again, so the loop needs no
+  // branches.
+  auto issue_one = [&](int pair, int l, int ab, int bb) {
     const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1));
-    char* const st = smem + buf * BUF;
     if (l < A_BPW) {
-      load_lds16(a_base + (a_off[l] + pc * kLineBytes), st + a_dst + l * 1024);
+      load_lds16(a_base + (a_off[l] + pc * kLineBytes), abuf(ab) + a_dst + l * 1024);
     } else if constexpr (BT) {
       const bool second = static_cast<int>(pc) >= bt_pairs0;
       const uint32_t prow = (second ? pc - bt_pairs0 : pc) * 64u * ldb;
       load_lds16((second ? b_base1 : b_base) + (b_off[l - A_BPW] + prow),
-                 st + b_dst + (l - A_BPW) * 1024);
+                 bbuf(bb) + b_dst + (l - A_BPW) * 1024);
     } else {
-      load_lds16(b_base + (b_off[l - A_BPW] + pc * BROW), st + b_dst + (l - A_BPW) * 1024);
+      load_lds16(b_base + (b_off[l - A_BPW] + pc * BROW), bbuf(bb) + b_dst + (l - A_BPW) * 1024);
     }
   };
 
@@ -222,14 +237,15 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   const int ca1 = FP8W ? 2 * (lane >> 4) + 1 : 4 + (lane >> 4);
   const int flane0 = frow * kLineBytes + ((ca0 ^ fkey) << 4);
   const int flane1 = frow * kLineBytes + ((ca1 ^ fkey) << 4);
+  // (A fragments: inside the A rows; weight fragments: inside the weight rows)
   auto frag_off = [&](int f, int t) {
     int r;
     if (f < MB) {
       r = wm * WTM + f * 16;
     } else {
       const int j = f - MB;
-      if (GATED) r = BM + (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
-      else r = BM + wn * WTN + j * 16;
+      if (GATED) r = (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
+      else r = wn * WTN + j * 16;
     }
     return r * kLineBytes + (t ? flane1 : flane0);
   };
@@ -241,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   auto frag8_off = [&](int j) {
     const int rb = GATED ? (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16
                          : wn * WTN + j * 16;
-    return BM * kLineBytes + rb * 64 + f8lane;
+    return rb * 64 + f8lane;
   };
 
   f32x4 acc[MB][NB];
@@ -252,19 +268,20 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
 
   u32x4 fr[2][NF];  // fragments of the two K steps of a buffer
   u32x4 fb[2][NB];  // FP8 weights: their raw weight fragments (both steps' codes)
-  // fragment f of K step t from buffer base `b` into fragment set SET
+  // fragment f of K step t from buffer q (A rows at abuf(q), weight rows at
+  // bbuf(qb)) into fragment set SET
   // BT: lane constants of the transpose reads (row 8 (lane / 16) + (lane %
   // 16) / 4 of a K step, columns 4 (lane % 4) .. of the fragment's 16)
   const int bt_lane = (8 * (lane >> 4) + ((lane & 15) >> 2)) * 512 + ((lane & 3) >> 1) * 16 +
                       (lane & 1) * 8;
   const int bt_s = bt_key(8 * (lane >> 4) + ((lane & 15) >> 2));
-  auto read_frag = [&](auto set_, int f, const char* b, int t) {
+  auto read_frag = [&](auto set_, int f, const char* a, const char* b, int t) {
     constexpr int SET = decltype(set_)::value;
     if (FP8W && f >= MB) {
       fb[SET][f - MB] = *reinterpret_cast<const u32x4*>(b + frag8_off(f - MB));
     } else if (BT && f >= MB) {
       const int nl = wn * WTN + (f - MB) * 16;  // first local column of the fragment
-      const char* p = b + BM * kLineBytes + t * 32 * 512 + bt_lane + (((nl >> 3) ^ bt_s) << 4);
+      const char* p = b + t * 32 * 512 + bt_lane + (((nl >> 3) ^ bt_s) << 4);
       typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
@@ -275,24 +292,36 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
       v[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3));
       fr[SET][f] = v;
     } else {
-      fr[SET][f] = *reinterpret_cast<const u32x4*>(b + frag_off(f, t));
+      fr[SET][f] = *reinterpret_cast<const u32x4*>((f < MB ? a : b) + frag_off(f, t));
     }
   };
 
   // prologue: pairs 0 .. NBUF-2 and the first half of pair NBUF-1 in
   // flight; pair 0 landed; the first step's fragments in fr[0].  A group
   // with nothing to reduce (KMAJ) skips to the epilogue and writes zeros.
+  // TRIPB: pair 0, then the weight rows of pair 1, then its A rows, in
+  // flight; pair 0 landed.
   if (npairs > 0) {
+  if constexpr (TRIPB) {
 #pragma unroll
-  for (int q = 0; q < NBUF - 1; ++q)
+    for (int l = 0; l < LPB; ++l) issue_one(0, l, 0, 0);
 #pragma unroll
-    for (int l = 0; l < LPB; ++l) issue_one(q, l, q);
+    for (int l = A_BPW; l < LPB; ++l) issue_one(1, l, 1, 1);
 #pragma unroll
-  for (int l = 0; l < LH1; ++l) issue_one(NBUF - 1, l, NBUF - 1);
-  wait_vmem<(NBUF - 2) * LPB + LH1>();
+    for (int l = 0; l < A_BPW; ++l) issue_one(1, l, 1, 1);
+    wait_vmem<LPB>();
+  } else {
+#pragma unroll
+    for (int q = 0; q < NBUF - 1; ++q)
+#pragma unroll
+      for (int l = 0; l < LPB; ++l) issue_one(q, l, q, q);
+#pragma unroll
+    for (int l = 0; l < LH1; ++l) issue_one(NBUF - 1, l, NBUF - 1, NBUF - 1);
+    wait_vmem<(NBUF - 2) * LPB + LH1>();
+  }
   stage_barrier();
 #pragma unroll
-  for (int f = 0; f < NF; ++f) read_frag(CInt<0>{}, f, smem, 0);
+  for (int f = 0; f < NF; ++f) read_frag(CInt<0>{}, f, abuf(0), bbuf(0), 0);
 
   // Pair p (buffer cur = p mod NBUF) = K steps 2p (fragments in fr[0]) and
   // 2p + 1.
@@ -305,6 +334,12 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   //               rest of the MFMAs while reading step 2p + 2's fragments
   //               from buffer cur + 1 into fr[0] and issuing the first LH1
   //               loads of pair p + NBUF into buffer cur.
+  // TRIPB (A ring of 2, weight ring of 3): the same steps, but the loads in
+  // step 2p are the weight rows of pair p + 2 (into weight buffer (p + 2)
+  // mod 3, free since the previous barrier) and those after the barrier the
+  // A rows of pair p + 2 (into A buffer p mod 2); the wait before the barrier
+  // leaves only pair p + 2's weight rows in flight.  A pair's weight rows are
+  // thus issued two barriers before they are read, its A rows one.
   // The last row tile of a group is usually part empty: a wavefront runs the
   // MFMAs (and reads the A fragments) of its first LIVE 16-row blocks only,
   // LIVE the smallest of MB, MB/2, MB/4, 0 that covers its rows.  Loads and
@@ -352,23 +387,54 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
     constexpr int LIVE = decltype(live_)::value;
     constexpr int NR = LIVE > 0 ? LIVE + NB : 0;  // fragments a K step reads
     auto none = [](int) {};
-    int cur = 0;  // wave-uniform
-    for (int p = 0; p < npairs; ++p) {
-      const int prv = cur == 0 ? NBUF - 1 : cur - 1;
-      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-      const char* const bcur = smem + cur * BUF;
-      const char* const bnxt = smem + nxt * BUF;
-      auto read1 = [&](int r) { read_frag(CInt<1>{}, r < LIVE ? r : MB + r - LIVE, bcur, 1); };
-      auto read0 = [&](int r) { read_frag(CInt<0>{}, r < LIVE ? r : MB + r - LIVE, bnxt, 0); };
-      auto load2 = [&](int l) { issue_one(p + NBUF - 1, LH1 + l, prv); };
-      auto load1 = [&](int l) { issue_one(p + NBUF, l, cur); };
-      half_step(CInt<0>{}, CInt<0>{}, live_, CInt<LH2>{}, CInt<0>{}, load2, none);
-      half_step(CInt<0>{}, CInt<HALF>{}, live_, CInt<0>{}, CInt<NR>{}, none, read1);
-      half_step(CInt<1>{}, CInt<0>{}, live_, CInt<0>{}, CInt<0>{}, none, none);
-      wait_vmem<(NBUF - 2) * LPB>();
-      stage_barrier();
-      half_step(CInt<1>{}, CInt<HALF>{}, live_, CInt<LH1>{}, CInt<NR>{}, load1, read0);
-      cur = nxt;
+    if constexpr (TRIPB) {
+      int ca = 0, cb = 0;  // A and weight buffers of pair p (wave-uniform)
+      for (int p = 0; p < npairs; ++p) {
+        const int na = ca ^ 1;
+        const int nb = cb == 2 ? 0 : cb + 1;  // weight buffer of pair p + 1
+        const int fb_ = cb == 0 ? 2 : cb - 1;  // of pair p + 2
+        const char* const acur = abuf(ca);
+        const char* const bcur = bbuf(cb);
+        const char* const anxt = abuf(na);
+        const char* const bnxt = bbuf(nb);
+        auto read1 = [&](int r) {
+          read_frag(CInt<1>{}, r < LIVE ? r : MB + r - LIVE, acur, bcur, 1);
+        };
+        auto read0 = [&](int r) {
+          read_frag(CInt<0>{}, r < LIVE ? r : MB + r - LIVE, anxt, bnxt, 0);
+        };
+        auto load_b = [&](int l) { issue_one(p + 2, A_BPW + l, ca, fb_); };
+        auto load_a = [&](int l) { issue_one(p + 2, l, ca, fb_); };
+        half_step(CInt<0>{}, CInt<0>{}, live_, CInt<B_BPW>{}, CInt<0>{}, load_b, none);
+        half_step(CInt<0>{}, CInt<HALF>{}, live_, CInt<0>{}, CInt<NR>{}, none, read1);
+        half_step(CInt<1>{}, CInt<0>{}, live_, CInt<0>{}, CInt<0>{}, none, none);
+        wait_vmem<B_BPW>();
+        stage_barrier();
+        half_step(CInt<1>{}, CInt<HALF>{}, live_, CInt<A_BPW>{}, CInt<NR>{}, load_a, read0);
+        ca = na;
+        cb = nb;
+      }
+    } else {
+      int cur = 0;  // wave-uniform
+      for (int p = 0; p < npairs; ++p) {
+        const int prv = cur == 0 ? NBUF - 1 : cur - 1;
+        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+        auto read1 = [&](int r) {
+          read_frag(CInt<1>{}, r < LIVE ? r : MB + r - LIVE, abuf(cur), bbuf(cur), 1);
+        };
+        auto read0 = [&](int r) {
+          read_frag(CInt<0>{}, r < LIVE ? r : MB + r - LIVE, abuf(nxt), bbuf(nxt), 0);
+        };
+        auto load2 = [&](int l) { issue_one(p + NBUF - 1, LH1 + l, prv, prv); };
+        auto load1 = [&](int l) { issue_one(p + NBUF, l, cur, cur); };
+        half_step(CInt<0>{}, CInt<0>{}, live_, CInt<LH2>{}, CInt<0>{}, load2, none);
+        half_step(CInt<0>{}, CInt<HALF>{}, live_, CInt<0>{}, CInt<NR>{}, none, read1);
+        half_step(CInt<1>{}, CInt<0>{}, live_, CInt<0>{}, CInt<0>{}, none, none);
+        wait_vmem<(NBUF - 2) * LPB>();
+        stage_barrier();
+        half_step(CInt<1>{}, CInt<HALF>{}, live_, CInt<LH1>{}, CInt<NR>{}, load1, read0);
+        cur = nxt;
+      }
     }
   };
   if (mlive > MB / 2) k_loop(CInt<MB>{});
@@ -382,7 +448,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   stage_barrier();  // and every wavefront is done with the ring
   mfma_drain();
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
-  static_assert(4 * WTM * (128 + 16) <= NBUF * BUF, "staging space");
+  static_assert(4 * WTM * (128 + 16) <= SMEM, "staging space");
   char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
   const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
@@ -413,11 +479,13 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <bool GATED, int BM, int BNE, int NBUF, bool FP8W = false, bool BT = false>
+template <bool GATED, int BM, int BNE, int NBUF, bool FP8W = false, bool BT = false,
+          bool TRIPB = false>
 hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   constexpr int COLS = GATED ? BNE / 2 : BNE;
   const long blocks = expert_grid(g, GATED, COLS);
-  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF, FP8W, false, BT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((expert_gemm_kernel<GATED, BM, BNE, NBUF, FP8W, false, BT, TRIPB>),
+                     dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -477,9 +545,9 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
     if (gated) return launch_v<true, 128, 256, 4, true>(g, s);
     return launch_v<false, 128, 256, 4, true>(g, s);
   }
-  if (bm == 256) {
-    if (gated) return launch_v<true, 256, 256, 2>(g, s);
-    return launch_v<false, 256, 256, 2>(g, s);
+  if (bm == 256) {  // A rows in 2 buffers, weight rows in 3 (the whole 160 KB)
+    if (gated) return launch_v<true, 256, 256, 2, false, false, true>(g, s);
+    return launch_v<false, 256, 256, 2, false, false, true>(g, s);
   }
   if (bm != 128) return hipErrorInvalidValue;
   if (gated) return launch_v<true, 128, 256, 3>(g, s);
