@@ -490,6 +490,237 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------
+// Ping-pong variant of the 256 x 256 bf16 tile: 8 wavefronts, two per SIMD.
+//
+// The tile, its work items, its LDS layout (A rows in 2 buffers, weight rows
+// in 3, 128 bytes of every row per buffer) and its epilogue are those of
+// expert_gemm_kernel; what differs is who does what when.  Wavefronts 0-3
+// (group 0) and 4-7 (group 1) sit one per SIMD each, and each owns a 64 x 128
+// block (rows 64 q .., columns 128 g .. of the effective tile, q = wave mod 4,
+// g = group).  Every wavefront alternates two phases per pair of K steps:
+//   memory : issue its share of later pairs' loads, read all its fragments of
+//            this pair from LDS (24 ds_read_b128), wait for them;
+//   compute: its 64 MFMAs (two K steps x 4 x 8 blocks), registers only.
+// Group 1 runs one phase behind group 0, so in every phase one wavefront of
+// each SIMD issues MFMAs while the other does its memory work; a workgroup
+// barrier ends every phase.  Group 0 loads the A rows (pair p + 1 during its
+// memory phase of pair p), group 1 the weight rows (pair p + 2 during its
+// memory phase of pair p), so each buffer is refilled only after both groups
+// have read it, and each group waits for its own loads at the end of the
+// phase before they are needed.  Phases (h = 0 .. 2n for n pairs):
+//   group 0: h = 2p memory(p), h = 2p + 1 compute(p), h = 2n idle;
+//   group 1: h = 0 idle, h = 2p + 1 memory(p), h = 2p + 2 compute(p).
+// With one wavefront per SIMD (expert_gemm_kernel) the matrix core idles
+// whenever that wavefront waits for LDS data, for its loads or at the
+// barrier; here the other wavefront of the SIMD covers those waits.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
+  constexpr int BM = 256, BNE = 256;
+  constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
+  constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
+  constexpr int SMEM = NA * ABUF + NBB * BBUF;  // 160 KB
+  constexpr int WTM = 64, WTN = 128;           // wavefront block
+  constexpr int MB = WTM / 16, NB = WTN / 16;  // 4 x 8 MFMA blocks
+  constexpr int NOUT = GATED ? NB / 2 : NB;
+  constexpr int COLS = GATED ? BNE / 2 : BNE;  // output columns per tile
+  constexpr int LPW = 8;                       // 1 KB loads per wavefront per pair
+  constexpr int NF = MB + NB;                  // fragments per K step
+  static_assert(4 * LPW * 1024 == ABUF && 4 * LPW * 1024 == BBUF, "one group fills a ring");
+  static_assert(8 * WTM * (128 + 16) <= SMEM, "staging space");
+
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  auto abuf = [&](int q) -> char* { return smem + q * ABUF; };
+  auto bbuf = [&](int q) -> char* { return smem + NA * ABUF + q * BBUF; };
+
+  int part = -1, parts = 1, tile = 0, nt = 0;
+  if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
+  const int2 te = g.tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int seg = g.offsets[e];
+  const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+  const int n0 = nt * COLS;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, q = wave & 3;
+  const int wm = q, wn = grp;  // rows 64 q .., effective columns 128 g ..
+  const int mlive = __builtin_amdgcn_readfirstlane(min(max((mvalid - wm * WTM + 15) / 16, 0), MB));
+
+  const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
+  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
+  const bool routed = e < g.n_experts;
+  const int es = routed ? e : e - g.n_experts;
+  const char* const w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
+  const char* const w1 =
+      GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_bytes : nullptr;
+
+  // This wavefront's loads: group 0 the 8 A blocks of rows 64 q .. 64 q + 63,
+  // group 1 the 8 weight blocks of staged weight rows 64 q .. (gated: rows
+  // below COLS are gate rows, the rest up rows of the same columns).  Lane l
+  // of a block fetches row l / 8 of it, the chunk line_lane_chunk assigns;
+  // rows past the tile or the matrix are clamped to a valid row.
+  const char* src_base;
+  uint32_t off[LPW];
+  if (grp == 0) {
+    src_base = reinterpret_cast<const char*>(g.a);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int R = q * 64 + j * 8 + (lane >> 3);
+      const int grow = seg + m0 + min(R, mvalid - 1);
+      const int srow = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
+      off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) +
+               line_lane_chunk(lane, j) * 16;
+    }
+  } else {
+    const int jb0 = q * 64;
+    const bool up_rows = GATED && jb0 >= COLS;
+    src_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? COLS : 0);
+      const int n = min(n0 + jb, g.n_dim - 1);
+      off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
+               line_lane_chunk(lane, j) * 16;
+    }
+  }
+  int npairs = static_cast<int>(row_bytes / kLineBytes);
+  if (part >= 0) {
+    const int per = split_share(npairs, parts);
+    const int p0 = part * per;
+    npairs = min(per, npairs - p0);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) off[j] += static_cast<uint32_t>(p0) * kLineBytes;
+  }
+  const int dst = q * LPW * 1024;
+  // this wavefront's 8 loads of pair `pair` (past the end: the last pair
+  // again, into a buffer nobody reads again)
+  auto issue = [&](int pair, char* ring) {
+    const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) load_lds16(src_base + (off[j] + pc), ring + dst + j * 1024);
+  };
+
+  // Fragment reads: lane l takes row l mod 16 of a 16-row block, chunk
+  // l / 16 (+ 4 for the second K step) under the row-mod-8 swizzle.
+  const int frow = lane & 15;
+  const int fkey = frow & 7;
+  const int fl0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
+  const int fl1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  auto b_row = [&](int j) {  // first staged weight row of block j
+    if (GATED) return (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
+    return wn * WTN + j * 16;
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 fr[2][NF];
+
+  // prologue: group 0 A(0); group 1 B(0) then B(1); A(0) and B(0) landed
+  if (grp == 0) {
+    issue(0, abuf(0));
+    wait_vmem<0>();
+  } else {
+    issue(0, bbuf(0));
+    issue(1, bbuf(1));
+    wait_vmem<LPW>();
+  }
+  stage_barrier();
+
+  // Each group runs its own straight loop (a shared loop that branches on the
+  // group every phase made the compiler move the accumulators out of the
+  // AGPRs); both execute 2 n + 2 barriers in all, prologue included.
+  auto run = [&](auto live_, auto grp_) {
+    constexpr int LIVE = decltype(live_)::value;
+    constexpr int G = decltype(grp_)::value;
+    auto memory = [&](int p) {
+      const char* const a = abuf(p & 1);
+      const char* const b = bbuf(p % 3);
+      if (G == 0) issue(p + 1, abuf((p + 1) & 1));
+      else issue(p + 2, bbuf((p + 2) % 3));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int fl = t ? fl1 : fl0;
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i)
+          fr[t][i] = *reinterpret_cast<const u32x4*>(a + (wm * WTM + i * 16) * kLineBytes + fl);
+        if (LIVE > 0) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            fr[t][MB + j] = *reinterpret_cast<const u32x4*>(b + b_row(j) * kLineBytes + fl);
+        }
+      }
+      // fragments in registers; group 0 leaves A(p + 1) in flight (waited
+      // for after its compute phase), group 1 waits for B(p + 1) and leaves
+      // B(p + 2) in flight
+      if (G == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      else wait_vmem<LPW>();
+    };
+    auto compute = [&]() {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fr[t][i], fr[t][MB + j]);
+    };
+    if (G == 0) {
+      for (int p = 0; p < npairs; ++p) {
+        memory(p);  // phase 2p
+        stage_barrier();
+        compute();  // phase 2p + 1
+        wait_vmem<0>();  // A(p + 1) landed before anyone reads pair p + 1
+        stage_barrier();
+      }
+      stage_barrier();  // phase 2n: idle
+    } else {
+      stage_barrier();  // phase 0: idle
+      for (int p = 0; p < npairs; ++p) {
+        memory(p);  // phase 2p + 1
+        if (p == npairs - 1) wait_vmem<0>();  // nothing in flight past the last pair
+        stage_barrier();
+        compute();  // phase 2p + 2
+        stage_barrier();
+      }
+    }
+  };
+  auto run_g = [&](auto grp_) {
+    if (mlive > MB / 2) run(CInt<MB>{}, grp_);
+    else if (mlive > MB / 4) run(CInt<MB / 2>{}, grp_);
+    else if (mlive > 0) run(CInt<MB / 4>{}, grp_);
+    else run(CInt<0>{}, grp_);
+  };
+  if (grp == 0) run_g(CInt<0>{});
+  else run_g(CInt<1>{});
+
+  // epilogue: every ring read is done (the last barrier), every load landed
+  mfma_drain();
+  constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
+  char* const stg = smem + wave * WTM * (128 + 16);
+  const int col0 = n0 + wn * OC;
+  if (part < 0) {
+    store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
+                                           seg + m0 + wm * WTM, mvalid - wm * WTM, col0, g.n_dim);
+  } else if (!GATED) {  // fp32 partial rows of a split tail tile
+    const long prow = static_cast<long>(part) * g.plan[kPlanStride] + seg + m0 -
+                      g.plan[kPlanRowSplit] + wm * WTM;
+    store_block<GATED, false, MB, NB, WTM>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
+                                           mvalid - wm * WTM, col0, g.n_dim);
+  }
+}
+
+template <bool GATED>
+hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
+  constexpr int COLS = GATED ? 128 : 256;
+  const long blocks = expert_grid(g, GATED, COLS);
+  hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(512), 0, s, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s) {
@@ -545,9 +776,9 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
     if (gated) return launch_v<true, 128, 256, 4, true>(g, s);
     return launch_v<false, 128, 256, 4, true>(g, s);
   }
-  if (bm == 256) {  // A rows in 2 buffers, weight rows in 3 (the whole 160 KB)
-    if (gated) return launch_v<true, 256, 256, 2, false, false, true>(g, s);
-    return launch_v<false, 256, 256, 2, false, false, true>(g, s);
+  if (bm == 256) {  // 8-wavefront ping-pong tiles
+    if (gated) return launch_pp<true>(g, s);
+    return launch_pp<false>(g, s);
   }
   if (bm != 128) return hipErrorInvalidValue;
   if (gated) return launch_v<true, 128, 256, 3>(g, s);
