@@ -91,10 +91,11 @@ __device__ __forceinline__ uint64_t group16_max(uint64_t v) {
 
 // ---------------------------------------------------------------- selection
 // Top-k, gates, block statistics and ranks for the 64-token tile whose fp32
-// logits (logit_bias included) are in s_logit[tt * LD + e].  A group of 16
-// lanes handles one token (4 tokens per wavefront at a time); lane gl holds
-// experts gl, gl + 16, ...
-template <int NB>
+// logits (logit_bias included) are in s_logit[tt * LD + e], with NW
+// wavefronts (64 NW threads).  A group of 16 lanes handles one token (4
+// tokens per wavefront at a time, 64 / NW tokens per wavefront in all); lane
+// gl holds experts gl, gl + 16, ...
+template <int NB, int NW>
 __device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_tok, int N, int k,
                             const float* __restrict__ select_bias, int32_t* __restrict__ topk_idx,
                             float* __restrict__ topk_gate, int32_t* __restrict__ lrank,
@@ -102,25 +103,36 @@ __device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_
                             uint32_t (*s_mask)[2], float* s_psum, int32_t* s_sel) {
   using S = RouteShape<NB>;
   constexpr int G = S::G, EPL = S::EPL, TPW = S::TPW, LD = S::LD, NP = S::NP;
+  constexpr int TOKW = kRouteTokens / NW;  // tokens per wavefront
+  static_assert(TOKW % TPW == 0, "whole lane groups");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / G;
   const int gl = lane % G;
   float psum[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) psum[i] = 0.f;
+  // this lane's experts' selection biases, the same for every token
+  float sbias[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = gl + G * i;
+    sbias[i] = (e < N && select_bias != nullptr) ? select_bias[e] : 0.f;
+  }
 
 #pragma unroll 1
-  for (int base = 0; base < 16; base += TPW) {
-    const int tt = wave * 16 + base + grp;  // token inside the block
+  for (int base = 0; base < TOKW; base += TPW) {
+    const int tt = wave * TOKW + base + grp;  // token inside the block
     const int t = t0 + tt;
     const bool tok_ok = t < n_tok;          // uniform inside a lane group
 
-    float r[EPL], key[EPL];
+    float r[EPL];
+    uint64_t okey[EPL];  // selection order of each of this lane's experts
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = gl + G * i;
       r[i] = e < N ? s_logit[tt * LD + e] : -INFINITY;
-      key[i] = (e < N && select_bias != nullptr) ? __fadd_rn(r[i], select_bias[e]) : r[i];
+      const float key = (e < N && select_bias != nullptr) ? __fadd_rn(r[i], sbias[i]) : r[i];
+      okey[i] = e < N ? order_key(key, e) : 0ull;
     }
 
     // router probabilities over all N experts (balance statistic P)
@@ -150,8 +162,7 @@ __device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_
       uint64_t best = 0ull;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const int e = gl + G * i;
-        const uint64_t o = (e < N && !((taken >> i) & 1u)) ? order_key(key[i], e) : 0ull;
+        const uint64_t o = ((taken >> i) & 1u) ? 0ull : okey[i];
         best = o > best ? o : best;
       }
       best = group16_max(best);
@@ -189,7 +200,7 @@ __device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_
 
   // ---------------------------------------------- block statistics and ranks
   const int n_here = min(kRouteTokens, n_tok - t0);
-  for (int i = tid; i < n_here * k; i += 256) {
+  for (int i = tid; i < n_here * k; i += 64 * NW) {
     const int tt = i / k, s = i - tt * k;
     const int e = s_sel[tt * kMaxTopK + s];
     const uint64_t mk = static_cast<uint64_t>(s_mask[e][0]) |
@@ -197,11 +208,11 @@ __device__ __forceinline__ void select_tile(const float* s_logit, int t0, int n_
     const uint64_t below = tt == 0 ? 0ull : (mk & ((1ull << tt) - 1ull));
     lrank[static_cast<size_t>(t0 + tt) * k + s] = __popcll(below);
   }
-  for (int e = tid; e < N; e += 256) {
+  for (int e = tid; e < N; e += 64 * NW) {
     blk_counts[static_cast<size_t>(blockIdx.x) * N + e] =
         __popc(s_mask[e][0]) + __popc(s_mask[e][1]);
     float acc_p = 0.f;
-    for (int w = 0; w < 4; ++w) acc_p += s_psum[w * NP + e];
+    for (int w = 0; w < NW; ++w) acc_p += s_psum[w * NP + e];
     blk_psum[static_cast<size_t>(blockIdx.x) * N + e] = acc_p;
   }
 }
@@ -338,40 +349,46 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(RouteArgs a) {
       }
     }
   __syncthreads();
-  select_tile<NB>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate, a.lrank,
-                  a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
+  select_tile<NB, 4>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate,
+                     a.lrank, a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
 }
 
 // Sum of the split-K partial logits (fixed order) + logit_bias, then the
-// selection.
+// selection, with 16 wavefronts (8 for more than 256 experts, whose logits
+// tile and per-lane keys need the LDS and registers): each runs the
+// selection of 4 tokens at once (a 4-wavefront workgroup looped over 16
+// tokens per wavefront, and with one workgroup per 64-token block most CUs
+// idled).
+constexpr int select_threads(int nb) { return nb >= 32 ? 512 : 1024; }
 template <int NB>
-__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
+__global__ __launch_bounds__(select_threads(NB)) void route_select_kernel(RouteArgs a) {
   using S = RouteShape<NB>;
-  constexpr int NP = S::NP, LD = S::LD;
+  constexpr int NP = S::NP, LD = S::LD, NT = select_threads(NB);
   __shared__ float s_logit[kRouteTokens * LD];
   __shared__ uint32_t s_mask[NP][2];
-  __shared__ float s_psum[4 * NP];
+  __shared__ float s_psum[(NT / 64) * NP];
   __shared__ int32_t s_sel[kRouteTokens * kMaxTopK];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kRouteTokens;
-  for (int i = tid; i < NP * 2; i += 256) (&s_mask[0][0])[i] = 0u;
+  for (int i = tid; i < NP * 2; i += NT) (&s_mask[0][0])[i] = 0u;
   const int n_here = min(kRouteTokens, a.n_tok - t0);
   if (a.N % 4 == 0 && a.ksplit <= 8) {
     // (many tokens, few splits) 16-byte loads of 4 experts; every (token, 4 experts) quad of the tile
     // is a lane's, and its ksplit partials are all requested before the sum
     // (added in split order), so the loads overlap instead of queueing
     const int nq = a.N / 4;
-    for (int q0 = tid; q0 < kRouteTokens * nq; q0 += 256 * 4) {
-      f32x4 v[4];
+    constexpr int U = 1;  // quads per thread and pass (the 1024 threads cover a tile in 4 passes)
+    for (int q0 = tid; q0 < kRouteTokens * nq; q0 += NT * U) {
+      f32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {  // 8 splits x 4 quads in flight
-        f32x4 pv[8][4];
+      for (int u = 0; u < U; ++u) v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < a.ksplit; k0 += 8) {  // 8 splits x U quads in flight
+        f32x4 pv[8][U];
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int q = q0 + u * 256, tt = q / nq;
+          for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * NT, tt = q / nq;
             pv[kk][u] = (k0 + kk < a.ksplit && q < kRouteTokens * nq && tt < n_here)
                             ? *reinterpret_cast<const f32x4*>(
                                   a.partial +
@@ -382,12 +399,12 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < U; ++u)
             if (k0 + kk < a.ksplit) v[u] += pv[kk][u];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = q0 + u * 256;
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * NT;
         if (q >= kRouteTokens * nq) continue;
         const int tt = q / nq, e0 = (q - tt * nq) * 4;
 #pragma unroll
@@ -401,16 +418,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
         }
       }
     }
-    for (int i = tid; i < kRouteTokens * (NP - a.N); i += 256) {  // padding experts
+    for (int i = tid; i < kRouteTokens * (NP - a.N); i += NT) {  // padding experts
       const int tt = i / (NP - a.N);
       s_logit[tt * LD + a.N + (i - tt * (NP - a.N))] = 0.f;
     }
   } else {  // (few tokens, many splits) one (token, expert) pair per lane
-    for (int i = tid; i < kRouteTokens * NP; i += 256) {  // padding tokens and experts
+    for (int i = tid; i < kRouteTokens * NP; i += NT) {  // padding tokens and experts
       const int tt = i / NP, e = i - tt * NP;
       if (tt >= n_here || e >= a.N) s_logit[tt * LD + e] = 0.f;
     }
-    for (int i = tid; i < n_here * a.N; i += 256) {
+    for (int i = tid; i < n_here * a.N; i += NT) {
       const int tt = i / a.N, e = i - tt * a.N;
       const int t = t0 + tt;
       // up to 32 partials requested before the first is added (in split order)
@@ -432,8 +449,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  select_tile<NB>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx, a.topk_gate, a.lrank,
-                  a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
+  select_tile<NB, NT / 64>(s_logit, t0, a.n_tok, a.N, a.k, a.select_bias, a.topk_idx,
+                           a.topk_gate, a.lrank, a.blk_counts, a.blk_psum, s_mask, s_psum, s_sel);
 }
 
 template <typename T, int NB>
@@ -447,7 +464,7 @@ hipError_t launch_nb(const RouteArgs& a, hipStream_t s) {
                      a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((route_select_kernel<NB>), dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((route_select_kernel<NB>), dim3(blocks), dim3(select_threads(NB)), 0, s, a);
   return hipGetLastError();
 }
 
