@@ -161,12 +161,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   const int b_lo = mine ? static_cast<int>((static_cast<long>(B) * part) / P) : 0;
   const int b_hi = mine ? static_cast<int>((static_cast<long>(B) * (part + 1)) / P) : 0;
 
-  // partial column sums over this thread's range of blocks
+  // partial column sums over this thread's range of blocks, 8 blocks' loads
+  // requested before they are added (in block order), so a long range costs
+  // a few round trips to L2 instead of one per block
   int c = 0;
   float ps = 0.f;
-  for (int b = b_lo; b < b_hi; ++b) {
-    c += blk_counts[static_cast<size_t>(b) * N + e];
-    ps += blk_psum[static_cast<size_t>(b) * N + e];
+  for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
+    int cv[8];
+    float pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = b0 + u < b_hi;
+      const size_t o = static_cast<size_t>(in ? b0 + u : b_lo) * N + e;
+      cv[u] = in ? blk_counts[o] : 0;
+      pv[u] = in ? blk_psum[o] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c += cv[u];
+      if (b0 + u < b_hi) ps += pv[u];
+    }
   }
   s_cnt[tid] = c;
   s_ps[tid] = ps;
@@ -189,10 +203,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __syncthreads();
   if (mine) {
     int run = s_cnt[tid];
-    for (int b = b_lo; b < b_hi; ++b) {
-      const size_t o = static_cast<size_t>(b) * N + e;
-      blk_base[o] = run;
-      run += blk_counts[o];
+    for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
+      int cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        cv[u] = b0 + u < b_hi ? blk_counts[static_cast<size_t>(b0 + u) * N + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < b_hi) blk_base[static_cast<size_t>(b0 + u) * N + e] = run;
+        run += cv[u];
+      }
     }
   }
   __syncthreads();
