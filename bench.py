@@ -52,11 +52,10 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
 # the sources that decide the expert GEMMs' memory traffic
 GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
 PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 1024
-# matrix-core counters of the expert GEMMs, one --pmc pass (3 SQ + 1 GRBM):
+# matrix-core counters of the expert GEMMs, one --pmc pass (2 SQ + 1 GRBM):
 # busy cycles of the MFMA units summed over the SIMDs, MFMA bf16 operations / 512,
 # and the GPU's active cycles summed over the 8 XCDs
-MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CU_CYCLES",
-                 "GRBM_GUI_ACTIVE")
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
 SIMDS, XCDS = 1024, 8
 
 
@@ -259,7 +258,7 @@ def cpu_baseline(shape, inputs, n_tok, gpu_idx):
 
 def profile_commands(d, workload):
     """The rocprofv3 runs that --summarize-profiles reads (d: their output root)."""
-    run = f"python3 bench.py --workload {workload} --no-cpu-baseline --no-backward"
+    run = f"python3 bench.py --workload {workload} --also= --no-cpu-baseline --no-backward"
     return {
         "trace": (f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- {run} "
                   f"--steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} > {d}/trace_bench.json"),
@@ -278,18 +277,19 @@ def profile_commands(d, workload):
 
 def gemm_template_args(name):
     """(kernel, [template arguments]) of a grouped GEMM kernel name, or None."""
-    m = re.search(r"(expert_gemm_kernel|grouped_gemm_kernel)<([^>]*)>", name)
+    m = re.search(r"(expert_gemm_pp_kernel|expert_gemm_kernel|grouped_gemm_kernel)<([^>]*)>", name)
     return None if m is None else (m.group(1), [a.strip() for a in m.group(2).split(",")])
 
 
 def is_up_gemm(name):
     """The gate/up launch: a grouped GEMM kernel instantiated with GATED = true
-    (expert_gemm_kernel's first template argument, grouped_gemm_kernel's third)."""
+    (the first template argument of expert_gemm_kernel and expert_gemm_pp_kernel,
+    grouped_gemm_kernel's third)."""
     ka = gemm_template_args(name)
     if ka is None:
         return False
     kern, args = ka
-    i = 0 if kern == "expert_gemm_kernel" else 2
+    i = 0 if kern.startswith("expert_gemm") else 2
     return len(args) > i and args[i] == "true"
 
 
@@ -307,8 +307,10 @@ def is_down_gemm(name):
     if ka is None:
         return False
     kern, args = ka
+    if kern == "expert_gemm_pp_kernel":
+        return args[0] == "false"
     if kern == "expert_gemm_kernel":
-        return args[0] == "false" and all(a == "false" for a in args[5:])
+        return args[0] == "false" and all(a == "false" for a in args[5:7])
     return len(args) > 2 and args[2] == "false"
 
 
@@ -436,7 +438,6 @@ def summarize_profiles(d, workload):
             ent = {"kernel": (up[0] if role == "up" else (dn[0][0] if len(dn) == 1 else None)),
                    "gpu_active_cycles": round(cycles),
                    "mfma_busy_frac": round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS), 4),
-                   "cu_busy_frac": round(vals["SQ_BUSY_CU_CYCLES"] * 4 / (cycles * 256), 4),
                    "mfma_flops_issued": int(issued),
                    "algorithmic_flops": alg_flops[role],
                    "issued_over_algorithmic": round(issued / alg_flops[role], 4)}
@@ -480,17 +481,16 @@ def summarize_profiles(d, workload):
     if mrec is not None:
         md += ["", "## Matrix-core counters of the expert GEMMs (--pmc)", "",
                f"Counters {', '.join(MFMA_COUNTERS)}, one pass. MFMA busy = "
-               f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs); CU busy ="
-               " SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x 256 CUs); issued FLOPs ="
+               f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs); issued FLOPs ="
                " SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against the algorithmic"
                " 4 rows d F (gate/up) or 2 rows d F (down); clock = active cycles per XCD over"
                " the kernel trace's mean duration.", "",
-               "| launch | MFMA busy | CU busy | issued / algorithmic FLOPs | clock (GHz) |",
-               "|---|---:|---:|---:|---:|"]
+               "| launch | MFMA busy | issued / algorithmic FLOPs | clock (GHz) |",
+               "|---|---:|---:|---:|"]
         for role in ("up", "down"):
             e_ = mrec[role]
             md.append(f"| {role} `{e_['kernel']}` | {e_['mfma_busy_frac']:.3f} | "
-                      f"{e_['cu_busy_frac']:.3f} | {e_['issued_over_algorithmic']:.3f} | "
+                      f"{e_['issued_over_algorithmic']:.3f} | "
                       f"{e_.get('clock_ghz', float('nan')):.2f} |")
     with open(os.path.join(ROOT, "profiles", f"expert_up_gemm_{workload}.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
