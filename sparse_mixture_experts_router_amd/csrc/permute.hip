@@ -154,10 +154,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   const int tid = threadIdx.x;
   const int B = (n_tok + kRouteTokens - 1) / kRouteTokens;
   // threads per expert (N <= 512 -> up to 2 or more), no more than there are
-  // blocks: their partial sums are added one after another below
+  // blocks: their partial sums are added one after another below.  Lane l
+  // of a wavefront takes expert (wave * 64 + l) mod N, so each load of a block
+  // row is one contiguous read of consecutive experts.
   const int P = min(kScanThreads / N, B > 0 ? B : 1);
-  const int e = tid / P, part = tid - e * P;
-  const bool mine = e < N;
+  const int e = tid % N, part = tid / N;
+  const bool mine = part < P;
+  const int slot = e * P + part;  // this thread's partial in s_cnt / s_ps
   const int b_lo = mine ? static_cast<int>((static_cast<long>(B) * part) / P) : 0;
   const int b_hi = mine ? static_cast<int>((static_cast<long>(B) * (part + 1)) / P) : 0;
 
@@ -182,8 +185,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
       if (b0 + u < b_hi) ps += pv[u];
     }
   }
-  s_cnt[tid] = c;
-  s_ps[tid] = ps;
+  if (mine) {
+    s_cnt[slot] = c;
+    s_ps[slot] = ps;
+  }
   __syncthreads();
   if (mine && part == 0) {
     int run = 0;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   }
   __syncthreads();
   if (mine) {
-    int run = s_cnt[tid];
+    int run = s_cnt[slot];
     for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
       int cv[8];
 #pragma unroll
