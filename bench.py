@@ -63,7 +63,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="deepseek_v3")
     ap.add_argument("--also", default="mixtral_prefill,mixtral_decode,qwen3_skew",
                     help="comma-separated workloads timed after the headline one "
@@ -990,7 +990,11 @@ def time_forward(moe, shape, inputs, steps, warmup, extras=True):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
-        graph.replay()
+        # the capture leaves the GPU idle for a moment; after any idle spell the
+        # GEMMs run up to a third slower for the next ~30 ms while the clock
+        # settles, so the replays get the same warm-up as the eager steps
+        for _ in range(max(warmup, 1)):
+            graph.replay()
         torch.cuda.synchronize()
         gs = torch.cuda.Event(enable_timing=True)
         ge = torch.cuda.Event(enable_timing=True)
