@@ -168,6 +168,10 @@ size_t moe_workspace_size(const moe_config* cfg);
  *   up_tile_rows / down_tile_rows: rows per tile of each grouped GEMM;
  *   route_split: workgroups the router GEMM's reduction is split over
  *     (1 = the router GEMM and the selection run in one kernel);
+ *   route_kernel: 0 = the router kernel (64-token tiles), 1 = the router
+ *     GEMM on the large-tile expert GEMM kernel (256-token tiles, bf16, 129
+ *     to 256 experts, 2048 or more tokens); either way a selection kernel
+ *     adds the route_split partial logits in a fixed order when it is > 1;
  *   down_split: pieces every row of the down pass is split into over its
  *     reduction (decode shapes), else 1;
  *   tail_split_cols: column tiles of the down pass when its last row tiles
@@ -183,6 +187,7 @@ typedef struct {
   int32_t down_kernel;
   int32_t down_tile_rows;
   int32_t route_split;
+  int32_t route_kernel;
   int32_t down_split;
   int32_t tail_split_cols;
   int32_t compute_units;

@@ -533,12 +533,29 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   auto abuf = [&](int q) -> char* { return smem + q * ABUF; };
   auto bbuf = [&](int q) -> char* { return smem + NA * ABUF + q * BBUF; };
 
-  int part = -1, parts = 1, tile = 0, nt = 0;
-  if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
-  const int2 te = g.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int seg = g.offsets[e];
-  const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+  int part = -1, parts = 1, tile = 0, nt = 0, e = 0, m0 = 0, seg = 0, mvalid = 0;
+  const bool dense = !GATED && g.dense_parts > 0;
+  if (dense) {
+    // block b: part b mod parts (with 8 parts every XCD holds one part, so
+    // the tiles it runs at once share that part's weight columns in its
+    // L2), then column tile and row tile
+    const int bid = blockIdx.x;
+    parts = g.dense_parts;
+    part = bid % parts;
+    const int n_nt = (g.n_dim + COLS - 1) / COLS, w = bid / parts;
+    tile = w / n_nt;
+    nt = w - tile * n_nt;
+    m0 = tile * BM;
+    if (m0 >= g.a_rows) return;
+    mvalid = min(BM, g.a_rows - m0);
+  } else {
+    if (!decode_work(g, GATED, COLS, tile, nt, part, parts)) return;
+    const int2 te = g.tiles[tile];
+    e = te.x;
+    m0 = te.y;
+    seg = g.offsets[e];
+    mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+  }
   const int n0 = nt * COLS;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -704,9 +721,10 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   if (part < 0) {
     store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
                                            seg + m0 + wm * WTM, mvalid - wm * WTM, col0, g.n_dim);
-  } else if (!GATED) {  // fp32 partial rows of a split tail tile
-    const long prow = static_cast<long>(part) * g.plan[kPlanStride] + seg + m0 -
-                      g.plan[kPlanRowSplit] + wm * WTM;
+  } else if (!GATED) {  // fp32 partial rows of a split tail tile or of a dense part
+    const long stride = dense ? g.a_rows : g.plan[kPlanStride];
+    const long first = dense ? 0 : g.plan[kPlanRowSplit];
+    const long prow = static_cast<long>(part) * stride + seg + m0 - first + wm * WTM;
     store_block<GATED, false, MB, NB, WTM>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
                                            mvalid - wm * WTM, col0, g.n_dim);
   }
@@ -714,6 +732,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
 
 template <bool GATED>
 hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
+  if (g.dense_parts > 0) return hipErrorInvalidValue;  // launch_dense_gemm
   constexpr int COLS = GATED ? 128 : 256;
   const long blocks = expert_grid(g, GATED, COLS);
   hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED>), dim3(static_cast<unsigned>(blocks)),
@@ -754,6 +773,28 @@ hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s) {
   if (bm == 256) return launch_v<false, 256, 256, 2, false, true>(g, s);
   if (bm == 128) return launch_v<false, 128, 256, 3, false, true>(g, s);
   return hipErrorInvalidValue;
+}
+
+bool dense_gemm_fits(long a_rows, int k_dim, int n_dim, int parts) {
+  // whole pairs of 128-byte buffers, each part at least one; 32-bit lane
+  // offsets into a and into the weights
+  return a_rows > 0 && k_dim % 64 == 0 && n_dim > 0 && n_dim % 8 == 0 && parts >= 1 &&
+         parts <= k_dim / 64 && static_cast<size_t>(a_rows) * k_dim * 2 < (size_t{1} << 32) &&
+         static_cast<size_t>(n_dim) * k_dim * 2 < (size_t{1} << 32);
+}
+
+hipError_t launch_dense_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.dense_parts <= 0 || g.out_part == nullptr || g.w0 == nullptr || g.gather != nullptr ||
+      !dense_gemm_fits(g.a_rows, g.k_dim, g.n_dim, g.dense_parts))
+    return hipErrorInvalidValue;
+  // every part must hold at least one pair of K steps
+  const int npairs = g.k_dim * 2 / kLineBytes;
+  if ((g.dense_parts - 1) * split_share(npairs, g.dense_parts) >= npairs) return hipErrorInvalidValue;
+  const long tiles = (g.a_rows + 255) / 256, n_nt = (g.n_dim + 255) / 256;
+  const long blocks = tiles * n_nt * g.dense_parts;
+  hipLaunchKernelGGL((expert_gemm_pp_kernel<false>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(512), 0, s, g);
+  return hipGetLastError();
 }
 
 int expert_gemm_cols(bool gated, int bm) {

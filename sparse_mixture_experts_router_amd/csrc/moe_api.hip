@@ -66,6 +66,7 @@ long tile_capacity(const moe_config& c, int bm) {
 struct Plan {
   GemmPick up, down;
   int ksplit;  // router reduction split
+  int rdense;  // > 0: the router GEMM on the large-tile kernel, ksplit = rdense parts
   int dsplit;  // down-pass reduction split
   SplitSpec split;  // what the scan may record in the down pass's split plan
   int nnt_up, nnt_down;  // column tiles of the large-tile GEMMs (0: generic kernel)
@@ -113,6 +114,7 @@ moe_status scratch_address(void** ptr) {
 // any reduction, and no forward activations.
 Plan make_plan(const moe_config& c, bool bwd = false) {
   Plan p{};
+  p.cus = device_cus();
   const long rows_per_expert = static_cast<long>(c.T) * c.top_k / c.n_experts;
   const size_t eb_ = c.dtype == MOE_BF16 ? 2 : 4;
   const bool fp8w = c.weight_format == MOE_WEIGHTS_FP8_E4M3;
@@ -145,7 +147,8 @@ Plan make_plan(const moe_config& c, bool bwd = false) {
   sz[R_IDX] = T * k * 4;
   sz[R_GATE] = T * k * 4;
   sz[R_LRANK] = T * k * 4;
-  p.ksplit = route_split(c.T, c.d_model, c.dtype);
+  p.rdense = route_dense_parts(c.T, c.d_model, c.n_experts, c.dtype, p.cus);
+  p.ksplit = p.rdense > 0 ? p.rdense : route_split(c.T, c.d_model, c.dtype);
   sz[R_PART] = p.ksplit > 1 ? static_cast<size_t>(p.ksplit) * T * N * 4 : 0;
   sz[R_BCNT] = B * N * 4;
   sz[R_BPS] = B * N * 4;
@@ -173,7 +176,6 @@ Plan make_plan(const moe_config& c, bool bwd = false) {
   sz[R_NT] = kPlanInts * 4;
   sz[R_HID] = bwd ? 0 : rows * static_cast<size_t>(c.d_ff) * eb;
 
-  p.cus = device_cus();
   {
     // row tiles the down pass will have: about one per expert that gets
     // rows (at most min(N, T k) of them) or T k / bm, whichever is more,
@@ -301,7 +303,8 @@ moe_status run_route(const moe_config& c, const Plan& p, const Workspace& ws, co
                      const moe_weights& w, moe_routing* out, int32_t* idx, float* gate,
                      hipStream_t s) {
   hipError_t err = launch_route(c.dtype, x, w.w_router, w.logit_bias, w.select_bias, c.T,
-                                c.d_model, c.n_experts, c.top_k, p.ksplit, ws.route_partial,
+                                c.d_model, c.n_experts, c.top_k, p.ksplit, p.rdense > 0,
+                                ws.route_partial,
                                 out ? out->logits : nullptr, idx, gate, ws.lrank, ws.blk_counts,
                                 ws.blk_psum, s);
   if (err != hipSuccess) return hip_fail(err, "route kernel");
@@ -479,6 +482,7 @@ moe_status moe_forward_plan(const moe_config* cfg, moe_plan_info* out) {
   out->down_kernel = p.down.variant;
   out->down_tile_rows = p.down.bm;
   out->route_split = p.ksplit;
+  out->route_kernel = p.rdense > 0 ? 1 : 0;
   out->down_split = p.dsplit;
   out->tail_split_cols = p.split.tail_nnt;
   out->compute_units = p.cus;
@@ -715,7 +719,7 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
   // routing and grouping, as in the forward
   mark(ev, MOE_BSTAGE_ROUTE, s);
   err = launch_route(dt, x, w->w_router, w->logit_bias, w->select_bias, T, d, N, k, p.ksplit,
-                     ws.route_partial, logits, ws.topk_idx, ws.topk_gate, ws.lrank, ws.blk_counts,
+                     p.rdense > 0, ws.route_partial, logits, ws.topk_idx, ws.topk_gate, ws.lrank, ws.blk_counts,
                      ws.blk_psum, s);
   if (err != hipSuccess) return hip_fail(err, "route kernel");
   if ((st = run_permute(c, p, ws, nullptr, ws.topk_idx, s)) != MOE_OK) return st;

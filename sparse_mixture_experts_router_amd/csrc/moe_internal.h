@@ -50,10 +50,15 @@ struct Workspace {
 // Router GEMM + selection.  ksplit > 1 splits the reduction over workgroups
 // (few tokens): fp32 partial logits [ksplit, T, N] go to `partial` and a
 // second kernel sums them in a fixed order before the selection.
+// route_dense_parts > 0: the router GEMM runs on the ping-pong expert GEMM
+// kernel in its dense mode (256-token tiles, the reduction split into that
+// many parts) and ksplit must equal it; 0: the router kernel, ksplit from
+// route_split.
 int route_split(int T, int d, int dtype);
+int route_dense_parts(int T, int d, int N, int dtype, int cus);
 hipError_t launch_route(int dtype, const void* x, const void* w_router,
                         const float* logit_bias, const float* select_bias,
-                        int T, int d, int N, int k, int ksplit, float* partial,
+                        int T, int d, int N, int k, int ksplit, bool dense, float* partial,
                         float* logits_out, int32_t* topk_idx, float* topk_gate,
                         int32_t* lrank, int32_t* blk_counts, float* blk_psum,
                         hipStream_t s);
@@ -139,6 +144,11 @@ struct GemmArgs {
   float* out_part;           // fp32 partial outputs [ksplit, a_rows, n_dim] when ksplit > 1
   const int32_t* plan;       // device split plan of the down pass (kPlan* entries), or null
   const int32_t* items;      // large-tile kernel: work items, (tile << 12) | column tile
+  // Dense mode of the ping-pong kernel (launch_dense_gemm): > 0 = the rows
+  // are all a_rows rows of a, in one group whose weights are w0, with no
+  // tile or item list; the reduction is split into this many parts, each
+  // writing fp32 partial outputs [parts, a_rows, n_dim] to out_part.
+  int dense_parts;
   int cus;                   // compute units of the device (grid sizing)
   bool wfp8;                 // weights are FP8 E4M3 codes with per-output-channel scales
   const float* sc0;          // routed scales [N, n_dim] (gate or down), FP8 weights only
@@ -210,6 +220,10 @@ hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s);
 bool expert_gemm_bt_fits(int bm, int k_dim, int n_dim, int rows0, long a_rows);
 hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
+// The plain (non-gated) bf16 ping-pong kernel in dense mode (GemmArgs'
+// dense_parts): hipErrorInvalidValue when the operands do not fit it.
+bool dense_gemm_fits(long a_rows, int k_dim, int n_dim, int parts);
+hipError_t launch_dense_gemm(const GemmArgs& g, hipStream_t s);
 // Output columns per tile of the large-tile kernel launch_expert_gemm picks.
 int expert_gemm_cols(bool gated, int bm);
 

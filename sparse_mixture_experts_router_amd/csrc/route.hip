@@ -494,10 +494,27 @@ int route_split(int T_, int d, int dtype) {
   return (nsteps + per - 1) / per;  // no empty split
 }
 
+int route_dense_parts(int T_, int d, int N, int dtype, int cus) {
+  // The router kernel streams all N router rows through LDS for every 64
+  // tokens, as 64-byte row pieces; with N > 128 that is most of its traffic
+  // (DeepSeek-V3 shape: 128 token blocks x 3.7 MB of router rows against
+  // 117 MB of x).  The large-tile kernel's 256-token tiles of whole 128-byte
+  // lines move a quarter of those router bytes.  Parts: enough to put
+  // about one workgroup on every compute unit, at most 8 (the selection
+  // kernel's fast path sums up to 8 partials per load round).
+  if (dtype != 1 || N <= 128 || N > 256 || T_ < 2048) return 0;
+  const int tiles = (T_ + 255) / 256;
+  int parts = (cus + tiles - 1) / tiles;
+  parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+  while (parts > 1 && (parts - 1) * split_share(d / 64, parts) >= d / 64) --parts;
+  return dense_gemm_fits(T_, d, N, parts) ? parts : 0;
+}
+
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* logit_bias,
                         const float* select_bias, int T_, int d, int N, int k, int ksplit,
-                        float* partial, float* logits_out, int32_t* topk_idx, float* topk_gate,
-                        int32_t* lrank, int32_t* blk_counts, float* blk_psum, hipStream_t s) {
+                        bool dense, float* partial, float* logits_out, int32_t* topk_idx,
+                        float* topk_gate, int32_t* lrank, int32_t* blk_counts, float* blk_psum,
+                        hipStream_t s) {
   RouteArgs a{};
   a.x = x;
   a.wr = w_router;
@@ -518,6 +535,25 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router, const fl
   a.blk_counts = blk_counts;
   a.blk_psum = blk_psum;
   if (a.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
+  if (dense) {
+    // the router GEMM on the large-tile kernel: fp32 partial logits
+    // [ksplit, T, N], then the selection kernel adds them in part order
+    if (dtype != 1 || N <= 128 || N > 256 || partial == nullptr) return hipErrorInvalidValue;
+    GemmArgs g{};
+    g.a = x;
+    g.w0 = w_router;
+    g.a_rows = T_;
+    g.n_experts = 1;
+    g.k_dim = d;
+    g.n_dim = N;
+    g.out_part = partial;
+    g.dense_parts = a.ksplit;
+    hipError_t e = launch_dense_gemm(g, s);
+    if (e != hipSuccess) return e;
+    const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
+    hipLaunchKernelGGL((route_select_kernel<16>), dim3(blocks), dim3(select_threads(16)), 0, s, a);
+    return hipGetLastError();
+  }
   if (dtype == 1) return launch_t<bf16_t>(a, s);
   return launch_t<float>(a, s);
 }

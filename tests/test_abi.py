@@ -303,6 +303,13 @@ def test_forward_plan_reports_the_path():
     assert off % 4 == 0 and off + 16 <= info["workspace_bytes"]
     dec = moe.moe_forward_plan(moe.make_config(32, 4096, 8, 2, 14336))
     assert (dec["up_kernel"], dec["up_tile_rows"]) == (0, 32) and dec["down_split"] >= 2
+    assert info["route_kernel"] == 0  # 8 experts: the router kernel
+    ds = moe.moe_forward_plan(moe.make_config(8192, 7168, 256, 8, 2048, 1))
+    # 256 experts: the router GEMM on the large-tile kernel, 32 tiles of 256
+    # tokens x 8 parts of the reduction on 256 compute units
+    if ds["compute_units"] == 256:
+        assert (ds["route_kernel"], ds["route_split"]) == (1, 8)
+    assert ds["route_kernel"] == 1 and 1 <= ds["route_split"] <= 8
     f32 = moe.moe_forward_plan(moe.make_config(64, 128, 4, 2, 256, 0, "f32"))
     assert f32["up_kernel"] == 0 and f32["tail_split_cols"] == 0
     with pytest.raises(moe.MoEError):

@@ -240,6 +240,28 @@ def test_route_entry_point_matches_forward():
         assert torch.equal(a, b)
 
 
+# Batches of 2048 or more bf16 tokens and 129-256 experts run the router GEMM
+# on the large-tile expert GEMM kernel (256-token tiles, the reduction split
+# into parts that the selection kernel adds in order): a ragged last tile,
+# an expert count that is no multiple of 16, 4 and 8 parts.
+ROUTER_TILE_CASES = [
+    ("ragged_160", MoEShape("rt160", T=2500, d=512, N=160, k=6, F=128, select_bias=True), 4),
+    ("full_256_shared", MoEShape("rt256", T=2048, d=1024, N=256, k=8, F=128, S=1,
+                                 select_bias=True), 8),
+]
+
+
+@pytest.mark.parametrize("label,shape,parts", ROUTER_TILE_CASES,
+                         ids=[c[0] for c in ROUTER_TILE_CASES])
+def test_router_gemm_on_the_large_tile_kernel(label, shape, parts):
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S)
+    info = moe.moe_forward_plan(cfg)
+    assert info["route_kernel"] == 1
+    if info["compute_units"] == 256:
+        assert info["route_split"] == parts
+    full_parity(shape, seed=3, label=label)
+
+
 @pytest.mark.parametrize("shape", [
     reduced(CONFIGS["mixtral_decode"], T=24, d=256, F=256),
     reduced(CONFIGS["qwen3_skew"], T=1000, d=256, F=128, N=128),
