@@ -514,8 +514,11 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 // With one wavefront per SIMD (expert_gemm_kernel) the matrix core idles
 // whenever that wavefront waits for LDS data, for its loads or at the
 // barrier; here the other wavefront of the SIMD covers those waits.
-template <bool GATED>
+// DENSE (plain pass only): GemmArgs' dense mode, a separate instance so that
+// the grouped launches carry no trace of it.
+template <bool GATED, bool DENSE = false>
 __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
+  static_assert(!(GATED && DENSE), "dense mode: plain pass");
   constexpr int BM = 256, BNE = 256;
   constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
   constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   auto bbuf = [&](int q) -> char* { return smem + NA * ABUF + q * BBUF; };
 
   int part = -1, parts = 1, tile = 0, nt = 0, e = 0, m0 = 0, seg = 0, mvalid = 0;
-  const bool dense = !GATED && g.dense_parts > 0;
+  constexpr bool dense = DENSE;
   if (dense) {
     // block b: part b mod parts (with 8 parts every XCD holds one part, so
     // the tiles it runs at once share that part's weight columns in its
@@ -792,7 +795,7 @@ hipError_t launch_dense_gemm(const GemmArgs& g, hipStream_t s) {
   if ((g.dense_parts - 1) * split_share(npairs, g.dense_parts) >= npairs) return hipErrorInvalidValue;
   const long tiles = (g.a_rows + 255) / 256, n_nt = (g.n_dim + 255) / 256;
   const long blocks = tiles * n_nt * g.dense_parts;
-  hipLaunchKernelGGL((expert_gemm_pp_kernel<false>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((expert_gemm_pp_kernel<false, true>), dim3(static_cast<unsigned>(blocks)),
                      dim3(512), 0, s, g);
   return hipGetLastError();
 }
