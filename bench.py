@@ -51,7 +51,7 @@ CPU_F64_WEIGHT_BUDGET = 40 << 30
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
 # the sources that decide the expert GEMMs' memory traffic
 GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
-PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 5, 3, 1, 1024
+PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 20, 3, 1, 1024
 # matrix-core counters of the expert GEMMs, one --pmc pass (2 SQ + 1 GRBM):
 # busy cycles of the MFMA units summed over the SIMDs, MFMA bf16 operations / 512,
 # and the GPU's active cycles summed over the 8 XCDs
