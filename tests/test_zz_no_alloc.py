@@ -62,12 +62,17 @@ def reference(shape, inputs):
     # shared expert and selection bias, 256 experts top-8
     (reduced(CONFIGS["deepseek_v3"], T=160, d=512, F=256),
      reduced(CONFIGS["deepseek_v3"], T=33, d=512, F=256)),
-], ids=["large_tiles", "decode_split_k", "shared_bias"])
+    # 256 experts and 2048+ tokens: the router GEMM on the large-tile kernel
+    # (8 parts of the reduction), then a batch on the router kernel
+    (reduced(CONFIGS["deepseek_v3"], T=2048, d=512, F=128),
+     reduced(CONFIGS["deepseek_v3"], T=300, d=512, F=128)),
+], ids=["large_tiles", "decode_split_k", "shared_bias", "router_tiles"])
 def test_noalloc_matches_forward_on_two_calls(big, small):
     for i, shape in enumerate((big, small)):
         cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S)
         need = moe.moe_workspace_size(cfg)
         assert need <= moe.NOALLOC_SCRATCH_BYTES
+        say(f"[noalloc] call {i + 1}: router kernel {moe.moe_forward_plan(cfg)['route_kernel']}")
         inputs = make_inputs(shape, seed=21 + i, device="cuda")
         got = run_noalloc(shape, inputs)
         ref = reference(shape, inputs)
