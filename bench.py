@@ -307,7 +307,7 @@ def is_down_gemm(name):
     if ka is None:
         return False
     kern, args = ka
-    if kern == "expert_gemm_pp_kernel":  # <GATED, DENSE>: DENSE is the router GEMM
+    if kern == "expert_gemm_pp_kernel":  # <GATED, DENSE, NARROW>: DENSE is the router GEMM
         return args[0] == "false" and (len(args) < 2 or args[1] == "false")
     if kern == "expert_gemm_kernel":
         return args[0] == "false" and all(a == "false" for a in args[5:7])

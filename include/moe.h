@@ -176,6 +176,10 @@ size_t moe_workspace_size(const moe_config* cfg);
  *     reduction (decode shapes), else 1;
  *   tail_split_cols: column tiles of the down pass when its last row tiles
  *     may be split over the reduction (0 = never);
+ *   up_narrow_tails / down_narrow_tails: 1 when an expert's last row tile
+ *     of at most 64 rows runs as one tile over two column tiles (the
+ *     ping-pong large-tile kernel, an even number of column tiles; the down
+ *     pass only with at most 384 rows per expert on average);
  *   split_plan_offset: byte offset in the workspace of the split plan each
  *     forward writes there on the device, int32 [4] = {pieces, first split
  *     row, rows per piece, split row tiles} (pieces = 0: nothing split);
@@ -190,6 +194,8 @@ typedef struct {
   int32_t route_kernel;
   int32_t down_split;
   int32_t tail_split_cols;
+  int32_t up_narrow_tails;
+  int32_t down_narrow_tails;
   int32_t compute_units;
   uint64_t split_plan_offset;
   uint64_t workspace_bytes;

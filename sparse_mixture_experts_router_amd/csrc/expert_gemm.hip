@@ -491,6 +491,142 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------
+// Narrow tail tile of the ping-pong kernel: an expert's last row tile when it
+// holds at most 64 rows, over two column tiles at once (512 effective
+// columns; gated: 256 gate rows then 256 up rows of the weights).
+//
+// An expert's 256-row tiles and its short last tile read the same weight
+// rows.  As a tile of its own the short one ran ahead of its partner (it has
+// almost no MFMA work), so the partner fetched the weights from HBM again,
+// and it still cost most of a full tile.  Over two column tiles it moves
+// about as many bytes per K step as a full tile (64 KB of weights and 8 KB of
+// A rows against 32 + 32 KB), so it keeps pace with the two full tiles it is
+// listed next to and finds their weight rows in L2, and there are half as
+// many of them.  LDS: 2 buffers of 8 KB (A) and 2 of 64 KB (weights).
+// Wavefront w owns rows 32 (w / 4) .. + 32 and effective columns 128 (w % 4)
+// .. + 128 (gated: 64 gate and 64 up columns of the same 64 outputs); one
+// barrier per pair of K steps, the next pair's loads in flight meanwhile.
+template <bool GATED>
+__device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e, int seg, int m0,
+                                            int mvalid, int nt) {
+  constexpr int ABUF = 64 * kLineBytes, BBUF = 512 * kLineBytes;
+  constexpr int COLS = GATED ? 128 : 256;      // output columns of one column tile
+  constexpr int HALF = 2 * COLS;               // gated: staged gate rows before the up rows
+  constexpr int WTM = 32, MB = 2, NB = 8;      // wavefront block: 32 x 128 effective
+  constexpr int NOUT = GATED ? NB / 2 : NB;
+  constexpr int OC = GATED ? 64 : 128;         // output columns per wavefront
+  static_assert(2 * ABUF + 2 * BBUF <= 160 * 1024, "LDS");
+  static_assert(8 * WTM * (128 + 16) <= 2 * ABUF + 2 * BBUF, "staging space");
+  auto abuf = [&](int q) -> char* { return smem + q * ABUF; };
+  auto bbuf = [&](int q) -> char* { return smem + 2 * ABUF + q * BBUF; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave >> 2, cw = wave & 3;
+  const int mlive =
+      __builtin_amdgcn_readfirstlane(min(max((mvalid - rh * WTM + 15) / 16, 0), MB));
+  const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
+  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
+  const bool routed = e < g.n_experts;
+  const int es = routed ? e : e - g.n_experts;
+  const char* const w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
+  const char* const w1 =
+      GATED ? reinterpret_cast<const char*>(routed ? g.w1 : g.ws1) + es * mat_bytes : nullptr;
+  const int n0 = nt * COLS;  // first output column; the tile covers 2 COLS of them
+
+  // loads of a pair: the A rows 8 w .. 8 w + 7 (one 1 KB block per
+  // wavefront) and the staged weight rows 64 w .. 64 w + 63 (eight blocks);
+  // lane l of a block fetches row l / 8, chunk line_lane_chunk; rows past
+  // the tile or the matrix are clamped to a valid row
+  const char* const a_base = reinterpret_cast<const char*>(g.a);
+  uint32_t a_off;
+  {
+    const int R = wave * 8 + (lane >> 3);
+    const int grow = seg + m0 + min(R, mvalid - 1);
+    const int srow = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
+    a_off = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) +
+            line_lane_chunk(lane, 0) * 16;
+  }
+  const int jb0 = wave * 64;
+  const bool up_rows = GATED && jb0 >= HALF;
+  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
+  uint32_t b_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? HALF : 0);
+    const int n = min(n0 + jb, g.n_dim - 1);
+    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
+               line_lane_chunk(lane, j) * 16;
+  }
+  const int npairs = static_cast<int>(row_bytes / kLineBytes);
+  auto issue = [&](int pair, int q) {  // past the end: the last pair again, never read
+    const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
+    load_lds16(a_base + (a_off + pc), abuf(q) + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      load_lds16(b_base + (b_off[j] + pc), bbuf(q) + wave * 8192 + j * 1024);
+  };
+
+  const int frow = lane & 15, fkey = frow & 7;
+  const int fl0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
+  const int fl1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  auto b_row = [&](int j) {  // first staged weight row of block j
+    if (GATED) return (j < NOUT ? 0 : HALF) + cw * (OC) + (j % NOUT) * 16;
+    return cw * 128 + j * 16;
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  wait_vmem<0>();
+  stage_barrier();
+  auto run = [&](auto live_) {
+    constexpr int LIVE = decltype(live_)::value;
+    u32x4 fa[2][MB], fb[2][NB];
+    for (int p = 0; p < npairs; ++p) {
+      issue(p + 1, (p + 1) & 1);  // into the buffer read in pair p - 1
+      const char* const a = abuf(p & 1);
+      const char* const b = bbuf(p & 1);
+      if (LIVE > 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int fl = t ? fl1 : fl0;
+#pragma unroll
+          for (int i = 0; i < LIVE; ++i)
+            fa[t][i] = *reinterpret_cast<const u32x4*>(a + (rh * WTM + i * 16) * kLineBytes + fl);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            fb[t][j] = *reinterpret_cast<const u32x4*>(b + b_row(j) * kLineBytes + fl);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fa[t][i], fb[t][j]);
+      }
+      wait_vmem<0>();  // pair p + 1 landed before anyone reads it
+      stage_barrier();
+    }
+  };
+  if (mlive == MB) run(CInt<MB>{});
+  else if (mlive > 0) run(CInt<MB / 2>{});
+  else run(CInt<0>{});
+
+  // epilogue: every ring read is done (the last barrier), every load landed
+  mfma_drain();
+  char* const stg = smem + wave * WTM * (128 + 16);
+  store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
+                                         seg + m0 + rh * WTM, mvalid - rh * WTM, n0 + cw * OC,
+                                         g.n_dim);
+}
+
+// ------------------------------------------------------------------------
 // Ping-pong variant of the 256 x 256 bf16 tile: 8 wavefronts, two per SIMD.
 //
 // The tile, its work items, its LDS layout (A rows in 2 buffers, weight rows
@@ -515,10 +651,12 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 // whenever that wavefront waits for LDS data, for its loads or at the
 // barrier; here the other wavefront of the SIMD covers those waits.
 // DENSE (plain pass only): GemmArgs' dense mode, a separate instance so that
-// the grouped launches carry no trace of it.
-template <bool GATED, bool DENSE = false>
+// the grouped launches carry no trace of it.  NARROW: the instance that also
+// runs narrow tail items (g.narrow); launches without them take the other.
+template <bool GATED, bool DENSE = false, bool NARROW = false>
 __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   static_assert(!(GATED && DENSE), "dense mode: plain pass");
+  static_assert(!(DENSE && NARROW), "dense mode: no tail items");
   constexpr int BM = 256, BNE = 256;
   constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
   constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
@@ -558,6 +696,10 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     m0 = te.y;
     seg = g.offsets[e];
     mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+    if (NARROW && part < 0 && mvalid <= kNarrowRows) {
+      narrow_tile<GATED>(g, smem, e, seg, m0, mvalid, nt);
+      return;
+    }
   }
   const int n0 = nt * COLS;
 
@@ -738,8 +880,12 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
   if (g.dense_parts > 0) return hipErrorInvalidValue;  // launch_dense_gemm
   constexpr int COLS = GATED ? 128 : 256;
   const long blocks = expert_grid(g, GATED, COLS);
-  hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(512), 0, s, g);
+  if (g.narrow)
+    hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, true>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
+  else
+    hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(512), 0, s, g);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ __device__ __forceinline__ bool decode_work(const GemmArgs& g, bool gated, int c
     if (tail > 0) parts = g.plan[kPlanParts];
   }
   const int nrm = ntl - tail;
-  const long w_nrm = static_cast<long>(nrm) * n_nt;
+  const long w_nrm = g.nitems != nullptr ? *g.nitems : static_cast<long>(nrm) * n_nt;
   const long w_spl = static_cast<long>(tail) * n_nt * parts;
   const long n_lo = w_nrm * xcd / 8, n_cnt = w_nrm * (xcd + 1) / 8 - n_lo;
   const long s_lo = w_spl * xcd / 8, s_cnt = w_spl * (xcd + 1) / 8 - s_lo;

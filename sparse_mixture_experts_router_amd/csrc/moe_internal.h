@@ -79,8 +79,22 @@ struct ItemSpec {
   int window;            // workgroups one XCD runs at once
   int32_t* items_up;
   int32_t* items_down;
-  int32_t* tbases;       // [2 (G + 1) + 2], or null: the scan writes nothing
+  int32_t* tbases;       // [kTbInts(G)], or null: the scan writes nothing
+  // Narrow tail tiles (ping-pong kernel only, an even number of column
+  // tiles): a group's last row tile with at most kNarrowRows rows becomes
+  // items of two column tiles each, listed next to the items of its full
+  // row tiles on the same columns, so that they stream the same weight rows
+  // at about the same time.
+  int narrow_up, narrow_down;
 };
+constexpr int kNarrowRows = 64;
+// Layout of tbases for G = N + S groups: tile bases of the gate/up list
+// [0, G], of the down list [G + 1, 2G + 1], the tiles each list covers
+// (2G + 2, 2G + 3), then item bases of the gate/up list [2G + 4, 3G + 4]
+// and of the down list [3G + 5, 4G + 5] (the last entry of each: its total).
+inline int kTbInts(int G) { return 4 * G + 6; }
+__host__ __device__ inline int tb_items_up(int G) { return 2 * G + 4; }
+__host__ __device__ inline int tb_items_down(int G) { return 3 * G + 5; }
 hipError_t launch_items(const ItemSpec& is, int groups, long max_items, hipStream_t s);
 constexpr int kItemColBits = 12;  // column tile in the low bits of an item
 constexpr int kItemMaxTiles = 1 << 19;
@@ -144,6 +158,8 @@ struct GemmArgs {
   float* out_part;           // fp32 partial outputs [ksplit, a_rows, n_dim] when ksplit > 1
   const int32_t* plan;       // device split plan of the down pass (kPlan* entries), or null
   const int32_t* items;      // large-tile kernel: work items, (tile << 12) | column tile
+  const int32_t* nitems;     // device count of those items (null: tiles x column tiles)
+  int narrow;                // ping-pong kernel: the list holds narrow tail items
   // Dense mode of the ping-pong kernel (launch_dense_gemm): > 0 = the rows
   // are all a_rows rows of a, in one group whose weights are w0, with no
   // tile or item list; the reduction is split into this many parts, each

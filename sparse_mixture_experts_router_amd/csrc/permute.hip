@@ -90,49 +90,83 @@ __device__ __forceinline__ void scatter_row(long i, const int32_t* __restrict__ 
   }
 }
 
+// Items of one row group: its row tiles below tlimit x nnt column tiles, but
+// a narrow last tile (ItemSpec) counts nnt / 2 items of two columns each.
+__device__ __forceinline__ int group_items(int tbase, int tiles, int tlimit, int rows, int bm,
+                                           int nnt, int narrow) {
+  const int T = min(tbase + tiles, tlimit) - tbase;
+  if (T <= 0) return 0;
+  const bool nb = narrow && nnt >= 2 && nnt % 2 == 0 && tbase + tiles <= tlimit &&
+                  rows - (tiles - 1) * bm <= kNarrowRows;
+  return T * nnt - (nb ? nnt / 2 : 0);
+}
+
 // Item i of a large-tile GEMM's list (nnt column tiles, row tiles [0,
-// tlimit)): per row group (tile range [tb[g], tb[g + 1])) blocks of up to 8
-// row tiles x (window / row tiles) column tiles, column by column, the group's
-// items starting at tb[g] * nnt.  The group of item i is found by binary
-// search over tb (ng + 1 entries, non-decreasing).
-__device__ void write_item(int32_t* __restrict__ items, int nnt, const int* tb, int ng,
-                           int tlimit, int window, int i) {
-  {  // item i of a list of tlimit * nnt
-    const int tt = i / nnt;
-    int lo = 0, hi = ng;  // largest g with tb[g] <= tt
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tb[mid] <= tt) lo = mid;
-      else hi = mid;
+// tlimit)): per row group (tile range [tb[g], tb[g + 1]), items from ib[g])
+// blocks of up to 8 row tiles x (window / row tiles) column tiles, column by
+// column.  A group whose item count is short of tiles x nnt ends with a
+// narrow tile: its last block then goes by pairs of columns, the block's
+// full tiles on the first column, on the second, then the narrow item of
+// both.  The group of item i is found by binary search over ib (ng + 1
+// entries, non-decreasing).
+__device__ void write_item(int32_t* __restrict__ items, int nnt, const int* tb, const int* ib,
+                           int ng, int tlimit, int window, int i) {
+  int lo = 0, hi = ng;  // largest g with ib[g] <= i
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ib[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  const int base = tb[lo];
+  const int T = min(tb[lo + 1], tlimit) - base;
+  const bool nb = ib[lo + 1] - ib[lo] != T * nnt;
+  const int TW = min(T, 8), CW = max(1, window / TW);
+  const int q = i - ib[lo];
+  const int nblk = (T + TW - 1) / TW;
+  const int b = min(q / (TW * nnt), nblk - 1);
+  const int r = q - b * TW * nnt;
+  const int tw = min(TW, T - b * TW);
+  int t, c;
+  if (nb && b == nblk - 1) {
+    const int P = 2 * (tw - 1) + 1;  // items per pair of columns
+    const int cp = r / P, s = r - cp * P;
+    if (s < tw - 1) {
+      t = s;
+      c = 2 * cp;
+    } else if (s < 2 * (tw - 1)) {
+      t = s - (tw - 1);
+      c = 2 * cp + 1;
+    } else {
+      t = tw - 1;
+      c = 2 * cp;
     }
-    const int base = tb[lo];
-    const int T = min(tb[lo + 1], tlimit) - base;
-    const int TW = min(T, 8), CW = max(1, window / TW);
-    const int q = i - base * nnt;
-    const int b = q / (TW * nnt);
-    const int r = q - b * TW * nnt;
-    const int tw = min(TW, T - b * TW);
+  } else {
     const int cbi = r / (tw * CW);
     const int r2 = r - cbi * tw * CW;
-    const int c = cbi * CW + r2 / tw;
-    const int t = b * TW + r2 % tw;
-    items[i] = ((base + t) << kItemColBits) | c;
+    c = cbi * CW + r2 / tw;
+    t = r2 % tw;
   }
+  items[i] = ((base + b * TW + t) << kItemColBits) | c;
 }
 
 // One thread per item; blockIdx.y: 0 = gate/up list, 1 = down list.
 __global__ __launch_bounds__(256) void items_kernel(ItemSpec is, int ng) {
   __shared__ int s_tb[kMaxExperts + kMaxShared + 1];
+  __shared__ int s_ib[kMaxExperts + kMaxShared + 1];
   const int pass = blockIdx.y;
   const int nnt = pass == 0 ? is.nnt_up : is.nnt_down;
   int32_t* items = pass == 0 ? is.items_up : is.items_down;
   if (nnt <= 0 || items == nullptr) return;
   const int32_t* tb = is.tbases + pass * (ng + 1);
-  for (int g = threadIdx.x; g <= ng; g += 256) s_tb[g] = tb[g];
+  const int32_t* ib = is.tbases + (pass == 0 ? tb_items_up(ng) : tb_items_down(ng));
+  for (int g = threadIdx.x; g <= ng; g += 256) {
+    s_tb[g] = tb[g];
+    s_ib[g] = ib[g];
+  }
   const int tlimit = is.tbases[2 * (ng + 1) + pass];
   __syncthreads();
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < tlimit * nnt) write_item(items, nnt, s_tb, ng, tlimit, is.window, i);
+  if (i < s_ib[ng]) write_item(items, nnt, s_tb, s_ib, ng, tlimit, is.window, i);
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
@@ -300,6 +334,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (tid == 0) {
       ispec.tbases[2 * (NG + 1)] = min(total_up, cap_up);
       ispec.tbases[2 * (NG + 1) + 1] = s_nrm_down;
+    }
+    // item bases of both lists (a narrow last tile counts half its columns)
+    int iu = 0, idn = 0;
+    if (tid < NG) {
+      iu = group_items(base_up, tu, min(total_up, cap_up), cg, bm_up, ispec.nnt_up,
+                       ispec.narrow_up);
+      idn = group_items(base_down, td, s_nrm_down, cg, bm_down, ispec.nnt_down,
+                        ispec.narrow_down);
+    }
+    int tot_u, tot_d;
+    const int ibu = block_exclusive_scan(iu, s_tmp, &tot_u);
+    const int ibd = block_exclusive_scan(idn, s_tmp, &tot_d);
+    if (tid < NG) {
+      ispec.tbases[tb_items_up(NG) + tid] = ibu;
+      ispec.tbases[tb_items_down(NG) + tid] = ibd;
+    }
+    if (tid == 0) {
+      ispec.tbases[tb_items_up(NG) + NG] = tot_u;
+      ispec.tbases[tb_items_down(NG) + NG] = tot_d;
     }
   }
   // small batches: the permutation too (offsets and block bases are complete

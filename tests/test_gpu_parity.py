@@ -240,6 +240,33 @@ def test_route_entry_point_matches_forward():
         assert torch.equal(a, b)
 
 
+# Narrow tail tiles: an expert's last row tile of at most 64 rows runs as one
+# tile over two column tiles, next to its expert's full tiles.  k = N gives
+# every expert 257 rows (a 256-row tile and a 1-row tail); ~300 rows per
+# expert give tails of assorted sizes on both passes; an odd number of down
+# column tiles (d = 768) keeps them on the gate/up pass only; a shared expert
+# adds a 4-tile group with no narrow tail.
+NARROW_CASES = [
+    ("one_row_tails", MoEShape("nar_k_eq_n", T=257, d=512, N=4, k=4, F=512), (1, 1)),
+    ("assorted_tails", MoEShape("nar_mixed", T=1200, d=512, N=8, k=2, F=512), (1, 1)),
+    ("odd_down_cols_shared", MoEShape("nar_odd", T=1200, d=768, N=8, k=2, F=512, S=1,
+                                      select_bias=True), (1, 0)),
+]
+
+
+@pytest.mark.parametrize("label,shape,flags", NARROW_CASES, ids=[c[0] for c in NARROW_CASES])
+def test_narrow_tail_tiles(label, shape, flags):
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S)
+    info = moe.moe_forward_plan(cfg)
+    assert (info["up_kernel"], info["up_tile_rows"]) == (1, 256)
+    assert (info["up_narrow_tails"], info["down_narrow_tails"]) == flags
+    _, out, _ = full_parity(shape, seed=4, label=label)
+    counts = to_np(out["counts"])
+    tails = [int(c) % 256 for c in counts if int(c) > 0]
+    say(f"[narrow] {label}: rows per expert {counts.tolist()}, last-tile rows {tails}")
+    assert any(0 < t <= 64 for t in tails), "no narrow tail in this case"
+
+
 # Batches of 2048 or more bf16 tokens and 129-256 experts run the router GEMM
 # on the large-tile expert GEMM kernel (256-token tiles, the reduction split
 # into parts that the selection kernel adds in order): a ragged last tile,
