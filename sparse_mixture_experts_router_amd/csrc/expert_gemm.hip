@@ -653,10 +653,21 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
 // DENSE (plain pass only): GemmArgs' dense mode, a separate instance so that
 // the grouped launches carry no trace of it.  NARROW: the instance that also
 // runs narrow tail items (g.narrow); launches without them take the other.
-template <bool GATED, bool DENSE = false, bool NARROW = false>
+// FP8W: E4M3 weights.  A weight buffer holds 128 codes of each weight row,
+// the K elements of two pairs, in the layout and with the loads of a bf16
+// buffer (whole 128-byte lines; 64-byte half rows per pair made as many L2
+// requests per pair as bf16 weights and gained nothing).  Group 1 loads a
+// buffer every second pair, two buffers ahead.  One 16-byte read (chunk
+// lane / 16 of the pair's half row) gives a lane the codes of its fragment
+// for both K steps of the pair (bytes 0-7 and 8-15), and the A chunks are
+// read in the matching order (chunk 2 (lane / 16) + t in step t).  The
+// compute phase widens each weight fragment to bf16 right before its MFMAs;
+// the epilogue applies the per-output-channel scales.
+template <bool GATED, bool DENSE = false, bool NARROW = false, bool FP8W = false>
 __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   static_assert(!(GATED && DENSE), "dense mode: plain pass");
   static_assert(!(DENSE && NARROW), "dense mode: no tail items");
+  static_assert(!(FP8W && (DENSE || NARROW)), "FP8 weights: grouped launches, no narrow items");
   constexpr int BM = 256, BNE = 256;
   constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
   constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
@@ -665,9 +676,10 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   constexpr int MB = WTM / 16, NB = WTN / 16;  // 4 x 8 MFMA blocks
   constexpr int NOUT = GATED ? NB / 2 : NB;
   constexpr int COLS = GATED ? BNE / 2 : BNE;  // output columns per tile
-  constexpr int LPW = 8;                       // 1 KB loads per wavefront per pair
+  constexpr int LPW = 8;                       // group 0: 1 KB A loads per wavefront per pair
+  constexpr int LPWB = BBUF / 4 / 1024;        // group 1: 1 KB weight loads per buffer
   constexpr int NF = MB + NB;                  // fragments per K step
-  static_assert(4 * LPW * 1024 == ABUF && 4 * LPW * 1024 == BBUF, "one group fills a ring");
+  static_assert(4 * LPW * 1024 == ABUF && 4 * LPWB * 1024 == BBUF, "one group fills a ring");
   static_assert(8 * WTM * (128 + 16) <= SMEM, "staging space");
 
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -710,7 +722,8 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   const int mlive = __builtin_amdgcn_readfirstlane(min(max((mvalid - wm * WTM + 15) / 16, 0), MB));
 
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
-  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
+  const size_t wrow_bytes = static_cast<size_t>(g.k_dim) * (FP8W ? 1 : 2);
+  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * wrow_bytes;
   const bool routed = e < g.n_experts;
   const int es = routed ? e : e - g.n_experts;
   const char* const w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
@@ -723,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // of a block fetches row l / 8 of it, the chunk line_lane_chunk assigns;
   // rows past the tile or the matrix are clamped to a valid row.
   const char* src_base;
-  uint32_t off[LPW];
+  uint32_t off[LPW] = {};
   if (grp == 0) {
     src_base = reinterpret_cast<const char*>(g.a);
 #pragma unroll
@@ -737,38 +750,50 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   } else {
     const int jb0 = q * 64;
     const bool up_rows = GATED && jb0 >= COLS;
-    src_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
+    src_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * wrow_bytes;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
+    for (int j = 0; j < LPWB; ++j) {
       const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? COLS : 0);
       const int n = min(n0 + jb, g.n_dim - 1);
-      off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
+      off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) +
                line_lane_chunk(lane, j) * 16;
     }
   }
   int npairs = static_cast<int>(row_bytes / kLineBytes);
+  // source bytes of a row per buffer: A 128 (a pair), weights 128 (a pair;
+  // FP8 two pairs, so a pair is 64)
+  const int pstep = grp == 0 || !FP8W ? kLineBytes : kLineBytes / 2;
   if (part >= 0) {
-    const int per = split_share(npairs, parts);
+    const int per = split_share(npairs, parts);  // even: FP8 buffers stay whole
     const int p0 = part * per;
     npairs = min(per, npairs - p0);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) off[j] += static_cast<uint32_t>(p0) * kLineBytes;
+    for (int j = 0; j < LPW; ++j) off[j] += static_cast<uint32_t>(p0 * pstep);
   }
-  const int dst = q * LPW * 1024;
-  // this wavefront's 8 loads of pair `pair` (past the end: the last pair
-  // again, into a buffer nobody reads again)
-  auto issue = [&](int pair, char* ring) {
-    const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
+  // this wavefront's 8 loads of buffer `buf` (a pair; FP8 weights: the pair
+  // pair 2 buf and 2 buf + 1); past the end the last one again, into a buffer
+  // nobody reads again
+  const int nbufs = grp == 0 || !FP8W ? npairs : npairs / 2;
+  auto issue = [&](int buf, char* ring) {
+    const uint32_t pc = static_cast<uint32_t>(min(buf, nbufs - 1) * kLineBytes);
+    const int dst = q * LPW * 1024;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) load_lds16(src_base + (off[j] + pc), ring + dst + j * 1024);
   };
 
   // Fragment reads: lane l takes row l mod 16 of a 16-row block, chunk
-  // l / 16 (+ 4 for the second K step) under the row-mod-8 swizzle.
+  // l / 16 (+ 4 for the second K step; FP8 weights: chunk 2 (l / 16) + t)
+  // under the row-mod-8 swizzle; an FP8 weight fragment is 16 bytes of a
+  // 64-byte staged row.
   const int frow = lane & 15;
   const int fkey = frow & 7;
-  const int fl0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
-  const int fl1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  const int ca0 = FP8W ? 2 * (lane >> 4) : (lane >> 4);
+  const int ca1 = FP8W ? 2 * (lane >> 4) + 1 : 4 + (lane >> 4);
+  const int fl0 = frow * kLineBytes + ((ca0 ^ fkey) << 4);
+  const int fl1 = frow * kLineBytes + ((ca1 ^ fkey) << 4);
+  // FP8 weight fragment of the first / second pair of a buffer
+  const int f8l0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
+  const int f8l1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
   auto b_row = [&](int j) {  // first staged weight row of block j
     if (GATED) return (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
     return wn * WTN + j * 16;
@@ -782,13 +807,14 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   u32x4 fr[2][NF];
 
   // prologue: group 0 A(0); group 1 B(0) then B(1); A(0) and B(0) landed
+  // (FP8: weight buffers 0 and 1, pairs 0 .. 3)
   if (grp == 0) {
     issue(0, abuf(0));
     wait_vmem<0>();
   } else {
     issue(0, bbuf(0));
     issue(1, bbuf(1));
-    wait_vmem<LPW>();
+    wait_vmem<LPWB>();
   }
   stage_barrier();
 
@@ -800,34 +826,61 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     constexpr int G = decltype(grp_)::value;
     auto memory = [&](int p) {
       const char* const a = abuf(p & 1);
-      const char* const b = bbuf(p % 3);
+      const int qb = FP8W ? (p >> 1) % 3 : p % 3;  // weight buffer of pair p
+      const char* const b = bbuf(qb);
       if (G == 0) issue(p + 1, abuf((p + 1) & 1));
-      else issue(p + 2, bbuf((p + 2) % 3));
+      else if (!FP8W) issue(p + 2, bbuf((p + 2) % 3));
+      else if ((p & 1) == 0) issue((p >> 1) + 2, bbuf(((p >> 1) + 2) % 3));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int fl = t ? fl1 : fl0;
 #pragma unroll
         for (int i = 0; i < LIVE; ++i)
           fr[t][i] = *reinterpret_cast<const u32x4*>(a + (wm * WTM + i * 16) * kLineBytes + fl);
-        if (LIVE > 0) {
+        if (LIVE > 0 && (!FP8W || t == 0)) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            fr[t][MB + j] = *reinterpret_cast<const u32x4*>(b + b_row(j) * kLineBytes + fl);
+            fr[t][MB + j] = *reinterpret_cast<const u32x4*>(
+                b + b_row(j) * kLineBytes + (FP8W ? ((p & 1) ? f8l1 : f8l0) : fl));
         }
       }
       // fragments in registers; group 0 leaves A(p + 1) in flight (waited
       // for after its compute phase), group 1 waits for B(p + 1) and leaves
-      // B(p + 2) in flight
+      // B(p + 2) in flight (FP8: after an odd pair, waits for the buffer of
+      // the next two pairs and leaves the one after in flight; after an even
+      // pair the next pair's buffer is the current one)
       if (G == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      else wait_vmem<LPW>();
+      else if (!FP8W || (p & 1)) wait_vmem<LPWB>();
     };
     auto compute = [&]() {
+      if constexpr (FP8W) {
+        // weight fragment j of step t widened from its 8 codes; the first
+        // MFMA reading it carries the VALU -> MFMA wait states.  The previous
+        // widened fragment stays allocated until the next one's MFMAs are
+        // issued, so a widening never writes registers an MFMA just issued
+        // still reads.
+        u32x4 wprev = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+          for (int j = 0; j < NB; ++j) {
+            if (LIVE == 0) continue;
+            const u32x4 c = fr[0][MB + j];
+            const u32x4 w = e4m3x8_to_bf16(t ? make_uint2(c[2], c[3]) : make_uint2(c[0], c[1]));
+            mfma_bf16_agpr_after_valu(acc[0][j], fr[t][0], w);
 #pragma unroll
-          for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fr[t][i], fr[t][MB + j]);
+            for (int i = 1; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fr[t][i], w);
+            asm volatile("" ::"v"(wprev));
+            wprev = w;
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fr[t][i], fr[t][MB + j]);
+      }
     };
     if (G == 0) {
       for (int p = 0; p < npairs; ++p) {
@@ -863,15 +916,22 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
   char* const stg = smem + wave * WTM * (128 + 16);
   const int col0 = n0 + wn * OC;
+  const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
+  const float* sc1 = nullptr;
+  if (FP8W) {
+    sc0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
+    if (GATED) sc1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
+  }
   if (part < 0) {
-    store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
-                                           seg + m0 + wm * WTM, mvalid - wm * WTM, col0, g.n_dim);
+    store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
+                                                 seg + m0 + wm * WTM, mvalid - wm * WTM, col0,
+                                                 g.n_dim, sc0, sc1);
   } else if (!GATED) {  // fp32 partial rows of a split tail tile or of a dense part
     const long stride = dense ? g.a_rows : g.plan[kPlanStride];
     const long first = dense ? 0 : g.plan[kPlanRowSplit];
     const long prow = static_cast<long>(part) * stride + seg + m0 - first + wm * WTM;
-    store_block<GATED, false, MB, NB, WTM>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
-                                           mvalid - wm * WTM, col0, g.n_dim);
+    store_block<GATED, false, MB, NB, WTM, FP8W>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
+                                                 mvalid - wm * WTM, col0, g.n_dim, sc0, sc1);
   }
 }
 
@@ -880,7 +940,11 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
   if (g.dense_parts > 0) return hipErrorInvalidValue;  // launch_dense_gemm
   constexpr int COLS = GATED ? 128 : 256;
   const long blocks = expert_grid(g, GATED, COLS);
-  if (g.narrow)
+  if (g.wfp8) {
+    if (g.narrow) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, false, true>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
+  } else if (g.narrow)
     hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, true>),
                        dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
   else
@@ -958,9 +1022,9 @@ hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t
   if (g.wfp8) {
     // FP8 weights: 48 KB (256-row tiles) or 32 KB (128-row tiles) per buffer,
     // so one more buffer of loads fits in flight than with bf16 weights
-    if (bm == 256) {
-      if (gated) return launch_v<true, 256, 256, 3, true>(g, s);
-      return launch_v<false, 256, 256, 3, true>(g, s);
+    if (bm == 256) {  // 8-wavefront ping-pong tiles
+      if (gated) return launch_pp<true>(g, s);
+      return launch_pp<false>(g, s);
     }
     if (bm != 128) return hipErrorInvalidValue;
     if (gated) return launch_v<true, 128, 256, 4, true>(g, s);
