@@ -506,7 +506,10 @@ hipError_t launch_v(const GemmArgs& g, hipStream_t s) {
 // Wavefront w owns rows 32 (w / 4) .. + 32 and effective columns 128 (w % 4)
 // .. + 128 (gated: 64 gate and 64 up columns of the same 64 outputs); one
 // barrier per pair of K steps, the next pair's loads in flight meanwhile.
-template <bool GATED>
+// FP8W: a weight buffer holds the 128 codes of two pairs per row (whole
+// lines, as in the full tiles), loaded every second pair; the fragments and
+// their widening are those of the full tiles.
+template <bool GATED, bool FP8W>
 __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e, int seg, int m0,
                                             int mvalid, int nt) {
   constexpr int ABUF = 64 * kLineBytes, BBUF = 512 * kLineBytes;
@@ -526,7 +529,8 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
   const int mlive =
       __builtin_amdgcn_readfirstlane(min(max((mvalid - rh * WTM + 15) / 16, 0), MB));
   const size_t row_bytes = static_cast<size_t>(g.k_dim) * 2;
-  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * row_bytes;
+  const size_t wrow_bytes = static_cast<size_t>(g.k_dim) * (FP8W ? 1 : 2);
+  const size_t mat_bytes = static_cast<size_t>(g.n_dim) * wrow_bytes;
   const bool routed = e < g.n_experts;
   const int es = routed ? e : e - g.n_experts;
   const char* const w0 = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) + es * mat_bytes;
@@ -549,27 +553,38 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
   }
   const int jb0 = wave * 64;
   const bool up_rows = GATED && jb0 >= HALF;
-  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * row_bytes;
+  const char* const b_base = (up_rows ? w1 : w0) + static_cast<size_t>(n0) * wrow_bytes;
   uint32_t b_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int jb = jb0 + j * 8 + (lane >> 3) - (up_rows ? HALF : 0);
     const int n = min(n0 + jb, g.n_dim - 1);
-    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(row_bytes) +
+    b_off[j] = static_cast<uint32_t>(n - n0) * static_cast<uint32_t>(wrow_bytes) +
                line_lane_chunk(lane, j) * 16;
   }
-  const int npairs = static_cast<int>(row_bytes / kLineBytes);
-  auto issue = [&](int pair, int q) {  // past the end: the last pair again, never read
+  const int npairs = static_cast<int>(row_bytes / kLineBytes);  // even
+  // the loads of pair `pair`: its A rows, and its weight buffer's rows (FP8:
+  // only for even pairs, the buffer of this pair and the next); past the end
+  // the last one again, never read
+  auto issue = [&](int pair, int q) {
     const uint32_t pc = static_cast<uint32_t>(min(pair, npairs - 1)) * kLineBytes;
     load_lds16(a_base + (a_off + pc), abuf(q) + wave * 1024);
+    if (FP8W && (pair & 1)) return;
+    const int bq = FP8W ? (pair >> 1) & 1 : q;
+    const uint32_t bc = FP8W ? static_cast<uint32_t>(min(pair >> 1, npairs / 2 - 1)) * kLineBytes : pc;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      load_lds16(b_base + (b_off[j] + pc), bbuf(q) + wave * 8192 + j * 1024);
+      load_lds16(b_base + (b_off[j] + bc), bbuf(bq) + wave * 8192 + j * 1024);
   };
 
   const int frow = lane & 15, fkey = frow & 7;
-  const int fl0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
-  const int fl1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  const int ca0 = FP8W ? 2 * (lane >> 4) : (lane >> 4);
+  const int ca1 = FP8W ? 2 * (lane >> 4) + 1 : 4 + (lane >> 4);
+  const int fl0 = frow * kLineBytes + ((ca0 ^ fkey) << 4);
+  const int fl1 = frow * kLineBytes + ((ca1 ^ fkey) << 4);
+  // FP8 weight fragment of the first / second pair of a buffer
+  const int f8l0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
+  const int f8l1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
   auto b_row = [&](int j) {  // first staged weight row of block j
     if (GATED) return (j < NOUT ? 0 : HALF) + cw * (OC) + (j % NOUT) * 16;
     return cw * 128 + j * 16;
@@ -588,9 +603,10 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
     constexpr int LIVE = decltype(live_)::value;
     u32x4 fa[2][MB], fb[2][NB];
     for (int p = 0; p < npairs; ++p) {
-      issue(p + 1, (p + 1) & 1);  // into the buffer read in pair p - 1
+      // into the buffers read in pairs p - 1 (A) and p - 2, p - 1 (FP8 weights)
+      issue(p + 1, (p + 1) & 1);
       const char* const a = abuf(p & 1);
-      const char* const b = bbuf(p & 1);
+      const char* const b = bbuf(FP8W ? (p >> 1) & 1 : p & 1);
       if (LIVE > 0) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -598,17 +614,39 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
 #pragma unroll
           for (int i = 0; i < LIVE; ++i)
             fa[t][i] = *reinterpret_cast<const u32x4*>(a + (rh * WTM + i * 16) * kLineBytes + fl);
+          if (!FP8W || t == 0) {
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            fb[t][j] = *reinterpret_cast<const u32x4*>(b + b_row(j) * kLineBytes + fl);
+            for (int j = 0; j < NB; ++j)
+              fb[t][j] = *reinterpret_cast<const u32x4*>(
+                  b + b_row(j) * kLineBytes + (FP8W ? ((p & 1) ? f8l1 : f8l0) : fl));
+          }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (FP8W) {
+          // as in the full tiles: widen, then the MFMAs, the first with the
+          // VALU -> MFMA wait states; the previous widened fragment stays
+          // allocated until the next one's MFMAs are issued
+          u32x4 wprev = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
+            for (int j = 0; j < NB; ++j) {
+              const u32x4 c = fb[0][j];
+              const u32x4 w = e4m3x8_to_bf16(t ? make_uint2(c[2], c[3]) : make_uint2(c[0], c[1]));
+              mfma_bf16_agpr_after_valu(acc[0][j], fa[t][0], w);
 #pragma unroll
-            for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fa[t][i], fb[t][j]);
+              for (int i = 1; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fa[t][i], w);
+              asm volatile("" ::"v"(wprev));
+              wprev = w;
+            }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+              for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fa[t][i], fb[t][j]);
+        }
       }
       wait_vmem<0>();  // pair p + 1 landed before anyone reads it
       stage_barrier();
@@ -621,9 +659,15 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
   // epilogue: every ring read is done (the last barrier), every load landed
   mfma_drain();
   char* const stg = smem + wave * WTM * (128 + 16);
-  store_block<GATED, GATED, MB, NB, WTM>(acc, stg, lane, g.out, false, g.n_dim,
-                                         seg + m0 + rh * WTM, mvalid - rh * WTM, n0 + cw * OC,
-                                         g.n_dim);
+  const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
+  const float* sc1 = nullptr;
+  if (FP8W) {
+    sc0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
+    if (GATED) sc1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
+  }
+  store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
+                                               seg + m0 + rh * WTM, mvalid - rh * WTM,
+                                               n0 + cw * OC, g.n_dim, sc0, sc1);
 }
 
 // ------------------------------------------------------------------------
@@ -667,7 +711,7 @@ template <bool GATED, bool DENSE = false, bool NARROW = false, bool FP8W = false
 __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   static_assert(!(GATED && DENSE), "dense mode: plain pass");
   static_assert(!(DENSE && NARROW), "dense mode: no tail items");
-  static_assert(!(FP8W && (DENSE || NARROW)), "FP8 weights: grouped launches, no narrow items");
+  static_assert(!(FP8W && DENSE), "FP8 weights: grouped launches");
   constexpr int BM = 256, BNE = 256;
   constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
   constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
@@ -709,7 +753,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     seg = g.offsets[e];
     mvalid = min(BM, g.offsets[e + 1] - seg - m0);
     if (NARROW && part < 0 && mvalid <= kNarrowRows) {
-      narrow_tile<GATED>(g, smem, e, seg, m0, mvalid, nt);
+      narrow_tile<GATED, FP8W>(g, smem, e, seg, m0, mvalid, nt);
       return;
     }
   }
@@ -940,11 +984,13 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
   if (g.dense_parts > 0) return hipErrorInvalidValue;  // launch_dense_gemm
   constexpr int COLS = GATED ? 128 : 256;
   const long blocks = expert_grid(g, GATED, COLS);
-  if (g.wfp8) {
-    if (g.narrow) return hipErrorInvalidValue;
+  if (g.wfp8 && g.narrow)
+    hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, true, true>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
+  else if (g.wfp8)
     hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, false, true>),
                        dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
-  } else if (g.narrow)
+  else if (g.narrow)
     hipLaunchKernelGGL((expert_gemm_pp_kernel<GATED, false, true>),
                        dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, g);
   else

@@ -171,15 +171,15 @@ Plan make_plan(const moe_config& c, bool bwd = false) {
     const int cols = expert_gemm_cols(false, p.down.bm);
     p.nnt_down = (c.d_model + cols - 1) / cols;
   }
-  // narrow tail items: forward passes on the ping-pong kernel (bf16 weights,
-  // 256-row tiles), with an even number of column tiles
-  p.narrow_up = !bwd && c.dtype == MOE_BF16 && !fp8w && p.up.variant == 1 && p.up.bm == 256 &&
+  // narrow tail items: forward passes on the ping-pong kernel (bf16 or FP8
+  // weights, 256-row tiles), with an even number of column tiles
+  p.narrow_up = !bwd && c.dtype == MOE_BF16 && p.up.variant == 1 && p.up.bm == 256 &&
                 p.nnt_up >= 2 && p.nnt_up % 2 == 0;
   // (down pass: only with few rows per expert.  Measured, same box: the
   // DeepSeek-V3 shape's down launch 2.39 -> 2.24 ms with them, but the
   // Mixtral- and Qwen3-shaped ones, ~1024 rows per expert, 0.717 -> 0.754
   // and 1.674 -> 1.730 ms)
-  p.narrow_down = !bwd && c.dtype == MOE_BF16 && !fp8w && p.down.variant == 1 &&
+  p.narrow_down = !bwd && c.dtype == MOE_BF16 && p.down.variant == 1 &&
                   p.down.bm == 256 && p.nnt_down >= 2 && p.nnt_down % 2 == 0 &&
                   rows_per_expert <= 384;
   sz[R_IUP] = static_cast<size_t>(p.cap_up) * p.nnt_up * 4;

@@ -73,6 +73,29 @@ def test_fp8_parity(label, shape):
     full_parity(shape, seed=4, label=f"fp8_{label}")
 
 
+# Narrow tail tiles with FP8 weights: 257 rows per expert (1-row tails), and
+# ~300 rows per expert (assorted tails on both passes, a shared expert's
+# 5-tile group beside them).
+FP8_NARROW_CASES = [
+    ("one_row_tails", MoEShape("fp8_nar1", T=257, d=512, N=4, k=4, F=512, fp8=True)),
+    ("assorted_tails_shared", MoEShape("fp8_nar", T=1200, d=512, N=8, k=2, F=512, S=1,
+                                       fp8=True)),
+]
+
+
+@pytest.mark.parametrize("label,shape", FP8_NARROW_CASES, ids=[c[0] for c in FP8_NARROW_CASES])
+def test_fp8_narrow_tail_tiles(label, shape):
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S,
+                          weight_format=moe.MOE_WEIGHTS_FP8_E4M3)
+    info = moe.moe_forward_plan(cfg)
+    assert (info["up_kernel"], info["up_tile_rows"]) == (1, 256)
+    assert (info["up_narrow_tails"], info["down_narrow_tails"]) == (1, 1)
+    _, out, _ = full_parity(shape, seed=4, label=f"fp8_{label}")
+    tails = [int(c) % 256 for c in to_np(out["counts"]) if int(c) > 0]
+    say(f"[fp8 narrow] {label}: last-tile rows {tails}")
+    assert any(0 < t <= 64 for t in tails), "no narrow tail in this case"
+
+
 @pytest.mark.parametrize("S", [0, 1])
 def test_fp8_tail_tiles_split_over_k(S):
     """The large-tile down pass's tail split with FP8 weights: every token on
