@@ -169,7 +169,7 @@ size_t moe_workspace_size(const moe_config* cfg);
  *   route_split: workgroups the router GEMM's reduction is split over
  *     (1 = the router GEMM and the selection run in one kernel);
  *   route_kernel: 0 = the router kernel (64-token tiles), 1 = the router
- *     GEMM on the large-tile expert GEMM kernel (256-token tiles, bf16, 129
+ *     GEMM on the large-tile expert GEMM kernel (256-token tiles, bf16, 128
  *     to 256 experts, 2048 or more tokens); either way a selection kernel
  *     adds the route_split partial logits in a fixed order when it is > 1;
  *   down_split: pieces every row of the down pass is split into over its

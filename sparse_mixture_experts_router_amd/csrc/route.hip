@@ -499,10 +499,12 @@ int route_dense_parts(int T_, int d, int N, int dtype, int cus) {
   // tokens, as 64-byte row pieces; with N > 128 that is most of its traffic
   // (DeepSeek-V3 shape: 128 token blocks x 3.7 MB of router rows against
   // 117 MB of x).  The large-tile kernel's 256-token tiles of whole 128-byte
-  // lines move a quarter of those router bytes.  Parts: enough to put
-  // about one workgroup on every compute unit, at most 8 (the selection
-  // kernel's fast path sums up to 8 partials per load round).
-  if (dtype != 1 || N <= 128 || N > 256 || T_ < 2048) return 0;
+  // lines move a quarter of those router bytes.  At 128 experts its 256
+  // columns are half idle and it still wins (Qwen3 shape: router GEMM and
+  // selection 73.6 -> 64.9 us).  Parts: enough to put about one workgroup on
+  // every compute unit, at most 8 (the selection kernel's fast path sums up
+  // to 8 partials per load round).
+  if (dtype != 1 || N < 128 || N > 256 || T_ < 2048) return 0;
   const int tiles = (T_ + 255) / 256;
   int parts = (cus + tiles - 1) / tiles;
   parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
@@ -538,7 +540,7 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router, const fl
   if (dense) {
     // the router GEMM on the large-tile kernel: fp32 partial logits
     // [ksplit, T, N], then the selection kernel adds them in part order
-    if (dtype != 1 || N <= 128 || N > 256 || partial == nullptr) return hipErrorInvalidValue;
+    if (dtype != 1 || N < 128 || N > 256 || partial == nullptr) return hipErrorInvalidValue;
     GemmArgs g{};
     g.a = x;
     g.w0 = w_router;
@@ -551,7 +553,10 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router, const fl
     hipError_t e = launch_dense_gemm(g, s);
     if (e != hipSuccess) return e;
     const int blocks = (T_ + kRouteTokens - 1) / kRouteTokens;
-    hipLaunchKernelGGL((route_select_kernel<16>), dim3(blocks), dim3(select_threads(16)), 0, s, a);
+    if (N > 128)
+      hipLaunchKernelGGL((route_select_kernel<16>), dim3(blocks), dim3(select_threads(16)), 0, s, a);
+    else
+      hipLaunchKernelGGL((route_select_kernel<8>), dim3(blocks), dim3(select_threads(8)), 0, s, a);
     return hipGetLastError();
   }
   if (dtype == 1) return launch_t<bf16_t>(a, s);

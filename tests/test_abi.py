@@ -310,6 +310,10 @@ def test_forward_plan_reports_the_path():
     if ds["compute_units"] == 256:
         assert (ds["route_kernel"], ds["route_split"]) == (1, 8)
     assert ds["route_kernel"] == 1 and 1 <= ds["route_split"] <= 8
+    qw = moe.moe_forward_plan(moe.make_config(16384, 4096, 128, 8, 1536))
+    assert qw["route_kernel"] == 1  # 128 experts: the large-tile kernel too
+    few = moe.moe_forward_plan(moe.make_config(4096, 4096, 96, 8, 1536))
+    assert few["route_kernel"] == 0  # 96 experts: the router kernel
     f32 = moe.moe_forward_plan(moe.make_config(64, 128, 4, 2, 256, 0, "f32"))
     assert f32["up_kernel"] == 0 and f32["tail_split_cols"] == 0
     with pytest.raises(moe.MoEError):

@@ -272,6 +272,8 @@ def test_narrow_tail_tiles(label, shape, flags):
 # into parts that the selection kernel adds in order): a ragged last tile,
 # an expert count that is no multiple of 16, 4 and 8 parts.
 ROUTER_TILE_CASES = [
+    ("n128_shared", MoEShape("rt128s", T=2600, d=768, N=128, k=4, F=256, S=1, select_bias=True), 6),
+    ("n128", MoEShape("rt128", T=2048, d=512, N=128, k=8, F=256), 4),
     ("ragged_160", MoEShape("rt160", T=2500, d=512, N=160, k=6, F=128, select_bias=True), 4),
     ("full_256_shared", MoEShape("rt256", T=2048, d=1024, N=256, k=8, F=128, S=1,
                                  select_bias=True), 8),
