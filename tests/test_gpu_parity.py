@@ -267,8 +267,9 @@ def test_narrow_tail_tiles(label, shape, flags):
     assert any(0 < t <= 64 for t in tails), "no narrow tail in this case"
 
 
-@pytest.mark.parametrize("S", [0, 1])
-def test_narrow_tails_beside_the_down_pass_tail_split(S):
+@pytest.mark.parametrize("S,fp8", [(0, False), (1, False), (1, True)],
+                         ids=["S0", "S1", "S1_fp8"])
+def test_narrow_tails_beside_the_down_pass_tail_split(S, fp8):
     """A down pass with narrow tail items and a last-round split over K:
     expert 14 gets 300 rows (a 256-row tile and a 44-row narrow tail in the
     paired item layout), expert 15 the other 4000 (16 tiles), and the scan
@@ -276,8 +277,9 @@ def test_narrow_tails_beside_the_down_pass_tail_split(S):
     expert's) over their reduction.  Routing is fixed by one-hot router rows
     and a large entry of x in the chosen expert's column."""
     T, N = 4300, 16
-    shp = MoEShape("nar_split", T=T, d=4096, N=N, k=1, F=1024, S=S)
-    cfg = moe.make_config(T, 4096, N, 1, 1024, S)
+    shp = MoEShape("nar_split", T=T, d=4096, N=N, k=1, F=1024, S=S, fp8=fp8)
+    cfg = moe.make_config(T, 4096, N, 1, 1024, S,
+                          weight_format=moe.MOE_WEIGHTS_FP8_E4M3 if fp8 else moe.MOE_WEIGHTS_DTYPE)
     info = moe.moe_forward_plan(cfg)
     assert info["down_narrow_tails"] == 1 and info["tail_split_cols"] > 0
     inputs = make_inputs(shp, seed=9, device="cuda")
@@ -290,11 +292,11 @@ def test_narrow_tails_beside_the_down_pass_tail_split(S):
     wr[torch.arange(N), torch.arange(N)] = 1.0
     inputs["x"] = x.to(torch.bfloat16)
     inputs["w_router"] = wr.to(torch.bfloat16)
-    _, out, _ = full_parity(shp, inputs=inputs, label=f"narrow_split_S{S}")
+    _, out, _ = full_parity(shp, inputs=inputs, label=f"narrow_split_S{S}{'_fp8' if fp8 else ''}")
     counts = to_np(out["counts"]).tolist()
     assert counts[14] == 300 and counts[15] == T - 300 and sum(counts) == T
     pieces, first_row, stride, tail = to_np(out["split_plan"]).tolist()
-    say(f"[narrow+split] S={S}: {pieces} pieces over the last {tail} row tiles from row "
+    say(f"[narrow+split] S={S} fp8={fp8}: {pieces} pieces over the last {tail} row tiles from row "
         f"{first_row} ({info['compute_units']} CUs)")
     if info["compute_units"] == 256:
         assert pieces >= 2 and tail >= 1, "the tail split was not taken"
