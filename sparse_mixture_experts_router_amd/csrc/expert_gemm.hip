@@ -49,6 +49,26 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 // chunk offsets, spreading the reads over the LDS banks.
 __device__ __forceinline__ int bt_key(int kk) { return 2 * ((kk & 3) + 4 * ((kk >> 3) & 3)); }
 
+// A K-row weight fragment (two ds_read_b64_tr_b16: K-rows k0 .. k0 + 3 into
+// the low half, k0 + 4 .. k0 + 7 into the high half) from LDS byte address
+// `addr` + OFF.  Inline asm rather than the builtin: the compiler makes a
+// read through the builtin wait for every global->LDS load in flight
+// (vmcnt(0)), which would drain the next buffers' loads each phase.  The
+// compiler does not track these reads, so the caller waits for them
+// (s_waitcnt lgkmcnt(0)) before anything reads `v`; the outputs are
+// early-clobber so that no returning data overwrites the address register.
+template <int OFF>
+__device__ __forceinline__ void ds_read_tr_frag(u32x4& v, uint32_t addr) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+  u32x2 lo, hi;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%4"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(addr), "i"(OFF), "i"(OFF + 2048));
+  v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 template <bool GATED, int BM, int BNE, int NBUF, bool FP8W, bool KMAJ = false, bool BT = false,
           bool TRIPB = false>
 __global__ __launch_bounds__(256, 1) void expert_gemm_kernel(GemmArgs g) {
@@ -585,6 +605,11 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
   // FP8 weight fragment of the first / second pair of a buffer
   const int f8l0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
   const int f8l1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  // BT: lane constants of the transpose reads (K-row 8 (lane / 16) + (lane
+  // mod 16) / 4 of a step, columns 4 (lane mod 4) .. of the fragment's 16)
+  const int bt_lane = (8 * (lane >> 4) + ((lane & 15) >> 2)) * 512 + ((lane & 3) >> 1) * 16 +
+                      (lane & 1) * 8;
+  const int bt_s = bt_key(8 * (lane >> 4) + ((lane & 15) >> 2));
   auto b_row = [&](int j) {  // first staged weight row of block j
     if (GATED) return (j < NOUT ? 0 : HALF) + cw * (OC) + (j % NOUT) * 16;
     return cw * 128 + j * 16;
@@ -707,11 +732,16 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
 // read in the matching order (chunk 2 (lane / 16) + t in step t).  The
 // compute phase widens each weight fragment to bf16 right before its MFMAs;
 // the epilogue applies the per-output-channel scales.
-template <bool GATED, bool DENSE = false, bool NARROW = false, bool FP8W = false>
+// BT: weights as K-rows, staged and read as in expert_gemm_kernel's BT mode
+// (a weight buffer: 64 K-rows x 512 contiguous bytes, chunks swizzled by
+// bt_key; a weight fragment: two ds_read_b64_tr_b16); plain bf16 grouped
+// launches without a split reduction.
+template <bool GATED, bool DENSE = false, bool NARROW = false, bool FP8W = false, bool BT = false>
 __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   static_assert(!(GATED && DENSE), "dense mode: plain pass");
   static_assert(!(DENSE && NARROW), "dense mode: no tail items");
   static_assert(!(FP8W && DENSE), "FP8 weights: grouped launches");
+  static_assert(!BT || (!GATED && !DENSE && !NARROW && !FP8W), "K-row mode: plain bf16 pass");
   constexpr int BM = 256, BNE = 256;
   constexpr int ABUF = BM * kLineBytes, BBUF = BNE * kLineBytes;
   constexpr int NA = 2, NBB = 3;               // A and weight ring buffers
@@ -780,6 +810,8 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // of a block fetches row l / 8 of it, the chunk line_lane_chunk assigns;
   // rows past the tile or the matrix are clamped to a valid row.
   const char* src_base;
+  const char* src_base1 = nullptr;  // BT: the weights of K-rows bt_rows0 ..
+  const uint32_t ldb = static_cast<uint32_t>(g.n_dim) * 2;  // BT: bytes per K-row
   uint32_t off[LPW] = {};
   if (grp == 0) {
     src_base = reinterpret_cast<const char*>(g.a);
@@ -790,6 +822,24 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       const int srow = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
       off[j] = static_cast<uint32_t>(srow) * static_cast<uint32_t>(row_bytes) +
                line_lane_chunk(lane, j) * 16;
+    }
+  } else if (BT) {
+    // block j of wavefront q: K-rows 2 (8 q + j) and + 1 of the buffer, 32
+    // lanes each; lane l writes physical chunk l mod 32 of its row and
+    // fetches the logical chunk the key maps there (columns past n_dim are
+    // clamped to a valid chunk; their results are discarded)
+    const char* const w0r = reinterpret_cast<const char*>(routed ? g.w0 : g.ws0) +
+                            static_cast<size_t>(es) * g.bt_rows0 * ldb;
+    const char* const w1r = reinterpret_cast<const char*>(routed ? g.w1 : g.ws1);
+    src_base = w0r + static_cast<size_t>(n0) * 2;
+    src_base1 = w1r == nullptr ? src_base
+                               : w1r + static_cast<size_t>(es) * (g.k_dim - g.bt_rows0) * ldb +
+                                     static_cast<size_t>(n0) * 2;
+#pragma unroll
+    for (int j = 0; j < LPWB; ++j) {
+      const int kk = 2 * (q * LPWB + j) + (lane >> 5);
+      const int col = min(n0 + 8 * ((lane & 31) ^ bt_key(kk)), g.n_dim - 8);
+      off[j] = static_cast<uint32_t>(kk) * ldb + static_cast<uint32_t>(col - n0) * 2;
     }
   } else {
     const int jb0 = q * 64;
@@ -818,9 +868,19 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // pair 2 buf and 2 buf + 1); past the end the last one again, into a buffer
   // nobody reads again
   const int nbufs = grp == 0 || !FP8W ? npairs : npairs / 2;
-  auto issue = [&](int buf, char* ring) {
-    const uint32_t pc = static_cast<uint32_t>(min(buf, nbufs - 1) * kLineBytes);
+  const int bt_pairs0 = BT ? g.bt_rows0 / 64 : 0;  // BT: buffers taken from w0
+  auto issue = [&](auto grp_, int buf, char* ring) {
+    const int bc = min(buf, nbufs - 1);
     const int dst = q * LPW * 1024;
+    if (BT && decltype(grp_)::value == 1) {
+      const bool second = bc >= bt_pairs0;
+      const uint32_t prow = static_cast<uint32_t>(second ? bc - bt_pairs0 : bc) * 64u * ldb;
+      const char* const base = second ? src_base1 : src_base;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) load_lds16(base + (off[j] + prow), ring + dst + j * 1024);
+      return;
+    }
+    const uint32_t pc = static_cast<uint32_t>(bc * kLineBytes);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) load_lds16(src_base + (off[j] + pc), ring + dst + j * 1024);
   };
@@ -838,6 +898,11 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // FP8 weight fragment of the first / second pair of a buffer
   const int f8l0 = frow * kLineBytes + (((lane >> 4) ^ fkey) << 4);
   const int f8l1 = frow * kLineBytes + (((4 + (lane >> 4)) ^ fkey) << 4);
+  // BT: lane constants of the transpose reads (K-row 8 (lane / 16) + (lane
+  // mod 16) / 4 of a step, columns 4 (lane mod 4) .. of the fragment's 16)
+  const int bt_lane = (8 * (lane >> 4) + ((lane & 15) >> 2)) * 512 + ((lane & 3) >> 1) * 16 +
+                      (lane & 1) * 8;
+  const int bt_s = bt_key(8 * (lane >> 4) + ((lane & 15) >> 2));
   auto b_row = [&](int j) {  // first staged weight row of block j
     if (GATED) return (j < NOUT ? 0 : COLS) + wn * (WTN / 2) + (j % NOUT) * 16;
     return wn * WTN + j * 16;
@@ -853,11 +918,11 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // prologue: group 0 A(0); group 1 B(0) then B(1); A(0) and B(0) landed
   // (FP8: weight buffers 0 and 1, pairs 0 .. 3)
   if (grp == 0) {
-    issue(0, abuf(0));
+    issue(CInt<0>{}, 0, abuf(0));
     wait_vmem<0>();
   } else {
-    issue(0, bbuf(0));
-    issue(1, bbuf(1));
+    issue(CInt<1>{}, 0, bbuf(0));
+    issue(CInt<1>{}, 1, bbuf(1));
     wait_vmem<LPWB>();
   }
   stage_barrier();
@@ -872,20 +937,37 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       const char* const a = abuf(p & 1);
       const int qb = FP8W ? (p >> 1) % 3 : p % 3;  // weight buffer of pair p
       const char* const b = bbuf(qb);
-      if (G == 0) issue(p + 1, abuf((p + 1) & 1));
-      else if (!FP8W) issue(p + 2, bbuf((p + 2) % 3));
-      else if ((p & 1) == 0) issue((p >> 1) + 2, bbuf(((p >> 1) + 2) % 3));
+      if (G == 0) issue(grp_, p + 1, abuf((p + 1) & 1));
+      else if (!FP8W) issue(grp_, p + 2, bbuf((p + 2) % 3));
+      else if ((p & 1) == 0) issue(grp_, (p >> 1) + 2, bbuf(((p >> 1) + 2) % 3));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int fl = t ? fl1 : fl0;
 #pragma unroll
         for (int i = 0; i < LIVE; ++i)
           fr[t][i] = *reinterpret_cast<const u32x4*>(a + (wm * WTM + i * 16) * kLineBytes + fl);
-        if (LIVE > 0 && (!FP8W || t == 0)) {
+        if (LIVE > 0 && (!FP8W || t == 0) && !BT) {
 #pragma unroll
           for (int j = 0; j < NB; ++j)
             fr[t][MB + j] = *reinterpret_cast<const u32x4*>(
                 b + b_row(j) * kLineBytes + (FP8W ? ((p & 1) ? f8l1 : f8l0) : fl));
+        }
+      }
+      if (LIVE > 0 && BT) {
+        // weight fragment j: columns wn WTN + 16 j .. of K-rows 32 t + 8
+        // (lane / 16) ..; its lane address is recomputed here from the
+        // opaque key, so that one address is live at a time instead of a
+        // loop-invariant register per fragment
+        uint32_t kx = static_cast<uint32_t>(bt_s) << 4;
+        uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                          (const __attribute__((address_space(3))) char*)(b))) +
+                      bt_lane;
+        asm volatile("" : "+v"(kx), "+v"(la));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const uint32_t pr = la + ((static_cast<uint32_t>((wn * WTN + j * 16) >> 3) << 4) ^ kx);
+          ds_read_tr_frag<0>(fr[0][MB + j], pr);
+          ds_read_tr_frag<16384>(fr[1][MB + j], pr);
         }
       }
       // fragments in registers; group 0 leaves A(p + 1) in flight (waited
@@ -939,12 +1021,20 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       stage_barrier();  // phase 0: idle
       for (int p = 0; p < npairs; ++p) {
         memory(p);  // phase 2p + 1
-        if (p == npairs - 1) wait_vmem<0>();  // nothing in flight past the last pair
+        // nothing in flight past the last pair (BT: after the loop, so that
+        // the compiler keeps one loop body; see below)
+        if (!BT && p == npairs - 1) wait_vmem<0>();
         stage_barrier();
         compute();  // phase 2p + 2
         stage_barrier();
       }
+      if (BT) wait_vmem<0>();
     }
+    // BT: one more barrier, after which group 1's last loads have landed.
+    // With the wait inside the loop the compiler peeled the last iteration
+    // and spilled fragment registers there right after their transpose
+    // reads, which it does not know are still in flight.
+    if (BT) stage_barrier();
   };
   auto run_g = [&](auto grp_) {
     if (mlive > MB / 2) run(CInt<MB>{}, grp_);
@@ -1029,7 +1119,11 @@ hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s) {
   if (!expert_gemm_bt_fits(bm, g.k_dim, g.n_dim, g.bt_rows0, g.a_rows) ||
       (g.bt_rows0 < g.k_dim && g.w1 == nullptr) || g.plan != nullptr)
     return hipErrorInvalidValue;
-  if (bm == 256) return launch_v<false, 256, 256, 2, false, true>(g, s);
+  if (bm == 256) {  // 8-wavefront ping-pong tiles
+    hipLaunchKernelGGL((expert_gemm_pp_kernel<false, false, false, false, true>),
+                       dim3(static_cast<unsigned>(expert_grid(g, false, 256))), dim3(512), 0, s, g);
+    return hipGetLastError();
+  }
   if (bm == 128) return launch_v<false, 128, 256, 3, false, true>(g, s);
   return hipErrorInvalidValue;
 }

@@ -129,6 +129,11 @@ BACKWARD_CASES = [
     # as K-rows on the large-tile kernel; dXp's 768-long reduction takes 6
     # buffers from W_gate, then 6 from W_up; D's 384 columns end in a part tile
     ("kmajor_rows", MoEShape("bwd_krows", T=512, d=512, N=16, k=4, F=384, S=1)),
+    # the same on 256-row tiles (~256 rows per expert, groups under 384 rows
+    # on average with the shared expert): the ping-pong kernel's K-row mode.
+    # dXp's 640-long reduction takes 5 buffers from W_gate, then 5 from W_up;
+    # D (320 columns) and dXp (640) both end in a part column tile
+    ("kmajor_rows_256", MoEShape("bwd_krows256", T=1024, d=640, N=8, k=2, F=320, S=1)),
     # DeepSeek-V3's routing structure: 256 experts, top-8, shared expert and
     # selection bias (257 segments, most a few rows long or empty)
     ("many_experts", MoEShape("bwd_many", T=100, d=128, N=256, k=8, F=128, S=1,
