@@ -386,6 +386,15 @@ struct BwdPlan {
   long kseg;  // columns of the transposed segments: sum over groups of rows rounded up to 128
   int Kr;     // N rounded up to 128
   int Tp;     // T rounded up to 128
+  // D = dy W_down and dXp = [dA dB] [W_gate; W_up] read the weights as
+  // K-rows on the large-tile kernels (bf16), else run on transposed copies
+  // (W_down -> [N, F, d], [W_gate | W_up] -> [N, d, 2F]) that the workspace
+  // then holds.  On 256-row tiles the K-row reads run as fast as the
+  // transposed operands (Mixtral-shaped backward: grad_h 1.03, grad_x 1.92
+  // ms either way), so the transposes' 1.2 ms go (step 9.0 -> 7.9 ms;
+  // Qwen3-shaped 17.3 -> 15.3 ms); 128-row tiles only arise with few rows
+  // per expert, where the transposes cost more than the slower K-row reads.
+  bool bt_h, bt_x;
 };
 
 BwdPlan make_bwd_plan(const moe_config& c) {
@@ -401,6 +410,11 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   b.Kr = static_cast<int>((N + 127) / 128 * 128);
   b.Tp = static_cast<int>((T + 127) / 128 * 128);
   const size_t rows = b.rows, ks = b.kseg, Kr = b.Kr, Tp = b.Tp;
+  const bool bf = c.dtype == MOE_BF16;
+  b.bt_h = bf && b.p.up.variant == 1 &&
+           expert_gemm_bt_fits(b.p.up.bm, c.d_model, c.d_ff, c.d_model, c.T);
+  b.bt_x = bf && b.p.down.variant == 1 &&
+           expert_gemm_bt_fits(b.p.down.bm, 2 * c.d_ff, c.d_model, c.d_ff, b.rows);
   size_t sz[B_COUNT];
   sz[B_LOGITS] = T * N * 4;
   sz[B_G] = sz[B_U] = sz[B_D] = sz[B_H] = rows * F * eb;
@@ -410,10 +424,10 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   sz[B_DR] = T * Kr * eb;
   sz[B_DR32] = T * N * 4;
   sz[B_DXR] = T * d * 4;
-  sz[B_WDT] = N * F * d * eb;
-  sz[B_WDT_S] = S * F * d * eb;
-  sz[B_WCAT] = N * d * 2 * F * eb;
-  sz[B_WCAT_S] = S * d * 2 * F * eb;
+  sz[B_WDT] = b.bt_h ? 0 : N * F * d * eb;
+  sz[B_WDT_S] = b.bt_h ? 0 : S * F * d * eb;
+  sz[B_WCAT] = b.bt_x ? 0 : N * d * 2 * F * eb;
+  sz[B_WCAT_S] = b.bt_x ? 0 : S * d * 2 * F * eb;
   sz[B_WRT] = d * Kr * eb;
   sz[B_KBASE] = (G + 1) * 4;
   sz[B_DOT] = d * ks * eb;
@@ -746,19 +760,8 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
   if (err != hipSuccess) return hip_fail(err, "route kernel");
   if ((st = run_permute(c, p, ws, nullptr, ws.topk_idx, s)) != MOE_OK) return st;
 
-  // D = dy W_down and dXp = [dA dB] [W_gate; W_up] either read the weights
-  // as K-rows on the large-tile kernel (bf16) or run on transposed copies:
-  // W_down -> [N, F, d], [W_gate | W_up] -> [N, d, 2F].  The K-row reads
-  // made those two GEMMs 1.7-2.1x slower, while a transpose costs in
-  // proportion to the weight bytes, so the K-row path is taken when a weight
-  // matrix serves few rows (< 384 per group on average: DeepSeek-V3-shaped
-  // backward 37.0 -> 34.6 ms; Mixtral-shaped, 1024 rows, 9.3 -> 11.4 ms had
-  // it been taken).  W_r -> [d, Kr] always.
-  const bool few_rows = rows < 384L * G;
-  const bool bt_h = dt == 1 && few_rows && p.up.variant == 1 &&
-                    expert_gemm_bt_fits(p.up.bm, d, F, d, T);
-  const bool bt_x = dt == 1 && few_rows && p.down.variant == 1 &&
-                    expert_gemm_bt_fits(p.down.bm, 2 * F, d, F, rows);
+  // expert weights as K-rows or transposed (BwdPlan); W_r -> [d, Kr] always
+  const bool bt_h = b.bt_h, bt_x = b.bt_x;
   mark(ev, MOE_BSTAGE_TRANSPOSE_W, s);
   const long fd = static_cast<long>(F) * d;
   if ((!bt_h &&

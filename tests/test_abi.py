@@ -217,6 +217,14 @@ def test_backward_workspace_size():
     assert bwd % 256 == 0 and bwd >= 3 * 5 * 256 * 128 * 2 and bwd > fwd
     bad = moe.make_config(64, 96, 4, 2, 256)
     assert lib.moe_backward_workspace_size(ctypes.byref(bad)) == 0
+    # bf16 on 256-row tiles reads the expert weights as K-rows: the workspace
+    # holds no transposed copies (those alone would be 22.6 GB here)
+    big = moe.make_config(8192, 7168, 256, 8, 2048, n_shared=1)
+    copies = 3 * 257 * 2048 * 7168 * 2
+    assert 0 < lib.moe_backward_workspace_size(ctypes.byref(big)) < copies // 2
+    # fp32 layers still transpose them
+    big32 = moe.make_config(8192, 7168, 256, 8, 2048, n_shared=1, dtype="f32")
+    assert lib.moe_backward_workspace_size(ctypes.byref(big32)) > 2 * copies
 
 
 def test_workspace_sizes_of_an_empty_batch():
