@@ -929,7 +929,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
 
   // Each group runs its own straight loop (a shared loop that branches on the
   // group every phase made the compiler move the accumulators out of the
-  // AGPRs); both execute 2 n + 2 barriers in all, prologue included.
+  // AGPRs); both execute 2 n + 3 barriers in all, prologue included.
   auto run = [&](auto live_, auto grp_) {
     constexpr int LIVE = decltype(live_)::value;
     constexpr int G = decltype(grp_)::value;
@@ -1021,20 +1021,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       stage_barrier();  // phase 0: idle
       for (int p = 0; p < npairs; ++p) {
         memory(p);  // phase 2p + 1
-        // nothing in flight past the last pair (BT: after the loop, so that
-        // the compiler keeps one loop body; see below)
-        if (!BT && p == npairs - 1) wait_vmem<0>();
         stage_barrier();
         compute();  // phase 2p + 2
         stage_barrier();
       }
-      if (BT) wait_vmem<0>();
+      wait_vmem<0>();  // the loads past the last pair (re-reads nobody uses)
     }
-    // BT: one more barrier, after which group 1's last loads have landed.
-    // With the wait inside the loop the compiler peeled the last iteration
-    // and spilled fragment registers there right after their transpose
-    // reads, which it does not know are still in flight.
-    if (BT) stage_barrier();
+    // one more barrier for both groups, after which nothing is in flight.
+    // (A wait for those loads inside the loop, in its last iteration, made
+    // the compiler peel that iteration and spill fragment registers there;
+    // with BT, right after their transpose reads, which it does not know
+    // are still in flight.)
+    stage_barrier();
   };
   auto run_g = [&](auto grp_) {
     if (mlive > MB / 2) run(CInt<MB>{}, grp_);
