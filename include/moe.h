@@ -180,6 +180,15 @@ size_t moe_workspace_size(const moe_config* cfg);
  *     of at most 64 rows runs as one tile over two column tiles (the
  *     ping-pong large-tile kernel, an even number of column tiles; the down
  *     pass only with at most 384 rows per expert on average);
+ *   compute_units: the device's compute units, as the plan used them;
+ *   all_token_pass: 1 when every expert (routed and shared) runs on all T
+ *     tokens: batches of at most 32 tokens, at most 64 experts, bf16 or
+ *     fp32 expert weights, where one 32-row tile per expert holds the whole
+ *     batch and (nearly) every expert is chosen anyway (expected idle
+ *     experts N (1 - k/N)^T at most 1/2).
+ *     The routing then runs inside the gate/up launch and only the combine
+ *     uses it; the result is the same y (each row's arithmetic is unchanged,
+ *     rows no slot chose are computed and never read);
  *   split_plan_offset: byte offset in the workspace of the split plan each
  *     forward writes there on the device, int32 [4] = {pieces, first split
  *     row, rows per piece, split row tiles} (pieces = 0: nothing split);
@@ -197,6 +206,7 @@ typedef struct {
   int32_t up_narrow_tails;
   int32_t down_narrow_tails;
   int32_t compute_units;
+  int32_t all_token_pass;
   uint64_t split_plan_offset;
   uint64_t workspace_bytes;
 } moe_plan_info;
@@ -220,7 +230,9 @@ moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
                      void* stream);
 
 /* Whole layer forward: routing as moe_route, then the SwiGLU experts on the
- * tokens routed to them (experts no token chose are never read), the shared
+ * tokens routed to them (experts no token chose are never read, except in
+ * the all-token pass of moe_plan_info, which runs every expert on every
+ * token of a small batch and combines only the routed rows), the shared
  * experts on every token, and the combine y [T, d] (required).  Optional
  * routing outputs as described at moe_routing. */
 moe_status moe_layer_forward(const moe_config* cfg, const void* x,

@@ -77,6 +77,7 @@ class MoEPlanInfo(ctypes.Structure):
                 ("down_split", ctypes.c_int32),
                 ("tail_split_cols", ctypes.c_int32), ("up_narrow_tails", ctypes.c_int32),
                 ("down_narrow_tails", ctypes.c_int32), ("compute_units", ctypes.c_int32),
+                ("all_token_pass", ctypes.c_int32),
                 ("split_plan_offset", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 
 

@@ -34,13 +34,19 @@
 
 #include "lds_ring.h"
 #include "mfma.h"
+#include "route_tile.h"
 
 namespace moe {
 namespace {
 
 
-template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
+// All-token expert pass (GemmArgs' all_tok = T > 0): workgroup row b < G =
+// all_groups is expert b on every token (rows b T .. b T + T - 1; the gated
+// pass reads x rows 0 .. T - 1, the plain pass its own group's rows), with
+// no tile list.  ROUTE (gated pass): workgroup (G, 0) routes the batch
+// meanwhile (all_token_route), in this kernel's LDS.
+template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN, bool ROUTE = false>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g, AllTokenRoute route) {
   constexpr bool FP8W = sizeof(TW) == 1;
   constexpr int PD = (GATED || FP8W) ? 2 : 1;  // K steps of loads in flight
   static_assert(!FP8W || sizeof(T) == 2, "FP8 weights with bf16 activations");
@@ -58,14 +64,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
   static_assert(MB >= 1 && NBK >= 1, "wave tile below one MFMA block");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  static_assert(!ROUTE || (GATED && BM == 32), "routing in the all-token gate/up pass");
+  static_assert(!ROUTE || RouteShape<4>::LDS_BYTES <= 2 * STAGE, "routing block LDS");
 
-  const int tile = blockIdx.x;
-  if (tile >= *g.ntiles) return;
-  const int2 te = g.tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int seg = g.offsets[e];
-  const int mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  int e, m0, seg, mvalid, arow0;
+  if (g.all_tok > 0) {
+    e = blockIdx.x;
+    if (e >= g.all_groups) {
+      if constexpr (ROUTE) {
+        if (blockIdx.y == 0) {
+          if (route.a.N <= 16) all_token_route<T, 1>(route, smem);
+          else if (route.a.N <= 32) all_token_route<T, 2>(route, smem);
+          else all_token_route<T, 4>(route, smem);
+        }
+      }
+      return;
+    }
+    m0 = 0;
+    seg = e * g.all_tok;
+    mvalid = g.all_tok;
+    arow0 = GATED ? 0 : seg;  // every expert of the gated pass reads x rows 0 .. T - 1
+  } else {
+    const int tile = blockIdx.x;
+    if (tile >= *g.ntiles) return;
+    const int2 te = g.tiles[tile];
+    e = te.x;
+    m0 = te.y;
+    seg = g.offsets[e];
+    mvalid = min(BM, g.offsets[e + 1] - seg - m0);
+    arow0 = seg;
+  }
   const int n0 = blockIdx.y * BN;
   const bool split = !GATED && g.ksplit > 1;   // blockIdx.z: part of the reduction
 
@@ -90,7 +120,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   for (int i = 0; i < A_LD; ++i) {
     const int c = tid + 256 * i;
     const int r = c >> 3, ch = c & 7;
-    const int grow = seg + m0 + min(r, mvalid - 1);
+    const int grow = arow0 + m0 + min(r, mvalid - 1);
     const int src_row = min(max(g.gather != nullptr ? g.gather[grow] : grow, 0), g.a_rows - 1);
     a_off[i] = static_cast<size_t>(src_row) * row_bytes + ch * 16;
     a_dst[i] = lds_swz(r, ch);
@@ -269,28 +299,45 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 template <typename T, typename TW, bool GATED, int BM, int BN, int WM, int WN>
-hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.tiles_cap, (g.n_dim + BN - 1) / BN, (!GATED && g.ksplit > 1) ? g.ksplit : 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, TW, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g);
+hipError_t launch_t(const GemmArgs& g, const AllTokenRoute* route, hipStream_t s) {
+  const unsigned rows = g.all_tok > 0 ? g.all_groups + (route != nullptr ? 1 : 0) : g.tiles_cap;
+  dim3 grid(rows, (g.n_dim + BN - 1) / BN, (!GATED && g.ksplit > 1) ? g.ksplit : 1);
+  if constexpr (GATED && BM == 32) {
+    if (route != nullptr) {
+      hipLaunchKernelGGL((grouped_gemm_kernel<T, TW, GATED, BM, BN, WM, WN, true>), grid, dim3(256),
+                         0, s, g, *route);
+      return hipGetLastError();
+    }
+  }
+  if (route != nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, TW, GATED, BM, BN, WM, WN>), grid, dim3(256), 0, s, g,
+                     AllTokenRoute{});
   return hipGetLastError();
 }
 
 template <typename T, typename TW, bool GATED>
-hipError_t launch_bm(const GemmArgs& g, int bm, hipStream_t s) {
-  if (bm == 32) return launch_t<T, TW, GATED, 32, 64, 1, 4>(g, s);
-  return launch_t<T, TW, GATED, 128, 128, 2, 2>(g, s);
+hipError_t launch_bm(const GemmArgs& g, int bm, const AllTokenRoute* route, hipStream_t s) {
+  if (bm == 32) return launch_t<T, TW, GATED, 32, 64, 1, 4>(g, route, s);
+  if (g.all_tok > 0) return hipErrorInvalidValue;  // all-token passes: 32-row tiles
+  return launch_t<T, TW, GATED, 128, 128, 2, 2>(g, route, s);
 }
 
 }  // namespace
 
-hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s,
+                               const AllTokenRoute* route) {
+  if (route != nullptr && (!gated || g.all_tok <= 0 || g.all_tok > kRouteTokens ||
+                           route->a.N > 64 || route->a.ksplit != 1))
+    return hipErrorInvalidValue;
   if (dtype == 1 && g.wfp8)
-    return gated ? launch_bm<bf16_t, uint8_t, true>(g, bm, s)
-                 : launch_bm<bf16_t, uint8_t, false>(g, bm, s);
+    return gated ? launch_bm<bf16_t, uint8_t, true>(g, bm, route, s)
+                 : launch_bm<bf16_t, uint8_t, false>(g, bm, route, s);
   if (g.wfp8) return hipErrorInvalidValue;
   if (dtype == 1)
-    return gated ? launch_bm<bf16_t, bf16_t, true>(g, bm, s) : launch_bm<bf16_t, bf16_t, false>(g, bm, s);
-  return gated ? launch_bm<float, float, true>(g, bm, s) : launch_bm<float, float, false>(g, bm, s);
+    return gated ? launch_bm<bf16_t, bf16_t, true>(g, bm, route, s)
+                 : launch_bm<bf16_t, bf16_t, false>(g, bm, route, s);
+  return gated ? launch_bm<float, float, true>(g, bm, route, s)
+               : launch_bm<float, float, false>(g, bm, route, s);
 }
 
 // Split of the down pass over workgroups for few-row (weight-streaming)
@@ -326,9 +373,11 @@ GemmPick pick_gemm(int dtype, bool /*fp8w*/, bool /*gated*/, long rows_per_exper
   return GemmPick{1, 128};
 }
 
-hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s,
+                       const AllTokenRoute* route) {
+  if (g.all_tok > 0 && pick.variant != 0) return hipErrorInvalidValue;
   if (pick.variant == 1 && dtype == 1) return launch_expert_gemm(gated, pick.bm, g, s);
-  return launch_generic_gemm(dtype, gated, pick.bm, g, s);
+  return launch_generic_gemm(dtype, gated, pick.bm, g, s, route);
 }
 
 }  // namespace moe

@@ -138,6 +138,56 @@ hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* lrank,
                           int T, int N, int k, int S, int capacity,
                           int32_t* sorted_tok, int32_t* inv_row, hipStream_t s);
 
+// Arguments of the routing kernels (route.hip, route_tile.h).
+struct RouteArgs {
+  const void* x;
+  const void* wr;
+  const float* logit_bias;
+  const float* select_bias;
+  int n_tok, d, N, k;
+  int ksplit;             // workgroups along the reduction dimension
+  int steps_per_split;    // K steps (64-byte row slices) per split
+  float* partial;         // [ksplit, T, N] when ksplit > 1
+  float* logits_out;      // [T, N] or NULL
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* lrank;
+  int32_t* blk_counts;
+  float* blk_psum;
+};
+
+// The routing of an all-token expert pass: every expert's GEMMs run on all T
+// (<= 64) tokens of the batch, expert-major (expert g's rows are g T .. g T +
+// T - 1, shared experts after the routed ones), so only the combine needs the
+// routing.  One workgroup routes the batch (one block, no split of the
+// reduction) and writes, besides the indices, gates and logits:
+//   inv_row[t, s] = e T + t for slot s's expert e, or -1 when the capacity
+//                   drops it (the expert keeps its first `capacity` tokens in
+//                   token order; the rank is the block rank the selection
+//                   computes);
+//   counts[e], prob_sum[e] (and the caller's copies): the router's choice
+//                   before any drop, counts[N + s] = T;
+//   offsets[g] = g T for g <= N + S (the combine finds shared rows there);
+//   plan: the down pass's split over its reduction (parts, first split row
+//         0, part stride (N + S) T), or no split;
+//   f, P and the loss (balance_block), when asked for.
+struct AllTokenRoute {
+  RouteArgs a;  // ksplit 1, steps_per_split = every K step
+  int S, capacity;
+  int down_parts;  // > 1: the down pass writes that many fp32 partial rows
+  int32_t* inv_row;
+  int32_t* counts;
+  float* prob_sum;
+  int32_t* user_counts;
+  float* user_prob_sum;
+  int32_t* offsets;
+  int32_t* plan;
+  float* f;
+  float* P;
+  float* aux;
+  float alpha;
+};
+
 struct GemmArgs {
   const void* a;             // x [T, d] (gather) or hidden [rows, F] (direct)
   const int32_t* gather;     // sorted_tok, or NULL for direct rows
@@ -186,6 +236,11 @@ struct GemmArgs {
   // reduction come from w0 / ws0 (expert stride bt_rows0 x n_dim), the rest
   // from w1 / ws1 (stride (k_dim - bt_rows0) x n_dim).
   int bt_rows0;
+  // All-token expert pass of the register-staged kernel (grouped_gemm.hip):
+  // all_tok = T > 0 makes workgroup row g < all_groups = N + S expert g on
+  // every token, rows g T .. g T + T - 1, with no tile list.
+  int all_tok;
+  int all_groups;
 };
 
 // Pairs of K steps (128-byte row buffers) that each of `parts` pieces of an
@@ -226,7 +281,9 @@ struct GemmPick {
 // widens them on their way into LDS, the large-tile one after its LDS reads).
 GemmPick pick_gemm(int dtype, bool fp8w, bool gated, long rows_per_expert, size_t a_bytes,
                    size_t w_bytes, int k_dim);
-hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s);
+// route: the all-token gate/up pass's routing workgroup, or null.
+hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s,
+                       const AllTokenRoute* route = nullptr);
 // bf16 weight-gradient products on the large-tile kernel (GemmArgs' kbase
 // fields); hipErrorInvalidValue when the operands do not fit it.
 hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s);
@@ -234,7 +291,8 @@ hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s);
 // (GemmArgs' bt_rows0); hipErrorInvalidValue when the shape does not fit it.
 hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s);
 bool expert_gemm_bt_fits(int bm, int k_dim, int n_dim, int rows0, long a_rows);
-hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s);
+hipError_t launch_generic_gemm(int dtype, bool gated, int bm, const GemmArgs& g, hipStream_t s,
+                               const AllTokenRoute* route = nullptr);
 hipError_t launch_expert_gemm(bool gated, int bm, const GemmArgs& g, hipStream_t s);
 // The plain (non-gated) bf16 ping-pong kernel in dense mode (GemmArgs'
 // dense_parts): hipErrorInvalidValue when the operands do not fit it.

@@ -309,8 +309,19 @@ def test_forward_plan_reports_the_path():
     assert info["workspace_bytes"] == moe.moe_workspace_size(pre)
     off = info["split_plan_offset"]
     assert off % 4 == 0 and off + 16 <= info["workspace_bytes"]
+    assert info["all_token_pass"] == 0
     dec = moe.moe_forward_plan(moe.make_config(32, 4096, 8, 2, 14336))
     assert (dec["up_kernel"], dec["up_tile_rows"]) == (0, 32) and dec["down_split"] >= 2
+    # the decode batch: every expert runs on all 32 tokens (8 (3/4)^32 idle
+    # experts expected); its expert rows are (N + S) T, not T (k + S)
+    assert dec["all_token_pass"] == 1
+    # one token of 8 experts (6 idle expected), 256 experts, or 33 tokens: not
+    assert moe.moe_forward_plan(moe.make_config(1, 4096, 8, 2, 14336))["all_token_pass"] == 0
+    assert moe.moe_forward_plan(moe.make_config(32, 7168, 256, 8, 2048, 1))["all_token_pass"] == 0
+    assert moe.moe_forward_plan(moe.make_config(33, 4096, 8, 2, 14336))["all_token_pass"] == 0
+    assert moe.moe_forward_plan(moe.make_config(1, 256, 4, 4, 256))["all_token_pass"] == 1
+    fp8 = moe.make_config(32, 4096, 8, 2, 14336, weight_format=moe.MOE_WEIGHTS_FP8_E4M3)
+    assert moe.moe_forward_plan(fp8)["all_token_pass"] == 0  # FP8 weights: the routed rows
     assert info["route_kernel"] == 0  # 8 experts: the router kernel
     ds = moe.moe_forward_plan(moe.make_config(8192, 7168, 256, 8, 2048, 1))
     # 256 experts: the router GEMM on the large-tile kernel, 32 tiles of 256

@@ -200,6 +200,53 @@ def test_unchosen_expert_weights_never_read():
     assert bool(torch.isfinite(out["y"].float()).all())
 
 
+ALL_TOKEN_CASES = [
+    # (label, shape, capacity): batches of at most 32 tokens where (nearly)
+    # every expert is chosen, so every expert runs on every token and the
+    # routing runs inside the gate/up launch
+    ("n8_k2", reduced(CONFIGS["mixtral_decode"], T=32, d=256, F=512), 0),
+    ("n20_k6_shared_bias", MoEShape("at20", T=32, d=192, N=20, k=6, F=256, S=1,
+                                    select_bias=True), 0),
+    ("n40_k10_zipf", MoEShape("at40", T=30, d=128, N=40, k=10, F=192, zipf_s=1.2), 0),
+    ("n64_k16", MoEShape("at64", T=32, d=128, N=64, k=16, F=128), 0),
+    ("one_token_k_equals_n", MoEShape("at1", T=1, d=256, N=4, k=4, F=256), 0),
+    ("capacity_split_k", reduced(CONFIGS["mixtral_decode"], T=28, d=256, F=2048), 5),
+    ("f32_shared", MoEShape("at32", T=17, d=128, N=4, k=2, F=320, S=2, dtype="f32"), 3),
+]
+
+
+@pytest.mark.parametrize("label,shape,capacity", ALL_TOKEN_CASES,
+                         ids=[c[0] for c in ALL_TOKEN_CASES])
+def test_all_token_pass(label, shape, capacity):
+    """The all-token expert pass of small batches: the plan takes it, and y,
+    the routing and the statistics match the oracle, capacity drops and the
+    down pass's split included."""
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S,
+                          shape.torch_dtype, capacity=capacity)
+    info = moe.moe_forward_plan(cfg)
+    assert info["all_token_pass"] == 1
+    _, out, _ = full_parity(shape, seed=6, label=f"all_token_{label}", capacity=capacity)
+    pieces = int(out["split_plan"][0])
+    say(f"[all-token] {label}: down pass in {max(pieces, 1)} pieces")
+    assert pieces == (info["down_split"] if info["down_split"] > 1 else 0)
+
+
+def test_all_token_pass_never_reads_unchosen_rows():
+    """Under the all-token pass an expert no token chose still runs (its
+    weights here are NaN), and the combine never reads its rows."""
+    shp = MoEShape("at_nan", T=32, d=128, N=6, k=2, F=128)
+    cfg = moe.make_config(shp.T, shp.d, shp.N, shp.k, shp.F)
+    assert moe.moe_forward_plan(cfg)["all_token_pass"] == 1
+    inputs = make_inputs(shp, seed=3, device="cuda")
+    inputs["logit_bias"] = torch.tensor([0, 0, 0, 0, 0, -1.0e4], dtype=torch.float32,
+                                        device="cuda")
+    for name in ("w_gate", "w_up", "w_down"):
+        inputs[name][5] = float("nan")
+    _, out, _ = full_parity(shp, inputs=inputs, label="all_token_nan_in_unused_expert")
+    assert int(out["counts"][5]) == 0
+    assert bool(torch.isfinite(out["y"].float()).all())
+
+
 def test_exact_ties_go_to_lower_index():
     # small integers make every logit an exact integer, so many keys tie exactly;
     # experts 1 and 2 have identical router rows and always tie
