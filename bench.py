@@ -50,7 +50,8 @@ CPU_MIN_S, CPU_TARGET_S = 8.0, 15.0
 CPU_F64_WEIGHT_BUDGET = 40 << 30
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc")
 # the sources that decide the expert GEMMs' memory traffic
-GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "mfma.h", "lds_ring.h")
+GEMM_SRCS = ("expert_gemm.hip", "expert_tile.h", "grouped_gemm.hip", "route_tile.h", "mfma.h",
+             "lds_ring.h")
 PROFILE_STEPS, PROFILE_WARMUP, PMC_STEPS, PMC_WARMUP, COPY_MIB = 20, 20, 3, 1, 1024
 # matrix-core counters of the expert GEMMs, one --pmc pass (2 SQ + 1 GRBM):
 # busy cycles of the MFMA units summed over the SIMDs, MFMA bf16 operations / 512,
