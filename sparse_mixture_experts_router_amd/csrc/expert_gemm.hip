@@ -979,6 +979,12 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       else if (!FP8W || (p & 1)) wait_vmem<LPWB>();
     };
     auto compute = [&]() {
+      // the wavefront issuing MFMAs goes first when both wavefronts of its
+      // SIMD want an issue slot (the other one's address arithmetic also
+      // takes the vector ALU); same box, 3 x 30 steps: Mixtral-shaped
+      // prefill 2.284 -> 2.261 ms, DeepSeek-V3 6.761 -> 6.729 ms (the memory
+      // phase first instead measured the same as this)
+      __builtin_amdgcn_s_setprio(2);
       if constexpr (FP8W) {
         // weight fragment j of step t widened from its 8 codes; the first
         // MFMA reading it carries the VALU -> MFMA wait states.  The previous
@@ -1007,6 +1013,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < LIVE; ++i) mfma_bf16_agpr(acc[i][j], fr[t][i], fr[t][MB + j]);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     if (G == 0) {
       for (int p = 0; p < npairs; ++p) {
