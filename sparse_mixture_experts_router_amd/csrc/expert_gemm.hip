@@ -974,9 +974,12 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       // for after its compute phase), group 1 waits for B(p + 1) and leaves
       // B(p + 2) in flight (FP8: after an odd pair, waits for the buffer of
       // the next two pairs and leaves the one after in flight; after an even
-      // pair the next pair's buffer is the current one)
+      // pair the next pair's buffer is the current one, and only its
+      // fragment reads are waited for: group 0 refills A(p)'s buffer right
+      // after the barrier)
       if (G == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       else if (!FP8W || (p & 1)) wait_vmem<LPWB>();
+      else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
     auto compute = [&]() {
       // the wavefront issuing MFMAs goes first when both wavefronts of its
