@@ -57,8 +57,12 @@ def reference(shape, inputs):
     (reduced(CONFIGS["mixtral_prefill"], T=600, d=512, F=1024),
      reduced(CONFIGS["mixtral_prefill"], T=200, d=512, F=1024)),
     # the Mixtral-shaped decode layer (register-staged tiles, down pass split
-    # over its reduction), then 8 tokens
+    # over its reduction; the all-token pass), then 8 tokens (routed rows)
     (CONFIGS["mixtral_decode"], reduced(CONFIGS["mixtral_decode"], T=8, d=4096, F=14336)),
+    # the all-token pass with a shared expert and a selection bias, then a
+    # batch of 12 tokens that takes the routed rows
+    (MoEShape("ats24", T=24, d=512, N=16, k=4, F=256, S=1, select_bias=True),
+     MoEShape("ats12", T=12, d=512, N=16, k=4, F=256, S=1, select_bias=True)),
     # shared expert and selection bias, 256 experts top-8
     (reduced(CONFIGS["deepseek_v3"], T=160, d=512, F=256),
      reduced(CONFIGS["deepseek_v3"], T=33, d=512, F=256)),
@@ -66,13 +70,15 @@ def reference(shape, inputs):
     # (8 parts of the reduction), then a batch on the router kernel
     (reduced(CONFIGS["deepseek_v3"], T=2048, d=512, F=128),
      reduced(CONFIGS["deepseek_v3"], T=300, d=512, F=128)),
-], ids=["large_tiles", "decode_split_k", "shared_bias", "router_tiles"])
+], ids=["large_tiles", "decode_split_k", "all_token_shared", "shared_bias", "router_tiles"])
 def test_noalloc_matches_forward_on_two_calls(big, small):
     for i, shape in enumerate((big, small)):
         cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S)
         need = moe.moe_workspace_size(cfg)
         assert need <= moe.NOALLOC_SCRATCH_BYTES
-        say(f"[noalloc] call {i + 1}: router kernel {moe.moe_forward_plan(cfg)['route_kernel']}")
+        plan = moe.moe_forward_plan(cfg)
+        say(f"[noalloc] call {i + 1}: router kernel {plan['route_kernel']}, all-token pass "
+            f"{plan['all_token_pass']}")
         inputs = make_inputs(shape, seed=21 + i, device="cuda")
         got = run_noalloc(shape, inputs)
         ref = reference(shape, inputs)
