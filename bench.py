@@ -295,10 +295,11 @@ def is_up_gemm(name):
 
 
 def is_grad_w_gemm(name):
-    """The weight-gradient launches: expert_gemm_kernel with KMAJ (its sixth
-    template argument) = true."""
+    """The weight-gradient launches: expert_gemm_pp_kernel with KMAJ (its
+    sixth template argument) = true."""
     ka = gemm_template_args(name)
-    return ka is not None and ka[0] == "expert_gemm_kernel" and len(ka[1]) >= 6 and ka[1][5] == "true"
+    return (ka is not None and ka[0] == "expert_gemm_pp_kernel" and len(ka[1]) >= 6
+            and ka[1][5] == "true")
 
 
 def is_down_gemm(name):
@@ -308,10 +309,11 @@ def is_down_gemm(name):
     if ka is None:
         return False
     kern, args = ka
-    if kern == "expert_gemm_pp_kernel":  # <GATED, DENSE, NARROW>: DENSE is the router GEMM
-        return args[0] == "false" and (len(args) < 2 or args[1] == "false")
-    if kern == "expert_gemm_kernel":
-        return args[0] == "false" and all(a == "false" for a in args[5:7])
+    if kern == "expert_gemm_pp_kernel":
+        # <GATED, DENSE, NARROW, FP8W, BT, KMAJ>: DENSE is the router GEMM
+        return args[0] == "false" and all(a == "false" for i, a in enumerate(args) if i in (1, 4, 5))
+    if kern == "expert_gemm_kernel":  # <GATED, BM, BNE, NBUF, FP8W, BT, TRIPB>
+        return args[0] == "false" and all(a == "false" for a in args[5:6])
     return len(args) > 2 and args[2] == "false"
 
 
