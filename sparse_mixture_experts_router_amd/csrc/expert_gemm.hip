@@ -513,7 +513,7 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
   constexpr int NOUT = GATED ? NB / 2 : NB;
   constexpr int OC = GATED ? 64 : 128;         // output columns per wavefront
   static_assert(2 * ABUF + 2 * BBUF <= 160 * 1024, "LDS");
-  static_assert(8 * WTM * (128 + 16) <= 2 * ABUF + 2 * BBUF, "staging space");
+  static_assert(8 * WTM * (256 + 16) <= 2 * ABUF + 2 * BBUF, "staging space");
   auto abuf = [&](int q) -> char* { return smem + q * ABUF; };
   auto bbuf = [&](int q) -> char* { return smem + 2 * ABUF + q * BBUF; };
 
@@ -657,16 +657,16 @@ __device__ __forceinline__ void narrow_tile(const GemmArgs& g, char* smem, int e
 
   // epilogue: every ring read is done (the last barrier), every load landed
   mfma_drain();
-  char* const stg = smem + wave * WTM * (128 + 16);
+  char* const stg = smem + wave * WTM * (256 + 16);
   const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
   const float* sc1 = nullptr;
   if (FP8W) {
     sc0 = (routed ? g.sc0 : g.ssc0) + static_cast<size_t>(es) * g.n_dim;
     if (GATED) sc1 = (routed ? g.sc1 : g.ssc1) + static_cast<size_t>(es) * g.n_dim;
   }
-  store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
-                                               seg + m0 + rh * WTM, mvalid - rh * WTM,
-                                               n0 + cw * OC, g.n_dim, sc0, sc1);
+  store_block<GATED, GATED, MB, NB, WTM, FP8W, 64>(acc, stg, lane, g.out, false, g.n_dim,
+                                                   seg + m0 + rh * WTM, mvalid - rh * WTM,
+                                                   n0 + cw * OC, g.n_dim, sc0, sc1);
 }
 
 // ------------------------------------------------------------------------
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   constexpr int LPWB = BBUF / 4 / 1024;        // group 1: 1 KB weight loads per buffer
   constexpr int NF = MB + NB;                  // fragments per K step
   static_assert(4 * LPW * 1024 == ABUF && 4 * LPWB * 1024 == BBUF, "one group fills a ring");
-  static_assert(8 * WTM * (128 + 16) <= SMEM, "staging space");
+  static_assert(8 * WTM * (256 + 16) <= SMEM, "staging space");
 
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   auto abuf = [&](int q) -> char* { return smem + q * ABUF; };
@@ -1052,7 +1052,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // epilogue: every ring read is done (the last barrier), every load landed
   mfma_drain();
   constexpr int OC = GATED ? WTN / 2 : WTN;  // output columns per wavefront
-  char* const stg = smem + wave * WTM * (128 + 16);
+  char* const stg = smem + wave * WTM * (256 + 16);
   const int col0 = n0 + wn * OC;
   const float* sc0 = nullptr;  // FP8 weights: this expert's output-channel scales
   const float* sc1 = nullptr;
@@ -1071,15 +1071,18 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     store_block<false, true, MB, NB, WTM>(acc, stg, lane, c, false, g.n_dim, m0 + wm * WTM,
                                           mvalid - wm * WTM, col0, g.n_dim);
   } else if (part < 0) {
-    store_block<GATED, GATED, MB, NB, WTM, FP8W>(acc, stg, lane, g.out, false, g.n_dim,
-                                                 seg + m0 + wm * WTM, mvalid - wm * WTM, col0,
-                                                 g.n_dim, sc0, sc1);
+    // (the plain pass: fp32 staging, 64 columns per pass, so every row write
+    // is a whole 128-byte line)
+    store_block<GATED, GATED, MB, NB, WTM, FP8W, 64>(acc, stg, lane, g.out, false, g.n_dim,
+                                                     seg + m0 + wm * WTM, mvalid - wm * WTM,
+                                                     col0, g.n_dim, sc0, sc1);
   } else if (!GATED) {  // fp32 partial rows of a split tail tile or of a dense part
     const long stride = dense ? g.a_rows : g.plan[kPlanStride];
     const long first = dense ? 0 : g.plan[kPlanRowSplit];
     const long prow = static_cast<long>(part) * stride + seg + m0 - first + wm * WTM;
-    store_block<GATED, false, MB, NB, WTM, FP8W>(acc, stg, lane, g.out_part, true, g.n_dim, prow,
-                                                 mvalid - wm * WTM, col0, g.n_dim, sc0, sc1);
+    store_block<GATED, false, MB, NB, WTM, FP8W, 64>(acc, stg, lane, g.out_part, true, g.n_dim,
+                                                     prow, mvalid - wm * WTM, col0, g.n_dim, sc0,
+                                                     sc1);
   }
 }
 

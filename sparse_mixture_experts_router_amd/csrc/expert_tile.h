@@ -98,29 +98,33 @@ inline long expert_grid(const GemmArgs& g, bool gated, int cols) {
 }
 
 // Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
-// passes of 128 staged bytes per row: each pass is staged row-major in LDS at
+// passes of PCOLS columns per row: each pass is staged row-major in LDS at
 // stg (rows padded by 16 bytes, so the four row groups of an MFMA result
 // land in distinct banks), then leaves in whole 16-byte row chunks.
-//  SBF16 : staged and written as bf16, 64 columns per pass;
-//  else  : staged as fp32, 32 columns per pass, written as bf16 (8 columns
-//          per lane) or, if out_f32, as fp32 (4 columns per lane).  The
-//          plain pass uses this one path for both of its outputs, so the
-//          accumulators have a single consumer.
+//  SBF16 : staged and written as bf16, 64 columns (128 bytes) per pass;
+//  else  : staged as fp32, FCOLS columns per pass (32, or 64 where the LDS
+//          holds 8 WTM (256 + 16) bytes of staging), written as bf16 (8
+//          columns per lane) or, if out_f32, as fp32 (4 columns per lane).
+//          The plain pass uses this one path for both of its outputs, so
+//          the accumulators have a single consumer.  With 64 columns every
+//          bf16 row write is a whole 128-byte line.
 // Row i of the block goes to out[(row0 + i) * ld + col0 + ...]; rows >=
 // rows_valid and columns >= cols_valid are not written.
 // SCALED (FP8 weights): each accumulator is first multiplied by its output
 // column's scale, sc0 for the gate (or plain) columns, sc1 for the up
 // columns; both indexed by the output column, col0 + ... .
-template <bool GATED, bool SBF16, int MB, int NB, int WTM, bool SCALED = false>
+template <bool GATED, bool SBF16, int MB, int NB, int WTM, bool SCALED = false, int FCOLS = 32>
 __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
                                             void* out, bool out_f32, size_t ld, long row0,
                                             int rows_valid, int col0, int cols_valid,
                                             const float* sc0 = nullptr,
                                             const float* sc1 = nullptr) {
   constexpr int NOUT = GATED ? NB / 2 : NB;
-  constexpr int ES = SBF16 ? 2 : 4;      // staged element bytes
-  constexpr int PB = 128 / (16 * ES);    // 16-column blocks per pass
-  constexpr int SROW = 128 + 16;
+  constexpr int ES = SBF16 ? 2 : 4;              // staged element bytes
+  constexpr int PCOLS = SBF16 ? 64 : FCOLS;      // columns per pass
+  constexpr int PB = PCOLS / 16;                 // 16-column blocks per pass
+  constexpr int SROW = PCOLS * ES + 16;
+  static_assert(FCOLS == 32 || FCOLS == 64, "fp32 staging width");
   static_assert(NOUT % PB == 0, "whole passes");
 #pragma unroll
   for (int pass = 0; pass < NOUT / PB; ++pass) {
@@ -170,21 +174,23 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
                                     col) = v;
       }
     } else if (out_f32) {
-      const int col = col0 + pass * 32 + (lane & 7) * 4;
+      constexpr int LPR = PCOLS / 4;  // lanes per row, 4 columns each
+      const int col = col0 + pass * PCOLS + (lane % LPR) * 4;
 #pragma unroll
-      for (int q = 0; q < WTM / 8; ++q) {
-        const int row = q * 8 + (lane >> 3);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
+      for (int q = 0; q < WTM * LPR / 64; ++q) {
+        const int row = q * (64 / LPR) + lane / LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane % LPR) * 16);
         if (row < rows_valid && col < cols_valid)
           *reinterpret_cast<u32x4*>(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld +
                                     col) = v;
       }
     } else {
-      const int col = col0 + pass * 32 + (lane & 3) * 8;
+      constexpr int LPR = PCOLS / 8;  // lanes per row, 8 columns each
+      const int col = col0 + pass * PCOLS + (lane % LPR) * 8;
 #pragma unroll
-      for (int q = 0; q < WTM / 16; ++q) {
-        const int row = q * 16 + (lane >> 2);
-        const char* src = stg + row * SROW + (lane & 3) * 32;
+      for (int q = 0; q < WTM * LPR / 64; ++q) {
+        const int row = q * (64 / LPR) + lane / LPR;
+        const char* src = stg + row * SROW + (lane % LPR) * 32;
         const f32x4 a = *reinterpret_cast<const f32x4*>(src);
         const f32x4 b = *reinterpret_cast<const f32x4*>(src + 16);
         u32x4 v;
