@@ -224,7 +224,10 @@ const char* moe_last_error(void);
  * x [T, d]; w->w_router, optional w->logit_bias / w->select_bias; writes
  * out->topk_idx and out->topk_gate (required) and out->logits, out->counts,
  * out->prob_sum when non-NULL.  `workspace` must hold moe_workspace_size(cfg)
- * bytes, 256-byte aligned; its contents are scratch. */
+ * bytes, 256-byte aligned; its contents are scratch.  The logits, selection
+ * and statistics are bitwise those moe_layer_forward computes for the same
+ * cfg and inputs (a batch that takes the all-token pass is routed here with
+ * the same one-workgroup reduction as inside that forward). */
 moe_status moe_route(const moe_config* cfg, const void* x, const moe_weights* w,
                      moe_routing* out, void* workspace, size_t ws_bytes,
                      void* stream);
@@ -321,8 +324,9 @@ typedef struct {
 } moe_grads;
 
 /* Bytes of device workspace moe_layer_backward needs for `cfg` (a multiple
- * of 256; it holds transposed copies of the expert weights, so it is about
- * three times their size plus per-row activations).  0 for an invalid cfg. */
+ * of 256): per-row activations and their K-major segments, plus transposed
+ * copies of the expert weights for fp32 layers (bf16 layers read the weights
+ * as K-rows and hold no copies).  0 for an invalid cfg. */
 size_t moe_backward_workspace_size(const moe_config* cfg);
 
 /* Layer backward: x [T, d] and weights as for moe_layer_forward, dy [T, d]
@@ -339,7 +343,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x,
 /* Stage markers for moe_layer_backward_timed. */
 enum {
   MOE_BSTAGE_ROUTE = 0,       /* routing and grouping, recomputed               */
-  MOE_BSTAGE_TRANSPOSE_W = 1, /* W_down, [W_gate | W_up] and W_r transposed      */
+  MOE_BSTAGE_TRANSPOSE_W = 1, /* W_r transposed; W_down, [W_gate | W_up] too in fp32 layers */
   MOE_BSTAGE_RECOMPUTE = 2,   /* gate and up projections of the rows (2 GEMMs)   */
   MOE_BSTAGE_GRAD_H = 3,      /* dy W_down (GEMM), then the SwiGLU backward      */
   MOE_BSTAGE_GRAD_X = 4,      /* [dA dB] [W_gate; W_up] (GEMM), router, dx       */
