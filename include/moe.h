@@ -325,8 +325,9 @@ typedef struct {
 
 /* Bytes of device workspace moe_layer_backward needs for `cfg` (a multiple
  * of 256): per-row activations and their K-major segments, plus transposed
- * copies of the expert weights for fp32 layers (bf16 layers read the weights
- * as K-rows and hold no copies).  0 for an invalid cfg. */
+ * copies of the expert weights for fp32 layers (bf16 layers whose d_model is
+ * a multiple of 128 read the weights as K-rows and hold no copies).  0 for an
+ * invalid cfg. */
 size_t moe_backward_workspace_size(const moe_config* cfg);
 
 /* Layer backward: x [T, d] and weights as for moe_layer_forward, dy [T, d]
@@ -343,7 +344,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const void* x,
 /* Stage markers for moe_layer_backward_timed. */
 enum {
   MOE_BSTAGE_ROUTE = 0,       /* routing and grouping, recomputed               */
-  MOE_BSTAGE_TRANSPOSE_W = 1, /* W_r transposed; W_down, [W_gate | W_up] too in fp32 layers */
+  MOE_BSTAGE_TRANSPOSE_W = 1, /* W_r transposed; W_down, [W_gate | W_up] only where not
+                                 read as K-rows (fp32 layers)                       */
   MOE_BSTAGE_RECOMPUTE = 2,   /* gate and up projections of the rows (2 GEMMs)   */
   MOE_BSTAGE_GRAD_H = 3,      /* dy W_down (GEMM), then the SwiGLU backward      */
   MOE_BSTAGE_GRAD_X = 4,      /* [dA dB] [W_gate; W_up] (GEMM), router, dx       */
