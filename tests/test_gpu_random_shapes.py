@@ -4,11 +4,13 @@ of them the backward (check_backward).  The shapes mix ragged T, d and F that
 are multiples of 64 but not of 128 or 256, odd expert counts, k up to 8,
 shared experts, capacities that drop, both biases and both dtypes, so that
 every GEMM path (32-row decode tiles, register-staged tiles, 128- and
-256-row large tiles) meets sizes the hand-picked cases do not.
+256-row large tiles) meets sizes the hand-picked cases do not; a second set of
+small batches takes the all-token decode pass.
 """
 import numpy as np
 import pytest
 
+import sparse_mixture_experts_router_amd as moe
 from gpu_harness import full_parity, say
 from test_gpu_backward import check_backward
 from workloads import MoEShape
@@ -43,6 +45,42 @@ SHAPES = _shapes()
 @pytest.mark.parametrize("shape,cap", SHAPES, ids=[s.name for s, _ in SHAPES])
 def test_random_shape_forward(shape, cap):
     full_parity(shape, seed=100 + int(shape.name[4:]), capacity=cap, label=shape.name)
+
+
+def _all_token_shapes(seed=77, n=10):
+    """Small batches (T <= 32, N <= 64) where (nearly) every expert is chosen,
+    so the forward runs every expert on every token (the all-token pass)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype = "f32" if len(out) % 4 == 3 else "bf16"
+        N = int(rng.choice([2, 3, 5, 8, 12, 17, 24, 40, 64]))
+        k = int(rng.integers(1, min(N, 16) + 1))
+        T = int(rng.integers(1, 33))
+        if N * (1.0 - k / N) ** T > 0.5:  # the plan would take the routed rows
+            continue
+        d = int(rng.choice([64, 128, 192, 320, 512]))
+        F = int(rng.choice([64, 128, 192, 320, 576, 2048]))
+        S = int(rng.choice([0, 0, 1, 2]))
+        cap = 0
+        if rng.random() < 0.3:
+            cap = max(1, int(T * k / N * 0.7))
+        shape = MoEShape(f"at_rand{len(out)}", T=T, d=d, N=N, k=k, F=F, S=S, dtype=dtype,
+                         select_bias=bool(rng.random() < 0.4),
+                         zipf_s=float(rng.choice([0.0, 0.0, 1.2])))
+        out.append((shape, cap))
+    return out
+
+
+ALL_TOKEN_SHAPES = _all_token_shapes()
+
+
+@pytest.mark.parametrize("shape,cap", ALL_TOKEN_SHAPES, ids=[s.name for s, _ in ALL_TOKEN_SHAPES])
+def test_random_all_token_forward(shape, cap):
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S,
+                          shape.torch_dtype, capacity=cap)
+    assert moe.moe_forward_plan(cfg)["all_token_pass"] == 1
+    full_parity(shape, seed=200 + int(shape.name[7:]), capacity=cap, label=shape.name)
 
 
 @pytest.mark.parametrize("shape,cap", SHAPES[::2], ids=[s.name for s, _ in SHAPES[::2]])
