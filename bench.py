@@ -1012,7 +1012,20 @@ def time_forward(moe, shape, inputs, steps, warmup, extras=True):
     return res
 
 
-def roofline_of(shape, active, up_ms, workload):
+def plan_of(moe, shape):
+    """How the library runs the workload on this device (moe_forward_plan):
+    the kernel and tile rows of each grouped GEMM, the router's kernel and
+    split, the down pass's split and whether the all-token pass runs."""
+    cfg = moe.make_config(shape.T, shape.d, shape.N, shape.k, shape.F, shape.S,
+                          shape.torch_dtype,
+                          weight_format=(moe.MOE_WEIGHTS_FP8_E4M3 if shape.fp8
+                                         else moe.MOE_WEIGHTS_DTYPE))
+    p = moe.moe_forward_plan(cfg)
+    return {k: p[k] for k in ("up_kernel", "up_tile_rows", "down_kernel", "down_tile_rows",
+                              "route_kernel", "route_split", "down_split", "all_token_pass")}
+
+
+def roofline_of(shape, active, up_ms, workload, plan=None):
     """The gate/up launch against both roofs.  `bound` is the roof that binds
     at its arithmetic intensity (time at the MFMA peak against time at the HBM
     peak); achieved and frac are in that roof's unit, and both fractions are
@@ -1033,6 +1046,10 @@ def roofline_of(shape, active, up_ms, workload):
     roof["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
     roof["arithmetic_intensity"] = round(uf / ub, 1)
     roof["kernel"] = "grouped gate/up GEMM with SiLU*up (expert_up stage)"
+    if plan is not None and plan.get("all_token_pass"):
+        roof["kernel"] = ("grouped gate/up GEMM with SiLU*up, every expert on all tokens, and "
+                          "the batch's routing in one more workgroup of the same launch "
+                          "(expert_up stage, all-token pass)")
     roof["avg_launch_ms"] = round(up_ms, 4)
     roof["algorithmic_bytes"] = ub
     roof["algorithmic_flops"] = uf
@@ -1104,7 +1121,8 @@ def main():
     r = time_forward(moe, shape, inputs, args.steps, args.warmup)
     ms_step = r["ms_step"]
     active = int(np.count_nonzero(r["counts"]))
-    roof = roofline_of(shape, active, r["up_ms"], args.workload)
+    plan = plan_of(moe, shape)
+    roof = roofline_of(shape, active, r["up_ms"], args.workload, plan)
     roof["timed_launches"] = (f"{r['marked']} of the {args.steps} timed steps "
                               f"(one in {r['every']})")
     result = {
@@ -1121,6 +1139,7 @@ def main():
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02^2) random weights of the model's shape)",
         "config": config_of(shape),
+        "plan": plan,
         "layer": layer_of(shape, active, ms_step),
         "stages_ms": {k_: round(v, 4) for k_, v in r["stage_ms"].items()},
         "down_launch_ms": round(r["down_ms"], 4),
@@ -1153,7 +1172,8 @@ def main():
             inp = make_inputs(shp, seed=args.seed, device=dev)
             o = time_forward(moe, shp, inp, args.steps, args.warmup, extras=False)
             act = int(np.count_nonzero(o["counts"]))
-            rf = roofline_of(shp, act, o["up_ms"], name)
+            pl = plan_of(moe, shp)
+            rf = roofline_of(shp, act, o["up_ms"], name, pl)
             others[name] = {
                 "ms_per_step": round(o["ms_step"], 4),
                 "tokens_per_s": round(shp.T / (o["ms_step"] * 1e-3), 1),
@@ -1163,6 +1183,7 @@ def main():
                                                   "hbm_frac", "avg_launch_ms")},
                 "down_launch_ms": round(o["down_ms"], 4),
                 "config": {k_: v for k_, v in config_of(shp).items() if k_ != "parallelism"},
+                "plan": pl,
             }
             del inp, o
             torch.cuda.empty_cache()
