@@ -846,6 +846,10 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   }
   int npairs = KMAJ ? static_cast<int>((g.kbase[e + 1] - kb) * 2 / kLineBytes)
                     : static_cast<int>(row_bytes / kLineBytes);
+  // the weight rows of a routed expert whose rows fit one tile are read by
+  // this tile alone: streamed (non-temporal) past L2, where the gathered A
+  // rows that the tile's column neighbours share stay longer
+  const bool w_once = !KMAJ && !DENSE && !BT && routed && g.offsets[e + 1] - seg <= BM;
   // source bytes of a row per buffer: A 128 (a pair), weights 128 (a pair;
   // FP8 two pairs, so a pair is 64)
   const int pstep = grp == 0 || !FP8W ? kLineBytes : kLineBytes / 2;
@@ -861,7 +865,7 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // nobody reads again
   const int nbufs = grp == 0 || !FP8W ? npairs : npairs / 2;
   const int bt_pairs0 = BT ? g.bt_rows0 / 64 : 0;  // BT: buffers taken from w0
-  auto issue = [&](auto grp_, int buf, char* ring) {
+  auto issue = [&](auto grp_, int buf, char* ring, auto nt_) {
     const int bc = min(buf, nbufs - 1);
     const int dst = q * LPW * 1024;
     if (BT && decltype(grp_)::value == 1) {
@@ -873,8 +877,13 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
       return;
     }
     const uint32_t pc = static_cast<uint32_t>(bc * kLineBytes);
+    if constexpr (decltype(grp_)::value == 1 && decltype(nt_)::value) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) load_lds16(src_base + (off[j] + pc), ring + dst + j * 1024);
+      for (int j = 0; j < LPW; ++j) load_lds16_nt(src_base + (off[j] + pc), ring + dst + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) load_lds16(src_base + (off[j] + pc), ring + dst + j * 1024);
+    }
   };
 
   // Fragment reads: lane l takes row l mod 16 of a 16-row block, chunk
@@ -913,11 +922,15 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // prologue: group 0 A(0); group 1 B(0) then B(1); A(0) and B(0) landed
   // (FP8: weight buffers 0 and 1, pairs 0 .. 3)
   if (grp == 0) {
-    issue(CInt<0>{}, 0, abuf(0));
+    issue(CInt<0>{}, 0, abuf(0), CInt<0>{});
     wait_vmem<0>();
+  } else if (w_once) {
+    issue(CInt<1>{}, 0, bbuf(0), CInt<1>{});
+    issue(CInt<1>{}, 1, bbuf(1), CInt<1>{});
+    wait_vmem<LPWB>();
   } else {
-    issue(CInt<1>{}, 0, bbuf(0));
-    issue(CInt<1>{}, 1, bbuf(1));
+    issue(CInt<1>{}, 0, bbuf(0), CInt<0>{});
+    issue(CInt<1>{}, 1, bbuf(1), CInt<0>{});
     wait_vmem<LPWB>();
   }
   stage_barrier();
@@ -925,16 +938,16 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
   // Each group runs its own straight loop (a shared loop that branches on the
   // group every phase made the compiler move the accumulators out of the
   // AGPRs); both execute 2 n + 3 barriers in all, prologue included.
-  auto run = [&](auto live_, auto grp_) {
+  auto run = [&](auto live_, auto grp_, auto nt_) {
     constexpr int LIVE = decltype(live_)::value;
     constexpr int G = decltype(grp_)::value;
     auto memory = [&](int p) {
       const char* const a = abuf(p & 1);
       const int qb = FP8W ? (p >> 1) % 3 : p % 3;  // weight buffer of pair p
       const char* const b = bbuf(qb);
-      if (G == 0) issue(grp_, p + 1, abuf((p + 1) & 1));
-      else if (!FP8W) issue(grp_, p + 2, bbuf((p + 2) % 3));
-      else if ((p & 1) == 0) issue(grp_, (p >> 1) + 2, bbuf(((p >> 1) + 2) % 3));
+      if (G == 0) issue(grp_, p + 1, abuf((p + 1) & 1), nt_);
+      else if (!FP8W) issue(grp_, p + 2, bbuf((p + 2) % 3), nt_);
+      else if ((p & 1) == 0) issue(grp_, (p >> 1) + 2, bbuf(((p >> 1) + 2) % 3), nt_);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int fl = t ? fl1 : fl0;
@@ -1039,14 +1052,15 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     // are still in flight.)
     stage_barrier();
   };
-  auto run_g = [&](auto grp_) {
-    if (mlive > MB / 2) run(CInt<MB>{}, grp_);
-    else if (mlive > MB / 4) run(CInt<MB / 2>{}, grp_);
-    else if (mlive > 0) run(CInt<MB / 4>{}, grp_);
-    else run(CInt<0>{}, grp_);
+  auto run_g = [&](auto grp_, auto nt_) {
+    if (mlive > MB / 2) run(CInt<MB>{}, grp_, nt_);
+    else if (mlive > MB / 4) run(CInt<MB / 2>{}, grp_, nt_);
+    else if (mlive > 0) run(CInt<MB / 4>{}, grp_, nt_);
+    else run(CInt<0>{}, grp_, nt_);
   };
-  if (grp == 0) run_g(CInt<0>{});
-  else run_g(CInt<1>{});
+  if (grp == 0) run_g(CInt<0>{}, CInt<0>{});
+  else if (w_once) run_g(CInt<1>{}, CInt<1>{});
+  else run_g(CInt<1>{}, CInt<0>{});
   }  // !KMAJ || npairs > 0
 
   // epilogue: every ring read is done (the last barrier), every load landed

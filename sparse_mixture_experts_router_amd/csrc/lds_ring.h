@@ -11,6 +11,11 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 __device__ __forceinline__ void load_lds16(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)(src), (lds_void_ptr)(lds_dst), 16, 0, 0);
 }
+// The same load with the non-temporal cache policy (nt): for lines read
+// once, so that they give way first in L2 to lines other workgroups reuse.
+__device__ __forceinline__ void load_lds16_nt(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(src), (lds_void_ptr)(lds_dst), 16, 0, 2);
+}
 
 // s_waitcnt vmcnt(N) lgkmcnt(0), expcnt untouched (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
