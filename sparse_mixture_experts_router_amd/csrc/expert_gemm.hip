@@ -1082,23 +1082,21 @@ __global__ __launch_bounds__(512, 1) void expert_gemm_pp_kernel(GemmArgs g) {
     // staged as bf16: 64 columns, whole 128-byte lines of a row, per pass
     // (32 fp32 columns per pass left half lines, and the weight gradients
     // wrote 1.37 GB for 0.94 GB)
-    store_block<false, true, MB, NB, WTM, false, 32, true>(acc, stg, lane, c, false, g.n_dim,
-                                                           m0 + wm * WTM, mvalid - wm * WTM, col0,
-                                                           g.n_dim);
+    store_block<false, true, MB, NB, WTM>(acc, stg, lane, c, false, g.n_dim, m0 + wm * WTM,
+                                          mvalid - wm * WTM, col0, g.n_dim);
   } else if (part < 0) {
     // (the plain pass: fp32 staging, 64 columns per pass, so every row write
     // is a whole 128-byte line)
-    store_block<GATED, GATED, MB, NB, WTM, FP8W, 64, !GATED>(acc, stg, lane, g.out, false,
-                                                             g.n_dim, seg + m0 + wm * WTM,
-                                                             mvalid - wm * WTM, col0, g.n_dim,
-                                                             sc0, sc1);
+    store_block<GATED, GATED, MB, NB, WTM, FP8W, 64>(acc, stg, lane, g.out, false, g.n_dim,
+                                                     seg + m0 + wm * WTM, mvalid - wm * WTM,
+                                                     col0, g.n_dim, sc0, sc1);
   } else if (!GATED) {  // fp32 partial rows of a split tail tile or of a dense part
     const long stride = dense ? g.a_rows : g.plan[kPlanStride];
     const long first = dense ? 0 : g.plan[kPlanRowSplit];
     const long prow = static_cast<long>(part) * stride + seg + m0 - first + wm * WTM;
-    store_block<GATED, false, MB, NB, WTM, FP8W, 64, !GATED>(acc, stg, lane, g.out_part, true,
-                                                             g.n_dim, prow, mvalid - wm * WTM,
-                                                             col0, g.n_dim, sc0, sc1);
+    store_block<GATED, false, MB, NB, WTM, FP8W, 64>(acc, stg, lane, g.out_part, true, g.n_dim,
+                                                     prow, mvalid - wm * WTM, col0, g.n_dim, sc0,
+                                                     sc1);
   }
 }
 

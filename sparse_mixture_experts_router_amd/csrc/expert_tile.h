@@ -97,13 +97,9 @@ inline long expert_grid(const GemmArgs& g, bool gated, int cols) {
   return 8 * per_xcd;
 }
 
-// 16-byte store, NT: with the non-temporal policy.
-template <bool NT>
+// 16-byte store with the non-temporal policy.
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
-  if constexpr (NT)
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else
-    *reinterpret_cast<u32x4*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 // Writes a wavefront's accumulator block (GATED: SiLU(gate) * up first) in
@@ -122,10 +118,10 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
 // SCALED (FP8 weights): each accumulator is first multiplied by its output
 // column's scale, sc0 for the gate (or plain) columns, sc1 for the up
 // columns; both indexed by the output column, col0 + ... .
-// NTS: the stores with the non-temporal policy (outputs no later work of the
-// same launch reads).
-template <bool GATED, bool SBF16, int MB, int NB, int WTM, bool SCALED = false, int FCOLS = 32,
-          bool NTS = false>
+// The global stores carry the non-temporal policy: no later work of the same
+// launch reads an output tile, and keeping them out of the caches leaves room
+// for the activation rows and weights other tiles still reuse.
+template <bool GATED, bool SBF16, int MB, int NB, int WTM, bool SCALED = false, int FCOLS = 32>
 __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* stg, int lane,
                                             void* out, bool out_f32, size_t ld, long row0,
                                             int rows_valid, int col0, int cols_valid,
@@ -182,7 +178,7 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
         const int row = q * 8 + (lane >> 3);
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane & 7) * 16);
         if (row < rows_valid && col < cols_valid)
-          store16<NTS>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
+          store16(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
       }
     } else if (out_f32) {
       constexpr int LPR = PCOLS / 4;  // lanes per row, 4 columns each
@@ -192,7 +188,7 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
         const int row = q * (64 / LPR) + lane / LPR;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * SROW + (lane % LPR) * 16);
         if (row < rows_valid && col < cols_valid)
-          store16<NTS>(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
+          store16(static_cast<float*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
       }
     } else {
       constexpr int LPR = PCOLS / 8;  // lanes per row, 8 columns each
@@ -209,7 +205,7 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[MB][NB], char* st
         v[2] = f32_to_bf16(b[0]) | (static_cast<uint32_t>(f32_to_bf16(b[1])) << 16);
         v[3] = f32_to_bf16(b[2]) | (static_cast<uint32_t>(f32_to_bf16(b[3])) << 16);
         if (row < rows_valid && col < cols_valid)
-          store16<NTS>(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
+          store16(static_cast<bf16_t*>(out) + static_cast<size_t>(row0 + row) * ld + col, v);
       }
     }
   }
