@@ -23,9 +23,13 @@
 //   dW_r = dr^T x
 //
 // The weight gradients reduce over rows.  Their operands are first transposed
-// into K-major segments, one per expert, each padded with zero columns to a
-// multiple of 128, so that one grouped GEMM (kgemm_kernel) with a reduction
-// length per group computes every expert's gradient.
+// into K-major segments, one per expert, each padded with zero columns, so
+// that one grouped GEMM with a reduction length per group computes every
+// expert's gradient: to a multiple of 64 when the large-tile kernel's
+// K-major mode takes the products (bf16), else to a multiple of 128 for
+// kgemm_kernel, which takes its K steps in pairs.  (Padding to 128 made the
+// DeepSeek-V3-shaped experts, 190-324 rows each, reduce over 321 columns on
+// average instead of 292.)
 #include "lds_ring.h"
 #include "vec.h"
 
@@ -86,12 +90,12 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 }
 
 // Segment starts: kbase[0] = 0, kbase[g + 1] = kbase[g] + (rows of group g
-// rounded up to 128).  One workgroup; groups <= 1024.
+// rounded up to `align`, a power of two).  One workgroup; groups <= 1024.
 __global__ __launch_bounds__(1024) void kbase_kernel(const int32_t* __restrict__ offsets, int G,
-                                                     int32_t* __restrict__ kbase) {
+                                                     int align, int32_t* __restrict__ kbase) {
   __shared__ int s[1024];
   const int t = threadIdx.x;
-  s[t] = t < G ? ((offsets[t + 1] - offsets[t] + 127) & ~127) : 0;
+  s[t] = t < G ? ((offsets[t + 1] - offsets[t] + align - 1) & ~(align - 1)) : 0;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int add = t >= off ? s[t - off] : 0;
@@ -575,8 +579,8 @@ hipError_t launch_transpose(int dtype, const void* src, int R, int C, long src_b
   return transpose_t<float>(src, R, C, src_batch, dst, ldd, col0, rpad, dst_batch, batch, s);
 }
 
-hipError_t launch_kbase(const int32_t* offsets, int G, int32_t* kbase, hipStream_t s) {
-  hipLaunchKernelGGL(kbase_kernel, dim3(1), dim3(1024), 0, s, offsets, G, kbase);
+hipError_t launch_kbase(const int32_t* offsets, int G, int align, int32_t* kbase, hipStream_t s) {
+  hipLaunchKernelGGL(kbase_kernel, dim3(1), dim3(1024), 0, s, offsets, G, align, kbase);
   return hipGetLastError();
 }
 

@@ -1122,12 +1122,15 @@ hipError_t launch_pp(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s) {
+bool kmajor_gemm_fits(long a_rows, long n_dim, long k_dim) {
   // whole 128-byte buffers from 16-byte aligned rows, 32-bit lane offsets
-  if (g.k_dim % 64 != 0 || g.n_dim % 8 != 0 ||
-      static_cast<size_t>(g.a_rows) * g.k_dim * 2 >= (size_t{1} << 32) ||
-      static_cast<size_t>(g.n_dim) * g.k_dim * 2 >= (size_t{1} << 32))
-    return hipErrorInvalidValue;
+  return a_rows > 0 && n_dim > 0 && k_dim % 64 == 0 && n_dim % 8 == 0 &&
+         static_cast<size_t>(a_rows) * k_dim * 2 < (size_t{1} << 32) &&
+         static_cast<size_t>(n_dim) * k_dim * 2 < (size_t{1} << 32);
+}
+
+hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s) {
+  if (!kmajor_gemm_fits(g.a_rows, g.n_dim, g.k_dim)) return hipErrorInvalidValue;
   const long blocks = kmajor_grid(g, 256, 256);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((expert_gemm_pp_kernel<false, false, false, false, false, true>),

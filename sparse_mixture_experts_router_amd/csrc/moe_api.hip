@@ -428,7 +428,8 @@ struct BwdPlan {
   size_t off[B_COUNT];
   size_t total;
   long rows;  // T (k + S): every permuted row the forward may have
-  long kseg;  // columns of the transposed segments: sum over groups of rows rounded up to 128
+  long kseg;  // columns of the transposed segments: their rows rounded up to kalign, summed over groups, in a multiple of 128
+  int kalign;  // 64 when the large-tile kernel takes the three segment products (bf16), else 128
   int Kr;     // N rounded up to 128
   int Tp;     // T rounded up to 128
   // D = dy W_down and dXp = [dA dB] [W_gate; W_up] read the weights as
@@ -449,9 +450,18 @@ BwdPlan make_bwd_plan(const moe_config& c) {
   const size_t G = N + S;
   const size_t eb = c.dtype == MOE_BF16 ? 2 : 4;
   b.rows = static_cast<long>(T) * (c.top_k + c.n_shared);
-  // the weight-gradient GEMM takes its reduction in pairs of 128-byte steps:
-  // segments, Kr and Tp are multiples of 128 elements
-  b.kseg = (b.rows + 127 * static_cast<long>(G) + 127) / 128 * 128;
+  // the weight-gradient GEMMs reduce over segments of a multiple of kalign
+  // elements (launch_kbase) and over Kr and Tp, multiples of 128; rows of
+  // the segment buffers are a multiple of 128 elements long.  64 only where
+  // all three segment products run on the large-tile kernel's K-major mode:
+  // kgemm_kernel takes its K steps in pairs of 128 bytes
+  const long ks128 = (b.rows + 127 * static_cast<long>(G) + 127) / 128 * 128;
+  const long dl = static_cast<long>(d), Fl = static_cast<long>(F);
+  b.kalign = c.dtype == MOE_BF16 && kmajor_gemm_fits(dl, Fl, ks128) &&
+                     kmajor_gemm_fits(Fl, dl, ks128)
+                 ? 64
+                 : 128;
+  b.kseg = b.kalign == 64 ? (b.rows + 63 * static_cast<long>(G) + 127) / 128 * 128 : ks128;
   b.Kr = static_cast<int>((N + 127) / 128 * 128);
   b.Tp = static_cast<int>((T + 127) / 128 * 128);
   const size_t rows = b.rows, ks = b.kseg, Kr = b.Kr, Tp = b.Tp;
@@ -921,7 +931,7 @@ moe_status moe_layer_backward_timed(const moe_config* cfg, const void* x, const 
   // weight gradients over each group's rows
   mark(ev, MOE_BSTAGE_SEGMENTS, s);
   const long ks = b.kseg;
-  if ((err = launch_kbase(ws.offsets, G, kbase, s)) != hipSuccess ||
+  if ((err = launch_kbase(ws.offsets, G, b.kalign, kbase, s)) != hipSuccess ||
       (err = launch_segment_transpose(dt, dy, d, T, ws.sorted_tok, rgate, ws.offsets, kbase, G, ks,
                                       at(B_DOT), ks, s)) != hipSuccess ||
       (err = launch_segment_transpose(dt, at(B_H), F, rows, nullptr, nullptr, ws.offsets, kbase, G,

@@ -285,8 +285,10 @@ GemmPick pick_gemm(int dtype, bool fp8w, bool gated, long rows_per_expert, size_
 hipError_t launch_gemm(int dtype, bool gated, GemmPick pick, const GemmArgs& g, hipStream_t s,
                        const AllTokenRoute* route = nullptr);
 // bf16 weight-gradient products on the large-tile kernel (GemmArgs' kbase
-// fields); hipErrorInvalidValue when the operands do not fit it.
+// fields, segments a multiple of 64); hipErrorInvalidValue when the operands
+// do not fit it, as kmajor_gemm_fits tells beforehand.
 hipError_t launch_kmajor_gemm(const GemmArgs& g, hipStream_t s);
+bool kmajor_gemm_fits(long a_rows, long n_dim, long k_dim);
 // The plain grouped GEMM on the large-tile kernel with B given as K-rows
 // (GemmArgs' bt_rows0); hipErrorInvalidValue when the shape does not fit it.
 hipError_t launch_expert_gemm_bt(int bm, const GemmArgs& g, hipStream_t s);
@@ -324,8 +326,9 @@ hipError_t launch_balance(int T, int N, int k, const int32_t* counts,
 hipError_t launch_transpose(int dtype, const void* src, int R, int C, long src_batch, void* dst,
                             long ldd, int col0, int rpad, long dst_batch, int batch,
                             hipStream_t s);
-// kbase[g + 1] = kbase[g] + (offsets[g + 1] - offsets[g] rounded up to 128).
-hipError_t launch_kbase(const int32_t* offsets, int G, int32_t* kbase, hipStream_t s);
+// kbase[g + 1] = kbase[g] + (offsets[g + 1] - offsets[g] rounded up to
+// align: 64 or 128).
+hipError_t launch_kbase(const int32_t* offsets, int G, int align, int32_t* kbase, hipStream_t s);
 // Group g's rows (source row gather[r] or r, times rscale[r] when given) into
 // columns kbase[g] .. of dst [C, ldd]; padding columns 0.  kmax: a multiple
 // of 64 at least kbase[G].
@@ -350,7 +353,9 @@ hipError_t launch_bias_update(const int32_t* counts, int N, float rate, float* b
                               hipStream_t s);
 // C_g[m][n] = sum over kbase[g] <= j < kbase[g + 1] (or 0 <= j < k_all when
 // kbase is null) of a[m][j] b[n][j]; groups >= alt_from write to c_alt.
-// Every segment (and k_all) a multiple of 128 elements; N a multiple of 64.
+// Every segment (and k_all) a multiple of 128 elements, or of 64 where the
+// bf16 large-tile kernel takes the product (kmajor_gemm_fits); N a multiple
+// of 64.
 hipError_t launch_kgemm(int dtype, bool out_f32, const void* a, long lda, const void* b, long ldb,
                         int M, int N, int groups, const int32_t* kbase, int k_all, void* c,
                         void* c_alt, int alt_from, hipStream_t s);
