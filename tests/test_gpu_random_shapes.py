@@ -87,3 +87,28 @@ def test_random_all_token_forward(shape, cap):
 def test_random_shape_backward(shape, cap):
     say(f"[rand-bwd] {shape.name} capacity={cap}")
     check_backward(shape, seed=3, capacity=cap, label=shape.name)
+
+
+# A second seeded set, and two batches with several 256-row tiles per expert
+# (narrow tail tiles, weight-gradient segments of an odd number of 64-row
+# pairs)
+SHAPES_B = _shapes(seed=9001, n=24) + [
+    (MoEShape("big0", T=2000, d=320, N=8, k=2, F=576, S=1, select_bias=True), 0),
+    (MoEShape("big1", T=1500, d=512, N=5, k=2, F=320, S=0), 0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SHAPES_B)), ids=[f"b_{s.name}" for s, _ in SHAPES_B])
+def test_random_shape_forward_second_set(i):
+    shape, cap = SHAPES_B[i]
+    full_parity(shape, seed=500 + i, capacity=cap, label=f"b_{shape.name}")
+
+
+@pytest.mark.parametrize("i", [i for i, (s, _) in enumerate(SHAPES_B)
+                               if i % 2 == 0 or s.name.startswith("big")],
+                         ids=[f"b_{s.name}" for i, (s, _) in enumerate(SHAPES_B)
+                              if i % 2 == 0 or s.name.startswith("big")])
+def test_random_shape_backward_second_set(i):
+    shape, cap = SHAPES_B[i]
+    say(f"[rand-bwd] b_{shape.name} capacity={cap}")
+    check_backward(shape, seed=7, capacity=cap, label=f"b_{shape.name}")
